@@ -1,0 +1,363 @@
+"""CPU oracle for the DFlash drafter step and greedy block verification.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or execute
+this module: only the tests, the smoke check and the bench's CPU-baseline leg use it.
+It shares no code with the HIP library; it only reads the same seeded inputs.
+
+Pages cited (by title, then section / equation / figure):
+  [DF]   "DFlash - Block Diffusion for Flash Speculative Decoding" (paper notes page)
+  [TRY]  "Trying "DFlash," a Diffusion-Model Approach to Parallel Draft-Token
+         Generation, on Gemma" (llama.cpp experiment write-up)
+  [LCPP] llama.cpp discussion "DFlash (Block Diffusion for Flash Speculative Decoding)"
+
+Everything is computed one sequence at a time in a plain float dtype (float32 by
+default; the pin tests also run it in float64), straight from the definitions, with
+no blocking, fusion or reordering.  Readings taken where the pages are silent are
+listed beside the function that takes them.
+
+Conventions: a model's weights are a dict (keys as produced by ``synth.model_weights``),
+matrices row-major [out, in]; ``shape`` is a ``synth.ModelShape``; a KV cache is a list
+over layers of ``(K, V)`` with ``K, V`` of shape [n, H_kv, d] (K stored after RoPE).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+# ----------------------------------------------------------------------------------------
+# Building blocks
+
+
+def rmsnorm(x, g, eps, dt=np.float32):
+    """RMSNorm over the last axis: x / sqrt(mean(x^2) + eps) * g.  eps = 1e-6 everywhere
+    (the pages give no value; the Qwen3-8B-shaped configuration states 1e-6)."""
+    x = np.asarray(x, dtype=dt)
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    return (x / np.sqrt(ms + dt(eps))) * np.asarray(g, dtype=dt)
+
+
+def silu(x):
+    return x / (1.0 + np.exp(-x))
+
+
+def rope_cos_sin(pos, d, base):
+    """Rotary angles p * base^(-2i/d), i < d/2, evaluated in float64 (reading: at
+    positions near 2.6e5 a float32 product p*theta errs by ~1e-2 rad)."""
+    i = np.arange(d // 2, dtype=np.float64)
+    theta = np.power(np.float64(base), -2.0 * i / d)
+    ang = np.asarray(pos, dtype=np.float64)[:, None] * theta[None, :]
+    return np.cos(ang), np.sin(ang)
+
+
+def rope(x, pos, base, dt=np.float32):
+    """Rotate-half RoPE on x [T, H, d] at positions pos [T]: the pair (i, i + d/2) is
+    rotated by angle p * theta_i (reading: the pages name no convention)."""
+    x = np.asarray(x, dtype=dt)
+    d = x.shape[-1]
+    c, s = rope_cos_sin(pos, d, base)
+    c = c.astype(dt)[:, None, :]
+    s = s.astype(dt)[:, None, :]
+    x1, x2 = x[..., : d // 2], x[..., d // 2:]
+    return np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=-1)
+
+
+def attention(q, k, v, visible, dt=np.float32):
+    """softmax(q k^T / sqrt(d) restricted to visible keys) v.
+    q [Tq, d], k [Tk, d], v [Tk, d], visible bool [Tq, Tk]."""
+    q = np.asarray(q, dtype=dt)
+    k = np.asarray(k, dtype=dt)
+    v = np.asarray(v, dtype=dt)
+    s = (q @ k.T) / dt(np.sqrt(q.shape[-1]))
+    s = np.where(visible, s, -np.inf)
+    s = s - np.max(s, axis=-1, keepdims=True)
+    p = np.exp(s)
+    p = p / np.sum(p, axis=-1, keepdims=True)
+    return p @ v
+
+
+def argmax_lowest(z):
+    """Argmax along the last axis; ties go to the lowest index (reading: the pages do not
+    say; numpy's first-occurrence rule)."""
+    return np.argmax(z, axis=-1).astype(np.int64)
+
+
+def top2_gap(z):
+    """z_(1) - z_(2) along the last axis (used to exclude near-tie positions)."""
+    part = np.partition(z, -2, axis=-1)
+    return part[..., -1] - part[..., -2]
+
+
+# ----------------------------------------------------------------------------------------
+# Feature fusion and KV injection  [DF §4.2 fusion equation, §4.3 injection equations]
+
+
+def tap_layers(n_layers, k):
+    """0-indexed target layers whose outputs are tapped: k layers spread uniformly from
+    the second layer to the third-to-last one ([DF §6.1]: "uniformly sampled between
+    layer 2 and third-to-last"; the Gemma tap list printed in [TRY]'s appendix follows
+    the same spacing).  When the range is empty (a 2-layer toy target) every layer
+    is tapped in order."""
+    lo, hi = 1, n_layers - 3
+    if hi < lo or hi - lo + 1 < k:
+        return tuple(range(min(k, n_layers)))
+    return tuple(int(x) for x in np.round(np.linspace(lo, hi, k)))
+
+
+def fuse(feats, w, shape, dt=np.float32):
+    """H_t = RMSNorm(W_c [H^(l1); ...; H^(lk)]) for rows of concatenated tapped features
+    [r, k*D] -> [r, D].  The norm follows the projection [DF §4.2] (the appendix of [TRY]
+    mentions normalisation before injection without its order; [DF] is followed)."""
+    x = np.asarray(feats, dtype=dt) @ np.asarray(w["w_c"], dtype=dt).T
+    return rmsnorm(x, w["g_c"], shape.rms_eps, dt)
+
+
+def inject(feats, positions, w, shape, dt=np.float32):
+    """Context K/V for every draft layer from tapped features [DF §4.3]:
+    K_i = RoPE(W_i^K H_t) at each row's absolute position, V_i = W_i^V H_t.
+    Returns a list over draft layers of (K [r, Hkv, d], V [r, Hkv, d]).
+    Reading: K is rotated at its own position and stored rotated."""
+    Ht = fuse(feats, w, shape, dt)
+    r = Ht.shape[0]
+    out = []
+    for i in range(shape.n_layers):
+        K = (Ht @ np.asarray(w[f"L{i}.wk"], dtype=dt).T).reshape(r, shape.n_kv_heads, shape.head_dim)
+        V = (Ht @ np.asarray(w[f"L{i}.wv"], dtype=dt).T).reshape(r, shape.n_kv_heads, shape.head_dim)
+        out.append((rope(K, positions, shape.rope_base, dt), V))
+    return out
+
+
+# ----------------------------------------------------------------------------------------
+# Decoder layer shared by the drafter (bidirectional block) and the target (causal block)
+
+
+def decoder_layer(h, w, i, shape, positions, ctx_k, ctx_v, causal, dt=np.float32):
+    """One pre-norm decoder layer over the block rows h [T, D].
+
+    The block's queries attend to the n context keys (all visible) followed by the
+    block's own T keys: all of them for the drafter (non-causal, [TRY] appendix;
+    masked-diffusion block), keys j' <= j for the target's verification pass
+    ([TRY] Fig. 1, causal attention in the main model).  The context rows take no part
+    in Q, O, the residual or the FFN ([DF §4.3]).  FFN: SwiGLU (the drafter is
+    described as Qwen-style in [TRY]'s appendix).  Returns (h_out, k_blk, v_blk)."""
+    T = h.shape[0]
+    Hq, Hkv, d = shape.n_q_heads, shape.n_kv_heads, shape.head_dim
+    G = Hq // Hkv
+    u = rmsnorm(h, w[f"L{i}.g_in"], shape.rms_eps, dt)
+    q = (u @ np.asarray(w[f"L{i}.wq"], dtype=dt).T).reshape(T, Hq, d)
+    kb = (u @ np.asarray(w[f"L{i}.wk"], dtype=dt).T).reshape(T, Hkv, d)
+    vb = (u @ np.asarray(w[f"L{i}.wv"], dtype=dt).T).reshape(T, Hkv, d)
+    q = rope(q, positions, shape.rope_base, dt)
+    kb = rope(kb, positions, shape.rope_base, dt)
+
+    n = 0 if ctx_k is None else ctx_k.shape[0]
+    visible = np.ones((T, n + T), dtype=bool)
+    if causal:
+        visible[:, n:] = np.tril(np.ones((T, T), dtype=bool))
+    o = np.empty((T, Hq, d), dtype=dt)
+    for kv in range(Hkv):
+        if n:
+            Kh = np.concatenate([np.asarray(ctx_k[:, kv, :], dtype=dt), kb[:, kv, :]], axis=0)
+            Vh = np.concatenate([np.asarray(ctx_v[:, kv, :], dtype=dt), vb[:, kv, :]], axis=0)
+        else:
+            Kh, Vh = kb[:, kv, :], vb[:, kv, :]
+        for j in range(kv * G, (kv + 1) * G):
+            o[:, j, :] = attention(q[:, j, :], Kh, Vh, visible, dt)
+    h = h + o.reshape(T, Hq * d) @ np.asarray(w[f"L{i}.wo"], dtype=dt).T
+    u = rmsnorm(h, w[f"L{i}.g_post"], shape.rms_eps, dt)
+    a = silu(u @ np.asarray(w[f"L{i}.wg"], dtype=dt).T) * (u @ np.asarray(w[f"L{i}.wu"], dtype=dt).T)
+    h = h + a @ np.asarray(w[f"L{i}.wd"], dtype=dt).T
+    return h, kb, vb
+
+
+def lm_logits(h, w, shared, shape, dt=np.float32):
+    """Final RMSNorm then the shared LM head [DF §5.2: embedding and LM head shared with
+    the target]; logits stay in the working float type."""
+    return rmsnorm(h, w["g_f"], shape.rms_eps, dt) @ np.asarray(shared["lm_head"], dtype=dt).T
+
+
+# ----------------------------------------------------------------------------------------
+# Drafter step  [DF §4.4 parallel drafting; §3.2 one forward pass for the whole block]
+
+
+def draft_block(w, shared, shape, ctx, anchor, n, block, dt=np.float32):
+    """One drafter forward pass over [anchor, MASK x (B-1)] at positions n .. n+B-1.
+
+    ctx: list over draft layers of (K [n, Hkv, d], V [n, Hkv, d]) - the injected context.
+    Each mask position is decoded independently by argmax of its logits ([DF §4.4],
+    greedy).  Returns (draft_ids [B-1], logits [B-1, V], hiddens [L+1, B, D]).
+    Readings: the anchor sits at position n, where the target later verifies it; no
+    timestep input ([DF §4.4], single step); the mask token is the last vocab row."""
+    tokens = np.array([anchor] + [shape.mask_token_id] * (block - 1), dtype=np.int64)
+    positions = n + np.arange(block)
+    h = np.asarray(shared["embed"], dtype=dt)[tokens]
+    hiddens = [h]
+    for i in range(shape.n_layers):
+        ck, cv = ctx[i] if n else (None, None)
+        if ck is not None:
+            ck, cv = ck[:n], cv[:n]
+        h, _, _ = decoder_layer(h, w, i, shape, positions, ck, cv, causal=False, dt=dt)
+        hiddens.append(h)
+    z = lm_logits(h[1:], w, shared, shape, dt)
+    return argmax_lowest(z), z, np.stack(hiddens)
+
+
+# ----------------------------------------------------------------------------------------
+# Target verification, acceptance, commit  [DF §4.5 decoding cycle]
+
+
+def target_forward(w, shared, shape, cache, tokens, n, taps, dt=np.float32):
+    """Causal target pass over `tokens` at positions n .. n+T-1 with the first n cache rows
+    visible.  Returns (g [T] greedy ids, logits [T, V], feats [T, k*D] = the tapped layer
+    outputs concatenated in tap order, new_kv list of (K [T,Hkv,d], V [T,Hkv,d]),
+    hiddens [L+1, T, D]).  A tap is the output of the whole decoder layer (after both
+    residual adds, before the final norm) - reading."""
+    tokens = np.asarray(tokens, dtype=np.int64)
+    T = tokens.shape[0]
+    positions = n + np.arange(T)
+    h = np.asarray(shared["embed"], dtype=dt)[tokens]
+    hiddens = [h]
+    tapped = {}
+    new_kv = []
+    for i in range(shape.n_layers):
+        if n and cache is not None:
+            ck, cv = cache[i][0][:n], cache[i][1][:n]
+        else:
+            ck, cv = None, None
+        h, kb, vb = decoder_layer(h, w, i, shape, positions, ck, cv, causal=True, dt=dt)
+        new_kv.append((kb, vb))
+        hiddens.append(h)
+        if i in taps:
+            tapped[i] = h
+    feats = np.concatenate([tapped[t] for t in taps], axis=-1) if taps else None
+    z = lm_logits(h, w, shared, shape, dt)
+    return argmax_lowest(z), z, feats, new_kv, np.stack(hiddens)
+
+
+def verify(w, shared, shape, cache, block_ids, n, taps, dt=np.float32):
+    """Verification of y = [x, d_1 .. d_{B-1}] in one causal target pass [DF §4.5 step 2]."""
+    return target_forward(w, shared, shape, cache, block_ids, n, taps, dt)
+
+
+def accept(draft_ids, g):
+    """Greedy longest-prefix acceptance [DF §4.5 step 3]: accept d_j while d_j equals the
+    target's greedy choice g_{j-1}; a = number accepted, tau = a + 1 (tau counts the bonus
+    token, [DF §2.2]), bonus = g_a.  Returns (a, tau, bonus)."""
+    a = 0
+    for j in range(1, len(draft_ids) + 1):
+        if int(draft_ids[j - 1]) != int(g[j - 1]):
+            break
+        a = j
+    return a, a + 1, int(g[a])
+
+
+def append_kv(cache, new_kv, count):
+    """Cache after appending the first `count` rows of new_kv to every layer."""
+    out = []
+    for (K, V), (k, v) in zip(cache, new_kv):
+        out.append((np.concatenate([K, k[:count]], axis=0), np.concatenate([V, v[:count]], axis=0)))
+    return out
+
+
+def commit(target_cache, draft_ctx, new_kv, feats, tau, n, draft_w, draft_shape, dt=np.float32):
+    """Commit/rollback [DF §4.5]: the target keeps rows n .. n+tau-1 (anchor and accepted
+    drafts) and drops the rest; the drafter's context receives the injected features of
+    the same rows at their positions ([TRY]: the drafter's own KV cache is fed by
+    injection from the main model's pass).  Returns (target_cache, draft_ctx)."""
+    target_cache = append_kv(target_cache, new_kv, tau)
+    inj = inject(feats[:tau], n + np.arange(tau), draft_w, draft_shape, dt)
+    draft_ctx = append_kv(draft_ctx, inj, tau)
+    return target_cache, draft_ctx
+
+
+def empty_cache(shape, dt=np.float32):
+    z = np.zeros((0, shape.n_kv_heads, shape.head_dim), dtype=dt)
+    return [(z, z) for _ in range(shape.n_layers)]
+
+
+def prefill(target_w, shared, tshape, draft_w, dshape, prompt, taps, dt=np.float32):
+    """Causal target pass over the prompt from an empty cache; the drafter's context is
+    injected from the prompt's tapped features; the first anchor is the greedy token at
+    the last prompt row.  Returns (target_cache, draft_ctx, anchor)."""
+    n = len(prompt)
+    g, _, feats, new_kv, _ = target_forward(target_w, shared, tshape, None, prompt, 0, taps, dt)
+    tcache = append_kv(empty_cache(tshape, dt), new_kv, n)
+    dctx = inject(feats, np.arange(n), draft_w, dshape, dt)
+    return tcache, dctx, int(g[-1])
+
+
+def greedy_decode(target_w, shared, tshape, prompt, n_new, dt=np.float32):
+    """Plain autoregressive greedy decoding with the target ([DF §1]); the reference that
+    speculative decoding must reproduce exactly ([DF §4.5] lossless guarantee)."""
+    prompt = list(int(t) for t in prompt)
+    g, _, _, new_kv, _ = target_forward(target_w, shared, tshape, None, prompt, 0, (), dt)
+    cache = append_kv(empty_cache(tshape, dt), new_kv, len(prompt))
+    out = [int(g[-1])]
+    n = len(prompt)
+    while len(out) < n_new:
+        g, _, _, new_kv, _ = target_forward(target_w, shared, tshape, cache, [out[-1]], n, (), dt)
+        cache = append_kv(cache, new_kv, 1)
+        n += 1
+        out.append(int(g[0]))
+    return out[:n_new]
+
+
+def spec_decode(target_w, draft_w, shared, tshape, dshape, prompt, n_new, block, taps,
+                draft_override=None, dt=np.float32):
+    """Speculative decoding cycles [DF §4.5]: draft a block, verify it, accept the longest
+    matching prefix plus the bonus token, commit, repeat.  `draft_override(cycle, anchor,
+    drafts)` may replace the drafter's ids (random or forced drafts) - the emitted stream
+    must not depend on it.  Returns (tokens [n_new], taus)."""
+    tcache, dctx, anchor = prefill(target_w, shared, tshape, draft_w, dshape, prompt, taps, dt)
+    n = len(prompt)
+    out = [anchor]
+    taus = []
+    cycle = 0
+    while len(out) < n_new:
+        drafts, _, _ = draft_block(draft_w, shared, dshape, dctx, anchor, n, block, dt)
+        if draft_override is not None:
+            drafts = np.asarray(draft_override(cycle, anchor, drafts), dtype=np.int64)
+        block_ids = np.concatenate([[anchor], drafts])
+        g, _, feats, new_kv, _ = verify(target_w, shared, tshape, tcache, block_ids, n, taps, dt)
+        a, tau, bonus = accept(drafts, g)
+        tcache, dctx = commit(tcache, dctx, new_kv, feats, tau, n, draft_w, dshape, dt)
+        out.extend(int(t) for t in drafts[:a])
+        out.append(bonus)
+        taus.append(tau)
+        n += tau
+        anchor = bonus
+        cycle += 1
+    return out[:n_new], taus
+
+
+# ----------------------------------------------------------------------------------------
+# Accounting  [DF §2.2 latency model; [TRY] acceptance tables and log lines]
+
+
+def cycle_stats(taus, block):
+    """Counters of a run of cycles: every cycle proposes B-1 drafts; accepted = sum(tau-1);
+    tokens emitted = sum(tau) = cycles + accepted; acceptance = accepted / generated;
+    mean accepted length = tokens / cycles."""
+    taus = np.asarray(taus, dtype=np.int64)
+    cycles = int(taus.size)
+    accepted = int(np.sum(taus - 1))
+    generated = cycles * (block - 1)
+    tokens = cycles + accepted
+    return {
+        "cycles": cycles,
+        "generated": generated,
+        "accepted": accepted,
+        "tokens": tokens,
+        "acceptance": accepted / generated if generated else 0.0,
+        "mean_len": tokens / cycles if cycles else 0.0,
+    }
+
+
+def latency_per_token(t_draft, t_verify, taus):
+    """L = (T_draft + T_verify) / tau as a ratio of sums over cycles [DF §2.2]."""
+    return (float(np.sum(t_draft)) + float(np.sum(t_verify))) / float(np.sum(taus))
+
+
+def expected_tau_forced(p, block):
+    """Mean tau when each draft position is independently forced to the target's choice
+    with probability p and the first unforced position is made to differ:
+    tau = 1 + (length of the leading run of forced positions)."""
+    return 1.0 + sum(p ** k for k in range(1, block))
