@@ -1,0 +1,184 @@
+"""Device-memory plumbing around libdflash: packed weights, paged caches, workspaces,
+and torch-tensor wrappers of the four entry points (same names as the C ABI).
+
+PyTorch only allocates device memory and supplies the current HIP stream; every step of
+the drafter / verifier runs in libdflash's kernels.
+"""
+from __future__ import annotations
+
+import ctypes
+from ctypes import POINTER, c_int32, c_void_p
+
+import torch
+
+from . import _lib
+
+PAGE = 64
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dt_code(t: torch.dtype) -> int:
+    if t == torch.bfloat16:
+        return _lib.DFLASH_BF16
+    if t == torch.float32:
+        return _lib.DFLASH_F32
+    raise ValueError(f"unsupported dtype {t}")
+
+
+class Model:
+    """A drafter (``draft=True``: needs W_c and g_c) or a target model.
+
+    ``weights`` uses the per-layer names L{i}.{g_in,wq,wk,wv,wo,g_post,wg,wu,wd}, plus g_f
+    and (drafter) w_c, g_c; ``shared`` holds embed and lm_head.  Q/K/V and gate/up are
+    packed into the row-concatenated matrices the library consumes."""
+
+    def __init__(self, shape, weights: dict, shared: dict, n_taps: int, taps=None,
+                 draft: bool = True):
+        self.shape = shape
+        dtype = shared["embed"].dtype
+        self.dtype = dtype
+        self._keep = []
+        lw = []
+        for i in range(shape.n_layers):
+            qkv = torch.cat([weights[f"L{i}.wq"], weights[f"L{i}.wk"], weights[f"L{i}.wv"]], 0).contiguous()
+            gu = torch.cat([weights[f"L{i}.wg"], weights[f"L{i}.wu"]], 0).contiguous()
+            tensors = [weights[f"L{i}.g_in"].contiguous(), qkv, weights[f"L{i}.wo"].contiguous(),
+                       weights[f"L{i}.g_post"].contiguous(), gu, weights[f"L{i}.wd"].contiguous()]
+            self._keep += tensors
+            lw += [t.data_ptr() for t in tensors]
+        self.qkv = [self._keep[6 * i + 1] for i in range(shape.n_layers)]
+        self._lw = (c_void_p * len(lw))(*lw)
+        for k in ("embed", "lm_head"):
+            self._keep.append(shared[k])
+        self._keep.append(weights["g_f"])
+        d = _lib.ModelDesc()
+        d.dtype = _dt_code(dtype)
+        d.n_layers, d.hidden = shape.n_layers, shape.hidden
+        d.n_q_heads, d.n_kv_heads, d.head_dim = shape.n_q_heads, shape.n_kv_heads, shape.head_dim
+        d.ffn, d.vocab = shape.ffn, shape.vocab
+        d.rms_eps, d.rope_base = shape.rms_eps, shape.rope_base
+        d.mask_token_id = shape.mask_token_id
+        d.n_taps = n_taps
+        if taps is not None and not draft:
+            self._taps = (c_int32 * len(taps))(*taps)
+            d.tap_layers = ctypes.cast(self._taps, POINTER(c_int32))
+        d.embed = shared["embed"].data_ptr()
+        d.lm_head = shared["lm_head"].data_ptr()
+        d.final_norm = weights["g_f"].data_ptr()
+        if draft:
+            self._keep += [weights["w_c"], weights["g_c"]]
+            d.w_c = weights["w_c"].data_ptr()
+            d.g_c = weights["g_c"].data_ptr()
+        d.layer_w = ctypes.cast(self._lw, POINTER(c_void_p))
+        self.desc = d
+        self.handle = _lib.model_create(d)
+        self.n_taps = n_taps
+
+    def workspace_bytes(self, batch, block, max_ctx, max_inject_rows=0) -> int:
+        return _lib.workspace_bytes(self.handle, batch, block, max_ctx, max_inject_rows)
+
+    def close(self):
+        if self.handle:
+            _lib.model_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class PagedKV:
+    """Paged K/V pools of one model for `batch` sequences of up to `capacity` positions.
+
+    K pool per layer [num_pages, Hkv, 64, d]; V pool [num_pages, Hkv, d, 64] (transposed
+    pages).  ``page_order`` may permute the physical pages handed to the sequences."""
+
+    def __init__(self, shape, batch, capacity, dtype, device, page_order=None, spare_pages=0):
+        self.shape = shape
+        self.batch = batch
+        self.max_pages = (capacity + PAGE - 1) // PAGE
+        self.capacity = self.max_pages * PAGE
+        self.num_pages = batch * self.max_pages + spare_pages
+        L, H, d = shape.n_layers, shape.n_kv_heads, shape.head_dim
+        self.k = [torch.zeros(self.num_pages, H, PAGE, d, dtype=dtype, device=device) for _ in range(L)]
+        self.v = [torch.zeros(self.num_pages, H, d, PAGE, dtype=dtype, device=device) for _ in range(L)]
+        if page_order is None:
+            page_order = torch.arange(batch * self.max_pages)
+        self.block_table = page_order.to(torch.int32).reshape(batch, self.max_pages).to(device).contiguous()
+        self.seq_len = torch.zeros(batch, dtype=torch.int32, device=device)
+        self.err = torch.zeros(1, dtype=torch.int32, device=device)
+        self._kp = (c_void_p * L)(*[t.data_ptr() for t in self.k])
+        self._vp = (c_void_p * L)(*[t.data_ptr() for t in self.v])
+        s = _lib.KV()
+        s.n_layers, s.n_kv_heads, s.head_dim = L, H, d
+        s.page_size, s.batch = PAGE, batch
+        s.max_pages_per_seq, s.num_pages = self.max_pages, self.num_pages
+        s.k_pool = ctypes.cast(self._kp, POINTER(c_void_p))
+        s.v_pool = ctypes.cast(self._vp, POINTER(c_void_p))
+        s.block_table = self.block_table.data_ptr()
+        s.seq_len = self.seq_len.data_ptr()
+        s.error_flags = self.err.data_ptr()
+        self.struct = s
+
+    # --- plumbing used to load a synthetic context and to read a cache back ---------------
+    def _slots(self, b, start, n):
+        pos = torch.arange(start, start + n, device=self.block_table.device)
+        pages = self.block_table[b, (pos // PAGE).long()].long()
+        return pages, (pos % PAGE).long()
+
+    def write_dense(self, layer, b, K, V, start=0):
+        """Store K, V [n, Hkv, d] (K already rotated) at positions start .. start+n-1."""
+        pages, slots = self._slots(b, start, K.shape[0])
+        self.k[layer][pages, :, slots, :] = K.to(self.k[layer].dtype)
+        self.v[layer].permute(0, 3, 1, 2)[pages, slots] = V.to(self.v[layer].dtype)
+
+    def read_dense(self, layer, b, n, start=0):
+        pages, slots = self._slots(b, start, n)
+        K = self.k[layer][pages, :, slots, :]
+        V = self.v[layer].permute(0, 3, 1, 2)[pages, slots]
+        return K, V
+
+
+class Workspace:
+    def __init__(self, nbytes, device):
+        self.nbytes = int(nbytes)
+        self.buf = torch.empty(max(self.nbytes, 256), dtype=torch.uint8, device=device)
+
+
+# --- entry points (torch tensors in, status checked) --------------------------------------
+
+def inject_ctx(model: Model, kv: PagedKV, feats, row_seq, row_pos, pos_relative, ws: Workspace):
+    st = _lib.inject_ctx(model.handle, kv.struct, _ptr(feats), int(feats.shape[0]), _ptr(row_seq),
+                         _ptr(row_pos), int(pos_relative), _ptr(ws.buf), ws.nbytes, _stream())
+    _lib._check(st, "dflash_inject_ctx")
+
+
+def draft_block(model: Model, kv: PagedKV, anchor, block, draft_ids, ws: Workspace,
+                logits_dbg=None, hidden_dbg=None):
+    st = _lib.draft_block(model.handle, kv.struct, _ptr(anchor), int(block), _ptr(draft_ids),
+                          _ptr(logits_dbg), _ptr(hidden_dbg), _ptr(ws.buf), ws.nbytes, _stream())
+    _lib._check(st, "dflash_draft_block")
+
+
+def verify_accept(model: Model, kv: PagedKV, block_ids, block, feats_out, target_argmax, tau, bonus,
+                  ws: Workspace, logits_dbg=None, hidden_dbg=None):
+    st = _lib.verify_accept(model.handle, kv.struct, _ptr(block_ids), int(block), _ptr(feats_out),
+                            _ptr(target_argmax), _ptr(tau), _ptr(bonus), _ptr(logits_dbg),
+                            _ptr(hidden_dbg), _ptr(ws.buf), ws.nbytes, _stream())
+    _lib._check(st, "dflash_verify_accept")
+
+
+def kv_commit(target_kv, draft_kv, tau, block):
+    st = _lib.kv_commit(target_kv.struct if target_kv is not None else None,
+                        draft_kv.struct if draft_kv is not None else None, _ptr(tau), int(block),
+                        _stream())
+    _lib._check(st, "dflash_kv_commit")

@@ -1,0 +1,210 @@
+/*
+ * dflash.h - C ABI of libdflash: the DFlash drafter step and greedy block verification
+ * on one AMD Instinct MI355X (gfx950).
+ *
+ * Pages the operations follow (cited by title and section):
+ *   [DF]  "DFlash - Block Diffusion for Flash Speculative Decoding" (paper notes page)
+ *   [TRY] "Trying "DFlash," a Diffusion-Model Approach to Parallel Draft-Token
+ *         Generation, on Gemma" (llama.cpp experiment write-up)
+ *
+ * One decoding cycle is   draft_block -> verify_accept -> inject_ctx -> kv_commit
+ * ([DF] section 4.5, "The Decoding Loop"): the drafter proposes B-1 tokens in one pass,
+ * the target checks the whole block in one causal pass, the longest matching prefix plus
+ * a bonus token is kept, and both KV caches advance by tau.
+ *
+ * Conventions for every call
+ *  - Tensor arguments are DEVICE pointers owned by the caller.  The library never
+ *    allocates or frees device memory and never synchronises the host: each call only
+ *    enqueues kernels on `stream` (a hipStream_t; NULL = the null stream).  Outputs are
+ *    valid once the stream reaches that point.
+ *  - Host-side arguments (descriptors, pointer tables, sizes) are read during the call
+ *    only and may be freed when it returns.
+ *  - Return value: DFLASH_OK (0) or a negative dflash_status.  Argument, shape, dtype,
+ *    capacity and workspace errors are detected before anything is enqueued, so no cache
+ *    or sequence length has been touched; DFLASH_E_HIP (a failed launch) may leave the
+ *    call's earlier kernels enqueued.
+ *  - The workspace `ws` is scratch for the duration of the call's kernels: calls that may
+ *    overlap on the device (different streams) need separate workspaces.
+ *  - Errors the host cannot see (an unmapped page, an out-of-range token id or tau) are
+ *    detected on the device: the offending row or sequence is skipped and a bit is OR-ed
+ *    into dflash_kv.error_flags (when that pointer is non-NULL).
+ *  - Matrices are row-major [out, in] (y = x W^T).  Storage dtype (weights, caches,
+ *    features, hidden activations) is the model's dtype: float32 or bfloat16; logits and
+ *    debug outputs are always float32; ids are int32.
+ *  - Calls on distinct caches and streams may run concurrently; a model is immutable
+ *    after creation.
+ */
+#ifndef DFLASH_H
+#define DFLASH_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DFLASH_OK = 0,
+  DFLASH_E_ARG = -1,        /* NULL pointer, non-positive size, bad enum            */
+  DFLASH_E_SHAPE = -2,      /* shape the kernels do not support, or inconsistent    */
+  DFLASH_E_DTYPE = -3,      /* unknown dtype or mismatch between model and cache    */
+  DFLASH_E_CAPACITY = -4,   /* cache cannot hold the rows the call would write      */
+  DFLASH_E_WORKSPACE = -5,  /* workspace NULL or smaller than dflash_workspace_bytes */
+  DFLASH_E_HIP = -6         /* a HIP launch failed                                   */
+} dflash_status;
+
+typedef enum { DFLASH_F32 = 0, DFLASH_BF16 = 1 } dflash_dtype;
+
+/* Device-side error bits OR-ed into dflash_kv.error_flags. */
+enum {
+  DFLASH_DEVERR_PAGE = 1,   /* a row's page was unmapped (-1) or out of the pool      */
+  DFLASH_DEVERR_TOKEN = 2,  /* a token id outside [0, vocab)                          */
+  DFLASH_DEVERR_TAU = 4     /* kv_commit got tau outside [1, block]                   */
+};
+
+/* Per-layer weight table: layer_w[l * DFLASH_LAYER_TENSORS + slot]. */
+enum {
+  DFLASH_W_G_IN = 0,     /* [hidden]                 RMSNorm gain before attention       */
+  DFLASH_W_QKV = 1,      /* [(Hq + 2 Hkv) d, hidden] rows: q heads, k heads, v heads      */
+  DFLASH_W_O = 2,        /* [hidden, Hq d]           attention output projection          */
+  DFLASH_W_G_POST = 3,   /* [hidden]                 RMSNorm gain before the FFN          */
+  DFLASH_W_GATE_UP = 4,  /* [2 ffn, hidden]          rows: gate (ffn rows), then up       */
+  DFLASH_W_DOWN = 5,     /* [hidden, ffn]            SwiGLU down projection               */
+  DFLASH_LAYER_TENSORS = 6
+};
+
+/*
+ * Model descriptor, for the drafter or the target.  A decoder layer is pre-norm:
+ * h += Attn(RMSNorm(h)) W_o^T; h += (SiLU(u W_g^T) * (u W_u^T)) W_d^T with
+ * u = RMSNorm(h); rotate-half RoPE on q and k.  The drafter shares the target's token
+ * embedding and LM head ([DF] section 5.2, shared embedding and LM head).
+ */
+typedef struct dflash_model_desc {
+  int32_t dtype;                /* dflash_dtype                                              */
+  int32_t n_layers, hidden, n_q_heads, n_kv_heads, head_dim, ffn, vocab;
+  float rms_eps;                /* RMSNorm epsilon                                            */
+  float rope_base;              /* RoPE base; angles p * base^(-2i/d) evaluated in float64    */
+  int32_t mask_token_id;        /* drafter: token placed at the B-1 masked positions          */
+  int32_t n_taps;               /* drafter: k, the W_c input is k * hidden wide;
+                                   target: number of tapped layers written to feats_out       */
+  const int32_t* tap_layers;    /* target: host array [n_taps] of 0-indexed layers whose
+                                   outputs are tapped, in concatenation order; drafter: NULL  */
+  const void* embed;            /* [vocab, hidden]                                            */
+  const void* lm_head;          /* [vocab, hidden]                                            */
+  const void* final_norm;       /* [hidden]                                                   */
+  const void* w_c;              /* drafter: fusion weight W_c [hidden, n_taps * hidden]       */
+  const void* g_c;              /* drafter: gain of the RMSNorm after W_c [hidden]            */
+  const void* const* layer_w;   /* host array [n_layers * DFLASH_LAYER_TENSORS]               */
+} dflash_model_desc;
+
+/*
+ * Paged KV cache (the target's cache, or the drafter's own injected-context cache -
+ * [TRY]: the drafter keeps an independent KV cache filled by injection).
+ * Pages hold `page_size` consecutive positions of one sequence.  Per layer:
+ *   K pool [num_pages, n_kv_heads, page_size, head_dim]   (K stored after RoPE)
+ *   V pool [num_pages, n_kv_heads, head_dim, page_size]   (V stored transposed per page)
+ * Position p of sequence b lives in page block_table[b * max_pages_per_seq + p / page_size]
+ * at slot p % page_size.  seq_len[b] is the committed length n_b.
+ */
+typedef struct dflash_kv {
+  int32_t n_layers, n_kv_heads, head_dim;
+  int32_t page_size;            /* must be 64                                                 */
+  int32_t batch;                /* number of sequences                                        */
+  int32_t max_pages_per_seq;    /* row length of block_table                                  */
+  int32_t num_pages;            /* pages in each pool                                         */
+  void* const* k_pool;          /* host array [n_layers] of device pointers                   */
+  void* const* v_pool;          /* host array [n_layers] of device pointers                   */
+  const int32_t* block_table;   /* device [batch, max_pages_per_seq]; -1 = unmapped          */
+  int32_t* seq_len;             /* device [batch]                                             */
+  int32_t* error_flags;         /* device [1] or NULL: DFLASH_DEVERR_* bits are OR-ed in      */
+} dflash_kv;
+
+typedef struct dflash_model dflash_model;   /* opaque: shapes + non-owning weight pointers */
+
+/* Validates the descriptor and copies it (host memory only).  Returns DFLASH_E_ARG,
+ * _SHAPE or _DTYPE for descriptors the kernels cannot run.  bf16 models need
+ * head_dim = 128, hidden and ffn multiples of 128, and n_q_heads a multiple of
+ * n_kv_heads; float32 models need an even head_dim. */
+int dflash_model_create(const dflash_model_desc* desc, dflash_model** out);
+void dflash_model_destroy(dflash_model* model);
+
+/* Human-readable name of a dflash_status. */
+const char* dflash_status_str(int status);
+
+/* Bytes of scratch workspace any call on `model` needs for `batch` sequences, blocks of
+ * up to `block` tokens, cache capacity up to `max_ctx_tokens` positions per sequence,
+ * and inject_ctx calls of up to `max_inject_rows` rows.  Returns 0 on bad arguments. */
+size_t dflash_workspace_bytes(const dflash_model* model, int32_t batch, int32_t block,
+                              int32_t max_ctx_tokens, int32_t max_inject_rows);
+
+/*
+ * KV injection ([DF] section 4.2 fusion equation and section 4.3 KV-injection equations):
+ *   H_t = RMSNorm(feats W_c^T; g_c),  and for every draft layer i
+ *   K_i = RoPE(H_t W_i^K^T, p),  V_i = H_t W_i^V^T,
+ * written into the drafter's cache at position p of sequence row_seq[r] for each row r.
+ * W_i^K, W_i^V are the k and v row blocks of layer i's DFLASH_W_QKV.
+ *   feats    device [n_rows, n_taps * hidden] (model dtype): tapped target features.
+ *   row_seq  device int32 [n_rows]: sequence of each row.
+ *   row_pos  device int32 [n_rows]: position of each row, absolute when pos_relative = 0,
+ *            else added to seq_len[row_seq[r]].
+ * seq_len is not changed (kv_commit advances it).
+ */
+int dflash_inject_ctx(const dflash_model* draft, dflash_kv* draft_ctx, const void* feats,
+                      int32_t n_rows, const int32_t* row_seq, const int32_t* row_pos,
+                      int32_t pos_relative, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * One drafter step ([DF] section 4.4, parallel diffusion drafting; [TRY] appendix on the
+ * drafter: mask-token queries and non-causal attention): the block
+ * [anchor[b], mask x (block-1)] sits at positions seq_len[b] .. seq_len[b]+block-1, runs
+ * through every draft layer in one pass with bidirectional attention over the injected
+ * context and the whole block, and each masked position takes the argmax of its logits.
+ *   anchor     device int32 [batch]
+ *   draft_ids  device int32 [batch, block-1] (out)
+ *   logits_dbg device float [batch, block-1, vocab] or NULL (out)
+ *   hidden_dbg device float [n_layers+1, batch, block, hidden] or NULL (out): residual
+ *              stream after the embedding and after each layer.
+ * 1 <= block <= 64; the cache must hold >= seq_len[b] context rows (it is only read).
+ */
+int dflash_draft_block(const dflash_model* draft, const dflash_kv* draft_ctx,
+                       const int32_t* anchor, int32_t block, int32_t* draft_ids,
+                       float* logits_dbg, float* hidden_dbg, void* ws, size_t ws_bytes,
+                       void* stream);
+
+/*
+ * Block verification and greedy acceptance ([DF] section 4.5 steps 2-3; [TRY] Fig. 1:
+ * the main model checks the block with causal attention in one parallel pass).
+ * The target runs block_ids[b] = [x, d_1 .. d_{block-1}] at positions
+ * n = seq_len[b] .. n+block-1, causal inside the block with the whole cache visible, and
+ * writes the block's K/V into the cache at those positions (tentatively: only kv_commit
+ * makes them part of the sequence).
+ *   feats_out     device [batch, block, n_taps * hidden] (model dtype) or NULL (out):
+ *                 outputs of the tapped layers, concatenated in tap order.
+ *   target_argmax device int32 [batch, block] (out): g_j, greedy id after row j.
+ *   tau, bonus    device int32 [batch] (out): a = leading j with d_j == g_{j-1},
+ *                 tau = a + 1 in [1, block], bonus = g_a.
+ *   logits_dbg    device float [batch, block, vocab] or NULL; hidden_dbg as in draft_block.
+ * The cache must map positions up to seq_len[b] + block - 1 (else the row is skipped and
+ * DFLASH_DEVERR_PAGE is flagged).
+ */
+int dflash_verify_accept(const dflash_model* target, dflash_kv* target_kv,
+                         const int32_t* block_ids, int32_t block, void* feats_out,
+                         int32_t* target_argmax, int32_t* tau, int32_t* bonus,
+                         float* logits_dbg, float* hidden_dbg, void* ws, size_t ws_bytes,
+                         void* stream);
+
+/*
+ * Commit / rollback ([DF] section 4.5: accepted tokens are appended, the cycle repeats
+ * from the updated context): seq_len[b] += tau[b] in the target cache and in the drafter
+ * context (either may be NULL).  Rows written beyond the new length by verify_accept or
+ * inject_ctx are left in place and are overwritten by later calls: rollback is a length
+ * truncation.  tau outside [1, block] is clamped and flagged DFLASH_DEVERR_TAU.
+ */
+int dflash_kv_commit(dflash_kv* target_kv, dflash_kv* draft_ctx, const int32_t* tau,
+                     int32_t block, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DFLASH_H */

@@ -1,0 +1,105 @@
+"""Helpers shared by the GPU parity tests: build the HIP-side objects and the oracle's
+inputs from the same seeded tensors, and compare results with the stated tolerances."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle as O
+import synth
+from block_diffusion_drafter_03_amd import runtime as rt
+
+DEV = "cuda"
+TOL = {"f32": 1e-4, "bf16": 2e-2}     # max |x - y| / max |y| per tensor (per row for logits)
+NEAR_TIE = 1e-2                        # oracle top-2 logit gap below which ids are not compared
+
+
+def maxrel(x, y):
+    x = np.asarray(x, dtype=np.float64)
+    y = np.asarray(y, dtype=np.float64)
+    den = np.max(np.abs(y))
+    return float(np.max(np.abs(x - y)) / den) if den > 0 else float(np.max(np.abs(x)))
+
+
+def assert_close(x, y, tol, what):
+    e = maxrel(x, y)
+    assert e <= tol, f"{what}: max relative error {e:.3e} > {tol:.1e}"
+    return e
+
+
+def assert_rows_close(x, y, tol, what):
+    worst = 0.0
+    for i in range(y.shape[0]):
+        worst = max(worst, assert_close(x[i], y[i], tol, f"{what} row {i}"))
+    return worst
+
+
+def assert_ids(gpu_ids, ora_ids, ora_logits, what):
+    """Ids must match wherever the oracle's top-2 gap is >= NEAR_TIE."""
+    gpu_ids = np.asarray(gpu_ids).reshape(-1)
+    ora_ids = np.asarray(ora_ids).reshape(-1)
+    gaps = O.top2_gap(np.asarray(ora_logits, dtype=np.float64).reshape(len(ora_ids), -1))
+    checked = gaps >= NEAR_TIE
+    bad = np.nonzero(checked & (gpu_ids != ora_ids))[0]
+    assert bad.size == 0, f"{what}: ids differ at {bad.tolist()} (gaps {gaps[bad].tolist()})"
+    return int(checked.sum())
+
+
+class Setup:
+    """Drafter (+ target) of a workload on the GPU, with numpy float32 copies for the oracle."""
+
+    def __init__(self, w: synth.Workload, target=False, device=DEV):
+        self.w = w
+        self.device = device
+        self.dw = synth.model_weights(w, "draft", device)
+        self.shared = synth.shared_weights(w, device)
+        self.draft = rt.Model(w.draft, self.dw, self.shared, n_taps=w.n_taps, draft=True)
+        self.np_dw = {k: synth.to_numpy(v) for k, v in self.dw.items()}
+        self.np_shared = {k: synth.to_numpy(v) for k, v in self.shared.items()}
+        self.target = None
+        if target:
+            self.tw = synth.model_weights(w, "target", device)
+            self.target = rt.Model(w.target, self.tw, self.shared, n_taps=len(w.taps), taps=w.taps,
+                                   draft=False)
+            self.np_tw = {k: synth.to_numpy(v) for k, v in self.tw.items()}
+
+    @property
+    def st(self):
+        return torch.float32 if self.w.dtype == "f32" else torch.bfloat16
+
+    def kv(self, shape, capacity, permute_pages=True, seed=0, spare=0):
+        g = torch.Generator().manual_seed(seed)
+        b = self.w.batch
+        maxp = (capacity + rt.PAGE - 1) // rt.PAGE
+        order = torch.randperm(b * maxp, generator=g) if permute_pages else None
+        return rt.PagedKV(shape, b, capacity, self.st, self.device, page_order=order, spare_pages=spare)
+
+    def workspace(self, model, block, capacity, inject_rows=0):
+        return rt.Workspace(model.workspace_bytes(self.w.batch, block, capacity, inject_rows),
+                            self.device)
+
+
+def inject_all(setup: Setup, kv, feats_per_seq, ws, chunk=None):
+    """Inject each sequence's feature rows at positions 0..n-1 (absolute), optionally in
+    chunks, and set seq_len to n."""
+    rows_seq, rows_pos, feats = [], [], []
+    for b, f in enumerate(feats_per_seq):
+        n = f.shape[0]
+        rows_seq.append(torch.full((n,), b, dtype=torch.int32))
+        rows_pos.append(torch.arange(n, dtype=torch.int32))
+        feats.append(f)
+    rs = torch.cat(rows_seq).to(setup.device)
+    rp = torch.cat(rows_pos).to(setup.device)
+    F = torch.cat(feats).contiguous()
+    R = F.shape[0]
+    step = chunk or R
+    for a in range(0, R, step):
+        e = min(R, a + step)
+        rt.inject_ctx(setup.draft, kv, F[a:e].contiguous(), rs[a:e].contiguous(),
+                      rp[a:e].contiguous(), 0, ws)
+    kv.seq_len.copy_(torch.tensor([f.shape[0] for f in feats_per_seq], dtype=torch.int32))
+
+
+def read_cache(kv, layer, b, n):
+    K, V = kv.read_dense(layer, b, n)
+    return synth.to_numpy(K), synth.to_numpy(V)

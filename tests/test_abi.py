@@ -1,0 +1,110 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function declared in
+include/dflash.h, and host-side validation rejects bad arguments before any launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from block_diffusion_drafter_03_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dflash.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(dflash_[a-z_]+)\s*\(", src)))
+
+
+def test_header_and_binding_agree():
+    assert _declared() == sorted(_lib.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = _lib.lib()
+    for name in _declared():
+        assert hasattr(L, name), name
+
+
+def test_status_strings():
+    assert _lib.status_str(0) == "DFLASH_OK"
+    for s in range(-1, -7, -1):
+        assert _lib.status_str(s).startswith("DFLASH_E_")
+
+
+def _desc(**kw):
+    d = _lib.ModelDesc()
+    d.dtype, d.n_layers, d.hidden = _lib.DFLASH_BF16, 1, 256
+    d.n_q_heads, d.n_kv_heads, d.head_dim, d.ffn, d.vocab = 4, 2, 128, 256, 100
+    d.rms_eps, d.rope_base, d.mask_token_id, d.n_taps = 1e-6, 10000.0, 99, 0
+    fake = ctypes.c_void_p(0x1000)
+    d.embed = d.lm_head = d.final_norm = fake.value
+    arr = (ctypes.c_void_p * 6)(*([0x1000] * 6))
+    d._arr = arr
+    d.layer_w = ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p))
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+def _create(d):
+    h = ctypes.c_void_p()
+    st = _lib.lib().dflash_model_create(ctypes.byref(d), ctypes.byref(h))
+    return st, h.value
+
+
+def test_model_create_validates():
+    st, h = _create(_desc())
+    assert st == 0 and h
+    _lib.model_destroy(h)
+    assert _create(_desc(dtype=7))[0] == -3
+    assert _create(_desc(head_dim=64))[0] == -2          # bf16 path needs head_dim 128
+    assert _create(_desc(hidden=200))[0] == -2           # hidden % 128
+    assert _create(_desc(n_kv_heads=3))[0] == -2         # GQA group must divide
+    assert _create(_desc(mask_token_id=100))[0] == -1
+    assert _create(_desc(embed=None))[0] == -1
+    st, _ = _create(_desc(dtype=_lib.DFLASH_F32, head_dim=64, hidden=256, ffn=768))
+    assert st == 0
+
+
+def test_workspace_bytes_and_entry_validation():
+    st, h = _create(_desc())
+    assert st == 0
+    try:
+        assert _lib.workspace_bytes(h, 1, 16, 4096, 0) > 0
+        assert _lib.workspace_bytes(h, 1, 65, 4096, 0) == 0
+        assert _lib.workspace_bytes(h, 0, 16, 4096, 0) == 0
+        kv = _lib.KV()
+        kv.n_layers, kv.n_kv_heads, kv.head_dim, kv.page_size = 1, 2, 128, 64
+        kv.batch, kv.max_pages_per_seq, kv.num_pages = 1, 4, 4
+        pools = (ctypes.c_void_p * 1)(0x2000)
+        kv.k_pool = kv.v_pool = ctypes.cast(pools, ctypes.POINTER(ctypes.c_void_p))
+        kv.block_table = kv.seq_len = 0x3000
+        L = _lib.lib()
+        one = ctypes.c_void_p(0x4000)
+        # every rejection below happens on the host, before any kernel launch
+        assert L.dflash_draft_block(h, ctypes.byref(kv), one, 0, one, None, None, one, 1 << 30, None) == -2
+        assert L.dflash_draft_block(h, ctypes.byref(kv), one, 16, one, None, None, one, 16, None) == -5
+        assert L.dflash_draft_block(h, ctypes.byref(kv), None, 16, one, None, None, one, 1 << 30, None) == -1
+        kv.page_size = 32
+        assert L.dflash_draft_block(h, ctypes.byref(kv), one, 16, one, None, None, one, 1 << 30, None) == -2
+        kv.page_size = 64
+        kv.head_dim = 64
+        assert L.dflash_verify_accept(h, ctypes.byref(kv), one, 16, None, one, one, one, None, None,
+                                      one, 1 << 30, None) == -2
+        kv.head_dim = 128
+        # drafter-only call on a model without W_c
+        assert L.dflash_inject_ctx(h, ctypes.byref(kv), one, 4, one, one, 0, one, 1 << 30, None) == -1
+        assert L.dflash_kv_commit(None, None, one, 16, None) == -1
+        assert L.dflash_kv_commit(ctypes.byref(kv), None, one, 0, None) == -2
+    finally:
+        _lib.model_destroy(h)
+
+
+def test_product_path_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(_lib, "_lib", None)
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError):
+        _lib.lib()
