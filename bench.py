@@ -1,0 +1,245 @@
+#!/usr/bin/env python3
+"""Benchmark of the DFlash drafter step on one MI355X.
+
+One timed step is one speculative cycle of the Qwen3-8B-shaped drafter (5 layers, hidden
+4096, 32/8 heads x 128, FFN 12288, vocab 151936, bf16) at batch 1 over a 4096-row injected
+context with blocks of 16: draft_block, verify_accept by an 8-layer Qwen3-8B-shaped target
+(FFN 14336) over a 4096-token cache, inject_ctx of the 16 verified feature rows, kv_commit.
+All inputs are seeded synthetic tensors already resident in HBM.
+
+Prints one JSON line: draft tokens/s of the draft block (b * (B-1) / T_draft_block) as
+`value`, the cycle time as `ms_per_step`, per-call microseconds, the roofline of the
+dominant kernel (skinny weight-streaming GEMM of the gate/up projections) timed with HIP
+events inside the timed region, and the CPU oracle timed on the host on a small sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "µs per draft block & draft tokens/s (B=16, ctx 4K–262K); % HBM/MFMA roofline"
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-reps", type=int, default=3)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the drafter step is data-parallel over sequences "
+              "and this build runs no collectives (see DESIGN.md for how it would shard).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    from block_diffusion_drafter_03_amd import _lib
+    from block_diffusion_drafter_03_amd import runtime as rt
+
+    dev = "cuda"
+    torch.cuda.set_device(0)
+    w = synth.workload("qwen3_8b_b1_ctx4k")
+    wt = synth.workload("qwen3_8b_cycle_b8")          # supplies the 8-layer target shape
+    D, B, n = w.draft, w.block, w.ctx[0]
+    T = wt.target
+    taps = wt.taps
+    K, W = args.steps, args.warmup
+    log("generating weights on the GPU")
+    dw = synth.model_weights(w, "draft", dev)
+    shared = synth.shared_weights(w, dev)
+    tw = synth.model_weights(wt, "target", dev)
+    draft = rt.Model(D, dw, shared, n_taps=w.n_taps, draft=True)
+    target = rt.Model(T, tw, shared, n_taps=len(taps), taps=taps, draft=False)
+    cap = n + B * (K + W + 3 * 8 + 4) + 64          # every cycle appends <= B rows
+    dkv = rt.PagedKV(D, 1, cap, torch.bfloat16, dev)
+    tkv = rt.PagedKV(T, 1, cap, torch.bfloat16, dev)
+    chunk = 512
+    ws_d = rt.Workspace(draft.workspace_bytes(1, B, dkv.capacity, chunk), dev)
+    ws_t = rt.Workspace(target.workspace_bytes(1, B, tkv.capacity), dev)
+
+    log("injecting the 4096-row drafter context (512-row chunks) and filling the target cache")
+    feats0 = synth.features(w, n, dev, tag="feats.b0")
+    seq0 = torch.zeros(chunk, dtype=torch.int32, device=dev)
+    inj_ms = []
+    for a in range(0, n, chunk):
+        pos = torch.arange(a, a + chunk, dtype=torch.int32, device=dev)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        rt.inject_ctx(draft, dkv, feats0[a:a + chunk].contiguous(), seq0, pos, 0, ws_d)
+        e1.record()
+        inj_ms.append((e0, e1))
+    dkv.seq_len.fill_(n)
+    tctx = synth.synthetic_ctx_kv(wt, "target", [n], dev)
+    for l in range(T.n_layers):
+        tkv.write_dense(l, 0, tctx[l][0][0], tctx[l][0][1])
+    del tctx
+    tkv.seq_len.fill_(n)
+    torch.cuda.synchronize()
+    chunk_us = [a.elapsed_time(b) * 1e3 for a, b in inj_ms]
+
+    anchor = synth.anchors(w, dev)
+    bonus = torch.zeros(1, dtype=torch.int32, device=dev)
+    drafts = torch.zeros(1, B - 1, dtype=torch.int32, device=dev)
+    feats = torch.zeros(1, B, w.n_taps * D.hidden, dtype=torch.bfloat16, device=dev)
+    g = torch.zeros(1, B, dtype=torch.int32, device=dev)
+    tau = torch.zeros(1, dtype=torch.int32, device=dev)
+    rseq = torch.zeros(B, dtype=torch.int32, device=dev)
+    rpos = torch.arange(B, dtype=torch.int32, device=dev)
+    feats2d = feats.view(B, -1)
+    state = {"anchor": anchor, "bonus": bonus}
+
+    def step(ev=None):
+        a, bo = state["anchor"], state["bonus"]
+        if ev: ev[0].record()
+        rt.draft_block(draft, dkv, a, B, drafts, ws_d)
+        if ev: ev[1].record()
+        rt.verify_accept(target, tkv, a, drafts, B, feats, g, tau, bo, ws_t)
+        if ev: ev[2].record()
+        rt.inject_ctx(draft, dkv, feats2d, rseq, rpos, 1, ws_d)
+        if ev: ev[3].record()
+        rt.kv_commit(tkv, dkv, tau, B)
+        if ev: ev[4].record()
+        state["anchor"], state["bonus"] = bo, a          # the bonus is the next anchor
+
+    log(f"warmup {W} steps")
+    for _ in range(W):
+        step()
+    torch.cuda.synchronize()
+    seq_before = int(tkv.seq_len.item())
+
+    # dominant kernel over the cycle: gate/up projection GEMMs (5 drafter + 8 target launches)
+    per_step = D.n_layers + T.n_layers
+    _lib.timing_arm(_lib.KERNEL_GEMM_GATE_UP, per_step * K)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(K)]
+    log(f"timing {K} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    gu_ms = _lib.timing_read(per_step * K)
+    seq_after = int(tkv.seq_len.item())
+    assert int(tkv.err.item()) == 0 and int(dkv.err.item()) == 0
+
+    ms_per_step = (t1 - t0) * 1e3 / K
+
+    def mean_us(i, j):
+        return sum(e[i].elapsed_time(e[j]) for e in evs) * 1e3 / K
+
+    us_draft, us_verify, us_inject, us_commit = mean_us(0, 1), mean_us(1, 2), mean_us(2, 3), mean_us(3, 4)
+    tau_mean = (seq_after - seq_before) / K
+    draft_tok_s = 1 * (B - 1) / (us_draft * 1e-6)
+
+    # roofline of the gate/up GEMM launches: algorithmic bytes = weights + input rows
+    bytes_d = 2 * D.ffn * D.hidden * 2 + B * D.hidden * 2
+    bytes_t = 2 * T.ffn * T.hidden * 2 + B * T.hidden * 2
+    nbytes = [bytes_d if (i % per_step) < D.n_layers else bytes_t for i in range(len(gu_ms))]
+    achieved = sum(nbytes) / (sum(gu_ms) * 1e-3) / 1e9
+    avg_bytes = sum(nbytes) / len(nbytes)
+    avg_us = sum(gu_ms) / len(gu_ms) * 1e3
+
+    # per-class breakdown over a few extra (untimed) cycles
+    classes = {"lm_head": _lib.KERNEL_LM_HEAD, "gemm_qkv": _lib.KERNEL_GEMM_QKV,
+               "gemm_o": _lib.KERNEL_GEMM_O, "gemm_gate_up": _lib.KERNEL_GEMM_GATE_UP,
+               "gemm_down": _lib.KERNEL_GEMM_DOWN, "attention": _lib.KERNEL_ATTENTION,
+               "inject_fuse": _lib.KERNEL_INJECT_FUSE, "inject_kv": _lib.KERNEL_INJECT_KV}
+    breakdown = {}
+    for name, kid in classes.items():
+        _lib.timing_arm(kid, 64)
+        for _ in range(3):
+            step()
+        torch.cuda.synchronize()
+        ms = _lib.timing_read(64)
+        breakdown[name] = {"launches_per_cycle": len(ms) / 3,
+                           "us_per_cycle": sum(ms) * 1e3 / 3}
+    hbm_bytes_draft = (D.n_layers * ((D.n_q_heads + 2 * D.n_kv_heads) * D.head_dim * D.hidden
+                                     + D.hidden * D.n_q_heads * D.head_dim + 3 * D.ffn * D.hidden) * 2
+                       + D.vocab * D.hidden * 2 + D.n_layers * n * D.n_kv_heads * D.head_dim * 2 * 2)
+
+    out = {
+        "metric": METRIC,
+        "value": round(draft_tok_s, 1),
+        "unit": "draft tok/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "qwen3_8b_b1_ctx4k: Qwen3-8B-shaped drafter (5 layers, 4096, 32/8x128, "
+                               "FFN 12288, V 151936), batch 1, 4096-row injected context, block 16; "
+                               "verify by an 8-layer Qwen3-8B-shaped target (FFN 14336, 4096-token cache)",
+                   "batch": 1, "block": B, "ctx": n},
+        "us_per_draft_block": round(us_draft, 2),
+        "us_per_verify": round(us_verify, 2),
+        "us_per_inject_16_rows": round(us_inject, 2),
+        "us_per_commit": round(us_commit, 2),
+        "us_per_inject_512_rows": round(sum(chunk_us[1:]) / max(1, len(chunk_us) - 1), 2),
+        "tau_mean": tau_mean,
+        "L_us_per_token": round((us_draft + us_verify + us_inject + us_commit) / max(tau_mean, 1e-9), 2),
+        "draft_block_hbm_gbs": round(hbm_bytes_draft / (us_draft * 1e-6) / 1e9, 1),
+        "draft_block_hbm_frac": round(hbm_bytes_draft / (us_draft * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+        "roofline": {"kernel": "gemm_skinny_bf16 (gate/up projections, M=16)", "bound": "hbm",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_launch": int(avg_bytes), "avg_launch_us": round(avg_us, 2),
+                     "launches": len(gu_ms)},
+        "kernels": breakdown,
+    }
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, dw, shared, feats0, anchor, args.cpu_reps, draft_tok_s)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(w, dw, shared, feats0, anchor, reps, gpu_value):
+    """The oracle's draft block on the host cores (bounded sample: `reps` blocks)."""
+    import numpy as np
+    import synth
+    import oracle as O
+    from threadpoolctl import threadpool_info, threadpool_limits
+
+    cores = len(os.sched_getaffinity(0))
+    with threadpool_limits(limits=cores):
+        used = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        log(f"cpu baseline: copying weights to host ({cores} cores)")
+        np_dw = {k: synth.to_numpy(v) for k, v in dw.items()}
+        np_sh = {k: synth.to_numpy(v) for k, v in shared.items()}
+        n = w.ctx[0]
+        ctx = O.inject(synth.to_numpy(feats0), np.arange(n), np_dw, w.draft)
+        a = int(anchor[0])
+        log(f"cpu baseline: timing {reps} oracle draft blocks")
+        ts = []
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            O.draft_block(np_dw, np_sh, w.draft, ctx, a, n, w.block)
+            ts.append(time.perf_counter() - t0)
+    t = sorted(ts)[len(ts) // 2]
+    return {"value": round((w.block - 1) / t, 2), "unit": "draft tok/s", "cores": used,
+            "kind": "oracle",
+            "sample": f"{reps} oracle draft blocks (float32 NumPy, same weights and injected context), "
+                      f"median {t:.3f} s",
+            "gpu_over_cpu": round(gpu_value / ((w.block - 1) / t), 1)}
+
+
+if __name__ == "__main__":
+    main()

@@ -19,7 +19,10 @@ DEVERR_PAGE, DEVERR_TOKEN, DEVERR_TAU = 1, 2, 4
 
 EXPORTS = ("dflash_model_create", "dflash_model_destroy", "dflash_status_str",
            "dflash_workspace_bytes", "dflash_inject_ctx", "dflash_draft_block",
-           "dflash_verify_accept", "dflash_kv_commit")
+           "dflash_verify_accept", "dflash_kv_commit", "dflash_timing_arm",
+           "dflash_timing_read")
+KERNEL_LM_HEAD, KERNEL_GEMM_QKV, KERNEL_GEMM_O, KERNEL_GEMM_GATE_UP, KERNEL_GEMM_DOWN, \
+    KERNEL_ATTENTION, KERNEL_INJECT_FUSE, KERNEL_INJECT_KV = range(8)
 
 
 class ModelDesc(ctypes.Structure):
@@ -70,12 +73,16 @@ def lib():
         L.dflash_draft_block.argtypes = [c_void_p, POINTER(KV), c_void_p, c_int32, c_void_p,
                                          c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
         L.dflash_draft_block.restype = c_int32
-        L.dflash_verify_accept.argtypes = [c_void_p, POINTER(KV), c_void_p, c_int32, c_void_p,
+        L.dflash_verify_accept.argtypes = [c_void_p, POINTER(KV), c_void_p, c_void_p, c_int32,
                                            c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
-                                           c_void_p, c_size_t, c_void_p]
+                                           c_void_p, c_void_p, c_size_t, c_void_p]
         L.dflash_verify_accept.restype = c_int32
         L.dflash_kv_commit.argtypes = [POINTER(KV), POINTER(KV), c_void_p, c_int32, c_void_p]
         L.dflash_kv_commit.restype = c_int32
+        L.dflash_timing_arm.argtypes = [c_int32, c_int32]
+        L.dflash_timing_arm.restype = c_int32
+        L.dflash_timing_read.argtypes = [POINTER(c_float), c_int32]
+        L.dflash_timing_read.restype = c_int32
         _lib = L
     return _lib
 
@@ -115,11 +122,23 @@ def draft_block(handle, kv: KV, anchor, block, draft_ids, logits_dbg, hidden_dbg
                                     logits_dbg, hidden_dbg, ws, ws_bytes, stream)
 
 
-def verify_accept(handle, kv: KV, block_ids, block, feats_out, target_argmax, tau, bonus,
+def verify_accept(handle, kv: KV, anchor, draft_ids, block, feats_out, target_argmax, tau, bonus,
                   logits_dbg, hidden_dbg, ws, ws_bytes, stream) -> int:
-    return lib().dflash_verify_accept(c_void_p(handle), ctypes.byref(kv), block_ids, block,
+    return lib().dflash_verify_accept(c_void_p(handle), ctypes.byref(kv), anchor, draft_ids, block,
                                       feats_out, target_argmax, tau, bonus, logits_dbg,
                                       hidden_dbg, ws, ws_bytes, stream)
+
+
+def timing_arm(kernel: int, capacity: int):
+    _check(lib().dflash_timing_arm(kernel, capacity), "dflash_timing_arm")
+
+
+def timing_read(capacity: int) -> list:
+    buf = (c_float * max(capacity, 1))()
+    n = lib().dflash_timing_read(buf, capacity)
+    if n < 0:
+        raise DFlashError(n, "dflash_timing_read")
+    return [float(buf[i]) for i in range(n)]
 
 
 def kv_commit(target_kv, draft_kv, tau, block, stream) -> int:

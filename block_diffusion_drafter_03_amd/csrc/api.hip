@@ -1,5 +1,15 @@
 // libdflash C ABI: argument validation, workspace layout and launch sequencing.
 // The operations are specified in include/dflash.h.
+//
+// One decoder layer is six launches (the norms, RoPE, SwiGLU and residual adds are fused
+// into them):
+//   QKV GEMM   A = h (model dtype), RMSNorm(g_in) applied on the A side; epilogue: RoPE,
+//              q / k_blk / v_blk^T (and, for verification, the block K/V into the cache)
+//   attention  split-K over [context ; block], then the log-sum-exp merge of the splits
+//   O GEMM     epilogue: h += o W_o^T
+//   GATE/UP    A = h, RMSNorm(g_post) on the A side; epilogue: SiLU(gate) * up
+//   DOWN GEMM  epilogue: h += act W_d^T (+ tapped-feature / debug copies)
+// and the LM head is one GEMM with RMSNorm(g_f) on the A side and an argmax epilogue.
 #include <string.h>
 
 #include <new>
@@ -21,6 +31,7 @@ namespace {
 const size_t kAlign = 256;
 inline size_t al(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 inline size_t esz(int dt) { return dt == DFLASH_BF16 ? 2 : 4; }
+inline int round_up(int x, int m) { return (x + m - 1) / m * m; }
 
 // Bump allocator over the caller's workspace (offsets only; nothing is allocated).
 struct Carve {
@@ -38,78 +49,76 @@ inline const void* W(const dflash_model* m, int l, int slot) {
   return m->layer_w[(size_t)l * DFLASH_LAYER_TENSORS + slot];
 }
 
-inline int round_up(int x, int m) { return (x + m - 1) / m * m; }
-
 // Scratch of one draft / verify step for `batch` sequences of `B` rows.
 struct StepWs {
   float* h;
-  void* u;
-  float* C;
+  void* hb;
   void* q;
   void* kblk;
   void* vblkT;
   float* part;
   void* o;
   void* act;
-  float* logits;
-  int32_t* ids;
+  unsigned long long* keys;
+  float2* rope;
   AttnPlan plan;
-  int Cs_max;   // max split count over the layer GEMMs
 };
 
 size_t step_ws(const dflash_model* m, int batch, int B, int ctx_cap, void* base, StepWs* w) {
   const dflash_model_desc& d = m->d;
   const int dt = d.dtype, M = batch * B, Bp = round_up(B, 32);
   const int D = d.hidden, Hq = d.n_q_heads, Hkv = d.n_kv_heads, hd = d.head_dim;
-  const int Nqkv = (Hq + 2 * Hkv) * hd;
-  size_t cmax = 0;
-  int smax = 1;
-  const int shapes[4][2] = {{Nqkv, D}, {D, Hq * hd}, {2 * d.ffn, D}, {D, d.ffn}};
-  for (auto& s : shapes) {
-    const int sp = gemm_splits(dt, M, s[0], s[1]);
-    if (sp > smax) smax = sp;
-    const size_t c = (size_t)sp * M * s[0];
-    if (c > cmax) cmax = c;
-  }
   StepWs t;
   t.plan = attn_plan(dt, batch, Hkv, Hq / Hkv, B, ctx_cap);
-  t.Cs_max = smax;
   Carve cv(base);
   t.h = (float*)cv.take((size_t)M * D * 4);
-  t.u = cv.take((size_t)M * D * esz(dt));
-  t.C = (float*)cv.take(cmax * 4);
+  t.hb = cv.take((size_t)M * D * esz(dt));
   t.q = cv.take((size_t)M * Hq * hd * esz(dt));
   t.kblk = cv.take((size_t)M * Hkv * hd * esz(dt));
   t.vblkT = cv.take((size_t)batch * Hkv * hd * Bp * esz(dt));
-  t.part = (float*)cv.take(attn_partial_floats(t.plan, batch, Hkv, hd) * 4);
+  t.part = (float*)cv.take(dt == DFLASH_BF16 ? attn_partial_floats(t.plan, batch, Hkv, hd) * 4 : 0);
   t.o = cv.take((size_t)M * Hq * hd * esz(dt));
   t.act = cv.take((size_t)M * d.ffn * esz(dt));
-  t.logits = (float*)cv.take((size_t)M * d.vocab * 4);
-  t.ids = (int32_t*)cv.take((size_t)M * 4);
+  t.keys = (unsigned long long*)cv.take((size_t)M * 8);
+  t.rope = (float2*)cv.take((size_t)M * (hd / 2) * sizeof(float2));
   if (w) *w = t;
   return cv.off;
 }
 
-struct InjWs {
-  float* C1;
-  void* Ht;
-  float* C2;
-  int S1, S2;
-};
-
-size_t inject_ws(const dflash_model* m, int rows, void* base, InjWs* w) {
-  const dflash_model_desc& d = m->d;
-  const int dt = d.dtype, D = d.hidden;
-  const int N2 = d.n_layers * 2 * d.n_kv_heads * d.head_dim;
-  InjWs t;
-  t.S1 = gemm_splits(dt, rows, D, d.n_taps * D);
-  t.S2 = gemm_splits(dt, rows, N2, D);
+size_t inject_ws(const dflash_model* m, int rows, void* base, void** x, float2** rope) {
   Carve cv(base);
-  t.C1 = (float*)cv.take((size_t)t.S1 * rows * D * 4);
-  t.Ht = cv.take((size_t)rows * D * esz(dt));
-  t.C2 = (float*)cv.take((size_t)t.S2 * rows * N2 * 4);
-  if (w) *w = t;
+  void* p = cv.take((size_t)rows * m->d.hidden * esz(m->d.dtype));
+  float2* r = (float2*)cv.take((size_t)rows * (m->d.head_dim / 2) * sizeof(float2));
+  if (x) *x = p;
+  if (rope) *rope = r;
   return cv.off;
+}
+
+EmbedArgs embed_args(const dflash_model* m, const dflash_kv* kv, const StepWs& w, int mode,
+                     const int32_t* ids, const int32_t* anchor, int B, float* hidden_dbg) {
+  const dflash_model_desc& d = m->d;
+  EmbedArgs a;
+  memset(&a, 0, sizeof(a));
+  a.ids = ids;
+  a.anchor = anchor;
+  a.mode = mode;
+  a.batch = kv->batch;
+  a.B = B;
+  a.mask_id = d.mask_token_id;
+  a.E = d.embed;
+  a.V = d.vocab;
+  a.D = d.hidden;
+  a.h = w.h;
+  a.hb = w.hb;
+  a.hdbg = hidden_dbg;
+  a.keys = w.keys;
+  a.n_keys = kv->batch * B;
+  a.err = kv->error_flags;
+  a.seq_len = kv->seq_len;
+  a.hd = d.head_dim;
+  a.rope_base = d.rope_base;
+  a.rope = w.rope;
+  return a;
 }
 
 int check_kv(const dflash_model* m, const dflash_kv* kv) {
@@ -132,6 +141,7 @@ KvLayer layer_view(const dflash_kv* kv, int l) {
   v.seq_len = kv->seq_len;
   v.max_pages = kv->max_pages_per_seq;
   v.num_pages = kv->num_pages;
+  v.batch = kv->batch;
   v.err = kv->error_flags;
   return v;
 }
@@ -140,6 +150,29 @@ KvLayer layer_view(const dflash_kv* kv, int l) {
   do {                                         \
     if ((x) != hipSuccess) return DFLASH_E_HIP; \
   } while (0)
+
+// ---- measurement hook: event pairs around the launches of one kernel class ----
+struct TimingState {
+  int kernel = -1;
+  int capacity = 0;
+  int count = 0;
+  std::vector<hipEvent_t> ev;   // 2 per launch
+};
+TimingState g_timing;
+
+struct Timed {
+  hipStream_t st;
+  int slot = -1;
+  Timed(int kernel, hipStream_t s) : st(s) {
+    if (g_timing.kernel == kernel && g_timing.count < g_timing.capacity) {
+      slot = g_timing.count++;
+      hipEventRecord(g_timing.ev[2 * slot], st);
+    }
+  }
+  ~Timed() {
+    if (slot >= 0) hipEventRecord(g_timing.ev[2 * slot + 1], st);
+  }
+};
 
 BSeg one_seg(const void* p, int rows, int ldb) {
   BSeg b;
@@ -151,88 +184,116 @@ BSeg one_seg(const void* p, int rows, int ldb) {
   return b;
 }
 
+GemmArgs gemm_args(const void* A, int lda, const BSeg& B, int M, int N, int K, const void* norm_g,
+                   float eps, int kind) {
+  GemmArgs g;
+  memset(&g, 0, sizeof(g));
+  g.A = A;
+  g.lda = lda;
+  g.B = B;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.norm_g = norm_g;
+  g.eps = eps;
+  g.e.kind = kind;
+  return g;
+}
+
+int run_gemm(int kernel_class, int dt, const GemmArgs& g, hipStream_t st) {
+  Timed t(kernel_class, st);
+  HIPCHK(launch_gemm(dt, g, st));
+  return DFLASH_OK;
+}
+
 // The decoder stack shared by the drafter (bidirectional block, no cache writes) and the
-// target (causal block, block K/V written into the cache, taps copied out).
+// target (causal block, block K/V written into the cache, taps copied out).  On entry h
+// and hb hold the embedded block; on exit they hold the last layer's output.
 int run_layers(const dflash_model* m, const dflash_kv* kv, int batch, int B, const StepWs& w,
-               int causal, int write_cache, void* feats_out, float* hidden_dbg,
-               const void* final_gain, int compact_final, hipStream_t st) {
+               int causal, int write_cache, void* feats_out, float* hidden_dbg, hipStream_t st) {
   const dflash_model_desc& d = m->d;
   const int dt = d.dtype, M = batch * B, Bp = round_up(B, 32);
   const int D = d.hidden, Hq = d.n_q_heads, Hkv = d.n_kv_heads, hd = d.head_dim, F = d.ffn;
   const int Nqkv = (Hq + 2 * Hkv) * hd;
-  const size_t es = esz(dt);
-  (void)es;
-  // u = RMSNorm(h, g_in[0])
-  {
-    RowFin f{};
-    f.h = w.h;
-    f.add_resid = 1;
-    f.N = D;
-    f.g = W(m, 0, DFLASH_W_G_IN);
-    f.u = w.u;
-    f.eps = d.rms_eps;
-    HIPCHK(launch_row_finalize(dt, f, M, st));
-  }
+  const float eps = d.rms_eps;
   for (int l = 0; l < d.n_layers; ++l) {
     const KvLayer kvl = layer_view(kv, l);
-    // QKV projection, rotation, (verify) cache write
-    int S = gemm_splits(dt, M, Nqkv, D);
-    HIPCHK(launch_gemm(dt, w.u, D, one_seg(W(m, l, DFLASH_W_QKV), Nqkv, D), w.C, M, Nqkv, D, S, st));
-    HIPCHK(launch_qkv_post(dt, w.C, S, (size_t)M * Nqkv, batch, B, Bp, Hq, Hkv, hd, d.rope_base,
-                           kv->seq_len, w.q, w.kblk, w.vblkT, write_cache ? &kvl : nullptr, st));
-    // attention over [context ; block]
-    HIPCHK(launch_attention(dt, w.plan, w.q, w.kblk, w.vblkT, kvl, batch, B, Bp, Hq, Hkv, hd,
-                            causal, w.part, w.o, st));
-    // O projection + residual, then u = RMSNorm(h, g_post)
-    S = gemm_splits(dt, M, D, Hq * hd);
-    HIPCHK(launch_gemm(dt, w.o, Hq * hd, one_seg(W(m, l, DFLASH_W_O), D, Hq * hd), w.C, M, D, Hq * hd, S, st));
-    {
-      RowFin f{};
-      f.C = w.C;
-      f.S = S;
-      f.split_stride = (size_t)M * D;
-      f.N = D;
-      f.h = w.h;
-      f.add_resid = 1;
-      f.write_h = 1;
-      f.g = W(m, l, DFLASH_W_G_POST);
-      f.u = w.u;
-      f.eps = d.rms_eps;
-      HIPCHK(launch_row_finalize(dt, f, M, st));
+    {  // QKV projection with RMSNorm(g_in) on the A side; RoPE / layout epilogue
+      GemmArgs g = gemm_args(w.hb, D, one_seg(W(m, l, DFLASH_W_QKV), Nqkv, D), M, Nqkv, D,
+                             W(m, l, DFLASH_W_G_IN), eps, EPI_QKV);
+      EpiArgs& e = g.e;
+      e.B = B;
+      e.Bp = Bp;
+      e.Hq = Hq;
+      e.Hkv = Hkv;
+      e.hd = hd;
+      e.rope = w.rope;
+      e.seq_len = kv->seq_len;
+      e.q = w.q;
+      e.kblk = w.kblk;
+      e.vblkT = w.vblkT;
+      e.has_cache = write_cache;
+      e.kp[0] = kvl.k;
+      e.vp[0] = kvl.v;
+      e.block_table = kv->block_table;
+      e.max_pages = kv->max_pages_per_seq;
+      e.num_pages = kv->num_pages;
+      e.batch = kv->batch;
+      e.err = kv->error_flags;
+      if (int s = run_gemm(DFLASH_KERNEL_GEMM_QKV, dt, g, st)) return s;
     }
-    // SwiGLU FFN + residual, then the next layer's (or the final) RMSNorm
-    S = gemm_splits(dt, M, 2 * F, D);
-    HIPCHK(launch_gemm(dt, w.u, D, one_seg(W(m, l, DFLASH_W_GATE_UP), 2 * F, D), w.C, M, 2 * F, D, S, st));
-    HIPCHK(launch_swiglu(dt, w.C, S, (size_t)M * 2 * F, M, F, w.act, st));
-    S = gemm_splits(dt, M, D, F);
-    HIPCHK(launch_gemm(dt, w.act, F, one_seg(W(m, l, DFLASH_W_DOWN), D, F), w.C, M, D, F, S, st));
     {
-      RowFin f{};
-      f.C = w.C;
-      f.S = S;
-      f.split_stride = (size_t)M * D;
-      f.N = D;
-      f.h = w.h;
-      f.add_resid = 1;
-      f.write_h = 1;
-      f.hdbg = hidden_dbg ? hidden_dbg + (size_t)(l + 1) * M * D : nullptr;
+      Timed t(DFLASH_KERNEL_ATTENTION, st);
+      HIPCHK(launch_attention(dt, w.plan, w.q, w.kblk, w.vblkT, kvl, batch, B, Bp, Hq, Hkv, hd,
+                              causal, w.part, w.o, st));
+    }
+    {  // O projection + residual
+      GemmArgs g = gemm_args(w.o, Hq * hd, one_seg(W(m, l, DFLASH_W_O), D, Hq * hd), M, D,
+                             Hq * hd, nullptr, eps, EPI_RESID);
+      g.e.h = w.h;
+      g.e.hb = w.hb;
+      g.e.ldh = D;
+      if (int s = run_gemm(DFLASH_KERNEL_GEMM_O, dt, g, st)) return s;
+    }
+    {  // gate/up with RMSNorm(g_post) on the A side; SwiGLU epilogue
+      GemmArgs g = gemm_args(w.hb, D, one_seg(W(m, l, DFLASH_W_GATE_UP), 2 * F, D), M, 2 * F, D,
+                             W(m, l, DFLASH_W_G_POST), eps, EPI_SWIGLU);
+      g.e.act = w.act;
+      g.e.F = F;
+      if (int s = run_gemm(DFLASH_KERNEL_GEMM_GATE_UP, dt, g, st)) return s;
+    }
+    {  // down projection + residual (+ tap / debug copies)
+      GemmArgs g = gemm_args(w.act, F, one_seg(W(m, l, DFLASH_W_DOWN), D, F), M, D, F, nullptr, eps,
+                             EPI_RESID);
+      g.e.h = w.h;
+      g.e.hb = w.hb;
+      g.e.ldh = D;
+      g.e.hdbg = hidden_dbg ? hidden_dbg + (size_t)(l + 1) * M * D : nullptr;
       if (feats_out) {
         for (size_t t = 0; t < m->taps.size(); ++t)
           if (m->taps[t] == l) {
-            f.tap = feats_out;
-            f.tap_ld = (int)m->taps.size() * D;
-            f.tap_col = (int)t * D;
+            g.e.tap = feats_out;
+            g.e.tap_ld = (int)m->taps.size() * D;
+            g.e.tap_col = (int)t * D;
           }
       }
-      const bool last = (l + 1 == d.n_layers);
-      f.g = last ? final_gain : W(m, l + 1, DFLASH_W_G_IN);
-      f.u = w.u;
-      f.compact_B = (last && compact_final) ? B : 0;
-      f.eps = d.rms_eps;
-      HIPCHK(launch_row_finalize(dt, f, M, st));
+      if (int s = run_gemm(DFLASH_KERNEL_GEMM_DOWN, dt, g, st)) return s;
     }
   }
   return DFLASH_OK;
+}
+
+// LM head with RMSNorm(g_f) on the A side and the argmax epilogue over rows of hb
+// (skipping each block's anchor row when skipB != 0).
+int run_lm_head(const dflash_model* m, const StepWs& w, int rows, int skipB, float* logits,
+                hipStream_t st) {
+  const dflash_model_desc& d = m->d;
+  GemmArgs g = gemm_args(w.hb, d.hidden, one_seg(d.lm_head, d.vocab, d.hidden), rows, d.vocab,
+                         d.hidden, d.final_norm, d.rms_eps, EPI_ARGMAX);
+  g.a_skip_B = skipB;
+  g.e.keys = w.keys;
+  g.e.logits = logits;
+  return run_gemm(DFLASH_KERNEL_LM_HEAD, d.dtype, g, st);
 }
 
 int validate_model(const dflash_model_desc* d) {
@@ -305,7 +366,7 @@ size_t dflash_workspace_bytes(const dflash_model* m, int32_t batch, int32_t bloc
     return 0;
   size_t s = step_ws(m, batch, block, max_ctx_tokens, nullptr, nullptr);
   if (max_inject_rows > 0 && m->d.w_c) {
-    const size_t i = inject_ws(m, max_inject_rows, nullptr, nullptr);
+    const size_t i = inject_ws(m, max_inject_rows, nullptr, nullptr, nullptr);
     if (i > s) s = i;
   }
   return s;
@@ -318,39 +379,52 @@ int dflash_inject_ctx(const dflash_model* m, dflash_kv* kv, const void* feats, i
   if (!m->d.w_c) return DFLASH_E_ARG;
   int e = check_kv(m, kv);
   if (e) return e;
-  InjWs w;
-  const size_t need = inject_ws(m, n_rows, ws, &w);
+  void* x = nullptr;
+  float2* rope = nullptr;
+  const size_t need = inject_ws(m, n_rows, ws, &x, &rope);
   if (!ws || ws_bytes < need) return DFLASH_E_WORKSPACE;
   const dflash_model_desc& d = m->d;
   const int dt = d.dtype, D = d.hidden, L = d.n_layers, Hkv = d.n_kv_heads, hd = d.head_dim;
   const int Kc = d.n_taps * D, N2 = L * 2 * Hkv * hd;
   hipStream_t st = (hipStream_t)stream;
-  // H_t = RMSNorm(feats W_c^T; g_c)
-  HIPCHK(launch_gemm(dt, feats, Kc, one_seg(d.w_c, D, Kc), w.C1, n_rows, D, Kc, w.S1, st));
-  {
-    RowFin f{};
-    f.C = w.C1;
-    f.S = w.S1;
-    f.split_stride = (size_t)n_rows * D;
-    f.N = D;
-    f.g = d.g_c;
-    f.u = w.Ht;
-    f.eps = d.rms_eps;
-    HIPCHK(launch_row_finalize(dt, f, n_rows, st));
+  {  // x = feats W_c^T
+    GemmArgs g = gemm_args(feats, Kc, one_seg(d.w_c, D, Kc), n_rows, D, Kc, nullptr, d.rms_eps,
+                           EPI_STORE_T);
+    g.e.out = x;
+    g.e.ldo = D;
+    if (int s = run_gemm(DFLASH_KERNEL_INJECT_FUSE, dt, g, st)) return s;
   }
-  // one GEMM over every draft layer's [W^K; W^V] row block, then RoPE(K) + page scatter
-  BSeg b;
-  memset(&b, 0, sizeof(b));
-  for (int l = 0; l < L; ++l)
-    b.ptr[l] = (const char*)W(m, l, DFLASH_W_QKV) + (size_t)d.n_q_heads * hd * D * esz(dt);
-  b.seg_rows = 2 * Hkv * hd;
-  b.nseg = L;
-  b.ldb = D;
-  HIPCHK(launch_gemm(dt, w.Ht, D, b, w.C2, n_rows, N2, D, w.S2, st));
-  HIPCHK(launch_inject_scatter(dt, w.C2, w.S2, (size_t)n_rows * N2, n_rows, L, Hkv, hd, d.rope_base,
-                               row_seq, row_pos, pos_relative, kv->k_pool, kv->v_pool,
-                               kv->block_table, kv->seq_len, kv->max_pages_per_seq, kv->num_pages,
-                               kv->batch, kv->error_flags, st));
+  HIPCHK(launch_rope_rows(row_seq, row_pos, pos_relative, kv->seq_len, kv->batch, n_rows, hd,
+                          d.rope_base, rope, st));
+  {  // H_t = RMSNorm(x; g_c) on the A side; one GEMM over every layer's [W^K; W^V] rows;
+     // epilogue: RoPE(K) and the page scatter of K and V
+    BSeg b;
+    memset(&b, 0, sizeof(b));
+    for (int l = 0; l < L; ++l)
+      b.ptr[l] = (const char*)W(m, l, DFLASH_W_QKV) + (size_t)d.n_q_heads * hd * D * esz(dt);
+    b.seg_rows = 2 * Hkv * hd;
+    b.nseg = L;
+    b.ldb = D;
+    GemmArgs g = gemm_args(x, D, b, n_rows, N2, D, d.g_c, d.rms_eps, EPI_INJECT_KV);
+    EpiArgs& ep = g.e;
+    ep.Hkv = Hkv;
+    ep.hd = hd;
+    ep.rope = rope;
+    ep.seq_len = kv->seq_len;
+    for (int l = 0; l < L; ++l) {
+      ep.kp[l] = kv->k_pool[l];
+      ep.vp[l] = kv->v_pool[l];
+    }
+    ep.block_table = kv->block_table;
+    ep.max_pages = kv->max_pages_per_seq;
+    ep.num_pages = kv->num_pages;
+    ep.batch = kv->batch;
+    ep.err = kv->error_flags;
+    ep.row_seq = row_seq;
+    ep.row_pos = row_pos;
+    ep.pos_relative = pos_relative;
+    if (int s = run_gemm(DFLASH_KERNEL_INJECT_KV, dt, g, st)) return s;
+  }
   return DFLASH_OK;
 }
 
@@ -367,28 +441,24 @@ int dflash_draft_block(const dflash_model* m, const dflash_kv* kv, const int32_t
   const size_t need = step_ws(m, batch, B, kv->max_pages_per_seq * 64, ws, &w);
   if (!ws || ws_bytes < need) return DFLASH_E_WORKSPACE;
   hipStream_t st = (hipStream_t)stream;
-  const int dt = d.dtype, D = d.hidden;
-  HIPCHK(launch_embed(dt, nullptr, anchor, 0, batch, B, d.mask_token_id, d.embed, d.vocab, D, w.h,
-                      hidden_dbg, kv->error_flags, st));
-  e = run_layers(m, kv, batch, B, w, /*causal=*/0, /*write_cache=*/0, nullptr, hidden_dbg,
-                 d.final_norm, /*compact_final=*/1, st);
+  HIPCHK(launch_embed(d.dtype, embed_args(m, kv, w, 0, nullptr, anchor, B, hidden_dbg), st));
+  e = run_layers(m, kv, batch, B, w, /*causal=*/0, /*write_cache=*/0, nullptr, hidden_dbg, st);
   if (e) return e;
   if (B == 1) return DFLASH_OK;   // a block of one has no masked position to draft
-  // LM head over the B-1 masked rows, argmax per row
   const int Mp = batch * (B - 1);
-  float* logits = logits_dbg ? logits_dbg : w.logits;
-  HIPCHK(launch_gemm(dt, w.u, D, one_seg(d.lm_head, d.vocab, D), logits, Mp, d.vocab, D, 1, st));
-  HIPCHK(launch_argmax(logits, Mp, d.vocab, draft_ids, st));
-  (void)M;
+  e = run_lm_head(m, w, Mp, B, logits_dbg, st);
+  if (e) return e;
+  HIPCHK(launch_unpack_ids(w.keys, Mp, draft_ids, st));
   return DFLASH_OK;
 }
 
-int dflash_verify_accept(const dflash_model* m, dflash_kv* kv, const int32_t* block_ids,
-                         int32_t block, void* feats_out, int32_t* target_argmax, int32_t* tau,
-                         int32_t* bonus, float* logits_dbg, float* hidden_dbg, void* ws,
-                         size_t ws_bytes, void* stream) {
-  if (!m || !block_ids || !target_argmax || !tau || !bonus) return DFLASH_E_ARG;
+int dflash_verify_accept(const dflash_model* m, dflash_kv* kv, const int32_t* anchor,
+                         const int32_t* draft_ids, int32_t block, void* feats_out,
+                         int32_t* target_argmax, int32_t* tau, int32_t* bonus, float* logits_dbg,
+                         float* hidden_dbg, void* ws, size_t ws_bytes, void* stream) {
+  if (!m || !anchor || !target_argmax || !tau || !bonus) return DFLASH_E_ARG;
   if (block < 1 || block > 64) return DFLASH_E_SHAPE;
+  if (block > 1 && !draft_ids) return DFLASH_E_ARG;
   int e = check_kv(m, kv);
   if (e) return e;
   if (feats_out && m->taps.empty()) return DFLASH_E_ARG;
@@ -398,16 +468,12 @@ int dflash_verify_accept(const dflash_model* m, dflash_kv* kv, const int32_t* bl
   const size_t need = step_ws(m, batch, B, kv->max_pages_per_seq * 64, ws, &w);
   if (!ws || ws_bytes < need) return DFLASH_E_WORKSPACE;
   hipStream_t st = (hipStream_t)stream;
-  const int dt = d.dtype, D = d.hidden;
-  HIPCHK(launch_embed(dt, block_ids, nullptr, 1, batch, B, d.mask_token_id, d.embed, d.vocab, D,
-                      w.h, hidden_dbg, kv->error_flags, st));
-  e = run_layers(m, kv, batch, B, w, /*causal=*/1, /*write_cache=*/1, feats_out, hidden_dbg,
-                 d.final_norm, /*compact_final=*/0, st);
+  HIPCHK(launch_embed(d.dtype, embed_args(m, kv, w, 1, draft_ids, anchor, B, hidden_dbg), st));
+  e = run_layers(m, kv, batch, B, w, /*causal=*/1, /*write_cache=*/1, feats_out, hidden_dbg, st);
   if (e) return e;
-  float* logits = logits_dbg ? logits_dbg : w.logits;
-  HIPCHK(launch_gemm(dt, w.u, D, one_seg(d.lm_head, d.vocab, D), logits, M, d.vocab, D, 1, st));
-  HIPCHK(launch_argmax(logits, M, d.vocab, target_argmax, st));
-  HIPCHK(launch_accept(block_ids, target_argmax, batch, B, tau, bonus, st));
+  e = run_lm_head(m, w, M, 0, logits_dbg, st);
+  if (e) return e;
+  HIPCHK(launch_accept(w.keys, draft_ids, batch, B, target_argmax, tau, bonus, st));
   return DFLASH_OK;
 }
 
@@ -423,6 +489,30 @@ int dflash_kv_commit(dflash_kv* tkv, dflash_kv* dkv, const int32_t* tau, int32_t
                        tkv ? tkv->error_flags : nullptr, dkv ? dkv->error_flags : nullptr, tau,
                        batch, block, (hipStream_t)stream));
   return DFLASH_OK;
+}
+
+int dflash_timing_arm(int32_t kernel, int32_t capacity) {
+  if (kernel < 0 || kernel >= DFLASH_KERNEL_COUNT || capacity < 1) return DFLASH_E_ARG;
+  for (hipEvent_t e : g_timing.ev) hipEventDestroy(e);
+  g_timing.ev.assign(2 * (size_t)capacity, nullptr);
+  for (auto& e : g_timing.ev)
+    if (hipEventCreate(&e) != hipSuccess) return DFLASH_E_HIP;
+  g_timing.kernel = kernel;
+  g_timing.capacity = capacity;
+  g_timing.count = 0;
+  return DFLASH_OK;
+}
+
+int dflash_timing_read(float* ms, int32_t capacity) {
+  if (!ms || capacity < 0) return DFLASH_E_ARG;
+  const int n = g_timing.count < capacity ? g_timing.count : capacity;
+  for (int i = 0; i < n; ++i) {
+    if (hipEventSynchronize(g_timing.ev[2 * i + 1]) != hipSuccess) return DFLASH_E_HIP;
+    if (hipEventElapsedTime(&ms[i], g_timing.ev[2 * i], g_timing.ev[2 * i + 1]) != hipSuccess)
+      return DFLASH_E_HIP;
+  }
+  g_timing.kernel = -1;
+  return n;
 }
 
 }  // extern "C"

@@ -2,26 +2,26 @@
 // inside the block) and for the target's verification pass (causal inside the block).
 //
 // bf16 path (head_dim 128): one workgroup per (sequence, KV head, 64-row query group,
-// key split).  The G*B query rows that share a KV head are kept in registers as MFMA
-// operands, so every context K/V byte is read from HBM once.  Each of the 4 waves walks
-// 32-key chunks of its split with its own online softmax; S^T = K Q^T and O^T = V^T P^T
-// run on v_mfma_f32_16x16x32_bf16:
-//   * the K rows of the two 16-key S^T tiles of a chunk are interleaved so that lane
-//     group g ends up holding keys 8g .. 8g+7 of the chunk for its query column - exactly
-//     the P^T operand layout of the PV product, with no data movement;
-//   * V pages are stored transposed ([d][64 keys]) so the V^T operand is a plain 16-byte
-//     load per lane.
-// The 4 waves' states are merged in LDS (fixed order) and the workgroup writes one
-// partial (m, l, O); a second kernel merges the splits with log-sum-exp weights.
-// Scores are kept in the log2 domain (scaled by log2(e)/sqrt(d)) and exponentiated with
-// exp2.
+// key split); split 0 also takes the block's own B keys.  The G*B query rows that share a
+// KV head are split over the 4 waves (16 rows each, held in registers as MFMA operands),
+// so every context K/V byte is read from HBM once per workgroup: a step is one 64-token
+// page slice of the head (16 KB of K, 16 KB of V^T, both contiguous), copied with 16-byte
+// coalesced loads into double-buffered LDS while the previous step is computed.  Each wave
+// runs its own online softmax; S^T = K Q^T and O^T = V^T P^T use v_mfma_f32_16x16x32_bf16:
+//   * the K rows of the two 16-key S^T tiles of each 32-key half are interleaved so that
+//     lane group g ends up holding keys 8g .. 8g+7 of the half for its query column -
+//     exactly the P^T operand layout of the PV product, with no data movement;
+//   * V pages are stored transposed ([d][64 keys]) so a V^T operand is one 16-byte read.
+// Each wave writes a partial (m, l, unnormalised O) of its rows; a second launch merges
+// the splits with log-sum-exp weights.  Scores are kept in the log2 domain (scaled by
+// log2(e)/sqrt(d)) and exponentiated with exp2.
 #include "common.h"
 #include "kernels.h"
 
 namespace dflash {
 
 #define AD 128      // head dim of the MFMA path
-#define ACHUNK 32   // keys per wave step
+#define PSTRIDE (AD + 4)    // floats per partial row: O[AD], m, l, 2 pad (16-byte rows)
 
 struct AttnArgs {
   const bf16* q;       // [batch*B, Hq*AD]
@@ -34,237 +34,243 @@ struct AttnArgs {
   int32_t* err;
   int max_pages, num_pages;
   int B, Bp, Hq, Hkv, G;
-  int n_ctx_splits, split_len, n_rg, causal;
+  int n_splits, split_len, n_rg, causal;
   float scale_log2;
-  float* part;         // [(b, kvh, rg, s)][64][AD + 2]  (O then m, l per row)
+  float* part;         // [(b, kvh, rg, s)][64][PSTRIDE]  (O, then m, l per row)
+  bf16* out;           // [batch*B, Hq*AD]
 };
 
+// LDS layouts of one 64-key step (one page slice of one KV head), padded by 16 bytes per row
+#define KROW (AD + 8)     // bf16 per K row   [64 keys][AD]
+#define VROW (64 + 8)     // bf16 per V^T row [AD][64 keys]
+#define KTILE (64 * KROW)
+#define VTILE (AD * VROW)
+
 __global__ __launch_bounds__(256) void attn_splitk_bf16(AttnArgs a) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  __shared__ __attribute__((aligned(16))) bf16 kt[2][KTILE];
+  __shared__ __attribute__((aligned(16))) bf16 vt[2][VTILE];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int r = lane & 15, g = lane >> 4;
   const int s = blockIdx.x;
   const int kvh = blockIdx.y % a.Hkv, rg = blockIdx.y / a.Hkv;
   const int b = blockIdx.z;
   const int R = a.G * a.B;
-  const int S_total = a.n_ctx_splits + 1;
-  const bool is_block = (s == a.n_ctx_splits);
 
   int n_ctx = a.seq_len[b];
   n_ctx = max(0, min(n_ctx, a.max_pages * 64));
-  int kbeg, kend;
-  if (is_block) {
-    kbeg = 0;
-    kend = a.B;
+  const int kbeg = s * a.split_len;                  // multiple of 64
+  const int kend = min(kbeg + a.split_len, n_ctx);
+  const int n_ctx_steps = kend > kbeg ? (kend - kbeg + 63) / 64 : 0;
+  const int n_steps = n_ctx_steps + (s == 0 ? 1 : 0); // split 0 also takes the block's keys
+
+  // this wave's query tile: rows rho = rg*64 + w*16 + r as the Q^T MFMA operand
+  const int rho = rg * 64 + w * 16 + r;
+  const int jq = rho < R ? rho % a.B : 0x7fffffff;
+  bf16x8 qf[4];
+  if (rho < R) {
+    const int gq = rho / a.B;
+    const bf16* src = a.q + (size_t)(b * a.B + jq) * a.Hq * AD + (size_t)(kvh * a.G + gq) * AD + g * 8;
+#pragma unroll
+    for (int cs = 0; cs < 4; ++cs) qf[cs] = *(const bf16x8*)(src + cs * 32);
   } else {
-    kbeg = s * a.split_len;
-    kend = min(kbeg + a.split_len, n_ctx);
+#pragma unroll
+    for (int cs = 0; cs < 4; ++cs)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qf[cs][e] = (bf16)0.f;
   }
 
-  // Q^T operand fragments for the 4 query tiles of this row group.
-  bf16x8 qf[4][4];
-  int jrow[4];
-#pragma unroll
-  for (int qt = 0; qt < 4; ++qt) {
-    const int rho = rg * 64 + qt * 16 + r;
-    jrow[qt] = rho < R ? rho % a.B : 0x7fffffff;
-    if (rho < R) {
-      const int gq = rho / a.B, j = rho % a.B;
-      const bf16* src = a.q + (size_t)(b * a.B + j) * a.Hq * AD + (size_t)(kvh * a.G + gq) * AD + g * 8;
-#pragma unroll
-      for (int cs = 0; cs < 4; ++cs) qf[qt][cs] = *(const bf16x8*)(src + cs * 32);
-    } else {
-#pragma unroll
-      for (int cs = 0; cs < 4; ++cs)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) qf[qt][cs][e] = (bf16)0.f;
-    }
-  }
-
-  float m[4], lsum[4];
-  f32x4 o[8][4];
-#pragma unroll
-  for (int qt = 0; qt < 4; ++qt) {
-    m[qt] = -INFINITY;
-    lsum[qt] = 0.f;
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) o[dt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-
-  // key row that this lane feeds into S^T tile t (interleaved so P^T needs no shuffle)
-  const int krow0 = 8 * (r >> 2) + (r & 3);
-
-  for (int c0 = kbeg + w * ACHUNK; c0 < kend; c0 += 4 * ACHUNK) {
-    const bf16* kp0;
-    const bf16* kp1;
-    const bf16* vp;
-    if (is_block) {
-      const int j0 = min(c0 + krow0, a.B - 1), j1 = min(c0 + krow0 + 4, a.B - 1);
-      kp0 = a.kblk + (size_t)(b * a.B + j0) * a.Hkv * AD + (size_t)kvh * AD + g * 8;
-      kp1 = a.kblk + (size_t)(b * a.B + j1) * a.Hkv * AD + (size_t)kvh * AD + g * 8;
-      vp = a.vblkT + ((size_t)(b * a.Hkv + kvh) * AD + r) * a.Bp + c0 + g * 8;
-    } else {
-      const int page = a.block_table[(size_t)b * a.max_pages + (c0 >> 6)];
+  // ---- global -> register staging of one step: 8 x 16 B per thread (K then V^T) ----
+  bf16x8 st[8];
+  auto load_step = [&](int i) {
+    if (i < n_ctx_steps) {
+      const int c0 = kbeg + i * 64;
+      int page = a.block_table[(size_t)b * a.max_pages + (c0 >> 6)];
       if (page < 0 || page >= a.num_pages) {
-        if (lane == 0) flag_error(a.err, DEVERR_PAGE);
-        continue;
+        if (tid == 0) flag_error(a.err, DEVERR_PAGE);
+        page = -1;
       }
-      const int off = c0 & 63;
-      const size_t pb = (size_t)page * a.Hkv + kvh;
-      kp0 = a.kpool + (pb * 64 + off + krow0) * AD + g * 8;
-      kp1 = kp0 + 4 * AD;
-      vp = a.vpool + (pb * AD + r) * 64 + off + g * 8;
-    }
-    bf16x8 kf0[4], kf1[4], vf[8];
+      const size_t pb = (size_t)(page < 0 ? 0 : page) * a.Hkv + kvh;
+      const bf16* ks = a.kpool + pb * 64 * AD;
+      const bf16* vs = a.vpool + pb * AD * 64;
 #pragma unroll
-    for (int cs = 0; cs < 4; ++cs) {
-      kf0[cs] = *(const bf16x8*)(kp0 + cs * 32);
-      kf1[cs] = *(const bf16x8*)(kp1 + cs * 32);
-    }
-    const int vstride = is_block ? 16 * a.Bp : 16 * 64;
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) vf[dt] = *(const bf16x8*)(vp + (size_t)dt * vstride);
-    // keys past the end of the range: zero V so stale or uninitialised page bytes
-    // cannot leak NaN through a zero probability
-    const int vkey = c0 + g * 8;
-    if (vkey + 8 > kend) {
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (vkey + e >= kend) vf[dt][e] = (bf16)0.f;
-    }
-
-#pragma unroll
-    for (int qt = 0; qt < 4; ++qt) {
-      f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int cs = 0; cs < 4; ++cs) {
-        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf0[cs], qf[qt][cs], s0, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf1[cs], qf[qt][cs], s1, 0, 0, 0);
+      for (int j = 0; j < 4; ++j) {
+        st[j] = *(const bf16x8*)(ks + (size_t)(tid + 256 * j) * 8);
+        st[4 + j] = *(const bf16x8*)(vs + (size_t)(tid + 256 * j) * 8);
       }
-      // this lane: keys c0 + 8g + i (s0) and c0 + 8g + 4 + i (s1), query column r
-      float sc[8];
-      float mx = -INFINITY;
+      if (page < 0) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int k0 = c0 + g * 8 + i, k1 = k0 + 4;
-        bool v0 = k0 < kend, v1 = k1 < kend;
-        if (is_block && a.causal) {
-          v0 = v0 && (k0 <= jrow[qt]);
-          v1 = v1 && (k1 <= jrow[qt]);
-        }
-        sc[i] = v0 ? s0[i] * a.scale_log2 : -INFINITY;
-        sc[4 + i] = v1 ? s1[i] * a.scale_log2 : -INFINITY;
-        mx = fmaxf(mx, fmaxf(sc[i], sc[4 + i]));
+        for (int j = 0; j < 8; ++j)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) st[j][e] = (bf16)0.f;
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float mnew = fmaxf(m[qt], mx);
-      float alpha, ps = 0.f;
-      bf16x8 pf;
-      if (mnew == -INFINITY) {
-        alpha = 1.f;
+    } else {
+      // the block's own keys: K rows from k_blk, V^T columns from v_blk^T (B <= 64)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) pf[e] = (bf16)0.f;
-      } else {
-        alpha = exp2f(m[qt] - mnew);
+      for (int j = 0; j < 4; ++j) {
+        const int idx = tid + 256 * j;       // K: key = idx / 16, 8-element column group idx % 16
+        const int key = idx >> 4, cg = idx & 15;
+        if (key < a.B)
+          st[j] = *(const bf16x8*)(a.kblk + (size_t)(b * a.B + key) * a.Hkv * AD + (size_t)kvh * AD + cg * 8);
+        else
+#pragma unroll
+          for (int e = 0; e < 8; ++e) st[j][e] = (bf16)0.f;
+        const int d = idx >> 3, kg = idx & 7;  // V^T: row d, keys kg*8 .. kg*8+7
+        const bf16* vs = a.vblkT + ((size_t)(b * a.Hkv + kvh) * AD + d) * a.Bp;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float p = exp2f(sc[e] - mnew);
-          ps += p;
-          pf[e] = (bf16)p;
+          const int key2 = kg * 8 + e;
+          st[4 + j][e] = key2 < a.B ? vs[key2] : (bf16)0.f;
         }
       }
-      m[qt] = mnew;
-      lsum[qt] = lsum[qt] * alpha + ps;
+    }
+  };
+  // keys at or past `lim` of a partial last page: their V^T columns are zeroed so stale
+  // bytes cannot leak NaN through a zero probability
+  auto store_step = [&](int buf, int lim) {
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        o[dt][qt] *= alpha;
-        o[dt][qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[dt], pf, o[dt][qt], 0, 0, 0);
+    for (int j = 0; j < 4; ++j) {
+      const int idx = tid + 256 * j;
+      *(bf16x8*)&kt[buf][(idx >> 4) * KROW + (idx & 15) * 8] = st[j];
+      bf16x8 v = st[4 + j];
+      const int k0 = (idx & 7) * 8;
+      if (k0 + 8 > lim) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (k0 + e >= lim) v[e] = (bf16)0.f;
       }
+      *(bf16x8*)&vt[buf][(idx >> 3) * VROW + k0] = v;
     }
-  }
+  };
+  auto step_lim = [&](int i) { return i < n_ctx_steps ? min(64, kend - (kbeg + i * 64)) : a.B; };
 
-  // ---- merge the 4 waves (fixed order) ----
-  __shared__ float sm_m[4][64], sm_l[4][64];
-  __shared__ float sm_o[64][AD + 4];
+  float m = -INFINITY, lsum = 0.f;
+  f32x4 o[8];
 #pragma unroll
-  for (int qt = 0; qt < 4; ++qt) {
-    const float lt = lsum[qt] + __shfl_xor(lsum[qt], 16, 64);
-    lsum[qt] = lt + __shfl_xor(lt, 32, 64);
-    if (g == 0) {
-      sm_m[w][qt * 16 + r] = m[qt];
-      sm_l[w][qt * 16 + r] = lsum[qt];
-    }
+  for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int krow0 = 8 * (r >> 2) + (r & 3);   // interleaved K rows: P^T needs no shuffle
+
+  if (n_steps > 0) {
+    load_step(0);
+    store_step(0, step_lim(0));
   }
   __syncthreads();
+  for (int i = 0; i < n_steps; ++i) {
+    const int buf = i & 1;
+    if (i + 1 < n_steps) load_step(i + 1);      // next step's loads in flight during compute
+    const bool blk = i >= n_ctx_steps;
+    const int lim = step_lim(i);
+    const bf16* K = kt[buf];
+    const bf16* VT = vt[buf];
+    f32x4 sc[2][2];
 #pragma unroll
-  for (int qt = 0; qt < 4; ++qt) {
-    const int q = qt * 16 + r;
-    const float ms = fmaxf(fmaxf(sm_m[0][q], sm_m[1][q]), fmaxf(sm_m[2][q], sm_m[3][q]));
-    const float sc = (m[qt] == -INFINITY) ? 0.f : exp2f(m[qt] - ms);
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) o[dt][qt] *= sc;
-  }
-  for (int ww = 0; ww < 4; ++ww) {
-    if (w == ww) {
+      for (int t = 0; t < 2; ++t) {
+        sc[h][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const bf16* kr = K + (h * 32 + krow0 + 4 * t) * KROW + g * 8;
 #pragma unroll
-      for (int qt = 0; qt < 4; ++qt)
+        for (int cs = 0; cs < 4; ++cs)
+          sc[h][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)(kr + cs * 32), qf[cs], sc[h][t], 0, 0, 0);
+      }
+    // lane holds keys h*32 + 8g + 4t + e (e < 4) of the step for query column r
+    float p[2][8];
+    float mx = -INFINITY;
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt) {
-          float* dst = &sm_o[qt * 16 + r][dt * 16 + g * 4];
-          if (ww == 0) {
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) dst[e] = o[dt][qt][e];
-          } else {
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) dst[e] += o[dt][qt][e];
-          }
+        for (int e = 0; e < 4; ++e) {
+          const int key = h * 32 + g * 8 + 4 * t + e;
+          bool ok = key < lim;
+          if (blk && a.causal) ok = ok && key <= jq;
+          const float x = ok ? sc[h][t][e] * a.scale_log2 : -INFINITY;
+          p[h][4 * t + e] = x;
+          mx = fmaxf(mx, x);
         }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float mnew = fmaxf(m, mx);
+    const float alpha = mnew == -INFINITY ? 1.f : exp2f(m - mnew);
+    bf16x8 pf[2];
+    float ps = 0.f;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float pe = mnew == -INFINITY ? 0.f : exp2f(p[h][e] - mnew);
+        ps += pe;
+        pf[h][e] = (bf16)pe;
+      }
+    m = mnew;
+    lsum = lsum * alpha + ps;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      o[dt] *= alpha;
+      const bf16* vr = VT + (dt * 16 + r) * VROW + g * 8;
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)(vr + h * 32), pf[h], o[dt], 0, 0, 0);
     }
+    if (i + 1 < n_steps) store_step(buf ^ 1, step_lim(i + 1));
     __syncthreads();
   }
-  float* dst = a.part + ((((size_t)b * a.Hkv + kvh) * a.n_rg + rg) * S_total + s) * 64 * (AD + 2);
-  for (int idx = threadIdx.x; idx < 64 * AD; idx += 256) {
-    const int q = idx / AD, d = idx % AD;
-    dst[q * (AD + 2) + d] = sm_o[q][d];
-  }
-  if (threadIdx.x < 64) {
-    const int q = threadIdx.x;
-    const float ms = fmaxf(fmaxf(sm_m[0][q], sm_m[1][q]), fmaxf(sm_m[2][q], sm_m[3][q]));
-    float lt = 0.f;
-    for (int ww = 0; ww < 4; ++ww)
-      if (sm_m[ww][q] != -INFINITY) lt += sm_l[ww][q] * exp2f(sm_m[ww][q] - ms);
-    dst[q * (AD + 2) + AD] = ms;
-    dst[q * (AD + 2) + AD + 1] = lt;
+
+  // ---- partial (m, l, unnormalised O) of this wave's 16 query rows ----
+  lsum += __shfl_xor(lsum, 16, 64);
+  lsum += __shfl_xor(lsum, 32, 64);
+  const size_t unit = ((size_t)b * a.Hkv + kvh) * a.n_rg + rg;
+  float* dst = a.part + (unit * a.n_splits + s) * 64 * PSTRIDE + (size_t)(w * 16 + r) * PSTRIDE;
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt)
+    *(float4*)(dst + dt * 16 + g * 4) = make_float4(o[dt][0], o[dt][1], o[dt][2], o[dt][3]);
+  if (g == 0) {
+    dst[AD] = m;
+    dst[AD + 1] = lsum;
   }
 }
 
-// Merge the key splits of every query row: O = sum_s O_s 2^(m_s - m*) / sum_s l_s 2^(m_s - m*).
-template <typename T>
-__global__ __launch_bounds__(AD) void attn_merge(const float* __restrict__ part, int S_total,
-                                                 int n_rg, int B, int Hq, int Hkv, int G,
-                                                 T* __restrict__ out) {
-  const int rho = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
-  const int R = G * B;
+
+// Split merge as its own launch: 8 query rows per workgroup, 32 threads x 4 columns per row.
+__global__ __launch_bounds__(256) void attn_merge_bf16(AttnArgs a) {
+  const int rl = threadIdx.x >> 5, t = threadIdx.x & 31;
+  const int rho = blockIdx.x * 8 + rl;
+  const int kvh = blockIdx.y, b = blockIdx.z;
+  const int R = a.G * a.B, S = a.n_splits;
   if (rho >= R) return;
   const int rg = rho / 64, q = rho % 64;
-  const float* base = part + (((size_t)b * Hkv + kvh) * n_rg + rg) * S_total * 64 * (AD + 2) +
-                      (size_t)q * (AD + 2);
-  const size_t sstride = 64 * (AD + 2);
+  const size_t unit = ((size_t)b * a.Hkv + kvh) * a.n_rg + rg;
+  const float* pr = a.part + unit * S * 64 * PSTRIDE + (size_t)q * PSTRIDE;
+  const size_t ss = 64 * PSTRIDE;
   float ms = -INFINITY;
-  for (int s = 0; s < S_total; ++s) ms = fmaxf(ms, base[s * sstride + AD]);
-  float lt = 0.f, acc = 0.f;
-  const int d = threadIdx.x;
-  for (int s = 0; s < S_total; ++s) {
-    const float mv = base[s * sstride + AD];
-    if (mv == -INFINITY) continue;
-    const float wgt = exp2f(mv - ms);
-    lt += base[s * sstride + AD + 1] * wgt;
-    acc += base[s * sstride + d] * wgt;
+  for (int sp = 0; sp < S; ++sp) ms = fmaxf(ms, pr[sp * ss + AD]);
+  float lt = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 4
+  for (int sp = 0; sp < S; ++sp) {
+    const float mv = pr[sp * ss + AD];
+    const float wgt = mv == -INFINITY ? 0.f : exp2f(mv - ms);
+    lt += pr[sp * ss + AD + 1] * wgt;
+    const float4 x = *(const float4*)(pr + sp * ss + 4 * t);
+    acc.x += x.x * wgt;
+    acc.y += x.y * wgt;
+    acc.z += x.z * wgt;
+    acc.w += x.w * wgt;
   }
-  const int gq = rho / B, j = rho % B;
-  out[(size_t)(b * B + j) * Hq * AD + (size_t)(kvh * G + gq) * AD + d] = from_f<T>(acc / lt);
+  const float inv = 1.f / lt;
+  const int gq = rho / a.B, j = rho % a.B;
+  bf16* out = a.out + (size_t)(b * a.B + j) * a.Hq * AD + (size_t)(kvh * a.G + gq) * AD + 4 * t;
+  out[0] = (bf16)(acc.x * inv);
+  out[1] = (bf16)(acc.y * inv);
+  out[2] = (bf16)(acc.z * inv);
+  out[3] = (bf16)(acc.w * inv);
+}
+
+// Tuning knob read once from the environment (benchmark sweeps): DFLASH_ATTN_SPLIT_LEN
+// forces the keys per split (rounded up to a multiple of 128).
+static int env_int(const char* name, int dflt) {
+  const char* s = getenv(name);
+  return s && *s ? atoi(s) : dflt;
 }
 
 // ---------------------------------------------------------------------------------------
@@ -292,7 +298,6 @@ __global__ __launch_bounds__(256) void attn_f32(AttnF32Args a) {
   float* qs = smem;            // [d]
   float* ps = smem + d;        // [256]
   __shared__ float red[16];
-  __shared__ int pages[4];
   const int tid = threadIdx.x;
   for (int c = tid; c < d; c += 256) qs[c] = a.q[(size_t)(b * a.B + j) * a.Hq * d + (size_t)h * d + c];
   int n_ctx = max(0, min(a.seq_len[b], a.max_pages * 64));
@@ -321,7 +326,6 @@ __global__ __launch_bounds__(256) void attn_f32(AttnF32Args a) {
         sc = t * a.scale;
       }
     }
-    // chunk max
     float mx = wave_max(sc);
     __syncthreads();
     if ((tid & 63) == 0) red[tid >> 6] = mx;
@@ -364,29 +368,44 @@ __global__ __launch_bounds__(256) void attn_f32(AttnF32Args a) {
 }
 
 // ---------------------------------------------------------------------------------------
+static int attn_num_cus() {
+  static int n = 0;
+  if (!n) {
+    int dev = 0;
+    hipGetDevice(&dev);
+    hipDeviceProp_t p;
+    n = (hipGetDeviceProperties(&p, dev) == hipSuccess && p.multiProcessorCount > 0) ? p.multiProcessorCount : 256;
+  }
+  return n;
+}
+
 AttnPlan attn_plan(int dt, int batch, int Hkv, int G, int B, int ctx_cap) {
   AttnPlan p;
   p.n_rg = (G * B + 63) / 64;
   if (dt != BF16) {
-    p.n_ctx_splits = 0;
+    p.n_ctx_splits = 1;
     p.split_len = 0;
     return p;
   }
   const int cap = ctx_cap > 0 ? ctx_cap : 1;
   const int units = batch * Hkv * p.n_rg;
-  int want = (512 + units - 1) / units;                       // ~2 workgroups per CU
-  const int max_splits = (cap + 127) / 128;
+  // two workgroups fit a CU (LDS-bound): aim for one wave of workgroups over the chip,
+  // with at least 256 keys (4 steps) in a split
+  int want = 2 * attn_num_cus() / units;
+  const int max_splits = (cap + 255) / 256;
   if (want > max_splits) want = max_splits;
   if (want < 1) want = 1;
   int len = (cap + want - 1) / want;
   len = (len + 127) / 128 * 128;
+  static const int forced = env_int("DFLASH_ATTN_SPLIT_LEN", 0);
+  if (forced >= 128) len = (forced + 127) / 128 * 128;
   p.split_len = len;
   p.n_ctx_splits = (cap + len - 1) / len;
   return p;
 }
 
 size_t attn_partial_floats(const AttnPlan& p, int batch, int Hkv, int d) {
-  return (size_t)batch * Hkv * p.n_rg * (p.n_ctx_splits + 1) * 64 * (d + 2);
+  return (size_t)batch * Hkv * p.n_rg * p.n_ctx_splits * 64 * (d + 4);
 }
 
 hipError_t launch_attention(int dt, const AttnPlan& p, const void* q, const void* kblk,
@@ -411,19 +430,19 @@ hipError_t launch_attention(int dt, const AttnPlan& p, const void* q, const void
     a.Hq = Hq;
     a.Hkv = Hkv;
     a.G = G;
-    a.n_ctx_splits = p.n_ctx_splits;
+    a.n_splits = p.n_ctx_splits;
     a.split_len = p.split_len;
     a.n_rg = p.n_rg;
     a.causal = causal;
     a.scale_log2 = 1.4426950408889634f / sqrtf((float)d);
     a.part = part;
-    dim3 grid(p.n_ctx_splits + 1, Hkv * p.n_rg, batch);
+    a.out = (bf16*)o;
+    dim3 grid(p.n_ctx_splits, Hkv * p.n_rg, batch);
     hipLaunchKernelGGL(attn_splitk_bf16, grid, dim3(256), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    dim3 g2(p.n_rg * 64, Hkv, batch);
-    hipLaunchKernelGGL(attn_merge<bf16>, g2, dim3(AD), 0, st, (const float*)part,
-                       p.n_ctx_splits + 1, p.n_rg, B, Hq, Hkv, G, (bf16*)o);
+    dim3 g2((p.n_rg * 64 + 7) / 8, Hkv, batch);
+    hipLaunchKernelGGL(attn_merge_bf16, g2, dim3(256), 0, st, a);
     return hipGetLastError();
   }
   AttnF32Args a;

@@ -1,0 +1,143 @@
+// Fused GEMM epilogues shared by the MFMA and VALU GEMM kernels.
+//
+// A GEMM computes acc[m][n] = sum_k A[m][k] W[n][k] over the FULL K inside one workgroup,
+// so every epilogue sees final values.  Optional A-side RMSNorm (norm_g != NULL): the
+// kernel accumulates sum_k A[m][k]^2 of the raw rows while loading them, multiplies the
+// operand by the gain, and scales acc by rstd[m] = 1/sqrt(mean_k A^2 + eps) here, so
+// RMSNorm(x) W^T never needs a separate pass over x.
+//
+// Packed weight layout that makes every pair-wise epilogue local to a pair of adjacent
+// output columns (2i, 2i+1):
+//   * q and k heads of DFLASH_W_QKV are stored rotary-interleaved: packed row 2i of a head
+//     is original row i and packed row 2i+1 is original row i + d/2, so the two inputs of
+//     one rotate-half rotation land in columns 2i, 2i+1 (v heads are stored plainly);
+//   * DFLASH_W_GATE_UP rows are interleaved: packed row 2j = gate row j, 2j+1 = up row j.
+#pragma once
+#include "common.h"
+#include "kernels.h"
+
+namespace dflash {
+
+DF_DEV unsigned long long pack_argmax_key(float v, int idx) {
+  unsigned u = __float_as_uint(v);
+  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);   // order-preserving map of the float
+  return ((unsigned long long)u << 32) | (unsigned)(0xFFFFFFFFu - (unsigned)idx);  // ties: lowest idx
+}
+DF_DEV int unpack_argmax_idx(unsigned long long key) {
+  return (int)(0xFFFFFFFFu - (unsigned)(key & 0xFFFFFFFFull));
+}
+
+template <typename T, int KIND>
+DF_DEV void epi_elem(const EpiArgs& e, int row, int col, float v) {
+  switch (KIND) {
+    case EPI_STORE_F32:
+      ((float*)e.out)[(size_t)row * e.ldo + col] = v;
+      break;
+    case EPI_STORE_T:
+      ((T*)e.out)[(size_t)row * e.ldo + col] = from_f<T>(v);
+      break;
+    case EPI_RESID: {
+      const size_t i = (size_t)row * e.ldh + col;
+      const float x = e.h[i] + v;
+      e.h[i] = x;
+      ((T*)e.hb)[i] = from_f<T>(x);
+      if (e.hdbg) e.hdbg[i] = x;
+      if (e.tap) ((T*)e.tap)[(size_t)row * e.tap_ld + e.tap_col + col] = from_f<T>(x);
+      break;
+    }
+    default:
+      break;
+  }
+}
+
+// cache slot of position `pos` of sequence `b`; returns false (and flags) when unmapped
+DF_DEV bool cache_slot(const EpiArgs& e, int b, int pos, int* page) {
+  const int pg = pos >> 6;
+  int p = -1;
+  if (b >= 0 && b < e.batch && pos >= 0 && pg < e.max_pages) p = e.block_table[(size_t)b * e.max_pages + pg];
+  if (p < 0 || p >= e.num_pages) {
+    flag_error(e.err, DEVERR_PAGE);
+    return false;
+  }
+  *page = p;
+  return true;
+}
+
+// (v0, v1) = acc[row][col], acc[row][col + 1] with col even.
+template <typename T, int KIND>
+DF_DEV void epi_pair(const EpiArgs& e, int row, int col, float v0, float v1) {
+  switch (KIND) {
+    case EPI_SWIGLU: {
+      ((T*)e.act)[(size_t)row * e.F + (col >> 1)] = from_f<T>(v0 / (1.f + expf(-v0)) * v1);
+      break;
+    }
+    case EPI_QKV: {
+      const int b = row / e.B, j = row - (row / e.B) * e.B;
+      const int pos = e.seq_len[b] + j;
+      const int hd = e.hd, head = col / hd, el = col - head * hd;
+      int page = -1;
+      const bool cache = e.has_cache && head >= e.Hq && cache_slot(e, b, pos, &page);
+      const int slot = pos & 63;
+      if (head < e.Hq + e.Hkv) {
+        const int i = el >> 1;
+        const float2 cs = e.rope[(size_t)row * (hd >> 1) + i];
+        const float y1 = v0 * cs.x - v1 * cs.y, y2 = v1 * cs.x + v0 * cs.y;
+        T* dst;
+        if (head < e.Hq) {
+          dst = (T*)e.q + (size_t)row * e.Hq * hd + (size_t)head * hd;
+        } else {
+          const int kh = head - e.Hq;
+          dst = (T*)e.kblk + (size_t)row * e.Hkv * hd + (size_t)kh * hd;
+          if (cache) {
+            T* kc = (T*)e.kp[0] + (((size_t)page * e.Hkv + kh) * 64 + slot) * hd;
+            kc[i] = from_f<T>(y1);
+            kc[i + hd / 2] = from_f<T>(y2);
+          }
+        }
+        dst[i] = from_f<T>(y1);
+        dst[i + hd / 2] = from_f<T>(y2);
+      } else {
+        const int vh = head - e.Hq - e.Hkv;
+        T* vt = (T*)e.vblkT + ((size_t)(b * e.Hkv + vh) * hd + el) * e.Bp + j;
+        vt[0] = from_f<T>(v0);
+        vt[e.Bp] = from_f<T>(v1);
+        if (cache) {
+          T* vc = (T*)e.vp[0] + (((size_t)page * e.Hkv + vh) * hd + el) * 64 + slot;
+          vc[0] = from_f<T>(v0);
+          vc[64] = from_f<T>(v1);
+        }
+      }
+      break;
+    }
+    case EPI_INJECT_KV: {
+      const int b = e.row_seq[row];
+      const int pos = e.row_pos[row] + ((e.pos_relative && b >= 0 && b < e.batch) ? e.seq_len[b] : 0);
+      int page;
+      if (!cache_slot(e, b, pos, &page)) break;
+      const int slot = pos & 63, hd = e.hd;
+      const int per_layer = 2 * e.Hkv * hd;
+      const int l = col / per_layer, c = col - l * per_layer;
+      if (c < e.Hkv * hd) {
+        const int kh = c / hd, el = c - kh * hd, i = el >> 1;
+        const float2 cs = e.rope[(size_t)row * (hd >> 1) + i];
+        T* kc = (T*)e.kp[l] + (((size_t)page * e.Hkv + kh) * 64 + slot) * hd;
+        kc[i] = from_f<T>(v0 * cs.x - v1 * cs.y);
+        kc[i + hd / 2] = from_f<T>(v1 * cs.x + v0 * cs.y);
+      } else {
+        const int cv = c - e.Hkv * hd, vh = cv / hd, el = cv - vh * hd;
+        T* vc = (T*)e.vp[l] + (((size_t)page * e.Hkv + vh) * hd + el) * 64 + slot;
+        vc[0] = from_f<T>(v0);
+        vc[64] = from_f<T>(v1);
+      }
+      break;
+    }
+    default:
+      break;
+  }
+}
+
+__host__ __device__ constexpr bool epi_is_pair(int kind) {
+  return kind == EPI_SWIGLU || kind == EPI_QKV || kind == EPI_INJECT_KV;
+}
+
+}  // namespace dflash

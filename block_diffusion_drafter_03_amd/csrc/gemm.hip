@@ -1,216 +1,546 @@
-// GEMM kernels: C[s][M][N] = A[M, K] x W^T with W [N, K] row-major (y = x W^T).
+// GEMM kernels with fused epilogues: acc[m][n] = sum_k A[m][k] W[n][k] (y = x W^T, W row-major
+// [N, K]), optional A-side RMSNorm, then one of the epilogues of epilogue.h.
 //
 //  * gemm_skinny_bf16  (M <= 32): the weight-streaming shape of a drafter step at small
-//    batch.  Each workgroup owns 16 output columns at a time and its waves split K; every
-//    lane streams 16-byte slices of W rows straight into MFMA B fragments (no LDS), the
-//    16x16 partial tiles of the waves are summed through LDS.  W is read exactly once.
-//  * gemm_tiled_bf16   (M > 32): LDS-staged 128x128 tiles, 2x2 waves of 64x64, BK = 64,
-//    global loads for the next K tile in flight while MFMAs consume the current one;
-//    optional split-K into separate partial planes (summed by the consumer).
+//    batch.  A workgroup owns 16 output columns at a time and its 4 waves split K; each
+//    lane streams 16-byte slices of W rows straight into MFMA B fragments (no LDS), and the
+//    waves' 16x16 partial tiles are summed through LDS.  W is read exactly once.
+//  * gemm_tiled_bf16   (M > 32): 64x64 output tiles, 2x2 waves of 32x32, BK = 64, A and W
+//    tiles staged through LDS with the next K tile's global loads in flight during the
+//    MFMAs; 1-D grid remapped so that the M tiles sharing a W column block run on the same
+//    XCD (one L2) back to back.
 //  * gemm_f32          (float32 models): VALU 64x64 tiles, BK = 16.
 //
-// MFMA used: v_mfma_f32_16x16x32_bf16.  Operand layout (lane l, r = l % 16, g = l / 16):
-// A fragment = A[r][8g .. 8g+7], B fragment = B[8g .. 8g+7][r] (i.e. W row r), and the
-// accumulator holds D[4g + i][r], i = 0..3.
-#include "common.h"
-#include "kernels.h"
+// MFMA: v_mfma_f32_16x16x32_bf16.  Lane l (r = l % 16, g = l / 16) supplies A[r][8g..8g+7]
+// and W row r's k-slice 8g..8g+7; the accumulator holds D[4g + i][r], i = 0..3.
+#include "epilogue.h"
 
 namespace dflash {
 
-struct BSegDev {
-  const bf16* ptr[8];
+template <typename T>
+struct BRows {
+  const T* ptr[8];
   int seg_rows, nseg, ldb;
-  DF_DEV const bf16* row(int n) const {
+  DF_DEV const T* row(int n) const {
     const int s = nseg > 1 ? n / seg_rows : 0;
     return ptr[s] + (size_t)(n - s * seg_rows) * ldb;
   }
 };
 
+template <typename T>
+static BRows<T> brows(const BSeg& b) {
+  BRows<T> o;
+  for (int i = 0; i < 8; ++i) o.ptr[i] = (const T*)b.ptr[i];
+  o.seg_rows = b.seg_rows;
+  o.nseg = b.nseg;
+  o.ldb = b.ldb;
+  return o;
+}
+
+// A row m of the GEMM -> row of the A buffer (skipping the anchor row of each block when
+// only the masked rows of the drafter feed the LM head).
+DF_DEV int a_row_index(int m, int skipB) { return skipB ? m + m / (skipB - 1) + 1 : m; }
+
+DF_DEV unsigned long long shfl_xor_u64(unsigned long long v, int mask) {
+  const unsigned lo = __shfl_xor((unsigned)(v & 0xFFFFFFFFull), mask, 64);
+  const unsigned hi = __shfl_xor((unsigned)(v >> 32), mask, 64);
+  return ((unsigned long long)hi << 32) | lo;
+}
+DF_DEV unsigned long long umax64(unsigned long long a, unsigned long long b) { return a > b ? a : b; }
+
+DF_DEV float sumsq8(const bf16x8& v) {
+  float s = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float x = (float)v[e];
+    s += x * x;
+  }
+  return s;
+}
+DF_DEV bf16x8 scale8(const bf16x8& v, const bf16x8& g) {
+  bf16x8 o;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = (bf16)((float)v[e] * (float)g[e]);
+  return o;
+}
+
+// Epilogue of one 16x16 MFMA tile held in the accumulator layout: v[i] = acc[row0+4g+i][col].
+// Pair epilogues are taken by even lanes (their odd neighbour holds column col + 1).
+template <typename T, int KIND>
+DF_DEV void tile_epilogue(const GemmArgs& ga, int row0, int col, const float v[4], int r,
+                          unsigned long long best[4]) {
+  const EpiArgs& e = ga.e;
+  const int M = ga.M, N = ga.N;
+  if constexpr (KIND == EPI_ARGMAX) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = row0 + i;
+      const bool ok = row < M && col < N;
+      if (ok && e.logits) e.logits[(size_t)row * N + col] = v[i];
+      unsigned long long k = ok ? pack_argmax_key(v[i], col) : 0ull;
+      k = umax64(k, shfl_xor_u64(k, 1));
+      k = umax64(k, shfl_xor_u64(k, 2));
+      k = umax64(k, shfl_xor_u64(k, 4));
+      k = umax64(k, shfl_xor_u64(k, 8));
+      best[i] = umax64(best[i], k);
+    }
+  } else if constexpr (epi_is_pair(KIND)) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float v1 = __shfl_xor(v[i], 1, 64);
+      const int row = row0 + i;
+      if (!(r & 1) && row < M && col + 1 < N) epi_pair<T, KIND>(e, row, col, v[i], v1);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = row0 + i;
+      if (row < M && col < N) epi_elem<T, KIND>(e, row, col, v[i]);
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------------------
-template <int MT, int NW, int U>
-__global__ __launch_bounds__(NW * 64) void gemm_skinny_bf16(const bf16* __restrict__ A, int lda,
-                                                            BSegDev B, float* __restrict__ C,
-                                                            int M, int N, int K) {
+// 16 < M <= 32: 4 waves split K; A and W fragments are both loaded per 32-wide K step.
+template <int MT, int NW, int U, bool NORM, int KIND>
+__global__ __launch_bounds__(NW * 64) void gemm_skinny_bf16(GemmArgs ga) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int r = lane & 15, g = lane >> 4;
+  const int M = ga.M, N = ga.N, K = ga.K;
   const int KS = K >> 5;
   const int ks0 = (w * KS) / NW, ks1 = ((w + 1) * KS) / NW;
   const int n_tiles = (N + 15) >> 4;
   __shared__ f32x4 red[NW][MT][64];
+  __shared__ float ss_red[NW][MT * 16];
+  __shared__ float rstd[MT * 16];
+  const BRows<bf16> Bd = *reinterpret_cast<const BRows<bf16>*>(&ga.B);
 
   const bf16* arow[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     const int m = min(mt * 16 + r, M - 1);
-    arow[mt] = A + (size_t)m * lda + g * 8;
+    arow[mt] = (const bf16*)ga.A + (size_t)a_row_index(m, ga.a_skip_B) * ga.lda + g * 8;
   }
+  const bf16* gk = NORM ? (const bf16*)ga.norm_g + g * 8 : nullptr;
+  unsigned long long best[4] = {0ull, 0ull, 0ull, 0ull};
+  bool first = true;
 
   for (int t = blockIdx.x; t < n_tiles; t += gridDim.x) {
     const int n = min(t * 16 + r, N - 1);
-    const bf16* wrow = B.row(n) + g * 8;
+    const bf16* wrow = Bd.row(n) + g * 8;
     f32x4 acc[MT];
+    float ss[MT];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    int ks = ks0;
-    for (; ks + U <= ks1; ks += U) {
+    for (int mt = 0; mt < MT; ++mt) {
+      acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      ss[mt] = 0.f;
+    }
+    for (int ks = ks0; ks < ks1; ks += U) {
       bf16x8 wf[U];
       bf16x8 af[U][MT];
 #pragma unroll
-      for (int u = 0; u < U; ++u) wf[u] = *(const bf16x8*)(wrow + (size_t)(ks + u) * 32);
+      for (int u = 0; u < U; ++u) {
+        const int k = min(ks + u, ks1 - 1);
+        wf[u] = *(const bf16x8*)(wrow + (size_t)k * 32);
 #pragma unroll
-      for (int u = 0; u < U; ++u)
+        for (int mt = 0; mt < MT; ++mt) af[u][mt] = *(const bf16x8*)(arow[mt] + (size_t)k * 32);
+      }
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) af[u][mt] = *(const bf16x8*)(arow[mt] + (size_t)(ks + u) * 32);
+      for (int u = 0; u < U; ++u) {
+        if (ks + u >= ks1) break;
+        bf16x8 gv;
+        if (NORM) gv = *(const bf16x8*)(gk + (size_t)(ks + u) * 32);
 #pragma unroll
-      for (int u = 0; u < U; ++u)
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
+        for (int mt = 0; mt < MT; ++mt) {
+          if (NORM) {
+            if (first) ss[mt] += sumsq8(af[u][mt]);
+            af[u][mt] = scale8(af[u][mt], gv);
+          }
           acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[u][mt], wf[u], acc[mt], 0, 0, 0);
-    }
-    for (; ks < ks1; ++ks) {
-      const bf16x8 wf = *(const bf16x8*)(wrow + (size_t)ks * 32);
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const bf16x8 af = *(const bf16x8*)(arow[mt] + (size_t)ks * 32);
-        acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, wf, acc[mt], 0, 0, 0);
+        }
       }
     }
-
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) red[w][mt][lane] = acc[mt];
+    if (NORM && first) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        float s = ss[mt] + __shfl_xor(ss[mt], 16, 64);
+        s += __shfl_xor(s, 32, 64);
+        if (g == 0) ss_red[w][mt * 16 + r] = s;
+      }
+    }
     __syncthreads();
+    if (NORM && first) {
+      if (threadIdx.x < MT * 16) {
+        float s = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < NW; ++ww) s += ss_red[ww][threadIdx.x];
+        rstd[threadIdx.x] = 1.0f / sqrtf(s / (float)K + ga.eps);
+      }
+      __syncthreads();
+    }
+    first = false;
     if (w < MT) {
       const int mt = w;
       f32x4 s = red[0][mt][lane];
 #pragma unroll
       for (int ww = 1; ww < NW; ++ww) s += red[ww][mt][lane];
-      const int col = t * 16 + r;
-      if (col < N) {
+      float v[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int row = mt * 16 + g * 4 + i;
-          if (row < M) C[(size_t)row * N + col] = s[i];
-        }
-      }
+      for (int i = 0; i < 4; ++i) v[i] = NORM ? s[i] * rstd[mt * 16 + g * 4 + i] : s[i];
+      tile_epilogue<bf16, KIND>(ga, mt * 16 + g * 4, t * 16 + r, v, r, best);
     }
     __syncthreads();
   }
+  if (KIND == EPI_ARGMAX && w < MT && r == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = w * 16 + g * 4 + i;
+      if (row < M && best[i]) atomicMax(&ga.e.keys[row], best[i]);
+    }
+  }
+}
+
+// M <= 16: 16 waves (1024 threads) split K, one 32-wide step per MFMA.  With ASTAT each
+// wave keeps its K-slice of the A rows in registers for all of the workgroup's tiles,
+// already multiplied by the RMSNorm gain (rstd is applied in the epilogue), so the vector
+// memory path carries only W: a wave issues all of its W loads of a tile at once (<= 8
+// steps, 8 KB) and 16 waves per CU keep >= 128 KB in flight.  Without ASTAT (K/16 > 256)
+// A and W are streamed together in chunks of 8 steps.
+#define GEMV_MAX_TILES 8   // tiles per workgroup whose epilogue is deferred (non-argmax kinds)
+
+template <bool NORM, bool ASTAT, int KIND>
+__global__ __launch_bounds__(1024) void gemm_gemv16_bf16(GemmArgs ga) {
+  constexpr int NW = 16, CH = 8;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int r = lane & 15, g = lane >> 4;
+  const int M = ga.M, N = ga.N, K = ga.K;
+  const int spw = (K >> 5) / NW;                 // K % 512 == 0
+  const int ks0 = w * spw;
+  const int n_tiles = (N + 15) >> 4;
+  __shared__ f32x4 red[NW][64];
+  __shared__ f32x4 done[GEMV_MAX_TILES][64];
+  __shared__ float ss_red[NW][16];
+  __shared__ float rstd[16];
+  const BRows<bf16> Bd = *reinterpret_cast<const BRows<bf16>*>(&ga.B);
+  const bf16* arow = (const bf16*)ga.A + (size_t)a_row_index(min(r, M - 1), ga.a_skip_B) * ga.lda + g * 8;
+  unsigned long long best[4] = {0ull, 0ull, 0ull, 0ull};
+  int nbuf = 0;
+
+  bf16x8 a[CH];
+  // W loads of this workgroup's first tile go out before the A prologue (independent)
+  bf16x8 wn[CH];
+  auto load_w = [&](int t) {
+    const bf16* wrow = Bd.row(min(t * 16 + r, N - 1)) + g * 8;
+#pragma unroll
+    for (int s = 0; s < CH; ++s)
+      if (s < spw) wn[s] = *(const bf16x8*)(wrow + (size_t)(ks0 + s) * 32);
+  };
+  if (ASTAT && blockIdx.x < n_tiles) load_w(blockIdx.x);
+  if (ASTAT) {
+    float ss = 0.f;
+#pragma unroll
+    for (int s = 0; s < CH; ++s) {
+      if (s < spw) {
+        a[s] = *(const bf16x8*)(arow + (size_t)(ks0 + s) * 32);
+        if (NORM) {
+          ss += sumsq8(a[s]);
+          a[s] = scale8(a[s], *(const bf16x8*)((const bf16*)ga.norm_g + (size_t)(ks0 + s) * 32 + g * 8));
+        }
+      }
+    }
+    if (NORM) {
+      ss += __shfl_xor(ss, 16, 64);
+      ss += __shfl_xor(ss, 32, 64);
+      if (g == 0) ss_red[w][r] = ss;
+      __syncthreads();
+      if (threadIdx.x < 16) {
+        float s = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < NW; ++ww) s += ss_red[ww][threadIdx.x];
+        rstd[threadIdx.x] = 1.0f / sqrtf(s / (float)K + ga.eps);
+      }
+      __syncthreads();
+    }
+  }
+
+  for (int t = blockIdx.x; t < n_tiles; t += gridDim.x) {
+    const bf16* wrow = Bd.row(min(t * 16 + r, N - 1)) + g * 8;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    if (ASTAT) {
+#pragma unroll
+      for (int s = 0; s < CH; ++s)
+        if (s < spw) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s], wn[s], acc, 0, 0, 0);
+      // the next tile's W loads are in flight across the barrier and the reduction
+      if (t + gridDim.x < n_tiles) load_w(t + gridDim.x);
+    } else {
+      for (int c0 = 0; c0 < spw; c0 += CH) {
+        bf16x8 wf[CH];
+#pragma unroll
+        for (int s = 0; s < CH; ++s) {
+          const int k = ks0 + min(c0 + s, spw - 1);
+          wf[s] = *(const bf16x8*)(wrow + (size_t)k * 32);
+          a[s] = *(const bf16x8*)(arow + (size_t)k * 32);
+        }
+#pragma unroll
+        for (int s = 0; s < CH; ++s)
+          if (c0 + s < spw) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s], wf[s], acc, 0, 0, 0);
+      }
+    }
+    red[w][lane] = acc;
+    __syncthreads();
+    if (w == 0) {
+      f32x4 s = red[0][lane];
+#pragma unroll
+      for (int ww = 1; ww < NW; ++ww) s += red[ww][lane];
+      if constexpr (KIND == EPI_ARGMAX) {
+        float v[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = NORM ? s[i] * rstd[g * 4 + i] : s[i];
+        tile_epilogue<bf16, KIND>(ga, g * 4, t * 16 + r, v, r, best);
+      } else {
+        done[nbuf][lane] = s;   // epilogue deferred until the A registers are dead
+      }
+    }
+    ++nbuf;
+    __syncthreads();
+  }
+  if constexpr (KIND != EPI_ARGMAX) {
+    // every wave takes buffered tiles: the epilogues run in parallel, off the main loop's
+    // register budget
+    for (int i = w; i < nbuf; i += NW) {
+      const f32x4 s = done[i][lane];
+      float v[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = NORM ? s[e] * rstd[g * 4 + e] : s[e];
+      tile_epilogue<bf16, KIND>(ga, g * 4, (blockIdx.x + i * gridDim.x) * 16 + r, v, r, best);
+    }
+  }
+  if (KIND == EPI_ARGMAX && w == 0 && r == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = g * 4 + i;
+      if (row < M && best[i]) atomicMax(&ga.e.keys[row], best[i]);
+    }
+  }
+}
+
+// M <= 16, many output tiles: every wave owns whole 16-column tiles over the full K, so
+// waves never wait for one another after the prologue (which computes the rows' rstd, the
+// 4 waves splitting K).  Per batch of 8 K steps a lane issues 8 W and 8 A loads (A hits
+// L1/L2: every wave reads the same 16 rows), then 8 MFMAs; the tile's epilogue runs in the
+// owning wave.
+template <bool NORM, int KIND>
+__global__ __launch_bounds__(256) void gemm_wave_bf16(GemmArgs ga) {
+  constexpr int U = 8;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int r = lane & 15, g = lane >> 4;
+  const int M = ga.M, N = ga.N, K = ga.K;
+  const int KS = K >> 5;
+  const int n_tiles = (N + 15) >> 4;
+  __shared__ float ss_red[4][16];
+  __shared__ float rstd[16];
+  const BRows<bf16> Bd = *reinterpret_cast<const BRows<bf16>*>(&ga.B);
+  const bf16* arow = (const bf16*)ga.A + (size_t)a_row_index(min(r, M - 1), ga.a_skip_B) * ga.lda + g * 8;
+  const bf16* gk = NORM ? (const bf16*)ga.norm_g + g * 8 : nullptr;
+  if (NORM) {
+    float ss = 0.f;
+    for (int ks = w; ks < KS; ks += 4) ss += sumsq8(*(const bf16x8*)(arow + (size_t)ks * 32));
+    ss += __shfl_xor(ss, 16, 64);
+    ss += __shfl_xor(ss, 32, 64);
+    if (g == 0) ss_red[w][r] = ss;
+    __syncthreads();
+    if (threadIdx.x < 16)
+      rstd[threadIdx.x] = 1.0f / sqrtf((ss_red[0][threadIdx.x] + ss_red[1][threadIdx.x] +
+                                        ss_red[2][threadIdx.x] + ss_red[3][threadIdx.x]) / (float)K + ga.eps);
+    __syncthreads();
+  }
+  unsigned long long best[4] = {0ull, 0ull, 0ull, 0ull};
+  for (int t = blockIdx.x * 4 + w; t < n_tiles; t += gridDim.x * 4) {
+    const bf16* wrow = Bd.row(min(t * 16 + r, N - 1)) + g * 8;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int ks = 0; ks < KS; ks += U) {
+      bf16x8 wf[U], af[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int k = min(ks + u, KS - 1);
+        wf[u] = *(const bf16x8*)(wrow + (size_t)k * 32);
+        af[u] = *(const bf16x8*)(arow + (size_t)k * 32);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (ks + u >= KS) break;
+        bf16x8 a = af[u];
+        if (NORM) a = scale8(a, *(const bf16x8*)(gk + (size_t)(ks + u) * 32));
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, wf[u], acc, 0, 0, 0);
+      }
+    }
+    float v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = NORM ? acc[i] * rstd[g * 4 + i] : acc[i];
+    tile_epilogue<bf16, KIND>(ga, g * 4, t * 16 + r, v, r, best);
+  }
+  if (KIND == EPI_ARGMAX && r == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = g * 4 + i;
+      if (row < M && best[i]) atomicMax(&ga.e.keys[row], best[i]);
+    }
+  }
+}
+
+// Variant selection for M <= 16 (benchmark sweeps may force one with DFLASH_GEMV=1..3):
+// 1 = 4-wave split-K, 2 = 16-wave split-K with stationary A, 3 = wave-owned tiles.
+static int gemv_variant() {
+  static int v = -1;
+  if (v < 0) {
+    const char* s = getenv("DFLASH_GEMV");
+    v = s && *s ? atoi(s) : 0;
+  }
+  return v;
 }
 
 // ---------------------------------------------------------------------------------------
-// 128 x 128 x 64 tiles, 256 threads (waves 2 x 2, 64 x 64 each).
-#define TBM 128
-#define TBN 128
-#define TBK 64
+#define TB 64
+#define TK 64
 #define TPAD 8
 
-__global__ __launch_bounds__(256) void gemm_tiled_bf16(const bf16* __restrict__ A, int lda,
-                                                       BSegDev B, float* __restrict__ C, int M,
-                                                       int N, int K, int k_per_split) {
-  __shared__ bf16 As[TBM][TBK + TPAD];
-  __shared__ bf16 Bs[TBN][TBK + TPAD];
+template <bool NORM, int KIND>
+__global__ __launch_bounds__(256) void gemm_tiled_bf16(GemmArgs ga) {
+  __shared__ __attribute__((aligned(16))) bf16 As[TB][TK + TPAD];
+  __shared__ __attribute__((aligned(16))) bf16 Bs[TB][TK + TPAD];
+  __shared__ float rstd_s[TB];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int r = lane & 15, g = lane >> 4;
   const int wm = w >> 1, wn = w & 1;
-  const int n0 = blockIdx.x * TBN, m0 = blockIdx.y * TBM;
-  const int s = blockIdx.z;
-  const int kbeg = s * k_per_split, kend = min(K, kbeg + k_per_split);
+  const int M = ga.M, N = ga.N, K = ga.K;
+  const int mt_n = (M + TB - 1) / TB, nt_n = (N + TB - 1) / TB;
+  const int T = mt_n * nt_n;
+  // tiles ordered M-fastest; give each XCD (WG id mod 8) a contiguous run of tiles so the
+  // M tiles that read the same W columns share an L2
+  int t = blockIdx.x;
+  if ((T & 7) == 0) t = (blockIdx.x & 7) * (T >> 3) + (blockIdx.x >> 3);
+  const int m0 = (t % mt_n) * TB, n0 = (t / mt_n) * TB;
+  const BRows<bf16> Bd = *reinterpret_cast<const BRows<bf16>*>(&ga.B);
 
-  // global -> register staging: 4 x 16 B of A and of B per thread per K tile
-  const bf16* ap[4];
-  const bf16* bp[4];
-  int lrow[4], lcol[4];
+  const bf16* ap[2];
+  const bf16* bp[2];
+  int lrow[2], lcol[2];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < 2; ++j) {
     const int c = tid + 256 * j;
     lrow[j] = c >> 3;
     lcol[j] = (c & 7) * 8;
-    ap[j] = A + (size_t)min(m0 + lrow[j], M - 1) * lda + lcol[j];
-    bp[j] = B.row(min(n0 + lrow[j], N - 1)) + lcol[j];
+    ap[j] = (const bf16*)ga.A + (size_t)a_row_index(min(m0 + lrow[j], M - 1), ga.a_skip_B) * ga.lda + lcol[j];
+    bp[j] = Bd.row(min(n0 + lrow[j], N - 1)) + lcol[j];
   }
-  bf16x8 ra[4], rb[4];
+  const bf16* gk = NORM ? (const bf16*)ga.norm_g : nullptr;
+  bf16x8 ra[2], rb[2];
+  float ss[2] = {0.f, 0.f};
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    ra[j] = *(const bf16x8*)(ap[j] + kbeg);
-    rb[j] = *(const bf16x8*)(bp[j] + kbeg);
+  for (int j = 0; j < 2; ++j) {
+    ra[j] = *(const bf16x8*)(ap[j]);
+    rb[j] = *(const bf16x8*)(bp[j]);
   }
+  f32x4 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  f32x4 acc[4][4];
+  for (int k0 = 0; k0 < K; k0 += TK) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  for (int k0 = kbeg; k0 < kend; k0 += TBK) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < 2; ++j) {
+      if (NORM) {
+        ss[j] += sumsq8(ra[j]);
+        ra[j] = scale8(ra[j], *(const bf16x8*)(gk + k0 + lcol[j]));
+      }
       *(bf16x8*)&As[lrow[j]][lcol[j]] = ra[j];
       *(bf16x8*)&Bs[lrow[j]][lcol[j]] = rb[j];
     }
     __syncthreads();
-    if (k0 + TBK < kend) {
+    if (k0 + TK < K) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        ra[j] = *(const bf16x8*)(ap[j] + k0 + TBK);
-        rb[j] = *(const bf16x8*)(bp[j] + k0 + TBK);
+      for (int j = 0; j < 2; ++j) {
+        ra[j] = *(const bf16x8*)(ap[j] + k0 + TK);
+        rb[j] = *(const bf16x8*)(bp[j] + k0 + TK);
       }
     }
 #pragma unroll
-    for (int kk = 0; kk < TBK; kk += 32) {
-      bf16x8 af[4], bfr[4];
+    for (int kk = 0; kk < TK; kk += 32) {
+      bf16x8 af[2], bfr[2];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) af[i] = *(const bf16x8*)&As[wm * 64 + i * 16 + r][kk + g * 8];
+      for (int i = 0; i < 2; ++i) af[i] = *(const bf16x8*)&As[wm * 32 + i * 16 + r][kk + g * 8];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) bfr[j] = *(const bf16x8*)&Bs[wn * 64 + j * 16 + r][kk + g * 8];
+      for (int j = 0; j < 2; ++j) bfr[j] = *(const bf16x8*)&Bs[wn * 32 + j * 16 + r][kk + g * 8];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 2; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
     }
     __syncthreads();
   }
-
-  float* Cs = C + (size_t)s * M * N;
+  if (NORM) {
+    // the 8 threads loading one A row are consecutive lanes
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+    for (int j = 0; j < 2; ++j) {
+      float s = ss[j];
+      s += __shfl_xor(s, 1, 64);
+      s += __shfl_xor(s, 2, 64);
+      s += __shfl_xor(s, 4, 64);
+      if ((tid & 7) == 0) rstd_s[lrow[j]] = 1.0f / sqrtf(s / (float)K + ga.eps);
+    }
+    __syncthreads();
+  }
+  unsigned long long best[2][4] = {{0ull, 0ull, 0ull, 0ull}, {0ull, 0ull, 0ull, 0ull}};
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int col = n0 + wn * 64 + j * 16 + r;
-      if (col >= N) continue;
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int lr0 = wm * 32 + i * 16 + g * 4;
+      float v[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = NORM ? acc[i][j][e] * rstd_s[lr0 + e] : acc[i][j][e];
+      tile_epilogue<bf16, KIND>(ga, m0 + lr0, n0 + wn * 32 + j * 16 + r, v, r, best[i]);
+    }
+  if (KIND == EPI_ARGMAX && r == 0) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int row = m0 + wm * 64 + i * 16 + g * 4 + e;
-        if (row < M) Cs[(size_t)row * N + col] = acc[i][j][e];
+        const int row = m0 + wm * 32 + i * 16 + g * 4 + e;
+        if (row < M && best[i][e]) atomicMax(&ga.e.keys[row], best[i][e]);
       }
-    }
+  }
 }
 
 // ---------------------------------------------------------------------------------------
-struct BSegF32 {
-  const float* ptr[8];
-  int seg_rows, nseg, ldb;
-  DF_DEV const float* row(int n) const {
-    const int s = nseg > 1 ? n / seg_rows : 0;
-    return ptr[s] + (size_t)(n - s * seg_rows) * ldb;
-  }
-};
-
-__global__ __launch_bounds__(256) void gemm_f32(const float* __restrict__ A, int lda, BSegF32 B,
-                                                float* __restrict__ C, int M, int N, int K) {
+template <bool NORM, int KIND>
+__global__ __launch_bounds__(256) void gemm_f32(GemmArgs ga) {
   __shared__ float As[16][64 + 4];
   __shared__ float Bs[16][64 + 4];
+  __shared__ float rstd_s[64];
   const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+  const int M = ga.M, N = ga.N, K = ga.K;
   const int m0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
+  const BRows<float> Bd = *reinterpret_cast<const BRows<float>*>(&ga.B);
   float acc[4][4] = {};
   const int lr = tid >> 2, lk = (tid & 3) * 4;
-  const float* ap = A + (size_t)min(m0 + lr, M - 1) * lda + lk;
-  const float* bp = B.row(min(n0 + lr, N - 1)) + lk;
+  const float* ap = (const float*)ga.A + (size_t)a_row_index(min(m0 + lr, M - 1), ga.a_skip_B) * ga.lda + lk;
+  const float* bp = Bd.row(min(n0 + lr, N - 1)) + lk;
+  const float* gk = NORM ? (const float*)ga.norm_g + lk : nullptr;
+  float ss = 0.f;
   for (int k0 = 0; k0 < K; k0 += 16) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      As[lk + e][lr] = ap[k0 + e];
+      float a = ap[k0 + e];
+      if (NORM) {
+        ss += a * a;
+        a *= gk[k0 + e];
+      }
+      As[lk + e][lr] = a;
       Bs[lk + e][lr] = bp[k0 + e];
     }
     __syncthreads();
@@ -228,14 +558,44 @@ __global__ __launch_bounds__(256) void gemm_f32(const float* __restrict__ A, int
     }
     __syncthreads();
   }
+  if (NORM) {
+    ss += __shfl_xor(ss, 1, 64);
+    ss += __shfl_xor(ss, 2, 64);
+    if ((tid & 3) == 0) rstd_s[lr] = 1.0f / sqrtf(ss / (float)K + ga.eps);
+    __syncthreads();
+  }
+  const EpiArgs& e = ga.e;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int row = m0 + ty * 4 + i;
-    if (row >= M) continue;
+    const float sc = NORM ? rstd_s[ty * 4 + i] : 1.f;
+    float v[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int col = n0 + tx * 4 + j;
-      if (col < N) C[(size_t)row * N + col] = acc[i][j];
+    for (int j = 0; j < 4; ++j) v[j] = acc[i][j] * sc;
+    const int col0 = n0 + tx * 4;
+    if constexpr (KIND == EPI_ARGMAX) {
+      unsigned long long k = 0ull;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (row < M && col0 + j < N) {
+          if (e.logits) e.logits[(size_t)row * N + col0 + j] = v[j];
+          k = umax64(k, pack_argmax_key(v[j], col0 + j));
+        }
+      k = umax64(k, shfl_xor_u64(k, 1));
+      k = umax64(k, shfl_xor_u64(k, 2));
+      k = umax64(k, shfl_xor_u64(k, 4));
+      k = umax64(k, shfl_xor_u64(k, 8));
+      if (tx == 0 && row < M && k) atomicMax(&e.keys[row], k);
+    } else if (row < M) {
+      if constexpr (epi_is_pair(KIND)) {
+#pragma unroll
+        for (int j = 0; j < 4; j += 2)
+          if (col0 + j + 1 < N) epi_pair<float, KIND>(e, row, col0 + j, v[j], v[j + 1]);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (col0 + j < N) epi_elem<float, KIND>(e, row, col0 + j, v[j]);
+      }
     }
   }
 }
@@ -255,49 +615,68 @@ static int num_cus() {
   return g_num_cus;
 }
 
-int gemm_splits(int dt, int M, int N, int K) {
-  if (dt != BF16 || M <= 32) return 1;
-  const int tiles = ((M + TBM - 1) / TBM) * ((N + TBN - 1) / TBN);
-  int s = 1;
-  // split K until the grid covers the chip twice, keeping >= 512 of K per split
-  while (tiles * s < 512 && s < 4 && (K / (s * 2)) % TBK == 0 && K / (s * 2) >= 512) s *= 2;
-  return s;
-}
-
-hipError_t launch_gemm(int dt, const void* A, int lda, const BSeg& B, float* C, int M, int N,
-                       int K, int splits, hipStream_t st) {
-  if (M <= 0 || N <= 0) return hipSuccess;
+template <bool NORM, int KIND>
+static hipError_t launch_kind(int dt, const GemmArgs& ga, hipStream_t st) {
+  const int M = ga.M, N = ga.N;
   if (dt == F32) {
-    BSegF32 b;
-    for (int i = 0; i < 8; ++i) b.ptr[i] = (const float*)B.ptr[i];
-    b.seg_rows = B.seg_rows;
-    b.nseg = B.nseg;
-    b.ldb = B.ldb;
     dim3 grid((N + 63) / 64, (M + 63) / 64);
-    hipLaunchKernelGGL(gemm_f32, grid, dim3(256), 0, st, (const float*)A, lda, b, C, M, N, K);
+    hipLaunchKernelGGL((gemm_f32<NORM, KIND>), grid, dim3(256), 0, st, ga);
     return hipGetLastError();
   }
-  BSegDev b;
-  for (int i = 0; i < 8; ++i) b.ptr[i] = (const bf16*)B.ptr[i];
-  b.seg_rows = B.seg_rows;
-  b.nseg = B.nseg;
-  b.ldb = B.ldb;
+  if (M <= 16) {
+    const int n_tiles = (N + 15) / 16;
+    int v = gemv_variant();
+    if (v == 2 && (ga.K % 512 != 0 || (NORM && ga.K > 4096))) v = 1;
+    // measured on MI355X at hidden 4096: the 16-wave stationary-A kernel wins for wide
+    // outputs (gate/up, LM head) and long K (down projection); the 4-wave kernel for QKV
+    if (v < 1 || v > 3) v = (n_tiles >= 4 * num_cus() || ga.K > 4096) ? 2 : 1;
+    if (v == 3) {
+      int grid = (n_tiles + 3) / 4;
+      if (grid > 4 * num_cus()) grid = 4 * num_cus();
+      hipLaunchKernelGGL((gemm_wave_bf16<NORM, KIND>), dim3(grid), dim3(256), 0, st, ga);
+    } else if (v == 2) {
+      int grid = n_tiles < 2 * num_cus() ? n_tiles : 2 * num_cus();
+      if (KIND != EPI_ARGMAX && grid * GEMV_MAX_TILES < n_tiles)
+        grid = (n_tiles + GEMV_MAX_TILES - 1) / GEMV_MAX_TILES;
+      if (ga.K <= 4096)
+        hipLaunchKernelGGL((gemm_gemv16_bf16<NORM, true, KIND>), dim3(grid), dim3(1024), 0, st, ga);
+      else
+        hipLaunchKernelGGL((gemm_gemv16_bf16<false, false, KIND>), dim3(grid), dim3(1024), 0, st, ga);
+    } else {
+      const int grid = n_tiles < 8 * num_cus() ? n_tiles : 8 * num_cus();
+      hipLaunchKernelGGL((gemm_skinny_bf16<1, 4, 8, NORM, KIND>), dim3(grid), dim3(256), 0, st, ga);
+    }
+    return hipGetLastError();
+  }
   if (M <= 32) {
     const int n_tiles = (N + 15) / 16;
     const int grid = n_tiles < 8 * num_cus() ? n_tiles : 8 * num_cus();
     if (M <= 16)
-      hipLaunchKernelGGL((gemm_skinny_bf16<1, 4, 8>), dim3(grid), dim3(256), 0, st,
-                         (const bf16*)A, lda, b, C, M, N, K);
+      hipLaunchKernelGGL((gemm_skinny_bf16<1, 4, 8, NORM, KIND>), dim3(grid), dim3(256), 0, st, ga);
     else
-      hipLaunchKernelGGL((gemm_skinny_bf16<2, 4, 8>), dim3(grid), dim3(256), 0, st,
-                         (const bf16*)A, lda, b, C, M, N, K);
+      hipLaunchKernelGGL((gemm_skinny_bf16<2, 4, 8, NORM, KIND>), dim3(grid), dim3(256), 0, st, ga);
     return hipGetLastError();
   }
-  const int kps = K / splits;
-  dim3 grid((N + TBN - 1) / TBN, (M + TBM - 1) / TBM, splits);
-  hipLaunchKernelGGL(gemm_tiled_bf16, grid, dim3(256), 0, st, (const bf16*)A, lda, b, C, M, N, K,
-                     kps);
+  const int tiles = ((M + TB - 1) / TB) * ((N + TB - 1) / TB);
+  hipLaunchKernelGGL((gemm_tiled_bf16<NORM, KIND>), dim3(tiles), dim3(256), 0, st, ga);
   return hipGetLastError();
+}
+
+hipError_t launch_gemm(int dt, const GemmArgs& ga, hipStream_t st) {
+  if (ga.M <= 0 || ga.N <= 0) return hipSuccess;
+  const bool norm = ga.norm_g != nullptr;
+  // the combinations the drafter / verifier use: normalised A feeds QKV, gate/up, LM head
+  // and the injection K/V projection; plain A feeds O, down and W_c
+  switch (ga.e.kind) {
+    case EPI_QKV: return norm ? launch_kind<true, EPI_QKV>(dt, ga, st) : launch_kind<false, EPI_QKV>(dt, ga, st);
+    case EPI_SWIGLU: return norm ? launch_kind<true, EPI_SWIGLU>(dt, ga, st) : launch_kind<false, EPI_SWIGLU>(dt, ga, st);
+    case EPI_ARGMAX: return norm ? launch_kind<true, EPI_ARGMAX>(dt, ga, st) : launch_kind<false, EPI_ARGMAX>(dt, ga, st);
+    case EPI_INJECT_KV: return norm ? launch_kind<true, EPI_INJECT_KV>(dt, ga, st) : launch_kind<false, EPI_INJECT_KV>(dt, ga, st);
+    case EPI_RESID: return norm ? launch_kind<true, EPI_RESID>(dt, ga, st) : launch_kind<false, EPI_RESID>(dt, ga, st);
+    case EPI_STORE_T: return norm ? launch_kind<true, EPI_STORE_T>(dt, ga, st) : launch_kind<false, EPI_STORE_T>(dt, ga, st);
+    case EPI_STORE_F32: return norm ? launch_kind<true, EPI_STORE_F32>(dt, ga, st) : launch_kind<false, EPI_STORE_F32>(dt, ga, st);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace dflash

@@ -10,8 +10,8 @@ namespace dflash {
 enum Dt { F32 = 0, BF16 = 1 };
 
 // B operand of a GEMM: rows of W [N, K] (row stride ldb elements), possibly split into
-// up to 8 equal row segments living at different addresses (one per draft layer when
-// the injection GEMM covers every layer's K/V projection in one launch).
+// up to 8 equal row segments at different addresses (the injection GEMM covers every
+// draft layer's K/V row block in one launch).
 struct BSeg {
   const void* ptr[8];
   int seg_rows;   // rows per segment (N when nseg == 1)
@@ -19,10 +19,67 @@ struct BSeg {
   int ldb;
 };
 
-// C[s][M][N] (float32; s < splits) = A[M, K] (row stride lda) x W^T.
-int gemm_splits(int dt, int M, int N, int K);
-hipError_t launch_gemm(int dt, const void* A, int lda, const BSeg& B, float* C, int M, int N,
-                       int K, int splits, hipStream_t st);
+enum EpiKind {
+  EPI_STORE_F32 = 0,  // out[row*ldo + col] = acc (float)
+  EPI_STORE_T,        // out[row*ldo + col] = acc (model dtype)
+  EPI_RESID,          // h += acc; hb = h (model dtype); optional hdbg / tap copies
+  EPI_QKV,            // RoPE q, k; write q, k_blk, v_blk^T (and the block K/V into a cache)
+  EPI_SWIGLU,         // act = SiLU(gate) * up
+  EPI_INJECT_KV,      // RoPE K, scatter K and V of every draft layer into the paged cache
+  EPI_ARGMAX          // per-row argmax (packed 64-bit atomic max); optional float logits
+};
+
+struct EpiArgs {
+  int kind;
+  // EPI_STORE_*
+  void* out;
+  int ldo;
+  // EPI_RESID
+  float* h;
+  void* hb;
+  int ldh;
+  float* hdbg;
+  void* tap;
+  int tap_ld, tap_col;
+  // EPI_QKV / EPI_INJECT_KV geometry
+  int B, Bp, Hq, Hkv, hd;
+  const float2* rope;       // [M, hd/2] (cos, sin) of each row's position
+  const int32_t* seq_len;
+  void* q;
+  void* kblk;
+  void* vblkT;
+  // paged cache: per-layer pools (EPI_QKV uses slot 0), block table, bounds
+  void* kp[8];
+  void* vp[8];
+  const int32_t* block_table;
+  int max_pages, num_pages, batch;
+  int32_t* err;
+  int has_cache;
+  // EPI_INJECT_KV rows
+  const int32_t* row_seq;
+  const int32_t* row_pos;
+  int pos_relative;
+  // EPI_SWIGLU
+  void* act;
+  int F;
+  // EPI_ARGMAX
+  unsigned long long* keys;
+  float* logits;   // optional [M, N] copy of the logits
+};
+
+struct GemmArgs {
+  const void* A;        // [M, K] model dtype
+  int lda;
+  int a_skip_B;         // 0: A row m is row m; else rows j == 0 of each B-row block are skipped
+  BSeg B;
+  int M, N, K;
+  const void* norm_g;   // A-side RMSNorm gain [K] (model dtype) or NULL
+  float eps;
+  EpiArgs e;
+};
+
+// acc = A x W^T over the full K, then the epilogue.
+hipError_t launch_gemm(int dt, const GemmArgs& g, hipStream_t st);
 
 // Paged-cache view of one layer.
 struct KvLayer {
@@ -30,7 +87,7 @@ struct KvLayer {
   void* v;                  // [num_pages, Hkv, d, 64]
   const int32_t* block_table;
   const int32_t* seq_len;
-  int max_pages, num_pages;
+  int max_pages, num_pages, batch;
   int32_t* err;
 };
 
@@ -43,62 +100,46 @@ AttnPlan attn_plan(int dt, int batch, int Hkv, int G, int B, int ctx_cap);
 size_t attn_partial_floats(const AttnPlan& p, int batch, int Hkv, int d);
 
 // o[M, Hq d] = softmax(q k^T / sqrt(d)) v over [context ; block] (causal inside the block
-// when `causal`), one query row per (sequence, block position, head).
+// when `causal`), one query row per (sequence, block position, head).  `part` holds the
+// per-split partials (attn_partial_floats floats).
 hipError_t launch_attention(int dt, const AttnPlan& p, const void* q, const void* kblk,
                             const void* vblkT, const KvLayer& kv, int batch, int B, int Bp,
                             int Hq, int Hkv, int d, int causal, float* part, void* o,
                             hipStream_t st);
 
-// ---- row / elementwise kernels (elementwise.hip) ----
-// h[r] = E[token(r)] (float32).  mode 0: token = j == 0 ? anchor[b] : mask_id; mode 1:
-// token = ids[r].  hdbg (if not NULL) receives a copy.
-hipError_t launch_embed(int dt, const int32_t* ids, const int32_t* anchor, int mode, int batch,
-                        int B, int mask_id, const void* E, int V, int D, float* h, float* hdbg,
-                        int32_t* err, hipStream_t st);
-
-struct RowFin {
-  const float* C;      // split partials [S][rows][N] (may be NULL: x = h)
-  int S;
-  size_t split_stride; // elements between splits
-  int N;               // row width (== D)
-  float* h;            // residual stream [rows, N] (NULL: x = sum of partials)
-  int add_resid;       // x = h + sum(C) (else x = sum(C))
-  int write_h;         // h = x
-  float* hdbg;         // copy of x [rows, N] or NULL
-  void* tap;           // tap output (model dtype) or NULL: tap[r * tap_ld + tap_col + c] = x
-  int tap_ld, tap_col;
-  const void* g;       // RMSNorm gain or NULL (no normalised output)
-  void* u;             // normalised output (model dtype)
-  int compact_B;       // 0: u row = r; else skip rows with r % B == 0 and write r - r/B - 1
-  float eps;
+// ---- row kernels (elementwise.hip) ----
+struct EmbedArgs {
+  const int32_t* ids;       // mode 1: drafts [batch, B-1]
+  const int32_t* anchor;    // [batch]
+  int mode, batch, B, mask_id;
+  const void* E;
+  int V, D;
+  float* h;
+  void* hb;
+  float* hdbg;
+  unsigned long long* keys;
+  int n_keys;
+  int32_t* err;
+  const int32_t* seq_len;   // rows sit at positions seq_len[b] + j
+  int hd;
+  double rope_base;
+  float2* rope;             // [batch*B, hd/2] out
 };
-hipError_t launch_row_finalize(int dt, const RowFin& f, int rows, hipStream_t st);
+// h[r] = E[token(r)] (float32) and hb[r] = the same row in the model dtype, r = b*B + j:
+// token = anchor[b] for j == 0, else mask_id (mode 0) or ids[b*(B-1) + j-1] (mode 1).
+// Also writes the rows' RoPE (cos, sin) table and zeroes the argmax keys.
+hipError_t launch_embed(int dt, const EmbedArgs& a, hipStream_t st);
 
-// q/k rotation + v transpose after the QKV projection.  Rows r = b*B + j at position
-// seq_len[b] + j.  When `cache` is set the block's K/V are also written into it.
-hipError_t launch_qkv_post(int dt, const float* C, int S, size_t split_stride, int batch, int B,
-                           int Bp, int Hq, int Hkv, int d, double rope_base,
-                           const int32_t* seq_len, void* q, void* kblk, void* vblkT,
-                           const KvLayer* cache, hipStream_t st);
+// RoPE (cos, sin) table of injection rows: position row_pos[r] (+ seq_len[row_seq[r]]).
+hipError_t launch_rope_rows(const int32_t* row_seq, const int32_t* row_pos, int pos_relative,
+                            const int32_t* seq_len, int batch, int rows, int hd, double base,
+                            float2* rope, hipStream_t st);
 
-// act[m, j] = SiLU(g) * u with g = C[m, j], u = C[m, F + j] (summed over splits).
-hipError_t launch_swiglu(int dt, const float* C, int S, size_t split_stride, int M, int F,
-                         void* act, hipStream_t st);
-
-// Injection scatter: C2[r] holds, per draft layer, [K (Hkv d) | V (Hkv d)]; K is rotated
-// at the row's position and both are written into the layer's pages.
-hipError_t launch_inject_scatter(int dt, const float* C2, int S, size_t split_stride, int rows,
-                                 int L, int Hkv, int d, double rope_base,
-                                 const int32_t* row_seq, const int32_t* row_pos, int pos_relative,
-                                 void* const* kpools, void* const* vpools,
-                                 const int32_t* block_table, const int32_t* seq_len,
-                                 int max_pages, int num_pages, int batch, int32_t* err,
-                                 hipStream_t st);
-
-// ids[r] = argmax_v logits[r, v] (lowest index on ties).
-hipError_t launch_argmax(const float* logits, int rows, int V, int32_t* ids, hipStream_t st);
-hipError_t launch_accept(const int32_t* block_ids, const int32_t* g, int batch, int B,
-                         int32_t* tau, int32_t* bonus, hipStream_t st);
+// ids[r] = argmax index decoded from keys[r].
+hipError_t launch_unpack_ids(const unsigned long long* keys, int n, int32_t* ids, hipStream_t st);
+// g[b*B + j] = argmax of verify row j; tau, bonus of the longest accepted draft prefix.
+hipError_t launch_accept(const unsigned long long* keys, const int32_t* drafts, int batch, int B,
+                         int32_t* g, int32_t* tau, int32_t* bonus, hipStream_t st);
 hipError_t launch_commit(int32_t* seq_t, int32_t* seq_d, int32_t* err_t, int32_t* err_d,
                          const int32_t* tau, int batch, int B, hipStream_t st);
 

@@ -32,12 +32,29 @@ def _dt_code(t: torch.dtype) -> int:
     raise ValueError(f"unsupported dtype {t}")
 
 
+def rotary_interleave(w, n_heads, d):
+    """Rows of each head reordered so rotate-half partners are adjacent: packed row 2i is
+    row i and packed row 2i+1 is row i + d/2 (the layout DFLASH_W_QKV expects for q, k)."""
+    D = w.shape[1]
+    return w.view(n_heads, 2, d // 2, D).transpose(1, 2).reshape(n_heads * d, D)
+
+
+def pack_qkv(wq, wk, wv, n_q_heads, n_kv_heads, d):
+    return torch.cat([rotary_interleave(wq, n_q_heads, d), rotary_interleave(wk, n_kv_heads, d),
+                      wv], 0).contiguous()
+
+
+def pack_gate_up(wg, wu):
+    """Packed row 2j = gate row j, packed row 2j+1 = up row j."""
+    return torch.stack([wg, wu], 1).reshape(2 * wg.shape[0], wg.shape[1]).contiguous()
+
+
 class Model:
     """A drafter (``draft=True``: needs W_c and g_c) or a target model.
 
     ``weights`` uses the per-layer names L{i}.{g_in,wq,wk,wv,wo,g_post,wg,wu,wd}, plus g_f
     and (drafter) w_c, g_c; ``shared`` holds embed and lm_head.  Q/K/V and gate/up are
-    packed into the row-concatenated matrices the library consumes."""
+    packed into the interleaved row layouts the library consumes (see include/dflash.h)."""
 
     def __init__(self, shape, weights: dict, shared: dict, n_taps: int, taps=None,
                  draft: bool = True):
@@ -47,8 +64,9 @@ class Model:
         self._keep = []
         lw = []
         for i in range(shape.n_layers):
-            qkv = torch.cat([weights[f"L{i}.wq"], weights[f"L{i}.wk"], weights[f"L{i}.wv"]], 0).contiguous()
-            gu = torch.cat([weights[f"L{i}.wg"], weights[f"L{i}.wu"]], 0).contiguous()
+            qkv = pack_qkv(weights[f"L{i}.wq"], weights[f"L{i}.wk"], weights[f"L{i}.wv"],
+                           shape.n_q_heads, shape.n_kv_heads, shape.head_dim)
+            gu = pack_gate_up(weights[f"L{i}.wg"], weights[f"L{i}.wu"])
             tensors = [weights[f"L{i}.g_in"].contiguous(), qkv, weights[f"L{i}.wo"].contiguous(),
                        weights[f"L{i}.g_post"].contiguous(), gu, weights[f"L{i}.wd"].contiguous()]
             self._keep += tensors
@@ -169,11 +187,13 @@ def draft_block(model: Model, kv: PagedKV, anchor, block, draft_ids, ws: Workspa
     _lib._check(st, "dflash_draft_block")
 
 
-def verify_accept(model: Model, kv: PagedKV, block_ids, block, feats_out, target_argmax, tau, bonus,
-                  ws: Workspace, logits_dbg=None, hidden_dbg=None):
-    st = _lib.verify_accept(model.handle, kv.struct, _ptr(block_ids), int(block), _ptr(feats_out),
-                            _ptr(target_argmax), _ptr(tau), _ptr(bonus), _ptr(logits_dbg),
-                            _ptr(hidden_dbg), _ptr(ws.buf), ws.nbytes, _stream())
+def verify_accept(model: Model, kv: PagedKV, anchor, draft_ids, block, feats_out, target_argmax,
+                  tau, bonus, ws: Workspace, logits_dbg=None, hidden_dbg=None):
+    """anchor [batch] and draft_ids [batch, block-1] (contiguous int32) form the block."""
+    st = _lib.verify_accept(model.handle, kv.struct, _ptr(anchor), _ptr(draft_ids), int(block),
+                            _ptr(feats_out), _ptr(target_argmax), _ptr(tau), _ptr(bonus),
+                            _ptr(logits_dbg), _ptr(hidden_dbg), _ptr(ws.buf), ws.nbytes,
+                            _stream())
     _lib._check(st, "dflash_verify_accept")
 
 

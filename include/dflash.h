@@ -175,22 +175,25 @@ int dflash_draft_block(const dflash_model* draft, const dflash_kv* draft_ctx,
 /*
  * Block verification and greedy acceptance ([DF] section 4.5 steps 2-3; [TRY] Fig. 1:
  * the main model checks the block with causal attention in one parallel pass).
- * The target runs block_ids[b] = [x, d_1 .. d_{block-1}] at positions
- * n = seq_len[b] .. n+block-1, causal inside the block with the whole cache visible, and
- * writes the block's K/V into the cache at those positions (tentatively: only kv_commit
- * makes them part of the sequence).
+ * The target runs the block y = [x, d_1 .. d_{block-1}] (x = anchor[b], d = draft_ids[b])
+ * at positions n = seq_len[b] .. n+block-1, causal inside the block with the whole cache
+ * visible, and writes the block's K/V into the cache at those positions (tentatively:
+ * only kv_commit makes them part of the sequence).  A prompt chunk is verified the same
+ * way (its first token as anchor, the rest as drafts) to fill the cache.
+ *   anchor        device int32 [batch]
+ *   draft_ids     device int32 [batch, block-1] (may be NULL when block == 1)
  *   feats_out     device [batch, block, n_taps * hidden] (model dtype) or NULL (out):
  *                 outputs of the tapped layers, concatenated in tap order.
  *   target_argmax device int32 [batch, block] (out): g_j, greedy id after row j.
  *   tau, bonus    device int32 [batch] (out): a = leading j with d_j == g_{j-1},
- *                 tau = a + 1 in [1, block], bonus = g_a.
+ *                 tau = a + 1 in [1, block], bonus = g_a (the next anchor).
  *   logits_dbg    device float [batch, block, vocab] or NULL; hidden_dbg as in draft_block.
  * The cache must map positions up to seq_len[b] + block - 1 (else the row is skipped and
  * DFLASH_DEVERR_PAGE is flagged).
  */
 int dflash_verify_accept(const dflash_model* target, dflash_kv* target_kv,
-                         const int32_t* block_ids, int32_t block, void* feats_out,
-                         int32_t* target_argmax, int32_t* tau, int32_t* bonus,
+                         const int32_t* anchor, const int32_t* draft_ids, int32_t block,
+                         void* feats_out, int32_t* target_argmax, int32_t* tau, int32_t* bonus,
                          float* logits_dbg, float* hidden_dbg, void* ws, size_t ws_bytes,
                          void* stream);
 
@@ -203,6 +206,28 @@ int dflash_verify_accept(const dflash_model* target, dflash_kv* target_kv,
  */
 int dflash_kv_commit(dflash_kv* target_kv, dflash_kv* draft_ctx, const int32_t* tau,
                      int32_t block, void* stream);
+
+/*
+ * Measurement hook (benchmarks only; not thread-safe).  dflash_timing_arm(kernel, n)
+ * makes the library record a HIP event pair on the launching stream around each of the
+ * next n launches of one kernel class; dflash_timing_read(ms, n) waits for those events,
+ * writes each launch's duration in milliseconds, disarms, and returns the number of
+ * launches recorded (or a negative dflash_status).  Events are host-side HIP objects;
+ * no device memory is allocated.
+ */
+typedef enum {
+  DFLASH_KERNEL_LM_HEAD = 0,      /* LM-head GEMM of draft_block / verify_accept          */
+  DFLASH_KERNEL_GEMM_QKV = 1,
+  DFLASH_KERNEL_GEMM_O = 2,
+  DFLASH_KERNEL_GEMM_GATE_UP = 3,
+  DFLASH_KERNEL_GEMM_DOWN = 4,
+  DFLASH_KERNEL_ATTENTION = 5,    /* split-K attention + split merge                      */
+  DFLASH_KERNEL_INJECT_FUSE = 6,  /* feats W_c^T GEMM of inject_ctx                       */
+  DFLASH_KERNEL_INJECT_KV = 7,    /* H_t [W^K; W^V]^T GEMM of inject_ctx                   */
+  DFLASH_KERNEL_COUNT = 8
+} dflash_kernel_id;
+int dflash_timing_arm(int32_t kernel, int32_t capacity);
+int dflash_timing_read(float* ms, int32_t capacity);
 
 #ifdef __cplusplus
 }

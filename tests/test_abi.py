@@ -92,8 +92,11 @@ def test_workspace_bytes_and_entry_validation():
         assert L.dflash_draft_block(h, ctypes.byref(kv), one, 16, one, None, None, one, 1 << 30, None) == -2
         kv.page_size = 64
         kv.head_dim = 64
-        assert L.dflash_verify_accept(h, ctypes.byref(kv), one, 16, None, one, one, one, None, None,
-                                      one, 1 << 30, None) == -2
+        assert L.dflash_verify_accept(h, ctypes.byref(kv), one, one, 16, None, one, one, one, None,
+                                      None, one, 1 << 30, None) == -2
+        kv.head_dim = 128
+        assert L.dflash_verify_accept(h, ctypes.byref(kv), one, None, 16, None, one, one, one, None,
+                                      None, one, 1 << 30, None) == -1
         kv.head_dim = 128
         # drafter-only call on a model without W_c
         assert L.dflash_inject_ctx(h, ctypes.byref(kv), one, 4, one, one, 0, one, 1 << 30, None) == -1

@@ -102,7 +102,8 @@ def test_verify_accept(name):
     logits = torch.zeros(w.batch, B, m.vocab, device=DEV)
     hid = torch.zeros(m.n_layers + 1, w.batch, B, m.hidden, device=DEV)
     ws = S.workspace(S.target, B, kv.capacity)
-    rt.verify_accept(S.target, kv, block_ids, B, feats, g, tau, bonus, ws, logits, hid)
+    rt.verify_accept(S.target, kv, block_ids[:, 0].contiguous(), block_ids[:, 1:].contiguous(), B,
+                     feats, g, tau, bonus, ws, logits, hid)
     torch.cuda.synchronize()
     assert kv.err.item() == 0
     for b, n in enumerate(lens):
@@ -146,7 +147,7 @@ def test_block_of_one_is_single_token_decode(name):
     hid = torch.zeros(m.n_layers + 1, w.batch, 1, m.hidden, device=DEV)
     logits = torch.zeros(w.batch, 1, m.vocab, device=DEV)
     ws = S.workspace(S.target, 1, kv.capacity)
-    rt.verify_accept(S.target, kv, tok, 1, None, g, tau, bonus, ws, logits, hid)
+    rt.verify_accept(S.target, kv, tok[:, 0].contiguous(), None, 1, None, g, tau, bonus, ws, logits, hid)
     torch.cuda.synchronize()
     for b, n in enumerate(lens):
         og, oz, _, _, ohid = O.verify(S.np_tw, S.np_shared, m, np_cache[b], [7 + b], n, ())
@@ -228,12 +229,12 @@ def test_speculative_cycles_reproduce_greedy_decoding(name):
     ws_d = S.workspace(S.draft, B, dkv.capacity, inject_rows=w.batch * max(B, n0))
     batch = w.batch
 
-    def verify(ids, blk):
+    def verify(anchor, drafts, blk):
         feats = torch.zeros(batch, blk, k * T.hidden, dtype=S.st, device=DEV)
         g = torch.zeros(batch, blk, dtype=torch.int32, device=DEV)
         tau = torch.zeros(batch, dtype=torch.int32, device=DEV)
         bonus = torch.zeros(batch, dtype=torch.int32, device=DEV)
-        rt.verify_accept(S.target, tkv, ids, blk, feats, g, tau, bonus, ws_t)
+        rt.verify_accept(S.target, tkv, anchor, drafts, blk, feats, g, tau, bonus, ws_t)
         return feats, g, tau, bonus
 
     def inject_rel(feats, blk):
@@ -243,7 +244,7 @@ def test_speculative_cycles_reproduce_greedy_decoding(name):
 
     # prefill: one causal pass over the prompt, inject its features, advance both caches
     ids = torch.tensor(np.stack(prompts), dtype=torch.int32, device=DEV)
-    feats, g, _, _ = verify(ids, n0)
+    feats, g, _, _ = verify(ids[:, 0].contiguous(), ids[:, 1:].contiguous(), n0)
     inject_rel(feats, n0)
     rt.kv_commit(tkv, dkv, torch.full((batch,), n0, dtype=torch.int32, device=DEV), n0)
     anchor = g[:, -1].contiguous()
@@ -251,8 +252,7 @@ def test_speculative_cycles_reproduce_greedy_decoding(name):
     drafts = torch.zeros(batch, B - 1, dtype=torch.int32, device=DEV)
     while min(len(e) for e in emitted) < n_new:
         rt.draft_block(S.draft, dkv, anchor, B, drafts, ws_d)
-        block_ids = torch.cat([anchor[:, None], drafts], 1).contiguous()
-        feats, g, tau, bonus = verify(block_ids, B)
+        feats, g, tau, bonus = verify(anchor, drafts, B)
         inject_rel(feats, B)
         rt.kv_commit(tkv, dkv, tau, B)
         t, bo, d = tau.cpu().numpy(), bonus.cpu().numpy(), drafts.cpu().numpy()
