@@ -3,7 +3,9 @@
 //
 // One decoder layer is six launches (the norms, RoPE, SwiGLU and residual adds are fused
 // into them):
-//   QKV GEMM   A = h (model dtype), RMSNorm(g_in) applied on the A side; epilogue: RoPE,
+// Activations stay float32 between launches (the bf16 MFMAs take them as compensated
+// hi/lo pairs); K/V and tapped features are written in the model dtype.
+//   QKV GEMM   A = h, RMSNorm(g_in) applied on the A side; epilogue: RoPE,
 //              q / k_blk / v_blk^T (and, for verification, the block K/V into the cache)
 //   attention  split-K over [context ; block], then the log-sum-exp merge of the splits
 //   O GEMM     epilogue: h += o W_o^T
@@ -52,13 +54,12 @@ inline const void* W(const dflash_model* m, int l, int slot) {
 // Scratch of one draft / verify step for `batch` sequences of `B` rows.
 struct StepWs {
   float* h;
-  void* hb;
-  void* q;
+  float* q;
   void* kblk;
   void* vblkT;
   float* part;
-  void* o;
-  void* act;
+  float* o;
+  float* act;
   unsigned long long* keys;
   float2* rope;
   AttnPlan plan;
@@ -72,22 +73,21 @@ size_t step_ws(const dflash_model* m, int batch, int B, int ctx_cap, void* base,
   t.plan = attn_plan(dt, batch, Hkv, Hq / Hkv, B, ctx_cap);
   Carve cv(base);
   t.h = (float*)cv.take((size_t)M * D * 4);
-  t.hb = cv.take((size_t)M * D * esz(dt));
-  t.q = cv.take((size_t)M * Hq * hd * esz(dt));
+  t.q = (float*)cv.take((size_t)M * Hq * hd * 4);
   t.kblk = cv.take((size_t)M * Hkv * hd * esz(dt));
   t.vblkT = cv.take((size_t)batch * Hkv * hd * Bp * esz(dt));
   t.part = (float*)cv.take(dt == DFLASH_BF16 ? attn_partial_floats(t.plan, batch, Hkv, hd) * 4 : 0);
-  t.o = cv.take((size_t)M * Hq * hd * esz(dt));
-  t.act = cv.take((size_t)M * d.ffn * esz(dt));
+  t.o = (float*)cv.take((size_t)M * Hq * hd * 4);
+  t.act = (float*)cv.take((size_t)M * d.ffn * 4);
   t.keys = (unsigned long long*)cv.take((size_t)M * 8);
   t.rope = (float2*)cv.take((size_t)M * (hd / 2) * sizeof(float2));
   if (w) *w = t;
   return cv.off;
 }
 
-size_t inject_ws(const dflash_model* m, int rows, void* base, void** x, float2** rope) {
+size_t inject_ws(const dflash_model* m, int rows, void* base, float** x, float2** rope) {
   Carve cv(base);
-  void* p = cv.take((size_t)rows * m->d.hidden * esz(m->d.dtype));
+  float* p = (float*)cv.take((size_t)rows * m->d.hidden * 4);
   float2* r = (float2*)cv.take((size_t)rows * (m->d.head_dim / 2) * sizeof(float2));
   if (x) *x = p;
   if (rope) *rope = r;
@@ -109,7 +109,6 @@ EmbedArgs embed_args(const dflash_model* m, const dflash_kv* kv, const StepWs& w
   a.V = d.vocab;
   a.D = d.hidden;
   a.h = w.h;
-  a.hb = w.hb;
   a.hdbg = hidden_dbg;
   a.keys = w.keys;
   a.n_keys = kv->batch * B;
@@ -208,7 +207,7 @@ int run_gemm(int kernel_class, int dt, const GemmArgs& g, hipStream_t st) {
 
 // The decoder stack shared by the drafter (bidirectional block, no cache writes) and the
 // target (causal block, block K/V written into the cache, taps copied out).  On entry h
-// and hb hold the embedded block; on exit they hold the last layer's output.
+// holds the embedded block; on exit it holds the last layer's output.
 int run_layers(const dflash_model* m, const dflash_kv* kv, int batch, int B, const StepWs& w,
                int causal, int write_cache, void* feats_out, float* hidden_dbg, hipStream_t st) {
   const dflash_model_desc& d = m->d;
@@ -219,7 +218,7 @@ int run_layers(const dflash_model* m, const dflash_kv* kv, int batch, int B, con
   for (int l = 0; l < d.n_layers; ++l) {
     const KvLayer kvl = layer_view(kv, l);
     {  // QKV projection with RMSNorm(g_in) on the A side; RoPE / layout epilogue
-      GemmArgs g = gemm_args(w.hb, D, one_seg(W(m, l, DFLASH_W_QKV), Nqkv, D), M, Nqkv, D,
+      GemmArgs g = gemm_args(w.h, D, one_seg(W(m, l, DFLASH_W_QKV), Nqkv, D), M, Nqkv, D,
                              W(m, l, DFLASH_W_G_IN), eps, EPI_QKV);
       EpiArgs& e = g.e;
       e.B = B;
@@ -251,12 +250,11 @@ int run_layers(const dflash_model* m, const dflash_kv* kv, int batch, int B, con
       GemmArgs g = gemm_args(w.o, Hq * hd, one_seg(W(m, l, DFLASH_W_O), D, Hq * hd), M, D,
                              Hq * hd, nullptr, eps, EPI_RESID);
       g.e.h = w.h;
-      g.e.hb = w.hb;
       g.e.ldh = D;
       if (int s = run_gemm(DFLASH_KERNEL_GEMM_O, dt, g, st)) return s;
     }
     {  // gate/up with RMSNorm(g_post) on the A side; SwiGLU epilogue
-      GemmArgs g = gemm_args(w.hb, D, one_seg(W(m, l, DFLASH_W_GATE_UP), 2 * F, D), M, 2 * F, D,
+      GemmArgs g = gemm_args(w.h, D, one_seg(W(m, l, DFLASH_W_GATE_UP), 2 * F, D), M, 2 * F, D,
                              W(m, l, DFLASH_W_G_POST), eps, EPI_SWIGLU);
       g.e.act = w.act;
       g.e.F = F;
@@ -266,7 +264,6 @@ int run_layers(const dflash_model* m, const dflash_kv* kv, int batch, int B, con
       GemmArgs g = gemm_args(w.act, F, one_seg(W(m, l, DFLASH_W_DOWN), D, F), M, D, F, nullptr, eps,
                              EPI_RESID);
       g.e.h = w.h;
-      g.e.hb = w.hb;
       g.e.ldh = D;
       g.e.hdbg = hidden_dbg ? hidden_dbg + (size_t)(l + 1) * M * D : nullptr;
       if (feats_out) {
@@ -283,12 +280,12 @@ int run_layers(const dflash_model* m, const dflash_kv* kv, int batch, int B, con
   return DFLASH_OK;
 }
 
-// LM head with RMSNorm(g_f) on the A side and the argmax epilogue over rows of hb
+// LM head with RMSNorm(g_f) on the A side and the argmax epilogue over rows of h
 // (skipping each block's anchor row when skipB != 0).
 int run_lm_head(const dflash_model* m, const StepWs& w, int rows, int skipB, float* logits,
                 hipStream_t st) {
   const dflash_model_desc& d = m->d;
-  GemmArgs g = gemm_args(w.hb, d.hidden, one_seg(d.lm_head, d.vocab, d.hidden), rows, d.vocab,
+  GemmArgs g = gemm_args(w.h, d.hidden, one_seg(d.lm_head, d.vocab, d.hidden), rows, d.vocab,
                          d.hidden, d.final_norm, d.rms_eps, EPI_ARGMAX);
   g.a_skip_B = skipB;
   g.e.keys = w.keys;
@@ -379,7 +376,7 @@ int dflash_inject_ctx(const dflash_model* m, dflash_kv* kv, const void* feats, i
   if (!m->d.w_c) return DFLASH_E_ARG;
   int e = check_kv(m, kv);
   if (e) return e;
-  void* x = nullptr;
+  float* x = nullptr;
   float2* rope = nullptr;
   const size_t need = inject_ws(m, n_rows, ws, &x, &rope);
   if (!ws || ws_bytes < need) return DFLASH_E_WORKSPACE;
@@ -387,9 +384,10 @@ int dflash_inject_ctx(const dflash_model* m, dflash_kv* kv, const void* feats, i
   const int dt = d.dtype, D = d.hidden, L = d.n_layers, Hkv = d.n_kv_heads, hd = d.head_dim;
   const int Kc = d.n_taps * D, N2 = L * 2 * Hkv * hd;
   hipStream_t st = (hipStream_t)stream;
-  {  // x = feats W_c^T
+  {  // x = feats W_c^T (float32)
     GemmArgs g = gemm_args(feats, Kc, one_seg(d.w_c, D, Kc), n_rows, D, Kc, nullptr, d.rms_eps,
-                           EPI_STORE_T);
+                           EPI_STORE_F32);
+    g.a_bf16 = dt == DFLASH_BF16;
     g.e.out = x;
     g.e.ldo = D;
     if (int s = run_gemm(DFLASH_KERNEL_INJECT_FUSE, dt, g, st)) return s;

@@ -7,7 +7,9 @@
 // so every context K/V byte is read from HBM once per workgroup: a step is one 64-token
 // page slice of the head (16 KB of K, 16 KB of V^T, both contiguous), copied with 16-byte
 // coalesced loads into double-buffered LDS while the previous step is computed.  Each wave
-// runs its own online softmax; S^T = K Q^T and O^T = V^T P^T use v_mfma_f32_16x16x32_bf16:
+// runs its own online softmax; S^T = K Q^T and O^T = V^T P^T use v_mfma_f32_16x16x32_bf16
+// with the float32 operand (q, scaled into the log2 domain, and the probabilities P)
+// taken as a compensated (hi, lo) bf16 pair against the stored bf16 K / V:
 //   * the K rows of the two 16-key S^T tiles of each 32-key half are interleaved so that
 //     lane group g ends up holding keys 8g .. 8g+7 of the half for its query column -
 //     exactly the P^T operand layout of the PV product, with no data movement;
@@ -24,7 +26,7 @@ namespace dflash {
 #define PSTRIDE (AD + 4)    // floats per partial row: O[AD], m, l, 2 pad (16-byte rows)
 
 struct AttnArgs {
-  const bf16* q;       // [batch*B, Hq*AD]
+  const float* q;      // [batch*B, Hq*AD]
   const bf16* kblk;    // [batch*B, Hkv*AD]
   const bf16* vblkT;   // [batch, Hkv, AD, Bp]
   const bf16* kpool;   // [num_pages, Hkv, 64, AD]
@@ -37,7 +39,7 @@ struct AttnArgs {
   int n_splits, split_len, n_rg, causal;
   float scale_log2;
   float* part;         // [(b, kvh, rg, s)][64][PSTRIDE]  (O, then m, l per row)
-  bf16* out;           // [batch*B, Hq*AD]
+  float* out;          // [batch*B, Hq*AD]
 };
 
 // LDS layouts of one 64-key step (one page slice of one KV head), padded by 16 bytes per row
@@ -46,7 +48,8 @@ struct AttnArgs {
 #define KTILE (64 * KROW)
 #define VTILE (AD * VROW)
 
-__global__ __launch_bounds__(256) void attn_splitk_bf16(AttnArgs a) {
+// two workgroups per CU (LDS holds two): registers are budgeted for 2 waves per SIMD
+__global__ __launch_bounds__(256, 2) void attn_splitk_bf16(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) bf16 kt[2][KTILE];
   __shared__ __attribute__((aligned(16))) bf16 vt[2][VTILE];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -66,17 +69,19 @@ __global__ __launch_bounds__(256) void attn_splitk_bf16(AttnArgs a) {
   // this wave's query tile: rows rho = rg*64 + w*16 + r as the Q^T MFMA operand
   const int rho = rg * 64 + w * 16 + r;
   const int jq = rho < R ? rho % a.B : 0x7fffffff;
-  bf16x8 qf[4];
-  if (rho < R) {
-    const int gq = rho / a.B;
-    const bf16* src = a.q + (size_t)(b * a.B + jq) * a.Hq * AD + (size_t)(kvh * a.G + gq) * AD + g * 8;
+  bf16x8 qh[4], ql[4];
+  {
+    const int gq = rho < R ? rho / a.B : 0;
+    const float* src = a.q + (size_t)(b * a.B + (rho < R ? jq : 0)) * a.Hq * AD +
+                       (size_t)(kvh * a.G + gq) * AD + g * 8;
 #pragma unroll
-    for (int cs = 0; cs < 4; ++cs) qf[cs] = *(const bf16x8*)(src + cs * 32);
-  } else {
+    for (int cs = 0; cs < 4; ++cs) {
+      float v[8];
+      load8(src + cs * 32, v);
 #pragma unroll
-    for (int cs = 0; cs < 4; ++cs)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) qf[cs][e] = (bf16)0.f;
+      for (int e = 0; e < 8; ++e) v[e] = rho < R ? v[e] * a.scale_log2 : 0.f;
+      split8(v, qh[cs], ql[cs]);
+    }
   }
 
   // ---- global -> register staging of one step: 8 x 16 B per thread (K then V^T) ----
@@ -169,8 +174,11 @@ __global__ __launch_bounds__(256) void attn_splitk_bf16(AttnArgs a) {
         sc[h][t] = f32x4{0.f, 0.f, 0.f, 0.f};
         const bf16* kr = K + (h * 32 + krow0 + 4 * t) * KROW + g * 8;
 #pragma unroll
-        for (int cs = 0; cs < 4; ++cs)
-          sc[h][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)(kr + cs * 32), qf[cs], sc[h][t], 0, 0, 0);
+        for (int cs = 0; cs < 4; ++cs) {
+          const bf16x8 kf = *(const bf16x8*)(kr + cs * 32);
+          sc[h][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qh[cs], sc[h][t], 0, 0, 0);
+          sc[h][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, ql[cs], sc[h][t], 0, 0, 0);
+        }
       }
     // lane holds keys h*32 + 8g + 4t + e (e < 4) of the step for query column r
     float p[2][8];
@@ -184,7 +192,7 @@ __global__ __launch_bounds__(256) void attn_splitk_bf16(AttnArgs a) {
           const int key = h * 32 + g * 8 + 4 * t + e;
           bool ok = key < lim;
           if (blk && a.causal) ok = ok && key <= jq;
-          const float x = ok ? sc[h][t][e] * a.scale_log2 : -INFINITY;
+          const float x = ok ? sc[h][t][e] : -INFINITY;
           p[h][4 * t + e] = x;
           mx = fmaxf(mx, x);
         }
@@ -192,16 +200,18 @@ __global__ __launch_bounds__(256) void attn_splitk_bf16(AttnArgs a) {
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
     const float mnew = fmaxf(m, mx);
     const float alpha = mnew == -INFINITY ? 1.f : exp2f(m - mnew);
-    bf16x8 pf[2];
+    bf16x8 ph[2], pl[2];
     float ps = 0.f;
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+    for (int h = 0; h < 2; ++h) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float pe = mnew == -INFINITY ? 0.f : exp2f(p[h][e] - mnew);
         ps += pe;
-        pf[h][e] = (bf16)pe;
+        p[h][e] = pe;
       }
+      split8(p[h], ph[h], pl[h]);
+    }
     m = mnew;
     lsum = lsum * alpha + ps;
 #pragma unroll
@@ -209,8 +219,11 @@ __global__ __launch_bounds__(256) void attn_splitk_bf16(AttnArgs a) {
       o[dt] *= alpha;
       const bf16* vr = VT + (dt * 16 + r) * VROW + g * 8;
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
-        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)(vr + h * 32), pf[h], o[dt], 0, 0, 0);
+      for (int h = 0; h < 2; ++h) {
+        const bf16x8 vf = *(const bf16x8*)(vr + h * 32);
+        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, ph[h], o[dt], 0, 0, 0);
+        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pl[h], o[dt], 0, 0, 0);
+      }
     }
     if (i + 1 < n_steps) store_step(buf ^ 1, step_lim(i + 1));
     __syncthreads();
@@ -259,11 +272,8 @@ __global__ __launch_bounds__(256) void attn_merge_bf16(AttnArgs a) {
   }
   const float inv = 1.f / lt;
   const int gq = rho / a.B, j = rho % a.B;
-  bf16* out = a.out + (size_t)(b * a.B + j) * a.Hq * AD + (size_t)(kvh * a.G + gq) * AD + 4 * t;
-  out[0] = (bf16)(acc.x * inv);
-  out[1] = (bf16)(acc.y * inv);
-  out[2] = (bf16)(acc.z * inv);
-  out[3] = (bf16)(acc.w * inv);
+  float* out = a.out + (size_t)(b * a.B + j) * a.Hq * AD + (size_t)(kvh * a.G + gq) * AD + 4 * t;
+  *(float4*)out = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
 }
 
 // Tuning knob read once from the environment (benchmark sweeps): DFLASH_ATTN_SPLIT_LEN
@@ -408,14 +418,14 @@ size_t attn_partial_floats(const AttnPlan& p, int batch, int Hkv, int d) {
   return (size_t)batch * Hkv * p.n_rg * p.n_ctx_splits * 64 * (d + 4);
 }
 
-hipError_t launch_attention(int dt, const AttnPlan& p, const void* q, const void* kblk,
+hipError_t launch_attention(int dt, const AttnPlan& p, const float* q, const void* kblk,
                             const void* vblkT, const KvLayer& kv, int batch, int B, int Bp,
-                            int Hq, int Hkv, int d, int causal, float* part, void* o,
+                            int Hq, int Hkv, int d, int causal, float* part, float* o,
                             hipStream_t st) {
   const int G = Hq / Hkv;
   if (dt == BF16) {
     AttnArgs a;
-    a.q = (const bf16*)q;
+    a.q = q;
     a.kblk = (const bf16*)kblk;
     a.vblkT = (const bf16*)vblkT;
     a.kpool = (const bf16*)kv.k;
@@ -436,7 +446,7 @@ hipError_t launch_attention(int dt, const AttnPlan& p, const void* q, const void
     a.causal = causal;
     a.scale_log2 = 1.4426950408889634f / sqrtf((float)d);
     a.part = part;
-    a.out = (bf16*)o;
+    a.out = o;
     dim3 grid(p.n_ctx_splits, Hkv * p.n_rg, batch);
     hipLaunchKernelGGL(attn_splitk_bf16, grid, dim3(256), 0, st, a);
     hipError_t e = hipGetLastError();
@@ -446,7 +456,7 @@ hipError_t launch_attention(int dt, const AttnPlan& p, const void* q, const void
     return hipGetLastError();
   }
   AttnF32Args a;
-  a.q = (const float*)q;
+  a.q = q;
   a.kblk = (const float*)kblk;
   a.vblkT = (const float*)vblkT;
   a.kpool = (const float*)kv.k;
@@ -464,7 +474,7 @@ hipError_t launch_attention(int dt, const AttnPlan& p, const void* q, const void
   a.d = d;
   a.causal = causal;
   a.scale = 1.0f / sqrtf((float)d);
-  a.out = (float*)o;
+  a.out = o;
   dim3 grid(B, Hq, batch);
   hipLaunchKernelGGL(attn_f32, grid, dim3(256), (size_t)(d + 256) * sizeof(float), st, a);
   return hipGetLastError();

@@ -16,6 +16,30 @@ template <typename T> DF_DEV T from_f(float x);
 template <> DF_DEV float from_f<float>(float x) { return x; }
 template <> DF_DEV bf16 from_f<bf16>(float x) { return (bf16)x; }
 
+// Compensated bf16 operands.  Activations live in float32; a bf16 MFMA that takes one as
+// an operand takes it as the pair hi = bf16(x) (nearest), lo = bf16(x - hi), which holds x
+// to ~2^-17 relative.  Against a bf16 operand w both products are exact and the MFMA
+// accumulates in float32, so hi*w + lo*w carries float32-class accuracy at the cost of a
+// second MFMA on the same fragment (spare issue slots in the bandwidth-bound kernels).
+DF_DEV void split8(const float v[8], bf16x8& hi, bf16x8& lo) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const bf16 h = (bf16)v[e];
+    hi[e] = h;
+    lo[e] = (bf16)(v[e] - (float)h);
+  }
+}
+DF_DEV void load8(const float* p, float v[8]) {
+  const float4 x0 = *(const float4*)p, x1 = *(const float4*)(p + 4);
+  v[0] = x0.x; v[1] = x0.y; v[2] = x0.z; v[3] = x0.w;
+  v[4] = x1.x; v[5] = x1.y; v[6] = x1.z; v[7] = x1.w;
+}
+DF_DEV void load8(const bf16* p, float v[8]) {
+  const bf16x8 x = *(const bf16x8*)p;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = (float)x[e];
+}
+
 // Wave64 reductions (xor butterflies over all 64 lanes).
 DF_DEV float wave_sum(float v) {
 #pragma unroll

@@ -18,10 +18,9 @@ __global__ __launch_bounds__(256) void embed_kernel(EmbedArgs a) {
   }
   const T* e = (const T*)a.E + (size_t)tok * D;
   for (int c = threadIdx.x; c < D; c += 256) {
-    const T x = e[c];
-    a.h[(size_t)row * D + c] = to_f(x);
-    ((T*)a.hb)[(size_t)row * D + c] = x;
-    if (a.hdbg) a.hdbg[(size_t)row * D + c] = to_f(x);
+    const float x = to_f(e[c]);
+    a.h[(size_t)row * D + c] = x;
+    if (a.hdbg) a.hdbg[(size_t)row * D + c] = x;
   }
   // RoPE angles of this row's position (float64, rounded to float32)
   const int pos = a.seq_len[b] + j;

@@ -33,14 +33,10 @@ DF_DEV void epi_elem(const EpiArgs& e, int row, int col, float v) {
     case EPI_STORE_F32:
       ((float*)e.out)[(size_t)row * e.ldo + col] = v;
       break;
-    case EPI_STORE_T:
-      ((T*)e.out)[(size_t)row * e.ldo + col] = from_f<T>(v);
-      break;
     case EPI_RESID: {
       const size_t i = (size_t)row * e.ldh + col;
       const float x = e.h[i] + v;
       e.h[i] = x;
-      ((T*)e.hb)[i] = from_f<T>(x);
       if (e.hdbg) e.hdbg[i] = x;
       if (e.tap) ((T*)e.tap)[(size_t)row * e.tap_ld + e.tap_col + col] = from_f<T>(x);
       break;
@@ -68,7 +64,7 @@ template <typename T, int KIND>
 DF_DEV void epi_pair(const EpiArgs& e, int row, int col, float v0, float v1) {
   switch (KIND) {
     case EPI_SWIGLU: {
-      ((T*)e.act)[(size_t)row * e.F + (col >> 1)] = from_f<T>(v0 / (1.f + expf(-v0)) * v1);
+      e.act[(size_t)row * e.F + (col >> 1)] = v0 / (1.f + expf(-v0)) * v1;
       break;
     }
     case EPI_QKV: {
@@ -82,20 +78,21 @@ DF_DEV void epi_pair(const EpiArgs& e, int row, int col, float v0, float v1) {
         const int i = el >> 1;
         const float2 cs = e.rope[(size_t)row * (hd >> 1) + i];
         const float y1 = v0 * cs.x - v1 * cs.y, y2 = v1 * cs.x + v0 * cs.y;
-        T* dst;
         if (head < e.Hq) {
-          dst = (T*)e.q + (size_t)row * e.Hq * hd + (size_t)head * hd;
+          float* dst = e.q + (size_t)row * e.Hq * hd + (size_t)head * hd;
+          dst[i] = y1;
+          dst[i + hd / 2] = y2;
         } else {
           const int kh = head - e.Hq;
-          dst = (T*)e.kblk + (size_t)row * e.Hkv * hd + (size_t)kh * hd;
+          T* dst = (T*)e.kblk + (size_t)row * e.Hkv * hd + (size_t)kh * hd;
+          dst[i] = from_f<T>(y1);
+          dst[i + hd / 2] = from_f<T>(y2);
           if (cache) {
             T* kc = (T*)e.kp[0] + (((size_t)page * e.Hkv + kh) * 64 + slot) * hd;
             kc[i] = from_f<T>(y1);
             kc[i + hd / 2] = from_f<T>(y2);
           }
         }
-        dst[i] = from_f<T>(y1);
-        dst[i + hd / 2] = from_f<T>(y2);
       } else {
         const int vh = head - e.Hq - e.Hkv;
         T* vt = (T*)e.vblkT + ((size_t)(b * e.Hkv + vh) * hd + el) * e.Bp + j;

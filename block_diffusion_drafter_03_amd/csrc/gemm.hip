@@ -48,21 +48,6 @@ DF_DEV unsigned long long shfl_xor_u64(unsigned long long v, int mask) {
 }
 DF_DEV unsigned long long umax64(unsigned long long a, unsigned long long b) { return a > b ? a : b; }
 
-DF_DEV float sumsq8(const bf16x8& v) {
-  float s = 0.f;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const float x = (float)v[e];
-    s += x * x;
-  }
-  return s;
-}
-DF_DEV bf16x8 scale8(const bf16x8& v, const bf16x8& g) {
-  bf16x8 o;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) o[e] = (bf16)((float)v[e] * (float)g[e]);
-  return o;
-}
 
 // Epilogue of one 16x16 MFMA tile held in the accumulator layout: v[i] = acc[row0+4g+i][col].
 // Pair epilogues are taken by even lanes (their odd neighbour holds column col + 1).
@@ -101,9 +86,32 @@ DF_DEV void tile_epilogue(const GemmArgs& ga, int row0, int col, const float v[4
 }
 
 // ---------------------------------------------------------------------------------------
-// 16 < M <= 32: 4 waves split K; A and W fragments are both loaded per 32-wide K step.
-template <int MT, int NW, int U, bool NORM, int KIND>
+// A operand helpers.  TA = float: activations, taken as a compensated (hi, lo) bf16 pair
+// (two MFMAs per W fragment); TA = bf16: inputs already in bf16 (one MFMA).
+template <typename TA> struct AIsFloat { static constexpr bool value = false; };
+template <> struct AIsFloat<float> { static constexpr bool value = true; };
+
+// v (8 raw A values) -> operand pair; with NORM, sum of squares of the raw values is added
+// to *ss and v is multiplied by the gain slice gp[0..7] first.
+template <bool NORM, bool ACC_SS>
+DF_DEV void a_operand(float v[8], const bf16* gp, float* ss, bf16x8& hi, bf16x8& lo) {
+  if (NORM) {
+    const bf16x8 gv = *(const bf16x8*)gp;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      if (ACC_SS) *ss += v[e] * v[e];
+      v[e] *= (float)gv[e];
+    }
+  }
+  split8(v, hi, lo);
+}
+
+// ---------------------------------------------------------------------------------------
+// 16 < M <= 32 (and M <= 16 with few output tiles): 4 waves split K; A and W fragments are
+// both loaded per 32-wide K step.
+template <typename TA, int MT, int NW, int U, bool NORM, int KIND>
 __global__ __launch_bounds__(NW * 64) void gemm_skinny_bf16(GemmArgs ga) {
+  constexpr bool TWO = AIsFloat<TA>::value;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int r = lane & 15, g = lane >> 4;
   const int M = ga.M, N = ga.N, K = ga.K;
@@ -115,11 +123,11 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_bf16(GemmArgs ga) {
   __shared__ float rstd[MT * 16];
   const BRows<bf16> Bd = *reinterpret_cast<const BRows<bf16>*>(&ga.B);
 
-  const bf16* arow[MT];
+  const TA* arow[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     const int m = min(mt * 16 + r, M - 1);
-    arow[mt] = (const bf16*)ga.A + (size_t)a_row_index(m, ga.a_skip_B) * ga.lda + g * 8;
+    arow[mt] = (const TA*)ga.A + (size_t)a_row_index(m, ga.a_skip_B) * ga.lda + g * 8;
   }
   const bf16* gk = NORM ? (const bf16*)ga.norm_g + g * 8 : nullptr;
   unsigned long long best[4] = {0ull, 0ull, 0ull, 0ull};
@@ -137,26 +145,26 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_bf16(GemmArgs ga) {
     }
     for (int ks = ks0; ks < ks1; ks += U) {
       bf16x8 wf[U];
-      bf16x8 af[U][MT];
+      float av[U][MT][8];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int k = min(ks + u, ks1 - 1);
         wf[u] = *(const bf16x8*)(wrow + (size_t)k * 32);
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) af[u][mt] = *(const bf16x8*)(arow[mt] + (size_t)k * 32);
+        for (int mt = 0; mt < MT; ++mt) load8(arow[mt] + (size_t)k * 32, av[u][mt]);
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         if (ks + u >= ks1) break;
-        bf16x8 gv;
-        if (NORM) gv = *(const bf16x8*)(gk + (size_t)(ks + u) * 32);
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
-          if (NORM) {
-            if (first) ss[mt] += sumsq8(af[u][mt]);
-            af[u][mt] = scale8(af[u][mt], gv);
-          }
-          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[u][mt], wf[u], acc[mt], 0, 0, 0);
+          bf16x8 hi, lo;
+          if (first)
+            a_operand<NORM, true>(av[u][mt], gk + (size_t)(ks + u) * 32, &ss[mt], hi, lo);
+          else
+            a_operand<NORM, false>(av[u][mt], gk + (size_t)(ks + u) * 32, &ss[mt], hi, lo);
+          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, wf[u], acc[mt], 0, 0, 0);
+          if (TWO) acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, wf[u], acc[mt], 0, 0, 0);
         }
       }
     }
@@ -202,17 +210,20 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_bf16(GemmArgs ga) {
   }
 }
 
-// M <= 16: 16 waves (1024 threads) split K, one 32-wide step per MFMA.  With ASTAT each
-// wave keeps its K-slice of the A rows in registers for all of the workgroup's tiles,
-// already multiplied by the RMSNorm gain (rstd is applied in the epilogue), so the vector
-// memory path carries only W: a wave issues all of its W loads of a tile at once (<= 8
-// steps, 8 KB) and 16 waves per CU keep >= 128 KB in flight.  Without ASTAT (K/16 > 256)
-// A and W are streamed together in chunks of 8 steps.
+// M <= 16: 16 waves (1024 threads) split K, one 32-wide step per MFMA (pair).  With ASTAT
+// each wave keeps its K-slice of the A rows for all of the workgroup's tiles, already
+// multiplied by the RMSNorm gain and split into (hi, lo) (rstd is applied in the
+// epilogue): hi in registers, lo in LDS (128 KB: the workgroup owns the CU anyway), so
+// the vector memory path carries only W: a wave issues all of its W loads of a tile at
+// once (<= 8 steps, 8 KB) and 16 waves per CU keep >= 128 KB in flight.  Without ASTAT
+// (K/16 > 256) A and W are streamed together in chunks of CHS steps.
 #define GEMV_MAX_TILES 8   // tiles per workgroup whose epilogue is deferred (non-argmax kinds)
 
-template <bool NORM, bool ASTAT, int KIND>
+template <typename TA, bool NORM, bool ASTAT, int KIND>
 __global__ __launch_bounds__(1024) void gemm_gemv16_bf16(GemmArgs ga) {
+  constexpr bool TWO = AIsFloat<TA>::value;
   constexpr int NW = 16, CH = 8;
+  constexpr int CHS = TWO ? 4 : 8;   // streamed chunk (raw float A costs 2x the registers)
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int r = lane & 15, g = lane >> 4;
   const int M = ga.M, N = ga.N, K = ga.K;
@@ -223,12 +234,18 @@ __global__ __launch_bounds__(1024) void gemm_gemv16_bf16(GemmArgs ga) {
   __shared__ f32x4 done[GEMV_MAX_TILES][64];
   __shared__ float ss_red[NW][16];
   __shared__ float rstd[16];
+  __shared__ bf16x8 alo[ASTAT && TWO ? NW : 1][ASTAT && TWO ? CH : 1][64];
+  // running argmax keys of wave 0's lanes (kept out of the main loop's registers)
+  __shared__ unsigned long long bsh[KIND == EPI_ARGMAX ? 4 : 1][64];
   const BRows<bf16> Bd = *reinterpret_cast<const BRows<bf16>*>(&ga.B);
-  const bf16* arow = (const bf16*)ga.A + (size_t)a_row_index(min(r, M - 1), ga.a_skip_B) * ga.lda + g * 8;
-  unsigned long long best[4] = {0ull, 0ull, 0ull, 0ull};
+  const TA* arow = (const TA*)ga.A + (size_t)a_row_index(min(r, M - 1), ga.a_skip_B) * ga.lda + g * 8;
+  const bf16* gk = NORM ? (const bf16*)ga.norm_g + g * 8 : nullptr;
   int nbuf = 0;
+  if (KIND == EPI_ARGMAX && w == 0)
+#pragma unroll
+    for (int i = 0; i < (KIND == EPI_ARGMAX ? 4 : 1); ++i) bsh[i][lane] = 0ull;
 
-  bf16x8 a[CH];
+  bf16x8 ah[ASTAT ? CH : 1];
   // W loads of this workgroup's first tile go out before the A prologue (independent)
   bf16x8 wn[CH];
   auto load_w = [&](int t) {
@@ -237,17 +254,17 @@ __global__ __launch_bounds__(1024) void gemm_gemv16_bf16(GemmArgs ga) {
     for (int s = 0; s < CH; ++s)
       if (s < spw) wn[s] = *(const bf16x8*)(wrow + (size_t)(ks0 + s) * 32);
   };
-  if (ASTAT && blockIdx.x < n_tiles) load_w(blockIdx.x);
-  if (ASTAT) {
+  if constexpr (ASTAT) {
+    if (blockIdx.x < n_tiles) load_w(blockIdx.x);
     float ss = 0.f;
 #pragma unroll
     for (int s = 0; s < CH; ++s) {
       if (s < spw) {
-        a[s] = *(const bf16x8*)(arow + (size_t)(ks0 + s) * 32);
-        if (NORM) {
-          ss += sumsq8(a[s]);
-          a[s] = scale8(a[s], *(const bf16x8*)((const bf16*)ga.norm_g + (size_t)(ks0 + s) * 32 + g * 8));
-        }
+        float v[8];
+        load8(arow + (size_t)(ks0 + s) * 32, v);
+        bf16x8 lo;
+        a_operand<NORM, true>(v, gk + (size_t)(ks0 + s) * 32, &ss, ah[s], lo);
+        if constexpr (TWO) alo[w][s][lane] = lo;
       }
     }
     if (NORM) {
@@ -266,29 +283,38 @@ __global__ __launch_bounds__(1024) void gemm_gemv16_bf16(GemmArgs ga) {
   }
 
   for (int t = blockIdx.x; t < n_tiles; t += gridDim.x) {
-    const bf16* wrow = Bd.row(min(t * 16 + r, N - 1)) + g * 8;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    if (ASTAT) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc2 = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (ASTAT) {
 #pragma unroll
       for (int s = 0; s < CH; ++s)
-        if (s < spw) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s], wn[s], acc, 0, 0, 0);
+        if (s < spw) {
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[s], wn[s], acc, 0, 0, 0);
+          if constexpr (TWO) acc2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo[w][s][lane], wn[s], acc2, 0, 0, 0);
+        }
       // the next tile's W loads are in flight across the barrier and the reduction
       if (t + gridDim.x < n_tiles) load_w(t + gridDim.x);
     } else {
-      for (int c0 = 0; c0 < spw; c0 += CH) {
-        bf16x8 wf[CH];
+      const bf16* wrow = Bd.row(min(t * 16 + r, N - 1)) + g * 8;
+      for (int c0 = 0; c0 < spw; c0 += CHS) {
+        bf16x8 wf[CHS];
+        float av[CHS][8];
 #pragma unroll
-        for (int s = 0; s < CH; ++s) {
+        for (int s = 0; s < CHS; ++s) {
           const int k = ks0 + min(c0 + s, spw - 1);
           wf[s] = *(const bf16x8*)(wrow + (size_t)k * 32);
-          a[s] = *(const bf16x8*)(arow + (size_t)k * 32);
+          load8(arow + (size_t)k * 32, av[s]);
         }
 #pragma unroll
-        for (int s = 0; s < CH; ++s)
-          if (c0 + s < spw) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s], wf[s], acc, 0, 0, 0);
+        for (int s = 0; s < CHS; ++s)
+          if (c0 + s < spw) {
+            bf16x8 hi, lo;
+            split8(av[s], hi, lo);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, wf[s], acc, 0, 0, 0);
+            if constexpr (TWO) acc2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, wf[s], acc2, 0, 0, 0);
+          }
       }
     }
-    red[w][lane] = acc;
+    red[w][lane] = acc + acc2;
     __syncthreads();
     if (w == 0) {
       f32x4 s = red[0][lane];
@@ -296,9 +322,15 @@ __global__ __launch_bounds__(1024) void gemm_gemv16_bf16(GemmArgs ga) {
       for (int ww = 1; ww < NW; ++ww) s += red[ww][lane];
       if constexpr (KIND == EPI_ARGMAX) {
         float v[4];
+        unsigned long long best[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] = NORM ? s[i] * rstd[g * 4 + i] : s[i];
+        for (int i = 0; i < 4; ++i) {
+          v[i] = NORM ? s[i] * rstd[g * 4 + i] : s[i];
+          best[i] = bsh[i][lane];
+        }
         tile_epilogue<bf16, KIND>(ga, g * 4, t * 16 + r, v, r, best);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) bsh[i][lane] = best[i];
       } else {
         done[nbuf][lane] = s;   // epilogue deferred until the A registers are dead
       }
@@ -309,6 +341,7 @@ __global__ __launch_bounds__(1024) void gemm_gemv16_bf16(GemmArgs ga) {
   if constexpr (KIND != EPI_ARGMAX) {
     // every wave takes buffered tiles: the epilogues run in parallel, off the main loop's
     // register budget
+    unsigned long long best[4];
     for (int i = w; i < nbuf; i += NW) {
       const f32x4 s = done[i][lane];
       float v[4];
@@ -319,79 +352,16 @@ __global__ __launch_bounds__(1024) void gemm_gemv16_bf16(GemmArgs ga) {
   }
   if (KIND == EPI_ARGMAX && w == 0 && r == 0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < (KIND == EPI_ARGMAX ? 4 : 1); ++i) {
       const int row = g * 4 + i;
-      if (row < M && best[i]) atomicMax(&ga.e.keys[row], best[i]);
+      const unsigned long long k = bsh[i][lane];
+      if (row < M && k) atomicMax(&ga.e.keys[row], k);
     }
   }
 }
 
-// M <= 16, many output tiles: every wave owns whole 16-column tiles over the full K, so
-// waves never wait for one another after the prologue (which computes the rows' rstd, the
-// 4 waves splitting K).  Per batch of 8 K steps a lane issues 8 W and 8 A loads (A hits
-// L1/L2: every wave reads the same 16 rows), then 8 MFMAs; the tile's epilogue runs in the
-// owning wave.
-template <bool NORM, int KIND>
-__global__ __launch_bounds__(256) void gemm_wave_bf16(GemmArgs ga) {
-  constexpr int U = 8;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int r = lane & 15, g = lane >> 4;
-  const int M = ga.M, N = ga.N, K = ga.K;
-  const int KS = K >> 5;
-  const int n_tiles = (N + 15) >> 4;
-  __shared__ float ss_red[4][16];
-  __shared__ float rstd[16];
-  const BRows<bf16> Bd = *reinterpret_cast<const BRows<bf16>*>(&ga.B);
-  const bf16* arow = (const bf16*)ga.A + (size_t)a_row_index(min(r, M - 1), ga.a_skip_B) * ga.lda + g * 8;
-  const bf16* gk = NORM ? (const bf16*)ga.norm_g + g * 8 : nullptr;
-  if (NORM) {
-    float ss = 0.f;
-    for (int ks = w; ks < KS; ks += 4) ss += sumsq8(*(const bf16x8*)(arow + (size_t)ks * 32));
-    ss += __shfl_xor(ss, 16, 64);
-    ss += __shfl_xor(ss, 32, 64);
-    if (g == 0) ss_red[w][r] = ss;
-    __syncthreads();
-    if (threadIdx.x < 16)
-      rstd[threadIdx.x] = 1.0f / sqrtf((ss_red[0][threadIdx.x] + ss_red[1][threadIdx.x] +
-                                        ss_red[2][threadIdx.x] + ss_red[3][threadIdx.x]) / (float)K + ga.eps);
-    __syncthreads();
-  }
-  unsigned long long best[4] = {0ull, 0ull, 0ull, 0ull};
-  for (int t = blockIdx.x * 4 + w; t < n_tiles; t += gridDim.x * 4) {
-    const bf16* wrow = Bd.row(min(t * 16 + r, N - 1)) + g * 8;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int ks = 0; ks < KS; ks += U) {
-      bf16x8 wf[U], af[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int k = min(ks + u, KS - 1);
-        wf[u] = *(const bf16x8*)(wrow + (size_t)k * 32);
-        af[u] = *(const bf16x8*)(arow + (size_t)k * 32);
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        if (ks + u >= KS) break;
-        bf16x8 a = af[u];
-        if (NORM) a = scale8(a, *(const bf16x8*)(gk + (size_t)(ks + u) * 32));
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, wf[u], acc, 0, 0, 0);
-      }
-    }
-    float v[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = NORM ? acc[i] * rstd[g * 4 + i] : acc[i];
-    tile_epilogue<bf16, KIND>(ga, g * 4, t * 16 + r, v, r, best);
-  }
-  if (KIND == EPI_ARGMAX && r == 0) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = g * 4 + i;
-      if (row < M && best[i]) atomicMax(&ga.e.keys[row], best[i]);
-    }
-  }
-}
-
-// Variant selection for M <= 16 (benchmark sweeps may force one with DFLASH_GEMV=1..3):
-// 1 = 4-wave split-K, 2 = 16-wave split-K with stationary A, 3 = wave-owned tiles.
+// Variant selection for M <= 16 (benchmark sweeps may force one with DFLASH_GEMV=1..2):
+// 1 = 4-wave split-K, 2 = 16-wave split-K with stationary A.
 static int gemv_variant() {
   static int v = -1;
   if (v < 0) {
@@ -406,9 +376,10 @@ static int gemv_variant() {
 #define TK 64
 #define TPAD 8
 
-template <bool NORM, int KIND>
+template <typename TA, bool NORM, int KIND>
 __global__ __launch_bounds__(256) void gemm_tiled_bf16(GemmArgs ga) {
-  __shared__ __attribute__((aligned(16))) bf16 As[TB][TK + TPAD];
+  constexpr bool TWO = AIsFloat<TA>::value;
+  __shared__ __attribute__((aligned(16))) bf16 As[TWO ? 2 : 1][TB][TK + TPAD];
   __shared__ __attribute__((aligned(16))) bf16 Bs[TB][TK + TPAD];
   __shared__ float rstd_s[TB];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -424,7 +395,7 @@ __global__ __launch_bounds__(256) void gemm_tiled_bf16(GemmArgs ga) {
   const int m0 = (t % mt_n) * TB, n0 = (t / mt_n) * TB;
   const BRows<bf16> Bd = *reinterpret_cast<const BRows<bf16>*>(&ga.B);
 
-  const bf16* ap[2];
+  const TA* ap[2];
   const bf16* bp[2];
   int lrow[2], lcol[2];
 #pragma unroll
@@ -432,15 +403,16 @@ __global__ __launch_bounds__(256) void gemm_tiled_bf16(GemmArgs ga) {
     const int c = tid + 256 * j;
     lrow[j] = c >> 3;
     lcol[j] = (c & 7) * 8;
-    ap[j] = (const bf16*)ga.A + (size_t)a_row_index(min(m0 + lrow[j], M - 1), ga.a_skip_B) * ga.lda + lcol[j];
+    ap[j] = (const TA*)ga.A + (size_t)a_row_index(min(m0 + lrow[j], M - 1), ga.a_skip_B) * ga.lda + lcol[j];
     bp[j] = Bd.row(min(n0 + lrow[j], N - 1)) + lcol[j];
   }
   const bf16* gk = NORM ? (const bf16*)ga.norm_g : nullptr;
-  bf16x8 ra[2], rb[2];
+  float ra[2][8];
+  bf16x8 rb[2];
   float ss[2] = {0.f, 0.f};
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    ra[j] = *(const bf16x8*)(ap[j]);
+    load8(ap[j], ra[j]);
     rb[j] = *(const bf16x8*)(bp[j]);
   }
   f32x4 acc[2][2];
@@ -452,33 +424,36 @@ __global__ __launch_bounds__(256) void gemm_tiled_bf16(GemmArgs ga) {
   for (int k0 = 0; k0 < K; k0 += TK) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      if (NORM) {
-        ss[j] += sumsq8(ra[j]);
-        ra[j] = scale8(ra[j], *(const bf16x8*)(gk + k0 + lcol[j]));
-      }
-      *(bf16x8*)&As[lrow[j]][lcol[j]] = ra[j];
+      bf16x8 hi, lo;
+      a_operand<NORM, true>(ra[j], gk + k0 + lcol[j], &ss[j], hi, lo);
+      *(bf16x8*)&As[0][lrow[j]][lcol[j]] = hi;
+      if constexpr (TWO) *(bf16x8*)&As[TWO ? 1 : 0][lrow[j]][lcol[j]] = lo;
       *(bf16x8*)&Bs[lrow[j]][lcol[j]] = rb[j];
     }
     __syncthreads();
     if (k0 + TK < K) {
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        ra[j] = *(const bf16x8*)(ap[j] + k0 + TK);
+        load8(ap[j] + k0 + TK, ra[j]);
         rb[j] = *(const bf16x8*)(bp[j] + k0 + TK);
       }
     }
 #pragma unroll
     for (int kk = 0; kk < TK; kk += 32) {
-      bf16x8 af[2], bfr[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i) af[i] = *(const bf16x8*)&As[wm * 32 + i * 16 + r][kk + g * 8];
+      bf16x8 bfr[2];
 #pragma unroll
       for (int j = 0; j < 2; ++j) bfr[j] = *(const bf16x8*)&Bs[wn * 32 + j * 16 + r][kk + g * 8];
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int p = 0; p < (TWO ? 2 : 1); ++p) {
+        bf16x8 af[2];
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+        for (int i = 0; i < 2; ++i) af[i] = *(const bf16x8*)&As[p][wm * 32 + i * 16 + r][kk + g * 8];
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+      }
     }
     __syncthreads();
   }
@@ -615,7 +590,7 @@ static int num_cus() {
   return g_num_cus;
 }
 
-template <bool NORM, int KIND>
+template <typename TA, bool NORM, int KIND>
 static hipError_t launch_kind(int dt, const GemmArgs& ga, hipStream_t st) {
   const int M = ga.M, N = ga.N;
   if (dt == F32) {
@@ -623,58 +598,54 @@ static hipError_t launch_kind(int dt, const GemmArgs& ga, hipStream_t st) {
     hipLaunchKernelGGL((gemm_f32<NORM, KIND>), grid, dim3(256), 0, st, ga);
     return hipGetLastError();
   }
+  const int n_tiles = (N + 15) / 16;
   if (M <= 16) {
-    const int n_tiles = (N + 15) / 16;
     int v = gemv_variant();
     if (v == 2 && (ga.K % 512 != 0 || (NORM && ga.K > 4096))) v = 1;
     // measured on MI355X at hidden 4096: the 16-wave stationary-A kernel wins for wide
     // outputs (gate/up, LM head) and long K (down projection); the 4-wave kernel for QKV
-    if (v < 1 || v > 3) v = (n_tiles >= 4 * num_cus() || ga.K > 4096) ? 2 : 1;
-    if (v == 3) {
-      int grid = (n_tiles + 3) / 4;
-      if (grid > 4 * num_cus()) grid = 4 * num_cus();
-      hipLaunchKernelGGL((gemm_wave_bf16<NORM, KIND>), dim3(grid), dim3(256), 0, st, ga);
-    } else if (v == 2) {
+    if (v < 1 || v > 2) v = (n_tiles >= 4 * num_cus() || ga.K > 4096) ? 2 : 1;
+    if (v == 2) {
       int grid = n_tiles < 2 * num_cus() ? n_tiles : 2 * num_cus();
       if (KIND != EPI_ARGMAX && grid * GEMV_MAX_TILES < n_tiles)
         grid = (n_tiles + GEMV_MAX_TILES - 1) / GEMV_MAX_TILES;
       if (ga.K <= 4096)
-        hipLaunchKernelGGL((gemm_gemv16_bf16<NORM, true, KIND>), dim3(grid), dim3(1024), 0, st, ga);
+        hipLaunchKernelGGL((gemm_gemv16_bf16<TA, NORM, true, KIND>), dim3(grid), dim3(1024), 0, st, ga);
       else
-        hipLaunchKernelGGL((gemm_gemv16_bf16<false, false, KIND>), dim3(grid), dim3(1024), 0, st, ga);
-    } else {
-      const int grid = n_tiles < 8 * num_cus() ? n_tiles : 8 * num_cus();
-      hipLaunchKernelGGL((gemm_skinny_bf16<1, 4, 8, NORM, KIND>), dim3(grid), dim3(256), 0, st, ga);
+        hipLaunchKernelGGL((gemm_gemv16_bf16<TA, false, false, KIND>), dim3(grid), dim3(1024), 0, st, ga);
+      return hipGetLastError();
     }
-    return hipGetLastError();
   }
   if (M <= 32) {
-    const int n_tiles = (N + 15) / 16;
     const int grid = n_tiles < 8 * num_cus() ? n_tiles : 8 * num_cus();
     if (M <= 16)
-      hipLaunchKernelGGL((gemm_skinny_bf16<1, 4, 8, NORM, KIND>), dim3(grid), dim3(256), 0, st, ga);
+      hipLaunchKernelGGL((gemm_skinny_bf16<TA, 1, 4, 8, NORM, KIND>), dim3(grid), dim3(256), 0, st, ga);
     else
-      hipLaunchKernelGGL((gemm_skinny_bf16<2, 4, 8, NORM, KIND>), dim3(grid), dim3(256), 0, st, ga);
+      hipLaunchKernelGGL((gemm_skinny_bf16<TA, 2, 4, 4, NORM, KIND>), dim3(grid), dim3(256), 0, st, ga);
     return hipGetLastError();
   }
   const int tiles = ((M + TB - 1) / TB) * ((N + TB - 1) / TB);
-  hipLaunchKernelGGL((gemm_tiled_bf16<NORM, KIND>), dim3(tiles), dim3(256), 0, st, ga);
+  hipLaunchKernelGGL((gemm_tiled_bf16<TA, NORM, KIND>), dim3(tiles), dim3(256), 0, st, ga);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm(int dt, const GemmArgs& ga, hipStream_t st) {
   if (ga.M <= 0 || ga.N <= 0) return hipSuccess;
   const bool norm = ga.norm_g != nullptr;
-  // the combinations the drafter / verifier use: normalised A feeds QKV, gate/up, LM head
-  // and the injection K/V projection; plain A feeds O, down and W_c
+  // the combinations the drafter / verifier use: normalised float32 A feeds QKV, gate/up,
+  // the LM head and the injection K/V projection; plain float32 A feeds O and down; the
+  // bf16 tapped features feed W_c
+  if (ga.a_bf16) {
+    if (norm || ga.e.kind != EPI_STORE_F32) return hipErrorInvalidValue;
+    return launch_kind<bf16, false, EPI_STORE_F32>(dt, ga, st);
+  }
   switch (ga.e.kind) {
-    case EPI_QKV: return norm ? launch_kind<true, EPI_QKV>(dt, ga, st) : launch_kind<false, EPI_QKV>(dt, ga, st);
-    case EPI_SWIGLU: return norm ? launch_kind<true, EPI_SWIGLU>(dt, ga, st) : launch_kind<false, EPI_SWIGLU>(dt, ga, st);
-    case EPI_ARGMAX: return norm ? launch_kind<true, EPI_ARGMAX>(dt, ga, st) : launch_kind<false, EPI_ARGMAX>(dt, ga, st);
-    case EPI_INJECT_KV: return norm ? launch_kind<true, EPI_INJECT_KV>(dt, ga, st) : launch_kind<false, EPI_INJECT_KV>(dt, ga, st);
-    case EPI_RESID: return norm ? launch_kind<true, EPI_RESID>(dt, ga, st) : launch_kind<false, EPI_RESID>(dt, ga, st);
-    case EPI_STORE_T: return norm ? launch_kind<true, EPI_STORE_T>(dt, ga, st) : launch_kind<false, EPI_STORE_T>(dt, ga, st);
-    case EPI_STORE_F32: return norm ? launch_kind<true, EPI_STORE_F32>(dt, ga, st) : launch_kind<false, EPI_STORE_F32>(dt, ga, st);
+    case EPI_QKV: return norm ? launch_kind<float, true, EPI_QKV>(dt, ga, st) : hipErrorInvalidValue;
+    case EPI_SWIGLU: return norm ? launch_kind<float, true, EPI_SWIGLU>(dt, ga, st) : hipErrorInvalidValue;
+    case EPI_ARGMAX: return norm ? launch_kind<float, true, EPI_ARGMAX>(dt, ga, st) : hipErrorInvalidValue;
+    case EPI_INJECT_KV: return norm ? launch_kind<float, true, EPI_INJECT_KV>(dt, ga, st) : hipErrorInvalidValue;
+    case EPI_RESID: return norm ? hipErrorInvalidValue : launch_kind<float, false, EPI_RESID>(dt, ga, st);
+    case EPI_STORE_F32: return norm ? hipErrorInvalidValue : launch_kind<float, false, EPI_STORE_F32>(dt, ga, st);
     default: return hipErrorInvalidValue;
   }
 }

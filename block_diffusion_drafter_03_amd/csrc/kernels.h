@@ -19,12 +19,13 @@ struct BSeg {
   int ldb;
 };
 
+// Activations (h, q, attention output, SwiGLU output, fused injection rows) are float32;
+// K/V (block and cache) and tapped features are stored in the model dtype.
 enum EpiKind {
   EPI_STORE_F32 = 0,  // out[row*ldo + col] = acc (float)
-  EPI_STORE_T,        // out[row*ldo + col] = acc (model dtype)
-  EPI_RESID,          // h += acc; hb = h (model dtype); optional hdbg / tap copies
-  EPI_QKV,            // RoPE q, k; write q, k_blk, v_blk^T (and the block K/V into a cache)
-  EPI_SWIGLU,         // act = SiLU(gate) * up
+  EPI_RESID,          // h += acc; optional hdbg / tap (model dtype) copies
+  EPI_QKV,            // RoPE q, k; write q (float), k_blk, v_blk^T (and the block K/V into a cache)
+  EPI_SWIGLU,         // act = SiLU(gate) * up (float)
   EPI_INJECT_KV,      // RoPE K, scatter K and V of every draft layer into the paged cache
   EPI_ARGMAX          // per-row argmax (packed 64-bit atomic max); optional float logits
 };
@@ -36,7 +37,6 @@ struct EpiArgs {
   int ldo;
   // EPI_RESID
   float* h;
-  void* hb;
   int ldh;
   float* hdbg;
   void* tap;
@@ -45,7 +45,7 @@ struct EpiArgs {
   int B, Bp, Hq, Hkv, hd;
   const float2* rope;       // [M, hd/2] (cos, sin) of each row's position
   const int32_t* seq_len;
-  void* q;
+  float* q;
   void* kblk;
   void* vblkT;
   // paged cache: per-layer pools (EPI_QKV uses slot 0), block table, bounds
@@ -60,7 +60,7 @@ struct EpiArgs {
   const int32_t* row_pos;
   int pos_relative;
   // EPI_SWIGLU
-  void* act;
+  float* act;
   int F;
   // EPI_ARGMAX
   unsigned long long* keys;
@@ -68,7 +68,8 @@ struct EpiArgs {
 };
 
 struct GemmArgs {
-  const void* A;        // [M, K] model dtype
+  const void* A;        // [M, K] float32 (bf16 when a_bf16)
+  int a_bf16;
   int lda;
   int a_skip_B;         // 0: A row m is row m; else rows j == 0 of each B-row block are skipped
   BSeg B;
@@ -102,9 +103,9 @@ size_t attn_partial_floats(const AttnPlan& p, int batch, int Hkv, int d);
 // o[M, Hq d] = softmax(q k^T / sqrt(d)) v over [context ; block] (causal inside the block
 // when `causal`), one query row per (sequence, block position, head).  `part` holds the
 // per-split partials (attn_partial_floats floats).
-hipError_t launch_attention(int dt, const AttnPlan& p, const void* q, const void* kblk,
+hipError_t launch_attention(int dt, const AttnPlan& p, const float* q, const void* kblk,
                             const void* vblkT, const KvLayer& kv, int batch, int B, int Bp,
-                            int Hq, int Hkv, int d, int causal, float* part, void* o,
+                            int Hq, int Hkv, int d, int causal, float* part, float* o,
                             hipStream_t st);
 
 // ---- row kernels (elementwise.hip) ----
@@ -115,7 +116,6 @@ struct EmbedArgs {
   const void* E;
   int V, D;
   float* h;
-  void* hb;
   float* hdbg;
   unsigned long long* keys;
   int n_keys;
@@ -125,7 +125,7 @@ struct EmbedArgs {
   double rope_base;
   float2* rope;             // [batch*B, hd/2] out
 };
-// h[r] = E[token(r)] (float32) and hb[r] = the same row in the model dtype, r = b*B + j:
+// h[r] = E[token(r)] (float32), r = b*B + j:
 // token = anchor[b] for j == 0, else mask_id (mode 0) or ids[b*(B-1) + j-1] (mode 1).
 // Also writes the rows' RoPE (cos, sin) table and zeroes the argmax keys.
 hipError_t launch_embed(int dt, const EmbedArgs& a, hipStream_t st);

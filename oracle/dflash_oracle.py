@@ -15,6 +15,14 @@ default; the pin tests also run it in float64), straight from the definitions, w
 no blocking, fusion or reordering.  Readings taken where the pages are silent are
 listed beside the function that takes them.
 
+Storage type (reading): the models the pages measure are held in bfloat16, so the
+buffers that carry values between passes - the K/V cache and the tapped features the
+target hands to the drafter - hold bfloat16 values for such a model.  With
+``store="bf16"`` K/V are rounded to bfloat16 (nearest, ties to even) where they are
+written, attention reads every key and value as stored (the block's own included) and
+tapped features are rounded where they are handed over; all arithmetic stays in the
+working float type.  ``store=None`` (float32 models) rounds nothing.
+
 Conventions: a model's weights are a dict (keys as produced by ``synth.model_weights``),
 matrices row-major [out, in]; ``shape`` is a ``synth.ModelShape``; a KV cache is a list
 over layers of ``(K, V)`` with ``K, V`` of shape [n, H_kv, d] (K stored after RoPE).
@@ -25,6 +33,18 @@ import numpy as np
 
 # ----------------------------------------------------------------------------------------
 # Building blocks
+
+
+def to_storage(x, store):
+    """x as held in a buffer of storage type `store`: rounded to the nearest bfloat16
+    (ties to even) for "bf16", unchanged for None / "f32".  Finite inputs only."""
+    if store in (None, "f32"):
+        return x
+    assert store == "bf16", store
+    x = np.asarray(x)
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
+    return u.astype(np.uint32).view(np.float32).astype(x.dtype)
 
 
 def rmsnorm(x, g, eps, dt=np.float32):
@@ -110,10 +130,10 @@ def fuse(feats, w, shape, dt=np.float32):
     return rmsnorm(x, w["g_c"], shape.rms_eps, dt)
 
 
-def inject(feats, positions, w, shape, dt=np.float32):
+def inject(feats, positions, w, shape, dt=np.float32, store=None):
     """Context K/V for every draft layer from tapped features [DF §4.3]:
     K_i = RoPE(W_i^K H_t) at each row's absolute position, V_i = W_i^V H_t.
-    Returns a list over draft layers of (K [r, Hkv, d], V [r, Hkv, d]).
+    Returns a list over draft layers of (K [r, Hkv, d], V [r, Hkv, d]) as stored.
     Reading: K is rotated at its own position and stored rotated."""
     Ht = fuse(feats, w, shape, dt)
     r = Ht.shape[0]
@@ -121,7 +141,7 @@ def inject(feats, positions, w, shape, dt=np.float32):
     for i in range(shape.n_layers):
         K = (Ht @ np.asarray(w[f"L{i}.wk"], dtype=dt).T).reshape(r, shape.n_kv_heads, shape.head_dim)
         V = (Ht @ np.asarray(w[f"L{i}.wv"], dtype=dt).T).reshape(r, shape.n_kv_heads, shape.head_dim)
-        out.append((rope(K, positions, shape.rope_base, dt), V))
+        out.append((to_storage(rope(K, positions, shape.rope_base, dt), store), to_storage(V, store)))
     return out
 
 
@@ -129,7 +149,7 @@ def inject(feats, positions, w, shape, dt=np.float32):
 # Decoder layer shared by the drafter (bidirectional block) and the target (causal block)
 
 
-def decoder_layer(h, w, i, shape, positions, ctx_k, ctx_v, causal, dt=np.float32):
+def decoder_layer(h, w, i, shape, positions, ctx_k, ctx_v, causal, dt=np.float32, store=None):
     """One pre-norm decoder layer over the block rows h [T, D].
 
     The block's queries attend to the n context keys (all visible) followed by the
@@ -137,7 +157,8 @@ def decoder_layer(h, w, i, shape, positions, ctx_k, ctx_v, causal, dt=np.float32
     masked-diffusion block), keys j' <= j for the target's verification pass
     ([TRY] Fig. 1, causal attention in the main model).  The context rows take no part
     in Q, O, the residual or the FFN ([DF §4.3]).  FFN: SwiGLU (the drafter is
-    described as Qwen-style in [TRY]'s appendix).  Returns (h_out, k_blk, v_blk)."""
+    described as Qwen-style in [TRY]'s appendix).  The block's K/V enter attention as
+    stored (`store`).  Returns (h_out, k_blk, v_blk)."""
     T = h.shape[0]
     Hq, Hkv, d = shape.n_q_heads, shape.n_kv_heads, shape.head_dim
     G = Hq // Hkv
@@ -146,7 +167,8 @@ def decoder_layer(h, w, i, shape, positions, ctx_k, ctx_v, causal, dt=np.float32
     kb = (u @ np.asarray(w[f"L{i}.wk"], dtype=dt).T).reshape(T, Hkv, d)
     vb = (u @ np.asarray(w[f"L{i}.wv"], dtype=dt).T).reshape(T, Hkv, d)
     q = rope(q, positions, shape.rope_base, dt)
-    kb = rope(kb, positions, shape.rope_base, dt)
+    kb = to_storage(rope(kb, positions, shape.rope_base, dt), store)
+    vb = to_storage(vb, store)
 
     n = 0 if ctx_k is None else ctx_k.shape[0]
     visible = np.ones((T, n + T), dtype=bool)
@@ -178,7 +200,7 @@ def lm_logits(h, w, shared, shape, dt=np.float32):
 # Drafter step  [DF §4.4 parallel drafting; §3.2 one forward pass for the whole block]
 
 
-def draft_block(w, shared, shape, ctx, anchor, n, block, dt=np.float32):
+def draft_block(w, shared, shape, ctx, anchor, n, block, dt=np.float32, store=None):
     """One drafter forward pass over [anchor, MASK x (B-1)] at positions n .. n+B-1.
 
     ctx: list over draft layers of (K [n, Hkv, d], V [n, Hkv, d]) - the injected context.
@@ -194,7 +216,7 @@ def draft_block(w, shared, shape, ctx, anchor, n, block, dt=np.float32):
         ck, cv = ctx[i] if n else (None, None)
         if ck is not None:
             ck, cv = ck[:n], cv[:n]
-        h, _, _ = decoder_layer(h, w, i, shape, positions, ck, cv, causal=False, dt=dt)
+        h, _, _ = decoder_layer(h, w, i, shape, positions, ck, cv, causal=False, dt=dt, store=store)
         hiddens.append(h)
     z = lm_logits(h[1:], w, shared, shape, dt)
     return argmax_lowest(z), z, np.stack(hiddens)
@@ -204,12 +226,12 @@ def draft_block(w, shared, shape, ctx, anchor, n, block, dt=np.float32):
 # Target verification, acceptance, commit  [DF §4.5 decoding cycle]
 
 
-def target_forward(w, shared, shape, cache, tokens, n, taps, dt=np.float32):
+def target_forward(w, shared, shape, cache, tokens, n, taps, dt=np.float32, store=None):
     """Causal target pass over `tokens` at positions n .. n+T-1 with the first n cache rows
     visible.  Returns (g [T] greedy ids, logits [T, V], feats [T, k*D] = the tapped layer
     outputs concatenated in tap order, new_kv list of (K [T,Hkv,d], V [T,Hkv,d]),
     hiddens [L+1, T, D]).  A tap is the output of the whole decoder layer (after both
-    residual adds, before the final norm) - reading."""
+    residual adds, before the final norm) - reading; feats and new_kv are as stored."""
     tokens = np.asarray(tokens, dtype=np.int64)
     T = tokens.shape[0]
     positions = n + np.arange(T)
@@ -222,19 +244,19 @@ def target_forward(w, shared, shape, cache, tokens, n, taps, dt=np.float32):
             ck, cv = cache[i][0][:n], cache[i][1][:n]
         else:
             ck, cv = None, None
-        h, kb, vb = decoder_layer(h, w, i, shape, positions, ck, cv, causal=True, dt=dt)
+        h, kb, vb = decoder_layer(h, w, i, shape, positions, ck, cv, causal=True, dt=dt, store=store)
         new_kv.append((kb, vb))
         hiddens.append(h)
         if i in taps:
             tapped[i] = h
-    feats = np.concatenate([tapped[t] for t in taps], axis=-1) if taps else None
+    feats = to_storage(np.concatenate([tapped[t] for t in taps], axis=-1), store) if taps else None
     z = lm_logits(h, w, shared, shape, dt)
     return argmax_lowest(z), z, feats, new_kv, np.stack(hiddens)
 
 
-def verify(w, shared, shape, cache, block_ids, n, taps, dt=np.float32):
+def verify(w, shared, shape, cache, block_ids, n, taps, dt=np.float32, store=None):
     """Verification of y = [x, d_1 .. d_{B-1}] in one causal target pass [DF §4.5 step 2]."""
-    return target_forward(w, shared, shape, cache, block_ids, n, taps, dt)
+    return target_forward(w, shared, shape, cache, block_ids, n, taps, dt, store)
 
 
 def accept(draft_ids, g):
@@ -257,13 +279,14 @@ def append_kv(cache, new_kv, count):
     return out
 
 
-def commit(target_cache, draft_ctx, new_kv, feats, tau, n, draft_w, draft_shape, dt=np.float32):
+def commit(target_cache, draft_ctx, new_kv, feats, tau, n, draft_w, draft_shape, dt=np.float32,
+           store=None):
     """Commit/rollback [DF §4.5]: the target keeps rows n .. n+tau-1 (anchor and accepted
     drafts) and drops the rest; the drafter's context receives the injected features of
     the same rows at their positions ([TRY]: the drafter's own KV cache is fed by
     injection from the main model's pass).  Returns (target_cache, draft_ctx)."""
     target_cache = append_kv(target_cache, new_kv, tau)
-    inj = inject(feats[:tau], n + np.arange(tau), draft_w, draft_shape, dt)
+    inj = inject(feats[:tau], n + np.arange(tau), draft_w, draft_shape, dt, store)
     draft_ctx = append_kv(draft_ctx, inj, tau)
     return target_cache, draft_ctx
 
@@ -273,27 +296,27 @@ def empty_cache(shape, dt=np.float32):
     return [(z, z) for _ in range(shape.n_layers)]
 
 
-def prefill(target_w, shared, tshape, draft_w, dshape, prompt, taps, dt=np.float32):
+def prefill(target_w, shared, tshape, draft_w, dshape, prompt, taps, dt=np.float32, store=None):
     """Causal target pass over the prompt from an empty cache; the drafter's context is
     injected from the prompt's tapped features; the first anchor is the greedy token at
     the last prompt row.  Returns (target_cache, draft_ctx, anchor)."""
     n = len(prompt)
-    g, _, feats, new_kv, _ = target_forward(target_w, shared, tshape, None, prompt, 0, taps, dt)
+    g, _, feats, new_kv, _ = target_forward(target_w, shared, tshape, None, prompt, 0, taps, dt, store)
     tcache = append_kv(empty_cache(tshape, dt), new_kv, n)
-    dctx = inject(feats, np.arange(n), draft_w, dshape, dt)
+    dctx = inject(feats, np.arange(n), draft_w, dshape, dt, store)
     return tcache, dctx, int(g[-1])
 
 
-def greedy_decode(target_w, shared, tshape, prompt, n_new, dt=np.float32):
+def greedy_decode(target_w, shared, tshape, prompt, n_new, dt=np.float32, store=None):
     """Plain autoregressive greedy decoding with the target ([DF §1]); the reference that
     speculative decoding must reproduce exactly ([DF §4.5] lossless guarantee)."""
     prompt = list(int(t) for t in prompt)
-    g, _, _, new_kv, _ = target_forward(target_w, shared, tshape, None, prompt, 0, (), dt)
+    g, _, _, new_kv, _ = target_forward(target_w, shared, tshape, None, prompt, 0, (), dt, store)
     cache = append_kv(empty_cache(tshape, dt), new_kv, len(prompt))
     out = [int(g[-1])]
     n = len(prompt)
     while len(out) < n_new:
-        g, _, _, new_kv, _ = target_forward(target_w, shared, tshape, cache, [out[-1]], n, (), dt)
+        g, _, _, new_kv, _ = target_forward(target_w, shared, tshape, cache, [out[-1]], n, (), dt, store)
         cache = append_kv(cache, new_kv, 1)
         n += 1
         out.append(int(g[0]))
@@ -301,24 +324,24 @@ def greedy_decode(target_w, shared, tshape, prompt, n_new, dt=np.float32):
 
 
 def spec_decode(target_w, draft_w, shared, tshape, dshape, prompt, n_new, block, taps,
-                draft_override=None, dt=np.float32):
+                draft_override=None, dt=np.float32, store=None):
     """Speculative decoding cycles [DF §4.5]: draft a block, verify it, accept the longest
     matching prefix plus the bonus token, commit, repeat.  `draft_override(cycle, anchor,
     drafts)` may replace the drafter's ids (random or forced drafts) - the emitted stream
     must not depend on it.  Returns (tokens [n_new], taus)."""
-    tcache, dctx, anchor = prefill(target_w, shared, tshape, draft_w, dshape, prompt, taps, dt)
+    tcache, dctx, anchor = prefill(target_w, shared, tshape, draft_w, dshape, prompt, taps, dt, store)
     n = len(prompt)
     out = [anchor]
     taus = []
     cycle = 0
     while len(out) < n_new:
-        drafts, _, _ = draft_block(draft_w, shared, dshape, dctx, anchor, n, block, dt)
+        drafts, _, _ = draft_block(draft_w, shared, dshape, dctx, anchor, n, block, dt, store)
         if draft_override is not None:
             drafts = np.asarray(draft_override(cycle, anchor, drafts), dtype=np.int64)
         block_ids = np.concatenate([[anchor], drafts])
-        g, _, feats, new_kv, _ = verify(target_w, shared, tshape, tcache, block_ids, n, taps, dt)
+        g, _, feats, new_kv, _ = verify(target_w, shared, tshape, tcache, block_ids, n, taps, dt, store)
         a, tau, bonus = accept(drafts, g)
-        tcache, dctx = commit(tcache, dctx, new_kv, feats, tau, n, draft_w, dshape, dt)
+        tcache, dctx = commit(tcache, dctx, new_kv, feats, tau, n, draft_w, dshape, dt, store)
         out.extend(int(t) for t in drafts[:a])
         out.append(bonus)
         taus.append(tau)

@@ -45,6 +45,23 @@ def assert_ids(gpu_ids, ora_ids, ora_logits, what):
     return int(checked.sum())
 
 
+def assert_accept(tau, bonus, gpu_g, drafts, og, oz, what):
+    """(tau, bonus) must equal the oracle's acceptance where none of the rows that decide
+    it (0 .. a) is a near-tie of the oracle's logits; otherwise they must be the greedy
+    rule applied to the kernel's own argmax row (checked here with a plain loop)."""
+    drafts = [int(x) for x in drafts]
+    a, t, bo = O.accept(np.asarray(drafts), og)
+    if np.all(O.top2_gap(np.asarray(oz[:a + 1], dtype=np.float64)) >= NEAR_TIE):
+        assert (int(tau), int(bonus)) == (t, bo), f"{what}: ({tau}, {bonus}) != oracle ({t}, {bo})"
+        return True
+    gg = [int(x) for x in gpu_g]
+    a2 = 0
+    while a2 < len(drafts) and drafts[a2] == gg[a2]:
+        a2 += 1
+    assert (int(tau), int(bonus)) == (a2 + 1, gg[a2]), f"{what}: not the rule on its own argmax"
+    return False
+
+
 class Setup:
     """Drafter (+ target) of a workload on the GPU, with numpy float32 copies for the oracle."""
 
@@ -66,6 +83,11 @@ class Setup:
     @property
     def st(self):
         return torch.float32 if self.w.dtype == "f32" else torch.bfloat16
+
+    @property
+    def store(self):
+        """Storage type of the cache and of handed-over features, as the oracle takes it."""
+        return None if self.w.dtype == "f32" else "bf16"
 
     def kv(self, shape, capacity, permute_pages=True, seed=0, spare=0):
         g = torch.Generator().manual_seed(seed)

@@ -9,8 +9,8 @@ import oracle as O
 import synth
 from block_diffusion_drafter_03_amd import runtime as rt
 
-from harness import (DEV, TOL, Setup, assert_close, assert_ids, assert_rows_close, inject_all,
-                     read_cache)
+from harness import (DEV, TOL, Setup, assert_accept, assert_close, assert_ids, assert_rows_close,
+                     inject_all, read_cache)
 
 pytestmark = pytest.mark.gpu
 
@@ -41,12 +41,12 @@ def test_inject_and_draft_block(name):
     assert kv.err.item() == 0
     a_np = anchor.cpu().numpy()
     for b, n in enumerate(lens):
-        ctx = O.inject(synth.to_numpy(feats[b]), np.arange(n), S.np_dw, m)
+        ctx = O.inject(synth.to_numpy(feats[b]), np.arange(n), S.np_dw, m, store=S.store)
         for l in range(m.n_layers):
             K, V = read_cache(kv, l, b, n)
             assert_close(K, ctx[l][0], tol, f"{name} ctx K layer {l} seq {b}")
             assert_close(V, ctx[l][1], tol, f"{name} ctx V layer {l} seq {b}")
-        o_ids, o_z, o_hid = O.draft_block(S.np_dw, S.np_shared, m, ctx, int(a_np[b]), n, B)
+        o_ids, o_z, o_hid = O.draft_block(S.np_dw, S.np_shared, m, ctx, int(a_np[b]), n, B, store=S.store)
         for l in range(m.n_layers + 1):
             assert_close(hid[l, b].cpu().numpy(), o_hid[l], tol, f"{name} hidden layer {l} seq {b}")
         assert_rows_close(logits[b].cpu().numpy(), o_z, tol, f"{name} logits seq {b}")
@@ -73,7 +73,7 @@ def _forced_block(S, np_cache, n, anchor, B, f, rng):
     w = S.w
     toks = [int(anchor)]
     for _ in range(f):
-        g, _, _, _, _ = O.verify(S.np_tw, S.np_shared, w.target, np_cache, toks, n, w.taps)
+        g, _, _, _, _ = O.verify(S.np_tw, S.np_shared, w.target, np_cache, toks, n, w.taps, store=S.store)
         toks.append(int(g[-1]))
     while len(toks) < B:
         toks.append(int(rng.integers(0, w.target.vocab)))
@@ -107,15 +107,14 @@ def test_verify_accept(name):
     torch.cuda.synchronize()
     assert kv.err.item() == 0
     for b, n in enumerate(lens):
-        og, oz, of, onew, ohid = O.verify(S.np_tw, S.np_shared, m, np_cache[b], blocks[b], n, w.taps)
+        og, oz, of, onew, ohid = O.verify(S.np_tw, S.np_shared, m, np_cache[b], blocks[b], n, w.taps,
+                                          store=S.store)
         for l in range(m.n_layers + 1):
             assert_close(hid[l, b].cpu().numpy(), ohid[l], tol, f"{name} verify hidden {l} seq {b}")
         assert_rows_close(logits[b].cpu().numpy(), oz, tol, f"{name} verify logits seq {b}")
         assert_close(synth.to_numpy(feats[b]), of, tol, f"{name} tapped feats seq {b}")
         assert_ids(g[b].cpu().numpy(), og, oz, f"{name} target argmax seq {b}")
-        gb = g[b].cpu().numpy()
-        a, t, bo = O.accept(np.array(blocks[b][1:]), gb)
-        assert (int(tau[b]), int(bonus[b])) == (t, bo)
+        assert_accept(tau[b], bonus[b], g[b].cpu().numpy(), blocks[b][1:], og, oz, f"{name} accept seq {b}")
         assert 1 <= int(tau[b]) <= B
         # the block's K/V were written at n .. n+B-1
         for l in range(m.n_layers):
@@ -125,7 +124,8 @@ def test_verify_accept(name):
             Kc, Vc = np_cache[b][l]
             np.testing.assert_array_equal(K[:n], Kc)   # the old rows are untouched
     # forced prefixes: full acceptance for sequence 0 (f = B-1), when no near-tie decides
-    og, oz, _, _, _ = O.verify(S.np_tw, S.np_shared, m, np_cache[0], blocks[0], lens[0], w.taps)
+    og, oz, _, _, _ = O.verify(S.np_tw, S.np_shared, m, np_cache[0], blocks[0], lens[0], w.taps,
+                               store=S.store)
     if np.all(O.top2_gap(oz) >= 1e-2):
         assert int(tau[0]) == B
 
@@ -150,7 +150,7 @@ def test_block_of_one_is_single_token_decode(name):
     rt.verify_accept(S.target, kv, tok[:, 0].contiguous(), None, 1, None, g, tau, bonus, ws, logits, hid)
     torch.cuda.synchronize()
     for b, n in enumerate(lens):
-        og, oz, _, _, ohid = O.verify(S.np_tw, S.np_shared, m, np_cache[b], [7 + b], n, ())
+        og, oz, _, _, ohid = O.verify(S.np_tw, S.np_shared, m, np_cache[b], [7 + b], n, (), store=S.store)
         assert_close(hid[-1, b].cpu().numpy(), ohid[-1], tol, f"{name} B=1 verify seq {b}")
         assert int(tau[b]) == 1 and int(bonus[b]) == int(g[b, 0])
     # drafter with B = 1
@@ -164,8 +164,8 @@ def test_block_of_one_is_single_token_decode(name):
     rt.draft_block(S.draft, dkv, anchor, 1, ids, dws, None, dh)
     torch.cuda.synchronize()
     for b, n in enumerate(lens):
-        ctx = O.inject(synth.to_numpy(feats[b]), np.arange(n), S.np_dw, w.draft)
-        _, _, ohid = O.draft_block(S.np_dw, S.np_shared, w.draft, ctx, int(anchor[b]), n, 1)
+        ctx = O.inject(synth.to_numpy(feats[b]), np.arange(n), S.np_dw, w.draft, store=S.store)
+        _, _, ohid = O.draft_block(S.np_dw, S.np_shared, w.draft, ctx, int(anchor[b]), n, 1, store=S.store)
         assert_close(dh[-1, b].cpu().numpy(), ohid[-1], tol, f"{name} B=1 draft seq {b}")
 
 
@@ -263,11 +263,11 @@ def test_speculative_cycles_reproduce_greedy_decoding(name):
     assert tkv.err.item() == 0 and dkv.err.item() == 0
     assert torch.equal(tkv.seq_len, dkv.seq_len)
     for b in range(batch):
-        ref = O.greedy_decode(S.np_tw, S.np_shared, T, prompts[b], n_new)
+        ref = O.greedy_decode(S.np_tw, S.np_shared, T, prompts[b], n_new, store=S.store)
         got = emitted[b][:n_new]
         if got != ref:
             # allowed only past a near-tie of the oracle's own logits
             i = next(i for i in range(n_new) if got[i] != ref[i])
             _, z, _, _, _ = O.target_forward(S.np_tw, S.np_shared, T, None,
-                                             np.concatenate([prompts[b], ref[:i]]), 0, ())
+                                             np.concatenate([prompts[b], ref[:i]]), 0, (), store=S.store)
             assert O.top2_gap(z[-1]) < 1e-2, f"{name} seq {b}: stream differs at {i}"

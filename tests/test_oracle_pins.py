@@ -516,3 +516,43 @@ def test_anchor_row_sits_where_the_target_verifies_it():
     _, _, hid_d = O.draft_block(dw, shw, sh, ctx, 11, 6, 1, F64)
     _, _, _, _, hid_t = O.verify(tw, shw, sh, cache, [11], 6, (), F64)
     np.testing.assert_allclose(hid_d[1, 0], hid_t[1, 0], rtol=1e-10, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------------------
+# storage type of the cache and of handed-over features (bfloat16 models)
+
+
+def test_bf16_storage_rounding_matches_library_and_hand_values():
+    import torch
+    g = np.random.default_rng(5)
+    x = np.concatenate([g.standard_normal(20000) * s for s in (1e-30, 1e-3, 1.0, 1e3, 1e30)])
+    # exact halfway cases between neighbouring bfloat16 values, both parities
+    base = g.standard_normal(2000).astype(np.float32)
+    u = (base.view(np.uint32) & 0xFFFF0000) | 0x8000
+    ties = u.view(np.float32)
+    x = np.concatenate([x.astype(np.float32), ties])
+    want = torch.from_numpy(x).to(torch.bfloat16).to(torch.float32).numpy()
+    got = O.to_storage(x, "bf16")
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+    # 1 + 2^-8 lies halfway between 1 and 1 + 2^-7: ties go to the even mantissa (1);
+    # 1 + 3*2^-8 lies halfway between 1 + 2^-7 (odd) and 1 + 2^-6 (even)
+    hand = np.array([1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, -(1 + 2.0 ** -8), 3.0, 1 + 2.0 ** -7], np.float32)
+    assert O.to_storage(hand, "bf16").tolist() == [1.0, 1 + 2.0 ** -6, -1.0, 3.0, 1 + 2.0 ** -7]
+    assert O.to_storage(hand, None) is hand and O.to_storage(hand, "f32") is hand
+
+
+def test_bf16_storage_applies_to_cache_rows_and_taps():
+    wl, dw, tw, sh = _models(931)
+    feats = np.random.default_rng(1).standard_normal((6, 2 * TINY_SHAPE.hidden))
+    raw = O.inject(feats, np.arange(6), dw, TINY_SHAPE, F64)
+    st = O.inject(feats, np.arange(6), dw, TINY_SHAPE, F64, store="bf16")
+    for (K, V), (Ks, Vs) in zip(raw, st):
+        assert np.array_equal(Ks, O.to_storage(K, "bf16")) and np.array_equal(Vs, O.to_storage(V, "bf16"))
+    g, z, f, new_kv, hid = O.target_forward(tw, sh, TINY_TGT, None, [3, 5, 7], 0, (0, 2), F64, store="bf16")
+    assert np.array_equal(f, O.to_storage(np.concatenate([hid[1], hid[3]], axis=-1), "bf16"))
+    for k, v in new_kv:
+        assert np.array_equal(k, O.to_storage(k, "bf16")) and np.array_equal(v, O.to_storage(v, "bf16"))
+    # only the storage differs: the first layer's queries see the same keys up to rounding
+    g0, z0, f0, _, hid0 = O.target_forward(tw, sh, TINY_TGT, None, [3, 5, 7], 0, (0, 2), F64)
+    assert np.array_equal(hid[0], hid0[0])
+    assert 0 < np.max(np.abs(hid[1] - hid0[1])) < 1e-2 * np.max(np.abs(hid0[1]))
