@@ -9,8 +9,8 @@ All inputs are seeded synthetic tensors already resident in HBM.
 
 Prints one JSON line: draft tokens/s of the draft block (b * (B-1) / T_draft_block) as
 `value`, the cycle time as `ms_per_step`, per-call microseconds, the roofline of the
-dominant kernel (skinny weight-streaming GEMM of the gate/up projections) timed with HIP
-events inside the timed region, and the CPU oracle timed on the host on a small sample.
+dominant kernel (the weight-streaming GEMV of the gate/up projections with its SwiGLU
+epilogue) timed with HIP events inside the timed region, and the CPU oracle timed on the host on a small sample.
 """
 from __future__ import annotations
 
@@ -32,6 +32,30 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "gemv_gate_up.qwen3_8b_b1_ctx4k.pmc_traffic.txt")
+
+
+def measured_traffic():
+    """HBM bytes per launch of the roofline kernel from the committed FETCH_SIZE/WRITE_SIZE
+    summary, or None when the kernel's sources have changed since the counters were taken."""
+    import hashlib
+    try:
+        fields = {}
+        for line in open(TRAFFIC_SUMMARY):
+            k, sep, v = line.partition(":")
+            if sep:
+                fields[k.strip()] = v.strip()
+        h = hashlib.sha256()
+        for src in fields["kernel_sources"].split():
+            with open(os.path.join(ROOT, src), "rb") as f:
+                h.update(f.read())
+        if h.hexdigest() != fields["kernel_sources_sha256"]:
+            return None
+        return int(fields["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -39,6 +63,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-reps", type=int, default=3)
+    ap.add_argument("--probe-copy", type=int, default=0, metavar="MB",
+                    help="after the run, one elementwise pass reading and writing MB MiB "
+                         "(calibrates HBM byte counters of profiler runs)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the drafter step is data-parallel over sequences "
@@ -146,9 +173,11 @@ def main():
     tau_mean = (seq_after - seq_before) / K
     draft_tok_s = 1 * (B - 1) / (us_draft * 1e-6)
 
-    # roofline of the gate/up GEMM launches: algorithmic bytes = weights + input rows
-    bytes_d = 2 * D.ffn * D.hidden * 2 + B * D.hidden * 2
-    bytes_t = 2 * T.ffn * T.hidden * 2 + B * T.hidden * 2
+    # roofline of the gate/up GEMM launches: algorithmic bytes = bf16 weights + gain, the
+    # float32 hidden rows read and the float32 SwiGLU rows written
+    def gu_bytes(m):
+        return 2 * m.ffn * m.hidden * 2 + m.hidden * 2 + B * m.hidden * 4 + B * m.ffn * 4
+    bytes_d, bytes_t = gu_bytes(D), gu_bytes(T)
     nbytes = [bytes_d if (i % per_step) < D.n_layers else bytes_t for i in range(len(gu_ms))]
     achieved = sum(nbytes) / (sum(gu_ms) * 1e-3) / 1e9
     avg_bytes = sum(nbytes) / len(nbytes)
@@ -198,9 +227,9 @@ def main():
         "L_us_per_token": round((us_draft + us_verify + us_inject + us_commit) / max(tau_mean, 1e-9), 2),
         "draft_block_hbm_gbs": round(hbm_bytes_draft / (us_draft * 1e-6) / 1e9, 1),
         "draft_block_hbm_frac": round(hbm_bytes_draft / (us_draft * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-        "roofline": {"kernel": "gemm_skinny_bf16 (gate/up projections, M=16)", "bound": "hbm",
+        "roofline": {"kernel": "gemm_gemv_bf16 (gate/up projection + SwiGLU, M=16)", "bound": "hbm",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
                      "bytes_per_launch": int(avg_bytes), "avg_launch_us": round(avg_us, 2),
                      "launches": len(gu_ms)},
         "kernels": breakdown,
@@ -209,6 +238,13 @@ def main():
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, dw, shared, feats0, anchor, args.cpu_reps, draft_tok_s)
     print(json.dumps(out), flush=True)
+    if args.probe_copy > 0:
+        src = torch.ones(args.probe_copy << 18, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.neg(src, out=dst)      # reads and writes exactly probe_copy MiB each
+        torch.cuda.synchronize()
+        log(f"probe copy: {args.probe_copy} MiB read + {args.probe_copy} MiB written")
 
 
 def cpu_baseline(w, dw, shared, feats0, anchor, reps, gpu_value):

@@ -40,6 +40,16 @@ DF_DEV void load8(const bf16* p, float v[8]) {
   for (int e = 0; e < 8; ++e) v[e] = (float)x[e];
 }
 
+// Entry i (< 8) of a small pointer table held in a kernel argument, by unrolled selects:
+// a dynamically indexed private array would be placed in scratch memory.
+template <typename P>
+DF_DEV P pick8(P const (&t)[8], int i) {
+  P p = t[0];
+#pragma unroll
+  for (int j = 1; j < 8; ++j) p = i == j ? t[j] : p;
+  return p;
+}
+
 // Wave64 reductions (xor butterflies over all 64 lanes).
 DF_DEV float wave_sum(float v) {
 #pragma unroll

@@ -117,12 +117,12 @@ DF_DEV void epi_pair(const EpiArgs& e, int row, int col, float v0, float v1) {
       if (c < e.Hkv * hd) {
         const int kh = c / hd, el = c - kh * hd, i = el >> 1;
         const float2 cs = e.rope[(size_t)row * (hd >> 1) + i];
-        T* kc = (T*)e.kp[l] + (((size_t)page * e.Hkv + kh) * 64 + slot) * hd;
+        T* kc = (T*)pick8(e.kp, l) + (((size_t)page * e.Hkv + kh) * 64 + slot) * hd;
         kc[i] = from_f<T>(v0 * cs.x - v1 * cs.y);
         kc[i + hd / 2] = from_f<T>(v1 * cs.x + v0 * cs.y);
       } else {
         const int cv = c - e.Hkv * hd, vh = cv / hd, el = cv - vh * hd;
-        T* vc = (T*)e.vp[l] + (((size_t)page * e.Hkv + vh) * hd + el) * 64 + slot;
+        T* vc = (T*)pick8(e.vp, l) + (((size_t)page * e.Hkv + vh) * hd + el) * 64 + slot;
         vc[0] = from_f<T>(v0);
         vc[64] = from_f<T>(v1);
       }

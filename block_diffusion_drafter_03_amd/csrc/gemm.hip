@@ -17,24 +17,12 @@
 
 namespace dflash {
 
+// Row n of the B operand (W rows, possibly split into equal segments at different
+// addresses), read straight from the kernel argument.
 template <typename T>
-struct BRows {
-  const T* ptr[8];
-  int seg_rows, nseg, ldb;
-  DF_DEV const T* row(int n) const {
-    const int s = nseg > 1 ? n / seg_rows : 0;
-    return ptr[s] + (size_t)(n - s * seg_rows) * ldb;
-  }
-};
-
-template <typename T>
-static BRows<T> brows(const BSeg& b) {
-  BRows<T> o;
-  for (int i = 0; i < 8; ++i) o.ptr[i] = (const T*)b.ptr[i];
-  o.seg_rows = b.seg_rows;
-  o.nseg = b.nseg;
-  o.ldb = b.ldb;
-  return o;
+DF_DEV const T* brow(const BSeg& b, int n) {
+  const int s = b.nseg > 1 ? n / b.seg_rows : 0;
+  return (const T*)pick8(b.ptr, s) + (size_t)(n - s * b.seg_rows) * b.ldb;
 }
 
 // A row m of the GEMM -> row of the A buffer (skipping the anchor row of each block when
@@ -121,7 +109,6 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_bf16(GemmArgs ga) {
   __shared__ f32x4 red[NW][MT][64];
   __shared__ float ss_red[NW][MT * 16];
   __shared__ float rstd[MT * 16];
-  const BRows<bf16> Bd = *reinterpret_cast<const BRows<bf16>*>(&ga.B);
 
   const TA* arow[MT];
 #pragma unroll
@@ -135,7 +122,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_bf16(GemmArgs ga) {
 
   for (int t = blockIdx.x; t < n_tiles; t += gridDim.x) {
     const int n = min(t * 16 + r, N - 1);
-    const bf16* wrow = Bd.row(n) + g * 8;
+    const bf16* wrow = brow<bf16>(ga.B, n) + g * 8;
     f32x4 acc[MT];
     float ss[MT];
 #pragma unroll
@@ -210,24 +197,26 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_bf16(GemmArgs ga) {
   }
 }
 
-// M <= 16: 16 waves (1024 threads) split K, one 32-wide step per MFMA (pair).  With ASTAT
-// each wave keeps its K-slice of the A rows for all of the workgroup's tiles, already
-// multiplied by the RMSNorm gain and split into (hi, lo) (rstd is applied in the
-// epilogue): hi in registers, lo in LDS (128 KB: the workgroup owns the CU anyway), so
-// the vector memory path carries only W: a wave issues all of its W loads of a tile at
-// once (<= 8 steps, 8 KB) and 16 waves per CU keep >= 128 KB in flight.  Without ASTAT
-// (K/16 > 256) A and W are streamed together in chunks of CHS steps.
+// M <= 16: NW waves split K, one 32-wide step per MFMA (pair).  With ASTAT each wave keeps
+// its K-slice of the A rows for all of the workgroup's tiles, already multiplied by the
+// RMSNorm gain and split into (hi, lo) (rstd is applied in the epilogue): hi in registers,
+// lo in LDS (128 KB: one workgroup owns the CU), so the vector memory path carries only W:
+// a wave issues all of its W loads of a tile at once (CH steps, 1 KB each) and the CU keeps
+// 128 KB in flight.  Without ASTAT (K > 4096) A and W are streamed together in chunks of
+// CHS steps.  8 waves of 512 threads leave each wave 256 registers, so the stationary A,
+// a full tile of W in flight and the epilogue never spill.
 #define GEMV_MAX_TILES 8   // tiles per workgroup whose epilogue is deferred (non-argmax kinds)
+#define GEMV_NW 8          // waves per workgroup
 
-template <typename TA, bool NORM, bool ASTAT, int KIND>
-__global__ __launch_bounds__(1024) void gemm_gemv16_bf16(GemmArgs ga) {
+template <typename TA, int NW, bool NORM, bool ASTAT, int KIND>
+__global__ __launch_bounds__(NW * 64) void gemm_gemv_bf16(GemmArgs ga) {
   constexpr bool TWO = AIsFloat<TA>::value;
-  constexpr int NW = 16, CH = 8;
-  constexpr int CHS = TWO ? 4 : 8;   // streamed chunk (raw float A costs 2x the registers)
+  constexpr int CH = 128 / NW;       // stationary steps per wave (K <= 4096)
+  constexpr int CHS = 8;             // streamed chunk
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int r = lane & 15, g = lane >> 4;
   const int M = ga.M, N = ga.N, K = ga.K;
-  const int spw = (K >> 5) / NW;                 // K % 512 == 0
+  const int spw = (K >> 5) / NW;                 // K % (32 NW) == 0
   const int ks0 = w * spw;
   const int n_tiles = (N + 15) >> 4;
   __shared__ f32x4 red[NW][64];
@@ -237,7 +226,6 @@ __global__ __launch_bounds__(1024) void gemm_gemv16_bf16(GemmArgs ga) {
   __shared__ bf16x8 alo[ASTAT && TWO ? NW : 1][ASTAT && TWO ? CH : 1][64];
   // running argmax keys of wave 0's lanes (kept out of the main loop's registers)
   __shared__ unsigned long long bsh[KIND == EPI_ARGMAX ? 4 : 1][64];
-  const BRows<bf16> Bd = *reinterpret_cast<const BRows<bf16>*>(&ga.B);
   const TA* arow = (const TA*)ga.A + (size_t)a_row_index(min(r, M - 1), ga.a_skip_B) * ga.lda + g * 8;
   const bf16* gk = NORM ? (const bf16*)ga.norm_g + g * 8 : nullptr;
   int nbuf = 0;
@@ -249,7 +237,7 @@ __global__ __launch_bounds__(1024) void gemm_gemv16_bf16(GemmArgs ga) {
   // W loads of this workgroup's first tile go out before the A prologue (independent)
   bf16x8 wn[CH];
   auto load_w = [&](int t) {
-    const bf16* wrow = Bd.row(min(t * 16 + r, N - 1)) + g * 8;
+    const bf16* wrow = brow<bf16>(ga.B, min(t * 16 + r, N - 1)) + g * 8;
 #pragma unroll
     for (int s = 0; s < CH; ++s)
       if (s < spw) wn[s] = *(const bf16x8*)(wrow + (size_t)(ks0 + s) * 32);
@@ -294,7 +282,7 @@ __global__ __launch_bounds__(1024) void gemm_gemv16_bf16(GemmArgs ga) {
       // the next tile's W loads are in flight across the barrier and the reduction
       if (t + gridDim.x < n_tiles) load_w(t + gridDim.x);
     } else {
-      const bf16* wrow = Bd.row(min(t * 16 + r, N - 1)) + g * 8;
+      const bf16* wrow = brow<bf16>(ga.B, min(t * 16 + r, N - 1)) + g * 8;
       for (int c0 = 0; c0 < spw; c0 += CHS) {
         bf16x8 wf[CHS];
         float av[CHS][8];
@@ -361,7 +349,7 @@ __global__ __launch_bounds__(1024) void gemm_gemv16_bf16(GemmArgs ga) {
 }
 
 // Variant selection for M <= 16 (benchmark sweeps may force one with DFLASH_GEMV=1..2):
-// 1 = 4-wave split-K, 2 = 16-wave split-K with stationary A.
+// 1 = 4-wave split-K (gemm_skinny_bf16), 2 = gemm_gemv_bf16 (default where it fits).
 static int gemv_variant() {
   static int v = -1;
   if (v < 0) {
@@ -393,7 +381,6 @@ __global__ __launch_bounds__(256) void gemm_tiled_bf16(GemmArgs ga) {
   int t = blockIdx.x;
   if ((T & 7) == 0) t = (blockIdx.x & 7) * (T >> 3) + (blockIdx.x >> 3);
   const int m0 = (t % mt_n) * TB, n0 = (t / mt_n) * TB;
-  const BRows<bf16> Bd = *reinterpret_cast<const BRows<bf16>*>(&ga.B);
 
   const TA* ap[2];
   const bf16* bp[2];
@@ -404,7 +391,7 @@ __global__ __launch_bounds__(256) void gemm_tiled_bf16(GemmArgs ga) {
     lrow[j] = c >> 3;
     lcol[j] = (c & 7) * 8;
     ap[j] = (const TA*)ga.A + (size_t)a_row_index(min(m0 + lrow[j], M - 1), ga.a_skip_B) * ga.lda + lcol[j];
-    bp[j] = Bd.row(min(n0 + lrow[j], N - 1)) + lcol[j];
+    bp[j] = brow<bf16>(ga.B, min(n0 + lrow[j], N - 1)) + lcol[j];
   }
   const bf16* gk = NORM ? (const bf16*)ga.norm_g : nullptr;
   float ra[2][8];
@@ -500,11 +487,10 @@ __global__ __launch_bounds__(256) void gemm_f32(GemmArgs ga) {
   const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
   const int M = ga.M, N = ga.N, K = ga.K;
   const int m0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
-  const BRows<float> Bd = *reinterpret_cast<const BRows<float>*>(&ga.B);
   float acc[4][4] = {};
   const int lr = tid >> 2, lk = (tid & 3) * 4;
   const float* ap = (const float*)ga.A + (size_t)a_row_index(min(m0 + lr, M - 1), ga.a_skip_B) * ga.lda + lk;
-  const float* bp = Bd.row(min(n0 + lr, N - 1)) + lk;
+  const float* bp = brow<float>(ga.B, min(n0 + lr, N - 1)) + lk;
   const float* gk = NORM ? (const float*)ga.norm_g + lk : nullptr;
   float ss = 0.f;
   for (int k0 = 0; k0 < K; k0 += 16) {
@@ -601,18 +587,18 @@ static hipError_t launch_kind(int dt, const GemmArgs& ga, hipStream_t st) {
   const int n_tiles = (N + 15) / 16;
   if (M <= 16) {
     int v = gemv_variant();
-    if (v == 2 && (ga.K % 512 != 0 || (NORM && ga.K > 4096))) v = 1;
-    // measured on MI355X at hidden 4096: the 16-wave stationary-A kernel wins for wide
-    // outputs (gate/up, LM head) and long K (down projection); the 4-wave kernel for QKV
-    if (v < 1 || v > 2) v = (n_tiles >= 4 * num_cus() || ga.K > 4096) ? 2 : 1;
+    const bool fits = ga.K % (32 * GEMV_NW) == 0 && !(NORM && ga.K > 4096);
+    if (v < 1 || v > 2 || !fits) v = fits ? 2 : 1;
     if (v == 2) {
-      int grid = n_tiles < 2 * num_cus() ? n_tiles : 2 * num_cus();
+      // one workgroup per CU (the stationary A's LDS) walking the tiles; the deferred
+      // epilogue buffer bounds the tiles per workgroup
+      int grid = n_tiles < num_cus() ? n_tiles : num_cus();
       if (KIND != EPI_ARGMAX && grid * GEMV_MAX_TILES < n_tiles)
         grid = (n_tiles + GEMV_MAX_TILES - 1) / GEMV_MAX_TILES;
       if (ga.K <= 4096)
-        hipLaunchKernelGGL((gemm_gemv16_bf16<TA, NORM, true, KIND>), dim3(grid), dim3(1024), 0, st, ga);
+        hipLaunchKernelGGL((gemm_gemv_bf16<TA, GEMV_NW, NORM, true, KIND>), dim3(grid), dim3(GEMV_NW * 64), 0, st, ga);
       else
-        hipLaunchKernelGGL((gemm_gemv16_bf16<TA, false, false, KIND>), dim3(grid), dim3(1024), 0, st, ga);
+        hipLaunchKernelGGL((gemm_gemv_bf16<TA, GEMV_NW, false, false, KIND>), dim3(grid), dim3(GEMV_NW * 64), 0, st, ga);
       return hipGetLastError();
     }
   }

@@ -28,9 +28,13 @@
  *  - Errors the host cannot see (an unmapped page, an out-of-range token id or tau) are
  *    detected on the device: the offending row or sequence is skipped and a bit is OR-ed
  *    into dflash_kv.error_flags (when that pointer is non-NULL).
- *  - Matrices are row-major [out, in] (y = x W^T).  Storage dtype (weights, caches,
- *    features, hidden activations) is the model's dtype: float32 or bfloat16; logits and
- *    debug outputs are always float32; ids are int32.
+ *  - Matrices are row-major [out, in] (y = x W^T), two of them with their rows packed
+ *    as described at DFLASH_W_QKV and DFLASH_W_GATE_UP.  Storage dtype (weights, caches,
+ *    tapped features) is the model's dtype: float32 or bfloat16; logits and debug hidden
+ *    states are always float32; ids are int32.  Between kernels the activations of a
+ *    step live in the workspace in float32; a bfloat16 model's matrix units take them as
+ *    a compensated pair of bfloat16 values (about 16 significant bits), so the result
+ *    tracks a float32 evaluation over bfloat16 weights and caches.
  *  - Calls on distinct caches and streams may run concurrently; a model is immutable
  *    after creation.
  */
@@ -66,10 +70,15 @@ enum {
 /* Per-layer weight table: layer_w[l * DFLASH_LAYER_TENSORS + slot]. */
 enum {
   DFLASH_W_G_IN = 0,     /* [hidden]                 RMSNorm gain before attention       */
-  DFLASH_W_QKV = 1,      /* [(Hq + 2 Hkv) d, hidden] rows: q heads, k heads, v heads      */
+  DFLASH_W_QKV = 1,      /* [(Hq + 2 Hkv) d, hidden] rows: q heads, k heads, v heads;
+                            within each q and k head the rows are rotary-interleaved:
+                            packed row 2i = original row i, packed row 2i+1 = original
+                            row i + d/2 (the two inputs of one rotate-half rotation sit
+                            side by side); v heads are stored as they are               */
   DFLASH_W_O = 2,        /* [hidden, Hq d]           attention output projection          */
   DFLASH_W_G_POST = 3,   /* [hidden]                 RMSNorm gain before the FFN          */
-  DFLASH_W_GATE_UP = 4,  /* [2 ffn, hidden]          rows: gate (ffn rows), then up       */
+  DFLASH_W_GATE_UP = 4,  /* [2 ffn, hidden]          rows interleaved: packed row 2j = gate
+                            row j, packed row 2j+1 = up row j                           */
   DFLASH_W_DOWN = 5,     /* [hidden, ffn]            SwiGLU down projection               */
   DFLASH_LAYER_TENSORS = 6
 };
