@@ -4,7 +4,9 @@
 // One decoder layer is six launches (the norms, RoPE, SwiGLU and residual adds are fused
 // into them):
 // Activations stay float32 between launches (the bf16 MFMAs take them as compensated
-// hi/lo pairs); K/V and tapped features are written in the model dtype.
+// hi/lo pairs); K/V and tapped features are written in the model dtype.  For bfloat16
+// models the GEMM inputs (h, attention output, SwiGLU output, fused injection rows) live in
+// the MFMA A-fragment order, their row count padded to a multiple of 16.
 //   QKV GEMM   A = h, RMSNorm(g_in) applied on the A side; epilogue: RoPE,
 //              q / k_blk / v_blk^T (and, for verification, the block K/V into the cache)
 //   attention  split-K over [context ; block], then the log-sum-exp merge of the splits
@@ -67,18 +69,18 @@ struct StepWs {
 
 size_t step_ws(const dflash_model* m, int batch, int B, int ctx_cap, void* base, StepWs* w) {
   const dflash_model_desc& d = m->d;
-  const int dt = d.dtype, M = batch * B, Bp = round_up(B, 32);
+  const int dt = d.dtype, M = batch * B, Mp = round_up(M, 16), Bp = round_up(B, 32);
   const int D = d.hidden, Hq = d.n_q_heads, Hkv = d.n_kv_heads, hd = d.head_dim;
   StepWs t;
   t.plan = attn_plan(dt, batch, Hkv, Hq / Hkv, B, ctx_cap);
   Carve cv(base);
-  t.h = (float*)cv.take((size_t)M * D * 4);
+  t.h = (float*)cv.take((size_t)Mp * D * 4);
   t.q = (float*)cv.take((size_t)M * Hq * hd * 4);
   t.kblk = cv.take((size_t)M * Hkv * hd * esz(dt));
   t.vblkT = cv.take((size_t)batch * Hkv * hd * Bp * esz(dt));
   t.part = (float*)cv.take(dt == DFLASH_BF16 ? attn_partial_floats(t.plan, batch, Hkv, hd) * 4 : 0);
-  t.o = (float*)cv.take((size_t)M * Hq * hd * 4);
-  t.act = (float*)cv.take((size_t)M * d.ffn * 4);
+  t.o = (float*)cv.take((size_t)Mp * Hq * hd * 4);
+  t.act = (float*)cv.take((size_t)Mp * d.ffn * 4);
   t.keys = (unsigned long long*)cv.take((size_t)M * 8);
   t.rope = (float2*)cv.take((size_t)M * (hd / 2) * sizeof(float2));
   if (w) *w = t;
@@ -87,7 +89,7 @@ size_t step_ws(const dflash_model* m, int batch, int B, int ctx_cap, void* base,
 
 size_t inject_ws(const dflash_model* m, int rows, void* base, float** x, float2** rope) {
   Carve cv(base);
-  float* p = (float*)cv.take((size_t)rows * m->d.hidden * 4);
+  float* p = (float*)cv.take((size_t)round_up(rows, 16) * m->d.hidden * 4);
   float2* r = (float2*)cv.take((size_t)rows * (m->d.head_dim / 2) * sizeof(float2));
   if (x) *x = p;
   if (rope) *rope = r;
@@ -109,6 +111,7 @@ EmbedArgs embed_args(const dflash_model* m, const dflash_kv* kv, const StepWs& w
   a.V = d.vocab;
   a.D = d.hidden;
   a.h = w.h;
+  a.afrag = d.dtype == DFLASH_BF16;
   a.hdbg = hidden_dbg;
   a.keys = w.keys;
   a.n_keys = kv->batch * B;
@@ -215,6 +218,7 @@ int run_layers(const dflash_model* m, const dflash_kv* kv, int batch, int B, con
   const int D = d.hidden, Hq = d.n_q_heads, Hkv = d.n_kv_heads, hd = d.head_dim, F = d.ffn;
   const int Nqkv = (Hq + 2 * Hkv) * hd;
   const float eps = d.rms_eps;
+  const int afrag = dt == DFLASH_BF16;
   for (int l = 0; l < d.n_layers; ++l) {
     const KvLayer kvl = layer_view(kv, l);
     {  // QKV projection with RMSNorm(g_in) on the A side; RoPE / layout epilogue
@@ -244,13 +248,14 @@ int run_layers(const dflash_model* m, const dflash_kv* kv, int batch, int B, con
     {
       Timed t(DFLASH_KERNEL_ATTENTION, st);
       HIPCHK(launch_attention(dt, w.plan, w.q, w.kblk, w.vblkT, kvl, batch, B, Bp, Hq, Hkv, hd,
-                              causal, w.part, w.o, st));
+                              causal, w.part, w.o, afrag, st));
     }
     {  // O projection + residual
       GemmArgs g = gemm_args(w.o, Hq * hd, one_seg(W(m, l, DFLASH_W_O), D, Hq * hd), M, D,
                              Hq * hd, nullptr, eps, EPI_RESID);
       g.e.h = w.h;
       g.e.ldh = D;
+      g.e.afrag = afrag;
       if (int s = run_gemm(DFLASH_KERNEL_GEMM_O, dt, g, st)) return s;
     }
     {  // gate/up with RMSNorm(g_post) on the A side; SwiGLU epilogue
@@ -258,6 +263,7 @@ int run_layers(const dflash_model* m, const dflash_kv* kv, int batch, int B, con
                              W(m, l, DFLASH_W_G_POST), eps, EPI_SWIGLU);
       g.e.act = w.act;
       g.e.F = F;
+      g.e.afrag = afrag;
       if (int s = run_gemm(DFLASH_KERNEL_GEMM_GATE_UP, dt, g, st)) return s;
     }
     {  // down projection + residual (+ tap / debug copies)
@@ -265,6 +271,7 @@ int run_layers(const dflash_model* m, const dflash_kv* kv, int batch, int B, con
                              EPI_RESID);
       g.e.h = w.h;
       g.e.ldh = D;
+      g.e.afrag = afrag;
       g.e.hdbg = hidden_dbg ? hidden_dbg + (size_t)(l + 1) * M * D : nullptr;
       if (feats_out) {
         for (size_t t = 0; t < m->taps.size(); ++t)
@@ -280,16 +287,17 @@ int run_layers(const dflash_model* m, const dflash_kv* kv, int batch, int B, con
   return DFLASH_OK;
 }
 
-// LM head with RMSNorm(g_f) on the A side and the argmax epilogue over rows of h
-// (skipping each block's anchor row when skipB != 0).
+// LM head with RMSNorm(g_f) on the A side and the argmax epilogue over every row of h
+// (argmax keys per row; the optional logits copy leaves out each block's anchor row when
+// skipB != 0).
 int run_lm_head(const dflash_model* m, const StepWs& w, int rows, int skipB, float* logits,
                 hipStream_t st) {
   const dflash_model_desc& d = m->d;
   GemmArgs g = gemm_args(w.h, d.hidden, one_seg(d.lm_head, d.vocab, d.hidden), rows, d.vocab,
                          d.hidden, d.final_norm, d.rms_eps, EPI_ARGMAX);
-  g.a_skip_B = skipB;
   g.e.keys = w.keys;
   g.e.logits = logits;
+  g.e.skipB = skipB;
   return run_gemm(DFLASH_KERNEL_LM_HEAD, d.dtype, g, st);
 }
 
@@ -388,6 +396,7 @@ int dflash_inject_ctx(const dflash_model* m, dflash_kv* kv, const void* feats, i
     GemmArgs g = gemm_args(feats, Kc, one_seg(d.w_c, D, Kc), n_rows, D, Kc, nullptr, d.rms_eps,
                            EPI_STORE_F32);
     g.a_bf16 = dt == DFLASH_BF16;
+    g.e.afrag = dt == DFLASH_BF16;
     g.e.out = x;
     g.e.ldo = D;
     if (int s = run_gemm(DFLASH_KERNEL_INJECT_FUSE, dt, g, st)) return s;
@@ -443,10 +452,9 @@ int dflash_draft_block(const dflash_model* m, const dflash_kv* kv, const int32_t
   e = run_layers(m, kv, batch, B, w, /*causal=*/0, /*write_cache=*/0, nullptr, hidden_dbg, st);
   if (e) return e;
   if (B == 1) return DFLASH_OK;   // a block of one has no masked position to draft
-  const int Mp = batch * (B - 1);
-  e = run_lm_head(m, w, Mp, B, logits_dbg, st);
+  e = run_lm_head(m, w, M, B, logits_dbg, st);
   if (e) return e;
-  HIPCHK(launch_unpack_ids(w.keys, Mp, draft_ids, st));
+  HIPCHK(launch_unpack_ids(w.keys, batch, B, draft_ids, st));
   return DFLASH_OK;
 }
 

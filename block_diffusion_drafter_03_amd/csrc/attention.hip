@@ -39,7 +39,8 @@ struct AttnArgs {
   int n_splits, split_len, n_rg, causal;
   float scale_log2;
   float* part;         // [(b, kvh, rg, s)][64][PSTRIDE]  (O, then m, l per row)
-  float* out;          // [batch*B, Hq*AD]
+  float* out;          // [batch*B, Hq*AD], A-fragment order when out_afrag
+  int out_afrag;
 };
 
 // LDS layouts of one 64-key step (one page slice of one KV head), padded by 16 bytes per row
@@ -272,7 +273,8 @@ __global__ __launch_bounds__(256) void attn_merge_bf16(AttnArgs a) {
   }
   const float inv = 1.f / lt;
   const int gq = rho / a.B, j = rho % a.B;
-  float* out = a.out + (size_t)(b * a.B + j) * a.Hq * AD + (size_t)(kvh * a.G + gq) * AD + 4 * t;
+  const int m = b * a.B + j, k = (kvh * a.G + gq) * AD + 4 * t;
+  float* out = a.out + (a.out_afrag ? afrag_off(m, k, (a.Hq * AD) >> 5) : (size_t)m * a.Hq * AD + k);
   *(float4*)out = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
 }
 
@@ -421,7 +423,7 @@ size_t attn_partial_floats(const AttnPlan& p, int batch, int Hkv, int d) {
 hipError_t launch_attention(int dt, const AttnPlan& p, const float* q, const void* kblk,
                             const void* vblkT, const KvLayer& kv, int batch, int B, int Bp,
                             int Hq, int Hkv, int d, int causal, float* part, float* o,
-                            hipStream_t st) {
+                            int o_afrag, hipStream_t st) {
   const int G = Hq / Hkv;
   if (dt == BF16) {
     AttnArgs a;
@@ -447,6 +449,7 @@ hipError_t launch_attention(int dt, const AttnPlan& p, const float* q, const voi
     a.scale_log2 = 1.4426950408889634f / sqrtf((float)d);
     a.part = part;
     a.out = o;
+    a.out_afrag = o_afrag;
     dim3 grid(p.n_ctx_splits, Hkv * p.n_rg, batch);
     hipLaunchKernelGGL(attn_splitk_bf16, grid, dim3(256), 0, st, a);
     hipError_t e = hipGetLastError();

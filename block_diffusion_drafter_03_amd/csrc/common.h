@@ -40,6 +40,22 @@ DF_DEV void load8(const bf16* p, float v[8]) {
   for (int e = 0; e < 8; ++e) v[e] = (float)x[e];
 }
 
+// ---- MFMA-fragment layouts in HBM (bfloat16 models) ----
+// A v_mfma_f32_16x16x32_bf16 operand covers 16 rows x 32 k as 64 lanes x 8 values: lane
+// l = 16 g + r holds row r, k = 8g .. 8g+7.  Data that feeds such operands is stored in
+// that order, so every wave-wide 16-byte load reads 1 KB contiguous.
+//  * bf16 weights W [N, K] (N padded to a multiple of 16): one 1 KB block per (16-row tile
+//    t, 32-wide step s), blocks ordered (t, s), lanes in order inside a block.
+//  * float32 activations A [M, K] (M padded to a multiple of 16): per (16-row block, step)
+//    two 1 KB halves, the first holding k % 8 < 4 of every lane, the second k % 8 >= 4.
+DF_DEV size_t wfrag_off(int n, int k, int KS) {
+  return ((size_t)((n >> 4) * KS + (k >> 5)) * 64 + ((k & 31) >> 3) * 16 + (n & 15)) * 8 + (k & 7);
+}
+DF_DEV size_t afrag_off(int m, int k, int KS) {
+  return ((size_t)(((m >> 4) * KS + (k >> 5)) * 2 + ((k & 7) >> 2))) * 256 +
+         (((k & 31) >> 3) * 16 + (m & 15)) * 4 + (k & 3);
+}
+
 // Entry i (< 8) of a small pointer table held in a kernel argument, by unrolled selects:
 // a dynamically indexed private array would be placed in scratch memory.
 template <typename P>

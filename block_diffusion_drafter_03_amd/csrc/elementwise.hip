@@ -19,7 +19,7 @@ __global__ __launch_bounds__(256) void embed_kernel(EmbedArgs a) {
   const T* e = (const T*)a.E + (size_t)tok * D;
   for (int c = threadIdx.x; c < D; c += 256) {
     const float x = to_f(e[c]);
-    a.h[(size_t)row * D + c] = x;
+    a.h[a.afrag ? afrag_off(row, c, D >> 5) : (size_t)row * D + c] = x;
     if (a.hdbg) a.hdbg[(size_t)row * D + c] = x;
   }
   // RoPE angles of this row's position (float64, rounded to float32)
@@ -67,13 +67,16 @@ hipError_t launch_rope_rows(const int32_t* row_seq, const int32_t* row_pos, int 
 // ---------------------------------------------------------------------------------------
 DF_DEV int key_index(unsigned long long k) { return (int)(0xFFFFFFFFu - (unsigned)(k & 0xFFFFFFFFull)); }
 
-__global__ void unpack_ids_kernel(const unsigned long long* keys, int n, int32_t* ids) {
+// draft ids of the masked rows j = 1 .. B-1 of every block (the anchor rows' argmax is unused)
+__global__ void unpack_ids_kernel(const unsigned long long* keys, int n, int B, int32_t* ids) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) ids[i] = key_index(keys[i]);
+  if (i < n) ids[i] = key_index(keys[(i / (B - 1)) * B + i % (B - 1) + 1]);
 }
 
-hipError_t launch_unpack_ids(const unsigned long long* keys, int n, int32_t* ids, hipStream_t st) {
-  hipLaunchKernelGGL(unpack_ids_kernel, dim3((n + 255) / 256), dim3(256), 0, st, keys, n, ids);
+hipError_t launch_unpack_ids(const unsigned long long* keys, int batch, int B, int32_t* ids,
+                             hipStream_t st) {
+  const int n = batch * (B - 1);
+  hipLaunchKernelGGL(unpack_ids_kernel, dim3((n + 255) / 256), dim3(256), 0, st, keys, n, B, ids);
   return hipGetLastError();
 }
 

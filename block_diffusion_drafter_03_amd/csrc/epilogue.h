@@ -6,8 +6,8 @@
 // operand by the gain, and scales acc by rstd[m] = 1/sqrt(mean_k A^2 + eps) here, so
 // RMSNorm(x) W^T never needs a separate pass over x.
 //
-// Packed weight layout that makes every pair-wise epilogue local to a pair of adjacent
-// output columns (2i, 2i+1):
+// Packed weight row order that makes every pair-wise epilogue local to a pair of adjacent
+// output columns (2i, 2i+1) (bfloat16 models then store the matrices in B-fragment order):
 //   * q and k heads of DFLASH_W_QKV are stored rotary-interleaved: packed row 2i of a head
 //     is original row i and packed row 2i+1 is original row i + d/2, so the two inputs of
 //     one rotate-half rotation land in columns 2i, 2i+1 (v heads are stored plainly);
@@ -31,12 +31,13 @@ template <typename T, int KIND>
 DF_DEV void epi_elem(const EpiArgs& e, int row, int col, float v) {
   switch (KIND) {
     case EPI_STORE_F32:
-      ((float*)e.out)[(size_t)row * e.ldo + col] = v;
+      ((float*)e.out)[e.afrag ? afrag_off(row, col, e.ldo >> 5) : (size_t)row * e.ldo + col] = v;
       break;
     case EPI_RESID: {
       const size_t i = (size_t)row * e.ldh + col;
-      const float x = e.h[i] + v;
-      e.h[i] = x;
+      const size_t ih = e.afrag ? afrag_off(row, col, e.ldh >> 5) : i;
+      const float x = e.h[ih] + v;
+      e.h[ih] = x;
       if (e.hdbg) e.hdbg[i] = x;
       if (e.tap) ((T*)e.tap)[(size_t)row * e.tap_ld + e.tap_col + col] = from_f<T>(x);
       break;
@@ -64,7 +65,8 @@ template <typename T, int KIND>
 DF_DEV void epi_pair(const EpiArgs& e, int row, int col, float v0, float v1) {
   switch (KIND) {
     case EPI_SWIGLU: {
-      e.act[(size_t)row * e.F + (col >> 1)] = v0 / (1.f + expf(-v0)) * v1;
+      const int c = col >> 1;
+      e.act[e.afrag ? afrag_off(row, c, e.F >> 5) : (size_t)row * e.F + c] = v0 / (1.f + expf(-v0)) * v1;
       break;
     }
     case EPI_QKV: {

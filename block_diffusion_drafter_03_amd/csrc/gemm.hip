@@ -1,15 +1,16 @@
-// GEMM kernels with fused epilogues: acc[m][n] = sum_k A[m][k] W[n][k] (y = x W^T, W row-major
-// [N, K]), optional A-side RMSNorm, then one of the epilogues of epilogue.h.
+// GEMM kernels with fused epilogues: acc[m][n] = sum_k A[m][k] W[n][k] (y = x W^T),
+// optional A-side RMSNorm, then one of the epilogues of epilogue.h.
 //
-//  * gemm_skinny_bf16  (M <= 32): the weight-streaming shape of a drafter step at small
-//    batch.  A workgroup owns 16 output columns at a time and its 4 waves split K; each
-//    lane streams 16-byte slices of W rows straight into MFMA B fragments (no LDS), and the
-//    waves' 16x16 partial tiles are summed through LDS.  W is read exactly once.
-//  * gemm_tiled_bf16   (M > 32): 64x64 output tiles, 2x2 waves of 32x32, BK = 64, A and W
-//    tiles staged through LDS with the next K tile's global loads in flight during the
-//    MFMAs; 1-D grid remapped so that the M tiles sharing a W column block run on the same
-//    XCD (one L2) back to back.
-//  * gemm_f32          (float32 models): VALU 64x64 tiles, BK = 16.
+// bfloat16 models: W in B-fragment order and float32 activations in A-fragment order
+// (common.h), so every operand load of a wave is one contiguous 1 KB burst.  Activations
+// enter the MFMAs as compensated (hi, lo) bf16 pairs; caller-supplied bf16 inputs (the
+// tapped features of the fusion GEMM) are row-major and enter as they are.
+//  * gemm_gemv_bf16   (M <= 16): the weight-streaming shape of a drafter step.  8 waves
+//    split K, a workgroup walks 16-column tiles; see the kernel.
+//  * gemm_tiled_bf16  (M > 16): 64x64 output tiles, 2x2 waves of 32x32, BK = 64, A and W
+//    staged through LDS with the next K tile's global loads in flight during the MFMAs;
+//    1-D grid remapped so that the M tiles sharing a W column block run on one XCD.
+//  * gemm_f32         (float32 models): VALU 64x64 tiles, BK = 16, row-major operands.
 //
 // MFMA: v_mfma_f32_16x16x32_bf16.  Lane l (r = l % 16, g = l / 16) supplies A[r][8g..8g+7]
 // and W row r's k-slice 8g..8g+7; the accumulator holds D[4g + i][r], i = 0..3.
@@ -17,17 +18,29 @@
 
 namespace dflash {
 
-// Row n of the B operand (W rows, possibly split into equal segments at different
-// addresses), read straight from the kernel argument.
+// Row n of a row-major B operand (float32 models), possibly split into equal segments.
 template <typename T>
 DF_DEV const T* brow(const BSeg& b, int n) {
   const int s = b.nseg > 1 ? n / b.seg_rows : 0;
   return (const T*)pick8(b.ptr, s) + (size_t)(n - s * b.seg_rows) * b.ldb;
 }
 
-// A row m of the GEMM -> row of the A buffer (skipping the anchor row of each block when
-// only the masked rows of the drafter feed the LM head).
-DF_DEV int a_row_index(int m, int skipB) { return skipB ? m + m / (skipB - 1) + 1 : m; }
+// 1 KB B-fragment block (16-row tile t, 32-wide step ks) of fragment-ordered weights,
+// possibly split into equal row segments (seg_rows a multiple of 16).
+DF_DEV const bf16* wblock(const BSeg& b, int t, int ks, int KS) {
+  const int tps = b.seg_rows >> 4;
+  const int s = b.nseg > 1 ? t / tps : 0;
+  return (const bf16*)pick8(b.ptr, s) + ((size_t)(t - s * tps) * KS + ks) * 512;
+}
+
+// the 8 A values of lane (r = lane % 16, g = lane / 16) at row block mb, step ks of
+// fragment-ordered float32 activations
+DF_DEV void afrag_load8(const float* A, int mb, int ks, int KS, int lane, float v[8]) {
+  const float* p = A + ((size_t)(mb * KS + ks) * 2) * 256 + lane * 4;
+  const float4 x0 = *(const float4*)p, x1 = *(const float4*)(p + 256);
+  v[0] = x0.x; v[1] = x0.y; v[2] = x0.z; v[3] = x0.w;
+  v[4] = x1.x; v[5] = x1.y; v[6] = x1.z; v[7] = x1.w;
+}
 
 DF_DEV unsigned long long shfl_xor_u64(unsigned long long v, int mask) {
   const unsigned lo = __shfl_xor((unsigned)(v & 0xFFFFFFFFull), mask, 64);
@@ -36,6 +49,16 @@ DF_DEV unsigned long long shfl_xor_u64(unsigned long long v, int mask) {
 }
 DF_DEV unsigned long long umax64(unsigned long long a, unsigned long long b) { return a > b ? a : b; }
 
+// debug copy of a logit: rows j == 0 of each skipB-row block (the drafter's anchors) are
+// not drafts and are left out
+DF_DEV void logit_store(const EpiArgs& e, int row, int col, int N, float v) {
+  if (e.skipB) {
+    const int j = row % e.skipB;
+    if (j == 0) return;
+    row = (row / e.skipB) * (e.skipB - 1) + j - 1;
+  }
+  e.logits[(size_t)row * N + col] = v;
+}
 
 // Epilogue of one 16x16 MFMA tile held in the accumulator layout: v[i] = acc[row0+4g+i][col].
 // Pair epilogues are taken by even lanes (their odd neighbour holds column col + 1).
@@ -49,7 +72,7 @@ DF_DEV void tile_epilogue(const GemmArgs& ga, int row0, int col, const float v[4
     for (int i = 0; i < 4; ++i) {
       const int row = row0 + i;
       const bool ok = row < M && col < N;
-      if (ok && e.logits) e.logits[(size_t)row * N + col] = v[i];
+      if (ok && e.logits) logit_store(e, row, col, N, v[i]);
       unsigned long long k = ok ? pack_argmax_key(v[i], col) : 0ull;
       k = umax64(k, shfl_xor_u64(k, 1));
       k = umax64(k, shfl_xor_u64(k, 2));
@@ -74,8 +97,8 @@ DF_DEV void tile_epilogue(const GemmArgs& ga, int row0, int col, const float v[4
 }
 
 // ---------------------------------------------------------------------------------------
-// A operand helpers.  TA = float: activations, taken as a compensated (hi, lo) bf16 pair
-// (two MFMAs per W fragment); TA = bf16: inputs already in bf16 (one MFMA).
+// A operand helpers.  TA = float: fragment-ordered activations, taken as a compensated
+// (hi, lo) bf16 pair (two MFMAs per W fragment); TA = bf16: caller rows, one MFMA.
 template <typename TA> struct AIsFloat { static constexpr bool value = false; };
 template <> struct AIsFloat<float> { static constexpr bool value = true; };
 
@@ -94,117 +117,17 @@ DF_DEV void a_operand(float v[8], const bf16* gp, float* ss, bf16x8& hi, bf16x8&
   split8(v, hi, lo);
 }
 
-// ---------------------------------------------------------------------------------------
-// 16 < M <= 32 (and M <= 16 with few output tiles): 4 waves split K; A and W fragments are
-// both loaded per 32-wide K step.
-template <typename TA, int MT, int NW, int U, bool NORM, int KIND>
-__global__ __launch_bounds__(NW * 64) void gemm_skinny_bf16(GemmArgs ga) {
-  constexpr bool TWO = AIsFloat<TA>::value;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int r = lane & 15, g = lane >> 4;
-  const int M = ga.M, N = ga.N, K = ga.K;
-  const int KS = K >> 5;
-  const int ks0 = (w * KS) / NW, ks1 = ((w + 1) * KS) / NW;
-  const int n_tiles = (N + 15) >> 4;
-  __shared__ f32x4 red[NW][MT][64];
-  __shared__ float ss_red[NW][MT * 16];
-  __shared__ float rstd[MT * 16];
-
-  const TA* arow[MT];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    const int m = min(mt * 16 + r, M - 1);
-    arow[mt] = (const TA*)ga.A + (size_t)a_row_index(m, ga.a_skip_B) * ga.lda + g * 8;
-  }
-  const bf16* gk = NORM ? (const bf16*)ga.norm_g + g * 8 : nullptr;
-  unsigned long long best[4] = {0ull, 0ull, 0ull, 0ull};
-  bool first = true;
-
-  for (int t = blockIdx.x; t < n_tiles; t += gridDim.x) {
-    const int n = min(t * 16 + r, N - 1);
-    const bf16* wrow = brow<bf16>(ga.B, n) + g * 8;
-    f32x4 acc[MT];
-    float ss[MT];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      ss[mt] = 0.f;
-    }
-    for (int ks = ks0; ks < ks1; ks += U) {
-      bf16x8 wf[U];
-      float av[U][MT][8];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int k = min(ks + u, ks1 - 1);
-        wf[u] = *(const bf16x8*)(wrow + (size_t)k * 32);
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) load8(arow[mt] + (size_t)k * 32, av[u][mt]);
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        if (ks + u >= ks1) break;
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          bf16x8 hi, lo;
-          if (first)
-            a_operand<NORM, true>(av[u][mt], gk + (size_t)(ks + u) * 32, &ss[mt], hi, lo);
-          else
-            a_operand<NORM, false>(av[u][mt], gk + (size_t)(ks + u) * 32, &ss[mt], hi, lo);
-          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, wf[u], acc[mt], 0, 0, 0);
-          if (TWO) acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, wf[u], acc[mt], 0, 0, 0);
-        }
-      }
-    }
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) red[w][mt][lane] = acc[mt];
-    if (NORM && first) {
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        float s = ss[mt] + __shfl_xor(ss[mt], 16, 64);
-        s += __shfl_xor(s, 32, 64);
-        if (g == 0) ss_red[w][mt * 16 + r] = s;
-      }
-    }
-    __syncthreads();
-    if (NORM && first) {
-      if (threadIdx.x < MT * 16) {
-        float s = 0.f;
-#pragma unroll
-        for (int ww = 0; ww < NW; ++ww) s += ss_red[ww][threadIdx.x];
-        rstd[threadIdx.x] = 1.0f / sqrtf(s / (float)K + ga.eps);
-      }
-      __syncthreads();
-    }
-    first = false;
-    if (w < MT) {
-      const int mt = w;
-      f32x4 s = red[0][mt][lane];
-#pragma unroll
-      for (int ww = 1; ww < NW; ++ww) s += red[ww][mt][lane];
-      float v[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] = NORM ? s[i] * rstd[mt * 16 + g * 4 + i] : s[i];
-      tile_epilogue<bf16, KIND>(ga, mt * 16 + g * 4, t * 16 + r, v, r, best);
-    }
-    __syncthreads();
-  }
-  if (KIND == EPI_ARGMAX && w < MT && r == 0) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = w * 16 + g * 4 + i;
-      if (row < M && best[i]) atomicMax(&ga.e.keys[row], best[i]);
-    }
-  }
-}
-
-// M <= 16: NW waves split K, one 32-wide step per MFMA (pair).  With ASTAT each wave keeps
-// its K-slice of the A rows for all of the workgroup's tiles, already multiplied by the
-// RMSNorm gain and split into (hi, lo) (rstd is applied in the epilogue): hi in registers,
-// lo in LDS (128 KB: one workgroup owns the CU), so the vector memory path carries only W:
-// a wave issues all of its W loads of a tile at once (CH steps, 1 KB each) and the CU keeps
-// 128 KB in flight.  Without ASTAT (K > 4096) A and W are streamed together in chunks of
-// CHS steps.  8 waves of 512 threads leave each wave 256 registers, so the stationary A,
-// a full tile of W in flight and the epilogue never spill.
+// M <= 16: NW waves split K, one 32-wide step per MFMA (pair).
+//  * ASTAT (many tiles, K <= 4096): one workgroup per CU walks the tiles; each wave keeps
+//    its K-slice of the A rows for all of them, already multiplied by the RMSNorm gain and
+//    split into (hi, lo) (rstd is applied in the epilogue): hi in registers, lo in LDS
+//    (128 KB: the workgroup owns the CU), so the vector memory path carries only W: a wave
+//    issues all of its W loads of a tile at once (CH steps, 1 KB each) and the next tile's
+//    loads go out right after the MFMAs, in flight across the reduction.
+//  * streamed (few tiles, or K > 4096): A and W are loaded together in chunks of CHS
+//    steps; no LDS for A, so several workgroups share a CU and every tile is in flight.
+// 8 waves of 512 threads leave each wave 256 registers, so the stationary A, a full tile
+// of W in flight and the epilogue never spill.
 #define GEMV_MAX_TILES 8   // tiles per workgroup whose epilogue is deferred (non-argmax kinds)
 #define GEMV_NW 8          // waves per workgroup
 
@@ -216,7 +139,8 @@ __global__ __launch_bounds__(NW * 64) void gemm_gemv_bf16(GemmArgs ga) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int r = lane & 15, g = lane >> 4;
   const int M = ga.M, N = ga.N, K = ga.K;
-  const int spw = (K >> 5) / NW;                 // K % (32 NW) == 0
+  const int KS = K >> 5;
+  const int spw = KS / NW;                       // K % (32 NW) == 0
   const int ks0 = w * spw;
   const int n_tiles = (N + 15) >> 4;
   __shared__ f32x4 red[NW][64];
@@ -226,21 +150,27 @@ __global__ __launch_bounds__(NW * 64) void gemm_gemv_bf16(GemmArgs ga) {
   __shared__ bf16x8 alo[ASTAT && TWO ? NW : 1][ASTAT && TWO ? CH : 1][64];
   // running argmax keys of wave 0's lanes (kept out of the main loop's registers)
   __shared__ unsigned long long bsh[KIND == EPI_ARGMAX ? 4 : 1][64];
-  const TA* arow = (const TA*)ga.A + (size_t)a_row_index(min(r, M - 1), ga.a_skip_B) * ga.lda + g * 8;
   const bf16* gk = NORM ? (const bf16*)ga.norm_g + g * 8 : nullptr;
+  // this lane's 8 A values of step ks (row r)
+  auto load_a = [&](int ks, float v[8]) {
+    if constexpr (TWO)
+      afrag_load8((const float*)ga.A, 0, ks, KS, lane, v);
+    else
+      load8((const bf16*)ga.A + (size_t)min(r, M - 1) * ga.lda + (size_t)ks * 32 + g * 8, v);
+  };
   int nbuf = 0;
+  bool first = true;
   if (KIND == EPI_ARGMAX && w == 0)
 #pragma unroll
     for (int i = 0; i < (KIND == EPI_ARGMAX ? 4 : 1); ++i) bsh[i][lane] = 0ull;
 
   bf16x8 ah[ASTAT ? CH : 1];
   // W loads of this workgroup's first tile go out before the A prologue (independent)
-  bf16x8 wn[CH];
+  bf16x8 wn[ASTAT ? CH : 1];
   auto load_w = [&](int t) {
-    const bf16* wrow = brow<bf16>(ga.B, min(t * 16 + r, N - 1)) + g * 8;
 #pragma unroll
     for (int s = 0; s < CH; ++s)
-      if (s < spw) wn[s] = *(const bf16x8*)(wrow + (size_t)(ks0 + s) * 32);
+      if (s < spw) wn[s] = *(const bf16x8*)(wblock(ga.B, t, ks0 + s, KS) + lane * 8);
   };
   if constexpr (ASTAT) {
     if (blockIdx.x < n_tiles) load_w(blockIdx.x);
@@ -249,7 +179,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_gemv_bf16(GemmArgs ga) {
     for (int s = 0; s < CH; ++s) {
       if (s < spw) {
         float v[8];
-        load8(arow + (size_t)(ks0 + s) * 32, v);
+        load_a(ks0 + s, v);
         bf16x8 lo;
         a_operand<NORM, true>(v, gk + (size_t)(ks0 + s) * 32, &ss, ah[s], lo);
         if constexpr (TWO) alo[w][s][lane] = lo;
@@ -282,28 +212,46 @@ __global__ __launch_bounds__(NW * 64) void gemm_gemv_bf16(GemmArgs ga) {
       // the next tile's W loads are in flight across the barrier and the reduction
       if (t + gridDim.x < n_tiles) load_w(t + gridDim.x);
     } else {
-      const bf16* wrow = brow<bf16>(ga.B, min(t * 16 + r, N - 1)) + g * 8;
+      float ss = 0.f;
       for (int c0 = 0; c0 < spw; c0 += CHS) {
         bf16x8 wf[CHS];
         float av[CHS][8];
 #pragma unroll
         for (int s = 0; s < CHS; ++s) {
           const int k = ks0 + min(c0 + s, spw - 1);
-          wf[s] = *(const bf16x8*)(wrow + (size_t)k * 32);
-          load8(arow + (size_t)k * 32, av[s]);
+          wf[s] = *(const bf16x8*)(wblock(ga.B, t, k, KS) + lane * 8);
+          load_a(k, av[s]);
         }
 #pragma unroll
         for (int s = 0; s < CHS; ++s)
           if (c0 + s < spw) {
             bf16x8 hi, lo;
-            split8(av[s], hi, lo);
+            if (first)
+              a_operand<NORM, true>(av[s], gk + (size_t)(ks0 + c0 + s) * 32, &ss, hi, lo);
+            else
+              a_operand<NORM, false>(av[s], gk + (size_t)(ks0 + c0 + s) * 32, &ss, hi, lo);
             acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, wf[s], acc, 0, 0, 0);
             if constexpr (TWO) acc2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, wf[s], acc2, 0, 0, 0);
           }
       }
+      if (NORM && first) {
+        ss += __shfl_xor(ss, 16, 64);
+        ss += __shfl_xor(ss, 32, 64);
+        if (g == 0) ss_red[w][r] = ss;
+      }
     }
     red[w][lane] = acc + acc2;
     __syncthreads();
+    if (NORM && !ASTAT && first) {
+      if (threadIdx.x < 16) {
+        float s = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < NW; ++ww) s += ss_red[ww][threadIdx.x];
+        rstd[threadIdx.x] = 1.0f / sqrtf(s / (float)K + ga.eps);
+      }
+      __syncthreads();
+    }
+    first = false;
     if (w == 0) {
       f32x4 s = red[0][lane];
 #pragma unroll
@@ -348,14 +296,20 @@ __global__ __launch_bounds__(NW * 64) void gemm_gemv_bf16(GemmArgs ga) {
   }
 }
 
-// Variant selection for M <= 16 (benchmark sweeps may force one with DFLASH_GEMV=1..2):
-// 1 = 4-wave split-K (gemm_skinny_bf16), 2 = gemm_gemv_bf16 (default where it fits).
+// Tuning knobs read once from the environment (benchmark sweeps): DFLASH_GEMV=1 forces the
+// tiled kernel for M <= 16; DFLASH_GEMV_STREAM_TILES sets the largest tile count that uses
+// the streamed-A form (default: one tile per CU).
+static int env_knob(const char* name, int dflt) {
+  const char* s = getenv(name);
+  return s && *s ? atoi(s) : dflt;
+}
 static int gemv_variant() {
-  static int v = -1;
-  if (v < 0) {
-    const char* s = getenv("DFLASH_GEMV");
-    v = s && *s ? atoi(s) : 0;
-  }
+  static const int v = env_knob("DFLASH_GEMV", 0);
+  return v;
+}
+static int num_cus();
+static int gemv_stream_tiles() {
+  static const int v = env_knob("DFLASH_GEMV_STREAM_TILES", num_cus());
   return v;
 }
 
@@ -364,16 +318,30 @@ static int gemv_variant() {
 #define TK 64
 #define TPAD 8
 
+// A tile (64 rows x 64 k) staging.  TA = float: 16 fragment halves of 1 KB (4 row blocks x
+// 2 steps x 2 halves); thread c, slot j covers row 16 j + c % 16, k = 32 (c / 128) +
+// 8 ((c % 64) / 16) + 4 ((c / 64) % 2) .. +3.  TA = bf16: row-major rows, 2 x 8 values.
+template <typename TA> struct ATile;
+template <> struct ATile<float> {
+  static constexpr int SLOTS = 4, VALS = 4;
+};
+template <> struct ATile<bf16> {
+  static constexpr int SLOTS = 2, VALS = 8;
+};
+
 template <typename TA, bool NORM, int KIND>
 __global__ __launch_bounds__(256) void gemm_tiled_bf16(GemmArgs ga) {
   constexpr bool TWO = AIsFloat<TA>::value;
+  constexpr int SLOTS = ATile<TA>::SLOTS, VALS = ATile<TA>::VALS;
   __shared__ __attribute__((aligned(16))) bf16 As[TWO ? 2 : 1][TB][TK + TPAD];
   __shared__ __attribute__((aligned(16))) bf16 Bs[TB][TK + TPAD];
+  __shared__ float ss_part[NORM ? TB : 1][NORM ? 17 : 1];
   __shared__ float rstd_s[TB];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int r = lane & 15, g = lane >> 4;
   const int wm = w >> 1, wn = w & 1;
-  const int M = ga.M, N = ga.N, K = ga.K;
+  const int M = ga.M, N = ga.N, K = ga.K, KS = K >> 5;
+  const int MB = (M + 15) >> 4, NT = (N + 15) >> 4;
   const int mt_n = (M + TB - 1) / TB, nt_n = (N + TB - 1) / TB;
   const int T = mt_n * nt_n;
   // tiles ordered M-fastest; give each XCD (WG id mod 8) a contiguous run of tiles so the
@@ -382,26 +350,54 @@ __global__ __launch_bounds__(256) void gemm_tiled_bf16(GemmArgs ga) {
   if ((T & 7) == 0) t = (blockIdx.x & 7) * (T >> 3) + (blockIdx.x >> 3);
   const int m0 = (t % mt_n) * TB, n0 = (t / mt_n) * TB;
 
-  const TA* ap[2];
+  // ---- this thread's A slots ----
+  int arow[SLOTS], acol[SLOTS];
+  const TA* ap[SLOTS];
+#pragma unroll
+  for (int j = 0; j < SLOTS; ++j) {
+    if constexpr (TWO) {
+      arow[j] = 16 * j + r;
+      acol[j] = 32 * (tid >> 7) + 8 * g + 4 * ((tid >> 6) & 1);
+      const int mb = min((m0 >> 4) + j, MB - 1);
+      ap[j] = (const TA*)ga.A + ((size_t)(mb * KS + (tid >> 7)) * 2 + ((tid >> 6) & 1)) * 256 + lane * 4;
+    } else {
+      const int c = tid + 256 * j;
+      arow[j] = c >> 3;
+      acol[j] = (c & 7) * 8;
+      ap[j] = (const TA*)ga.A + (size_t)min(m0 + arow[j], M - 1) * ga.lda + acol[j];
+    }
+  }
+  // A slot loads of the K tile at k0 (float: the step advances by 2 per K tile)
+  auto load_as = [&](int k0, float (*ra)[VALS]) {
+#pragma unroll
+    for (int j = 0; j < SLOTS; ++j) {
+      if constexpr (TWO) {
+        const float4 x = *(const float4*)(ap[j] + (size_t)(k0 >> 5) * 512);
+        ra[j][0] = x.x; ra[j][1] = x.y; ra[j][2] = x.z; ra[j][3] = x.w;
+      } else {
+        load8(ap[j] + k0, ra[j]);
+      }
+    }
+  };
+  // ---- this thread's W slots: 2 x 16 B of the 8 fragment blocks of the tile ----
   const bf16* bp[2];
-  int lrow[2], lcol[2];
+  int brow_[2], bcol[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    const int c = tid + 256 * j;
-    lrow[j] = c >> 3;
-    lcol[j] = (c & 7) * 8;
-    ap[j] = (const TA*)ga.A + (size_t)a_row_index(min(m0 + lrow[j], M - 1), ga.a_skip_B) * ga.lda + lcol[j];
-    bp[j] = brow<bf16>(ga.B, min(n0 + lrow[j], N - 1)) + lcol[j];
+    const int q = tid + 256 * j, blk = q >> 6, bl = q & 63;
+    brow_[j] = 16 * (blk >> 1) + (bl & 15);
+    bcol[j] = 32 * (blk & 1) + 8 * (bl >> 4);
+    bp[j] = wblock(ga.B, min((n0 >> 4) + (blk >> 1), NT - 1), blk & 1, KS) + bl * 8;
   }
   const bf16* gk = NORM ? (const bf16*)ga.norm_g : nullptr;
-  float ra[2][8];
+  float ra[SLOTS][VALS];
   bf16x8 rb[2];
-  float ss[2] = {0.f, 0.f};
+  float ss[SLOTS];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    load8(ap[j], ra[j]);
-    rb[j] = *(const bf16x8*)(bp[j]);
-  }
+  for (int j = 0; j < SLOTS; ++j) ss[j] = 0.f;
+  load_as(0, ra);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) rb[j] = *(const bf16x8*)bp[j];
   f32x4 acc[2][2];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
@@ -410,20 +406,36 @@ __global__ __launch_bounds__(256) void gemm_tiled_bf16(GemmArgs ga) {
 
   for (int k0 = 0; k0 < K; k0 += TK) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < SLOTS; ++j) {
+      float v[8];
+#pragma unroll
+      for (int e = 0; e < VALS; ++e) {
+        float x = ra[j][e];
+        if (NORM) {
+          ss[j] += x * x;
+          x *= (float)gk[k0 + acol[j] + e];
+        }
+        v[e] = x;
+      }
+#pragma unroll
+      for (int e = VALS; e < 8; ++e) v[e] = 0.f;
       bf16x8 hi, lo;
-      a_operand<NORM, true>(ra[j], gk + k0 + lcol[j], &ss[j], hi, lo);
-      *(bf16x8*)&As[0][lrow[j]][lcol[j]] = hi;
-      if constexpr (TWO) *(bf16x8*)&As[TWO ? 1 : 0][lrow[j]][lcol[j]] = lo;
-      *(bf16x8*)&Bs[lrow[j]][lcol[j]] = rb[j];
+      split8(v, hi, lo);
+      if constexpr (TWO) {
+        bf16x4 h4 = {hi[0], hi[1], hi[2], hi[3]}, l4 = {lo[0], lo[1], lo[2], lo[3]};
+        *(bf16x4*)&As[0][arow[j]][acol[j]] = h4;
+        *(bf16x4*)&As[TWO ? 1 : 0][arow[j]][acol[j]] = l4;
+      } else {
+        *(bf16x8*)&As[0][arow[j]][acol[j]] = hi;
+      }
     }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) *(bf16x8*)&Bs[brow_[j]][bcol[j]] = rb[j];
     __syncthreads();
     if (k0 + TK < K) {
+      load_as(k0 + TK, ra);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        load8(ap[j] + k0 + TK, ra[j]);
-        rb[j] = *(const bf16x8*)(bp[j] + k0 + TK);
-      }
+      for (int j = 0; j < 2; ++j) rb[j] = *(const bf16x8*)(bp[j] + (size_t)((k0 + TK) >> 5) * 512);
     }
 #pragma unroll
     for (int kk = 0; kk < TK; kk += 32) {
@@ -445,14 +457,26 @@ __global__ __launch_bounds__(256) void gemm_tiled_bf16(GemmArgs ga) {
     __syncthreads();
   }
   if (NORM) {
-    // the 8 threads loading one A row are consecutive lanes
+    if constexpr (TWO) {
+      // row 16 j + r collects its 16 contributors (tid / 16) in a fixed order
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      float s = ss[j];
-      s += __shfl_xor(s, 1, 64);
-      s += __shfl_xor(s, 2, 64);
-      s += __shfl_xor(s, 4, 64);
-      if ((tid & 7) == 0) rstd_s[lrow[j]] = 1.0f / sqrtf(s / (float)K + ga.eps);
+      for (int j = 0; j < SLOTS; ++j) ss_part[arow[j]][tid >> 4] = ss[j];
+      __syncthreads();
+      if (tid < TB) {
+        float s = 0.f;
+        for (int i = 0; i < 16; ++i) s += ss_part[tid][i];
+        rstd_s[tid] = 1.0f / sqrtf(s / (float)K + ga.eps);
+      }
+    } else {
+      // the 8 threads loading one A row are consecutive lanes
+#pragma unroll
+      for (int j = 0; j < SLOTS; ++j) {
+        float s = ss[j];
+        s += __shfl_xor(s, 1, 64);
+        s += __shfl_xor(s, 2, 64);
+        s += __shfl_xor(s, 4, 64);
+        if ((tid & 7) == 0) rstd_s[arow[j]] = 1.0f / sqrtf(s / (float)K + ga.eps);
+      }
     }
     __syncthreads();
   }
@@ -489,7 +513,7 @@ __global__ __launch_bounds__(256) void gemm_f32(GemmArgs ga) {
   const int m0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
   float acc[4][4] = {};
   const int lr = tid >> 2, lk = (tid & 3) * 4;
-  const float* ap = (const float*)ga.A + (size_t)a_row_index(min(m0 + lr, M - 1), ga.a_skip_B) * ga.lda + lk;
+  const float* ap = (const float*)ga.A + (size_t)min(m0 + lr, M - 1) * ga.lda + lk;
   const float* bp = brow<float>(ga.B, min(n0 + lr, N - 1)) + lk;
   const float* gk = NORM ? (const float*)ga.norm_g + lk : nullptr;
   float ss = 0.f;
@@ -539,7 +563,7 @@ __global__ __launch_bounds__(256) void gemm_f32(GemmArgs ga) {
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         if (row < M && col0 + j < N) {
-          if (e.logits) e.logits[(size_t)row * N + col0 + j] = v[j];
+          if (e.logits) logit_store(e, row, col0 + j, N, v[j]);
           k = umax64(k, pack_argmax_key(v[j], col0 + j));
         }
       k = umax64(k, shfl_xor_u64(k, 1));
@@ -585,29 +609,23 @@ static hipError_t launch_kind(int dt, const GemmArgs& ga, hipStream_t st) {
     return hipGetLastError();
   }
   const int n_tiles = (N + 15) / 16;
-  if (M <= 16) {
-    int v = gemv_variant();
-    const bool fits = ga.K % (32 * GEMV_NW) == 0 && !(NORM && ga.K > 4096);
-    if (v < 1 || v > 2 || !fits) v = fits ? 2 : 1;
-    if (v == 2) {
-      // one workgroup per CU (the stationary A's LDS) walking the tiles; the deferred
-      // epilogue buffer bounds the tiles per workgroup
+  if (M <= 16 && ga.K % (32 * GEMV_NW) == 0 && gemv_variant() != 1) {
+    // few tiles (up to gemv_stream_tiles(), default one per CU) or K > 4096: one workgroup
+    // per tile, A streamed with W, so that several workgroups may share a CU and every tile
+    // is in flight at once; otherwise one workgroup per CU with the A slice stationary,
+    // walking the tiles (the deferred epilogue buffer bounds the tiles per workgroup)
+    if (n_tiles <= gemv_stream_tiles() || ga.K > 4096) {
+      int grid = n_tiles;
+      if (grid > 8 * num_cus()) grid = 8 * num_cus();
+      if (KIND != EPI_ARGMAX && grid * GEMV_MAX_TILES < n_tiles)
+        grid = (n_tiles + GEMV_MAX_TILES - 1) / GEMV_MAX_TILES;
+      hipLaunchKernelGGL((gemm_gemv_bf16<TA, GEMV_NW, NORM, false, KIND>), dim3(grid), dim3(GEMV_NW * 64), 0, st, ga);
+    } else {
       int grid = n_tiles < num_cus() ? n_tiles : num_cus();
       if (KIND != EPI_ARGMAX && grid * GEMV_MAX_TILES < n_tiles)
         grid = (n_tiles + GEMV_MAX_TILES - 1) / GEMV_MAX_TILES;
-      if (ga.K <= 4096)
-        hipLaunchKernelGGL((gemm_gemv_bf16<TA, GEMV_NW, NORM, true, KIND>), dim3(grid), dim3(GEMV_NW * 64), 0, st, ga);
-      else
-        hipLaunchKernelGGL((gemm_gemv_bf16<TA, GEMV_NW, false, false, KIND>), dim3(grid), dim3(GEMV_NW * 64), 0, st, ga);
-      return hipGetLastError();
+      hipLaunchKernelGGL((gemm_gemv_bf16<TA, GEMV_NW, NORM, true, KIND>), dim3(grid), dim3(GEMV_NW * 64), 0, st, ga);
     }
-  }
-  if (M <= 32) {
-    const int grid = n_tiles < 8 * num_cus() ? n_tiles : 8 * num_cus();
-    if (M <= 16)
-      hipLaunchKernelGGL((gemm_skinny_bf16<TA, 1, 4, 8, NORM, KIND>), dim3(grid), dim3(256), 0, st, ga);
-    else
-      hipLaunchKernelGGL((gemm_skinny_bf16<TA, 2, 4, 4, NORM, KIND>), dim3(grid), dim3(256), 0, st, ga);
     return hipGetLastError();
   }
   const int tiles = ((M + TB - 1) / TB) * ((N + TB - 1) / TB);

@@ -20,7 +20,10 @@ struct BSeg {
 };
 
 // Activations (h, q, attention output, SwiGLU output, fused injection rows) are float32;
-// K/V (block and cache) and tapped features are stored in the model dtype.
+// K/V (block and cache) and tapped features are stored in the model dtype.  For bfloat16
+// models the activations that feed GEMMs (h, attention output, SwiGLU output, fused
+// injection rows) are kept in the MFMA A-fragment order of common.h (afrag = 1) and the
+// weight matrices in the B-fragment order; float32 models keep both row-major.
 enum EpiKind {
   EPI_STORE_F32 = 0,  // out[row*ldo + col] = acc (float)
   EPI_RESID,          // h += acc; optional hdbg / tap (model dtype) copies
@@ -32,6 +35,7 @@ enum EpiKind {
 
 struct EpiArgs {
   int kind;
+  int afrag;      // 1: out / h / act are float32 in the A-fragment order (row stride ignored)
   // EPI_STORE_*
   void* out;
   int ldo;
@@ -62,17 +66,19 @@ struct EpiArgs {
   // EPI_SWIGLU
   float* act;
   int F;
-  // EPI_ARGMAX
+  // EPI_ARGMAX: keys[row] for every row; the optional float logits copy skips the first
+  // row of every skipB-row block when skipB != 0 (the drafter's anchor rows)
   unsigned long long* keys;
-  float* logits;   // optional [M, N] copy of the logits
+  float* logits;
+  int skipB;
 };
 
 struct GemmArgs {
-  const void* A;        // [M, K] float32 (bf16 when a_bf16)
+  const void* A;        // [M, K]: float32 activations (A-fragment order for bf16 models), or
+                        // caller-supplied bf16 rows (row-major, stride lda) when a_bf16
   int a_bf16;
   int lda;
-  int a_skip_B;         // 0: A row m is row m; else rows j == 0 of each B-row block are skipped
-  BSeg B;
+  BSeg B;               // bf16 models: segments of B-fragment-ordered weights (ldb ignored)
   int M, N, K;
   const void* norm_g;   // A-side RMSNorm gain [K] (model dtype) or NULL
   float eps;
@@ -106,7 +112,7 @@ size_t attn_partial_floats(const AttnPlan& p, int batch, int Hkv, int d);
 hipError_t launch_attention(int dt, const AttnPlan& p, const float* q, const void* kblk,
                             const void* vblkT, const KvLayer& kv, int batch, int B, int Bp,
                             int Hq, int Hkv, int d, int causal, float* part, float* o,
-                            hipStream_t st);
+                            int o_afrag, hipStream_t st);
 
 // ---- row kernels (elementwise.hip) ----
 struct EmbedArgs {
@@ -116,6 +122,7 @@ struct EmbedArgs {
   const void* E;
   int V, D;
   float* h;
+  int afrag;
   float* hdbg;
   unsigned long long* keys;
   int n_keys;
@@ -135,8 +142,9 @@ hipError_t launch_rope_rows(const int32_t* row_seq, const int32_t* row_pos, int 
                             const int32_t* seq_len, int batch, int rows, int hd, double base,
                             float2* rope, hipStream_t st);
 
-// ids[r] = argmax index decoded from keys[r].
-hipError_t launch_unpack_ids(const unsigned long long* keys, int n, int32_t* ids, hipStream_t st);
+// ids[b*(B-1) + j-1] = argmax index decoded from keys[b*B + j], j = 1 .. B-1.
+hipError_t launch_unpack_ids(const unsigned long long* keys, int batch, int B, int32_t* ids,
+                             hipStream_t st);
 // g[b*B + j] = argmax of verify row j; tau, bonus of the longest accepted draft prefix.
 hipError_t launch_accept(const unsigned long long* keys, const int32_t* drafts, int batch, int B,
                          int32_t* g, int32_t* tau, int32_t* bonus, hipStream_t st);

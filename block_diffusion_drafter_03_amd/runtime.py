@@ -49,12 +49,24 @@ def pack_gate_up(wg, wu):
     return torch.stack([wg, wu], 1).reshape(2 * wg.shape[0], wg.shape[1]).contiguous()
 
 
+def frag_pack(w):
+    """bf16 matrix [N, K] -> the MFMA B-fragment order libdflash reads for bfloat16 models:
+    rows padded to a multiple of 16; one 1 KB block per (16-row tile t, 32-wide step s),
+    blocks in (t, s) order, and inside a block lane g*16 + r holding row r, k = 8g .. 8g+7."""
+    N, K = w.shape
+    NT = (N + 15) // 16
+    if NT * 16 != N:
+        w = torch.cat([w, w.new_zeros(NT * 16 - N, K)], 0)
+    return w.reshape(NT, 16, K // 32, 4, 8).permute(0, 2, 3, 1, 4).contiguous()
+
+
 class Model:
     """A drafter (``draft=True``: needs W_c and g_c) or a target model.
 
     ``weights`` uses the per-layer names L{i}.{g_in,wq,wk,wv,wo,g_post,wg,wu,wd}, plus g_f
     and (drafter) w_c, g_c; ``shared`` holds embed and lm_head.  Q/K/V and gate/up are
-    packed into the interleaved row layouts the library consumes (see include/dflash.h)."""
+    packed into the interleaved row layouts the library consumes, and for bfloat16 models
+    every matrix but the embedding into the B-fragment order (see include/dflash.h)."""
 
     def __init__(self, shape, weights: dict, shared: dict, n_taps: int, taps=None,
                  draft: bool = True):
@@ -62,20 +74,20 @@ class Model:
         dtype = shared["embed"].dtype
         self.dtype = dtype
         self._keep = []
+        mat = frag_pack if dtype == torch.bfloat16 else (lambda t: t.contiguous())
         lw = []
         for i in range(shape.n_layers):
             qkv = pack_qkv(weights[f"L{i}.wq"], weights[f"L{i}.wk"], weights[f"L{i}.wv"],
                            shape.n_q_heads, shape.n_kv_heads, shape.head_dim)
             gu = pack_gate_up(weights[f"L{i}.wg"], weights[f"L{i}.wu"])
-            tensors = [weights[f"L{i}.g_in"].contiguous(), qkv, weights[f"L{i}.wo"].contiguous(),
-                       weights[f"L{i}.g_post"].contiguous(), gu, weights[f"L{i}.wd"].contiguous()]
+            tensors = [weights[f"L{i}.g_in"].contiguous(), mat(qkv), mat(weights[f"L{i}.wo"]),
+                       weights[f"L{i}.g_post"].contiguous(), mat(gu), mat(weights[f"L{i}.wd"])]
             self._keep += tensors
             lw += [t.data_ptr() for t in tensors]
-        self.qkv = [self._keep[6 * i + 1] for i in range(shape.n_layers)]
         self._lw = (c_void_p * len(lw))(*lw)
-        for k in ("embed", "lm_head"):
-            self._keep.append(shared[k])
-        self._keep.append(weights["g_f"])
+        embed = shared["embed"].contiguous()
+        lm_head = mat(shared["lm_head"])
+        self._keep += [embed, lm_head, weights["g_f"]]
         d = _lib.ModelDesc()
         d.dtype = _dt_code(dtype)
         d.n_layers, d.hidden = shape.n_layers, shape.hidden
@@ -87,12 +99,13 @@ class Model:
         if taps is not None and not draft:
             self._taps = (c_int32 * len(taps))(*taps)
             d.tap_layers = ctypes.cast(self._taps, POINTER(c_int32))
-        d.embed = shared["embed"].data_ptr()
-        d.lm_head = shared["lm_head"].data_ptr()
+        d.embed = embed.data_ptr()
+        d.lm_head = lm_head.data_ptr()
         d.final_norm = weights["g_f"].data_ptr()
         if draft:
-            self._keep += [weights["w_c"], weights["g_c"]]
-            d.w_c = weights["w_c"].data_ptr()
+            w_c = mat(weights["w_c"])
+            self._keep += [w_c, weights["g_c"]]
+            d.w_c = w_c.data_ptr()
             d.g_c = weights["g_c"].data_ptr()
         d.layer_w = ctypes.cast(self._lw, POINTER(c_void_p))
         self.desc = d

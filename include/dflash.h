@@ -28,8 +28,15 @@
  *  - Errors the host cannot see (an unmapped page, an out-of-range token id or tau) are
  *    detected on the device: the offending row or sequence is skipped and a bit is OR-ed
  *    into dflash_kv.error_flags (when that pointer is non-NULL).
- *  - Matrices are row-major [out, in] (y = x W^T), two of them with their rows packed
- *    as described at DFLASH_W_QKV and DFLASH_W_GATE_UP.  Storage dtype (weights, caches,
+ *  - Matrices are [out, in] (y = x W^T), two of them with their rows packed as described
+ *    at DFLASH_W_QKV and DFLASH_W_GATE_UP.  float32 models pass them row-major.  bfloat16
+ *    models pass every matrix except the token embedding (W_qkv, W_o, W_gate_up, W_down,
+ *    lm_head, w_c) in the matrix-core fragment order: rows padded with zeros to a multiple
+ *    of 16; element (n, k) of W [N, K] at
+ *        ((n / 16 * (K / 32) + k / 32) * 64 + (k % 32) / 8 * 16 + n % 16) * 8 + k % 8,
+ *    i.e. one contiguous 1 KB block per 16-row x 32-column tile, tiles row-major, which
+ *    is the operand order of a 16x16x32 bf16 matrix instruction (lane l = 16 g + r holds
+ *    row r, columns 8 g .. 8 g + 7).  The embedding stays row-major [vocab, hidden].  Storage dtype (weights, caches,
  *    tapped features) is the model's dtype: float32 or bfloat16; logits and debug hidden
  *    states are always float32; ids are int32.  Between kernels the activations of a
  *    step live in the workspace in float32; a bfloat16 model's matrix units take them as
