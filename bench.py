@@ -63,6 +63,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-reps", type=int, default=3)
+    ap.add_argument("--no-context-sweep", action="store_true",
+                    help="skip the draft block / attention timing at 4K, 64K and 262K contexts")
     ap.add_argument("--probe-copy", type=int, default=0, metavar="MB",
                     help="after the run, one elementwise pass reading and writing MB MiB "
                          "(calibrates HBM byte counters of profiler runs)")
@@ -234,6 +236,8 @@ def main():
                      "launches": len(gu_ms)},
         "kernels": breakdown,
     }
+    if not args.no_context_sweep:
+        out["context_sweep"] = context_sweep(draft, D, B, dev)
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, dw, shared, feats0, anchor, args.cpu_reps, draft_tok_s)
@@ -245,6 +249,54 @@ def main():
         torch.neg(src, out=dst)      # reads and writes exactly probe_copy MiB each
         torch.cuda.synchronize()
         log(f"probe copy: {args.probe_copy} MiB read + {args.probe_copy} MiB written")
+
+
+def context_sweep(draft, shape, B, dev, contexts=(4096, 65536, 262144), reps=5):
+    """Draft block at batch 1 over synthetic N(0,1) context K/V of each length: µs per draft
+    block, and the attention launches (split-K kernel + merge) of every layer timed with
+    the library's event hook, with their algorithmic HBM bytes (context K/V, block K/V,
+    queries in, output out) per launch."""
+    import torch
+    from block_diffusion_drafter_03_amd import _lib
+    from block_diffusion_drafter_03_amd import runtime as rt
+
+    L, Hkv, d, Hq = shape.n_layers, shape.n_kv_heads, shape.head_dim, shape.n_q_heads
+    out = {}
+    for n in contexts:
+        kv = rt.PagedKV(shape, 1, n + B + 64, torch.bfloat16, dev)
+        gen = torch.Generator(device=dev).manual_seed(n)
+        for t in kv.k + kv.v:
+            t.normal_(generator=gen)
+        kv.seq_len.fill_(n)
+        ws = rt.Workspace(draft.workspace_bytes(1, B, kv.capacity), dev)
+        anchor = torch.zeros(1, dtype=torch.int32, device=dev)
+        ids = torch.zeros(1, B - 1, dtype=torch.int32, device=dev)
+        for _ in range(2):
+            rt.draft_block(draft, kv, anchor, B, ids, ws)
+        torch.cuda.synchronize()
+        _lib.timing_arm(_lib.KERNEL_ATTENTION, reps * L)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for e0, e1 in evs:
+            e0.record()
+            rt.draft_block(draft, kv, anchor, B, ids, ws)
+            e1.record()
+        torch.cuda.synchronize()
+        attn_ms = _lib.timing_read(reps * L)
+        assert int(kv.err.item()) == 0
+        blk_us = sum(e0.elapsed_time(e1) for e0, e1 in evs) * 1e3 / reps
+        attn_us = sum(attn_ms) * 1e3 / len(attn_ms)
+        nbytes = (n + B) * Hkv * d * 2 * 2 + B * Hq * d * 4 * 2
+        gbs = nbytes / (attn_us * 1e-6) / 1e9
+        out[str(n)] = {"us_per_draft_block": round(blk_us, 2),
+                       "draft_tok_s": round((B - 1) / (blk_us * 1e-6), 1),
+                       "attention_us_per_layer": round(attn_us, 2),
+                       "attention_bytes_per_layer": int(nbytes),
+                       "attention_gbs": round(gbs, 1),
+                       "attention_hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+        log(f"context {n}: draft block {blk_us:.1f} us, attention {attn_us:.1f} us/layer ({gbs:.0f} GB/s)")
+        del kv, ws
+        torch.cuda.empty_cache()
+    return out
 
 
 def cpu_baseline(w, dw, shared, feats0, anchor, reps, gpu_value):
@@ -261,13 +313,13 @@ def cpu_baseline(w, dw, shared, feats0, anchor, reps, gpu_value):
         np_dw = {k: synth.to_numpy(v) for k, v in dw.items()}
         np_sh = {k: synth.to_numpy(v) for k, v in shared.items()}
         n = w.ctx[0]
-        ctx = O.inject(synth.to_numpy(feats0), np.arange(n), np_dw, w.draft)
+        ctx = O.inject(synth.to_numpy(feats0), np.arange(n), np_dw, w.draft, store="bf16")
         a = int(anchor[0])
         log(f"cpu baseline: timing {reps} oracle draft blocks")
         ts = []
         for _ in range(reps):
             t0 = time.perf_counter()
-            O.draft_block(np_dw, np_sh, w.draft, ctx, a, n, w.block)
+            O.draft_block(np_dw, np_sh, w.draft, ctx, a, n, w.block, store="bf16")
             ts.append(time.perf_counter() - t0)
     t = sorted(ts)[len(ts) // 2]
     return {"value": round((w.block - 1) / t, 2), "unit": "draft tok/s", "cores": used,

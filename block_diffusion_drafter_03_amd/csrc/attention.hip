@@ -1,22 +1,26 @@
 // Block attention over [injected / cached context ; block] for the drafter (bidirectional
 // inside the block) and for the target's verification pass (causal inside the block).
 //
-// bf16 path (head_dim 128): one workgroup per (sequence, KV head, 64-row query group,
-// key split); split 0 also takes the block's own B keys.  The G*B query rows that share a
-// KV head are split over the 4 waves (16 rows each, held in registers as MFMA operands),
-// so every context K/V byte is read from HBM once per workgroup: a step is one 64-token
-// page slice of the head (16 KB of K, 16 KB of V^T, both contiguous), copied with 16-byte
-// coalesced loads into double-buffered LDS while the previous step is computed.  Each wave
-// runs its own online softmax; S^T = K Q^T and O^T = V^T P^T use v_mfma_f32_16x16x32_bf16
-// with the float32 operand (q, scaled into the log2 domain, and the probabilities P)
-// taken as a compensated (hi, lo) bf16 pair against the stored bf16 K / V:
-//   * the K rows of the two 16-key S^T tiles of each 32-key half are interleaved so that
-//     lane group g ends up holding keys 8g .. 8g+7 of the half for its query column -
-//     exactly the P^T operand layout of the PV product, with no data movement;
+// bf16 path (head_dim 128): one workgroup of 8 waves per CU and per (sequence, KV head,
+// 64-row query group, key split); split 0 also takes the block's own B keys, first.  The
+// G*B query rows that share a KV head are split into 4 tiles of 16 rows (held in registers
+// as MFMA operands) and each tile is taken by two waves, one per 32-key half of every step,
+// so every context K/V byte is read from HBM once per workgroup.  A step is one 64-token
+// page slice of the head (16 KB of K, 16 KB of V^T, both contiguous), loaded with 16-byte
+// coalesced loads into a 3-deep ring of registers and copied into double-buffered LDS, so
+// up to three steps are in flight while one is computed.  S^T = K Q^T and O^T = V^T P^T use
+// v_mfma_f32_16x16x32_bf16 with the float32 operand (q, scaled into the log2 domain, and
+// the probabilities P) taken as a compensated (hi, lo) bf16 pair against the stored bf16
+// K / V:
+//   * the K rows are placed in LDS so that the two 16-key S^T tiles of a 32-key half come
+//     out with lane group g holding keys 8g .. 8g+7 of the half for its query column -
+//     exactly the P^T operand layout of the PV product, with no data movement - while the
+//     16 lanes of every K read still hit 16 different banks;
 //   * V pages are stored transposed ([d][64 keys]) so a V^T operand is one 16-byte read.
-// Each wave writes a partial (m, l, unnormalised O) of its rows; a second launch merges
-// the splits with log-sum-exp weights.  Scores are kept in the log2 domain (scaled by
-// log2(e)/sqrt(d)) and exponentiated with exp2.
+// Each wave runs an online softmax over its half with a lazily moved reference maximum; the
+// halves are merged through LDS and the workgroup writes one partial (m, l, unnormalised O)
+// per row; a second launch merges the splits with log-sum-exp weights.  Scores are kept in
+// the log2 domain (scaled by log2(e)/sqrt(d)) and exponentiated with exp2.
 #include "common.h"
 #include "kernels.h"
 
@@ -48,12 +52,29 @@ struct AttnArgs {
 #define VROW (64 + 8)     // bf16 per V^T row [AD][64 keys]
 #define KTILE (64 * KROW)
 #define VTILE (AD * VROW)
+#define ATTN_MAX_SPLIT_PAGES 1024   // keys per split <= 65536: the split's page list fits LDS
 
-// two workgroups per CU (LDS holds two): registers are budgeted for 2 waves per SIMD
-__global__ __launch_bounds__(256, 2) void attn_splitk_bf16(AttnArgs a) {
+// LDS row of key kk (0..63) of a K tile.  The S^T tile t of lane (r, g) in key half h needs
+// key 32h + 8(r >> 2) + (r & 3) + 4t (so that the accumulator comes out in the P^T operand
+// layout); storing key kk at row (kk & 35) | ((kk >> 1) & 12) | ((kk << 2) & 16) (bit 2
+// moved to bit 4, bits 3-4 to bits 2-3) puts that key at row 32h + 16t + r, so the 16
+// lanes of a read hit 16 consecutive rows: distinct banks at the 68-dword row stride.
+DF_DEV int krow_phys(int kk) { return (kk & 35) | ((kk >> 1) & 12) | ((kk << 2) & 16); }
+
+// One workgroup of 8 waves per CU (two per SIMD).  Waves w and w + 4 hold the same 16
+// query rows; w < 4 takes keys 0..31 of every 64-key step and w + 4 keys 32..63, each with
+// its own online softmax, and the two halves are merged through LDS at the end.  The K/V
+// loads of a step are spread over all 512 threads (4 x 16 B each), which leaves room for a
+// 3-deep ring of register-staged steps: up to 96 KB of K/V in flight per CU while a fourth
+// step is computed from LDS.
+#define ATTN_THREADS 512
+__global__ __launch_bounds__(ATTN_THREADS, 1) void attn_splitk_bf16(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) bf16 kt[2][KTILE];
   __shared__ __attribute__((aligned(16))) bf16 vt[2][VTILE];
+  __shared__ float xo[4][64][33];      // key-half merge: O of waves 4..7
+  __shared__ float xm[4][64], xl[4][64];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int wq = w & 3, kh = w >> 2;
   const int r = lane & 15, g = lane >> 4;
   const int s = blockIdx.x;
   const int kvh = blockIdx.y % a.Hkv, rg = blockIdx.y / a.Hkv;
@@ -65,10 +86,24 @@ __global__ __launch_bounds__(256, 2) void attn_splitk_bf16(AttnArgs a) {
   const int kbeg = s * a.split_len;                  // multiple of 64
   const int kend = min(kbeg + a.split_len, n_ctx);
   const int n_ctx_steps = kend > kbeg ? (kend - kbeg + 63) / 64 : 0;
-  const int n_steps = n_ctx_steps + (s == 0 ? 1 : 0); // split 0 also takes the block's keys
+  // split 0 also takes the block's own keys
 
-  // this wave's query tile: rows rho = rg*64 + w*16 + r as the Q^T MFMA operand
-  const int rho = rg * 64 + w * 16 + r;
+  // the split's physical pages, read and checked once (a page index used straight from
+  // global memory would make every step wait for all loads in flight)
+  __shared__ int pages_s[ATTN_MAX_SPLIT_PAGES];
+  for (int i = tid; i < n_ctx_steps; i += ATTN_THREADS) {
+    int page = a.block_table[(size_t)b * a.max_pages + (kbeg >> 6) + i];
+    if (page < 0 || page >= a.num_pages) {
+      flag_error(a.err, DEVERR_PAGE);
+      page = 0;
+    }
+    pages_s[i] = page;
+  }
+  __syncthreads();
+
+  // this wave's query tile: rows rho = rg*64 + wq*16 + r as the Q^T MFMA operand, scaled
+  // into the log2 domain and split into a compensated (hi, lo) pair
+  const int rho = rg * 64 + wq * 16 + r;
   const int jq = rho < R ? rho % a.B : 0x7fffffff;
   bf16x8 qh[4], ql[4];
   {
@@ -85,61 +120,46 @@ __global__ __launch_bounds__(256, 2) void attn_splitk_bf16(AttnArgs a) {
     }
   }
 
-  // ---- global -> register staging of one step: 8 x 16 B per thread (K then V^T) ----
-  bf16x8 st[8];
-  auto load_step = [&](int i) {
-    if (i < n_ctx_steps) {
-      const int c0 = kbeg + i * 64;
-      int page = a.block_table[(size_t)b * a.max_pages + (c0 >> 6)];
-      if (page < 0 || page >= a.num_pages) {
-        if (tid == 0) flag_error(a.err, DEVERR_PAGE);
-        page = -1;
-      }
-      const size_t pb = (size_t)(page < 0 ? 0 : page) * a.Hkv + kvh;
-      const bf16* ks = a.kpool + pb * 64 * AD;
-      const bf16* vs = a.vpool + pb * AD * 64;
+  // ---- global -> register staging of one step: 4 x 16 B per thread (K then V^T) ----
+  // Every context step issues exactly these 4 loads, unconditionally and to valid
+  // addresses, so the compiler can count them and keep several steps in flight; masking
+  // happens when a step is copied to LDS.  An unmapped page is flagged and read as page 0
+  // (the outputs of that sequence are then invalid, which the error flag reports).
+  bf16x8 st0[4], st1[4], st2[4];
+  auto load_ctx = [&](int i, bf16x8 (&st)[4]) {
+    const size_t pb = (size_t)pages_s[i] * a.Hkv + kvh;
+    const bf16* ks = a.kpool + pb * 64 * AD;
+    const bf16* vs = a.vpool + pb * AD * 64;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        st[j] = *(const bf16x8*)(ks + (size_t)(tid + 256 * j) * 8);
-        st[4 + j] = *(const bf16x8*)(vs + (size_t)(tid + 256 * j) * 8);
-      }
-      if (page < 0) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) st[j][e] = (bf16)0.f;
-      }
-    } else {
-      // the block's own keys: K rows from k_blk, V^T columns from v_blk^T (B <= 64)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int idx = tid + 256 * j;       // K: key = idx / 16, 8-element column group idx % 16
-        const int key = idx >> 4, cg = idx & 15;
-        if (key < a.B)
-          st[j] = *(const bf16x8*)(a.kblk + (size_t)(b * a.B + key) * a.Hkv * AD + (size_t)kvh * AD + cg * 8);
-        else
-#pragma unroll
-          for (int e = 0; e < 8; ++e) st[j][e] = (bf16)0.f;
-        const int d = idx >> 3, kg = idx & 7;  // V^T: row d, keys kg*8 .. kg*8+7
-        const bf16* vs = a.vblkT + ((size_t)(b * a.Hkv + kvh) * AD + d) * a.Bp;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int key2 = kg * 8 + e;
-          st[4 + j][e] = key2 < a.B ? vs[key2] : (bf16)0.f;
-        }
-      }
+    for (int j = 0; j < 2; ++j) {
+      const int idx = tid + ATTN_THREADS * j;
+      st[j] = *(const bf16x8*)(ks + (size_t)idx * 8);
+      st[2 + j] = *(const bf16x8*)(vs + (size_t)idx * 8);
     }
   };
-  // keys at or past `lim` of a partial last page: their V^T columns are zeroed so stale
-  // bytes cannot leak NaN through a zero probability
-  auto store_step = [&](int buf, int lim) {
+  // the block's own keys (split 0 only): K rows from k_blk, V^T columns from v_blk^T
+  // (B <= 64); rows and columns past B are read from valid places and masked at the copy
+  auto load_blk = [&](bf16x8 (&st)[4]) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int idx = tid + 256 * j;
-      *(bf16x8*)&kt[buf][(idx >> 4) * KROW + (idx & 15) * 8] = st[j];
-      bf16x8 v = st[4 + j];
+    for (int j = 0; j < 2; ++j) {
+      const int idx = tid + ATTN_THREADS * j;
+      const int key = min(idx >> 4, a.B - 1);
+      const int k8 = min((idx & 7) * 8, a.Bp - 8);
+      st[j] = *(const bf16x8*)(a.kblk + (size_t)(b * a.B + key) * a.Hkv * AD + (size_t)kvh * AD + (idx & 15) * 8);
+      st[2 + j] = *(const bf16x8*)(a.vblkT + ((size_t)(b * a.Hkv + kvh) * AD + (idx >> 3)) * a.Bp + k8);
+    }
+  };
+  // keys at or past `lim` (a partial last page, the block's padding): their V^T columns are
+  // zeroed so stale bytes cannot leak NaN through a zero probability (their scores are
+  // masked to -inf, so K needs no masking)
+  auto store_step = [&](int buf, int lim, bf16x8 (&st)[4]) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int idx = tid + ATTN_THREADS * j;
+      *(bf16x8*)&kt[buf][krow_phys(idx >> 4) * KROW + (idx & 15) * 8] = st[j];
+      bf16x8 v = st[2 + j];
       const int k0 = (idx & 7) * 8;
-      if (k0 + 8 > lim) {
+      if (lim < 64 && k0 + 8 > lim) {
 #pragma unroll
         for (int e = 0; e < 8; ++e)
           if (k0 + e >= lim) v[e] = (bf16)0.f;
@@ -147,100 +167,146 @@ __global__ __launch_bounds__(256, 2) void attn_splitk_bf16(AttnArgs a) {
       *(bf16x8*)&vt[buf][(idx >> 3) * VROW + k0] = v;
     }
   };
-  auto step_lim = [&](int i) { return i < n_ctx_steps ? min(64, kend - (kbeg + i * 64)) : a.B; };
+  auto step_lim = [&](int i) { return min(64, kend - (kbeg + i * 64)); };
 
   float m = -INFINITY, lsum = 0.f;
   f32x4 o[8];
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int krow0 = 8 * (r >> 2) + (r & 3);   // interleaved K rows: P^T needs no shuffle
 
-  if (n_steps > 0) {
-    load_step(0);
-    store_step(0, step_lim(0));
-  }
-  __syncthreads();
-  for (int i = 0; i < n_steps; ++i) {
-    const int buf = i & 1;
-    if (i + 1 < n_steps) load_step(i + 1);      // next step's loads in flight during compute
-    const bool blk = i >= n_ctx_steps;
-    const int lim = step_lim(i);
+  // this wave's half (keys kh*32 .. kh*32+31) of the step in LDS buffer `buf` (keys >= lim
+  // masked; the block's own step is causal for the verifier)
+  auto compute = [&](int buf, bool blk, int lim) {
     const bf16* K = kt[buf];
     const bf16* VT = vt[buf];
-    f32x4 sc[2][2];
+    f32x4 sc[2];
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+    for (int t = 0; t < 2; ++t) {
+      sc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const bf16* kr = K + (kh * 32 + 16 * t + r) * KROW + g * 8;   // key kh*32 + 8(r>>2) + (r&3) + 4t
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        sc[h][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const bf16* kr = K + (h * 32 + krow0 + 4 * t) * KROW + g * 8;
-#pragma unroll
-        for (int cs = 0; cs < 4; ++cs) {
-          const bf16x8 kf = *(const bf16x8*)(kr + cs * 32);
-          sc[h][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qh[cs], sc[h][t], 0, 0, 0);
-          sc[h][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, ql[cs], sc[h][t], 0, 0, 0);
-        }
+      for (int cs = 0; cs < 4; ++cs) {
+        const bf16x8 kf = *(const bf16x8*)(kr + cs * 32);
+        sc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qh[cs], sc[t], 0, 0, 0);
+        sc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, ql[cs], sc[t], 0, 0, 0);
       }
-    // lane holds keys h*32 + 8g + 4t + e (e < 4) of the step for query column r
-    float p[2][8];
+    }
+    // lane holds keys kh*32 + 8g + 4t + e (e < 4) of the step for query column r
+    float p[8];
     float mx = -INFINITY;
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
+    if (!blk && lim == 64) {   // a full context page: nothing to mask
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int key = h * 32 + g * 8 + 4 * t + e;
+          p[4 * t + e] = sc[t][e];
+          mx = fmaxf(mx, sc[t][e]);
+        }
+    } else {
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int key = kh * 32 + g * 8 + 4 * t + e;
           bool ok = key < lim;
           if (blk && a.causal) ok = ok && key <= jq;
-          const float x = ok ? sc[h][t][e] : -INFINITY;
-          p[h][4 * t + e] = x;
+          const float x = ok ? sc[t][e] : -INFINITY;
+          p[4 * t + e] = x;
           mx = fmaxf(mx, x);
         }
+    }
     mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float mnew = fmaxf(m, mx);
-    const float alpha = mnew == -INFINITY ? 1.f : exp2f(m - mnew);
-    bf16x8 ph[2], pl[2];
+    // the reference max moves only when a step's max exceeds it by more than 8 (log2
+    // domain): probabilities relative to it stay <= 256, the softmax is the same for any
+    // reference, and deep into a context the O rescale is mostly skipped
+    const float mnew = mx > m + 8.f ? mx : m;
+    const float alpha = mnew == m ? 1.f : (m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mnew));
+    const float msub = mnew == -INFINITY ? 0.f : mnew;   // all scores -inf: p = 0
     float ps = 0.f;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float pe = mnew == -INFINITY ? 0.f : exp2f(p[h][e] - mnew);
-        ps += pe;
-        p[h][e] = pe;
-      }
-      split8(p[h], ph[h], pl[h]);
+    for (int e = 0; e < 8; ++e) {
+      const float pe = __builtin_amdgcn_exp2f(p[e] - msub);
+      ps += pe;
+      p[e] = pe;
     }
+    bf16x8 ph, pl;
+    split8(p, ph, pl);
     m = mnew;
     lsum = lsum * alpha + ps;
+    if (__any(alpha != 1.f)) {
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) o[dt] *= alpha;
+    }
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
-      o[dt] *= alpha;
-      const bf16* vr = VT + (dt * 16 + r) * VROW + g * 8;
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const bf16x8 vf = *(const bf16x8*)(vr + h * 32);
-        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, ph[h], o[dt], 0, 0, 0);
-        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pl[h], o[dt], 0, 0, 0);
-      }
+      const bf16x8 vf = *(const bf16x8*)(VT + (dt * 16 + r) * VROW + kh * 32 + g * 8);
+      o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, ph, o[dt], 0, 0, 0);
+      o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pl, o[dt], 0, 0, 0);
     }
-    if (i + 1 < n_steps) store_step(buf ^ 1, step_lim(i + 1));
+  };
+  // the block's own keys first (split 0): loaded together with the ring's first steps
+  bf16x8 stb[4];
+  const int last = n_ctx_steps - 1;
+  if (s == 0) load_blk(stb);
+  if (n_ctx_steps > 0) {
+    load_ctx(0, st0);
+    load_ctx(min(1, last), st1);
+    load_ctx(min(2, last), st2);
+  }
+  if (s == 0) {
+    store_step(0, a.B, stb);
+    __syncthreads();
+    compute(0, true, a.B);
     __syncthreads();
   }
+  // ring over the context steps: while step i is computed from LDS buffer i % 2, steps
+  // i+1 .. i+3 are in flight in the staging registers; step i+1 then moves to the other
+  // LDS buffer.  Loads and copies run for every slot (indices clamped to the last step) so
+  // each ring slot issues the same instructions; only the compute is skipped past the end.
+  if (n_ctx_steps > 0) {
+    store_step(0, step_lim(0), st0);
+    __syncthreads();
+    auto body = [&](int i, bf16x8 (&ld)[4], bf16x8 (&nx)[4]) {
+      load_ctx(min(i + 3, last), ld);
+      if (i < n_ctx_steps) compute(i & 1, false, step_lim(i));
+      store_step((i + 1) & 1, step_lim(min(i + 1, last)), nx);
+      __syncthreads();
+    };
+    for (int i = 0; i < n_ctx_steps; i += 3) {
+      body(i, st0, st1);
+      body(i + 1, st1, st2);
+      body(i + 2, st2, st0);
+    }
+  }
 
-  // ---- partial (m, l, unnormalised O) of this wave's 16 query rows ----
+  // ---- merge the two key halves, then the partial (m, l, unnormalised O) of the rows ----
   lsum += __shfl_xor(lsum, 16, 64);
   lsum += __shfl_xor(lsum, 32, 64);
+  if (kh == 1) {
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) xo[wq][lane][dt * 4 + e] = o[dt][e];
+    xm[wq][lane] = m;
+    xl[wq][lane] = lsum;
+  }
+  __syncthreads();
+  if (kh == 1) return;
+  const float m1 = xm[wq][lane], l1 = xl[wq][lane];
+  const float mt = fmaxf(m, m1);
+  const float a0 = m == -INFINITY ? 0.f : exp2f(m - mt);
+  const float a1 = m1 == -INFINITY ? 0.f : exp2f(m1 - mt);
   const size_t unit = ((size_t)b * a.Hkv + kvh) * a.n_rg + rg;
-  float* dst = a.part + (unit * a.n_splits + s) * 64 * PSTRIDE + (size_t)(w * 16 + r) * PSTRIDE;
+  float* dst = a.part + (unit * a.n_splits + s) * 64 * PSTRIDE + (size_t)(wq * 16 + r) * PSTRIDE;
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt)
-    *(float4*)(dst + dt * 16 + g * 4) = make_float4(o[dt][0], o[dt][1], o[dt][2], o[dt][3]);
+    *(float4*)(dst + dt * 16 + g * 4) =
+        make_float4(o[dt][0] * a0 + xo[wq][lane][dt * 4 + 0] * a1, o[dt][1] * a0 + xo[wq][lane][dt * 4 + 1] * a1,
+                    o[dt][2] * a0 + xo[wq][lane][dt * 4 + 2] * a1, o[dt][3] * a0 + xo[wq][lane][dt * 4 + 3] * a1);
   if (g == 0) {
-    dst[AD] = m;
-    dst[AD + 1] = lsum;
+    dst[AD] = mt;
+    dst[AD + 1] = lsum * a0 + l1 * a1;
   }
 }
 
@@ -401,9 +467,9 @@ AttnPlan attn_plan(int dt, int batch, int Hkv, int G, int B, int ctx_cap) {
   }
   const int cap = ctx_cap > 0 ? ctx_cap : 1;
   const int units = batch * Hkv * p.n_rg;
-  // two workgroups fit a CU (LDS-bound): aim for one wave of workgroups over the chip,
+  // one workgroup per CU (register-bound): aim for one wave of workgroups over the chip,
   // with at least 256 keys (4 steps) in a split
-  int want = 2 * attn_num_cus() / units;
+  int want = attn_num_cus() / units;
   const int max_splits = (cap + 255) / 256;
   if (want > max_splits) want = max_splits;
   if (want < 1) want = 1;
@@ -411,6 +477,7 @@ AttnPlan attn_plan(int dt, int batch, int Hkv, int G, int B, int ctx_cap) {
   len = (len + 127) / 128 * 128;
   static const int forced = env_int("DFLASH_ATTN_SPLIT_LEN", 0);
   if (forced >= 128) len = (forced + 127) / 128 * 128;
+  if (len > 64 * ATTN_MAX_SPLIT_PAGES) len = 64 * ATTN_MAX_SPLIT_PAGES;
   p.split_len = len;
   p.n_ctx_splits = (cap + len - 1) / len;
   return p;
@@ -451,7 +518,7 @@ hipError_t launch_attention(int dt, const AttnPlan& p, const float* q, const voi
     a.out = o;
     a.out_afrag = o_afrag;
     dim3 grid(p.n_ctx_splits, Hkv * p.n_rg, batch);
-    hipLaunchKernelGGL(attn_splitk_bf16, grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL(attn_splitk_bf16, grid, dim3(ATTN_THREADS), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     dim3 g2((p.n_rg * 64 + 7) / 8, Hkv, batch);
