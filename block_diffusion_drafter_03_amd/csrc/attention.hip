@@ -311,27 +311,52 @@ __global__ __launch_bounds__(ATTN_THREADS, 1) void attn_splitk_bf16(AttnArgs a) 
 }
 
 
-// Split merge as its own launch: 8 query rows per workgroup, 32 threads x 4 columns per row.
+// Split merge as its own launch: 8 query rows per workgroup, 32 threads x 4 columns per
+// row.  The splits' (m, l) of the 8 rows are read into LDS by all threads at once, the
+// log-sum-exp weights are formed there, and each thread then sums its 4 columns over the
+// splits with independent loads.
+#define MERGE_MAX_SPLITS 512
 __global__ __launch_bounds__(256) void attn_merge_bf16(AttnArgs a) {
+  __shared__ float wsh[8][MERGE_MAX_SPLITS];
+  __shared__ float lsh[8][MERGE_MAX_SPLITS];
   const int rl = threadIdx.x >> 5, t = threadIdx.x & 31;
-  const int rho = blockIdx.x * 8 + rl;
+  const int rho0 = blockIdx.x * 8;
   const int kvh = blockIdx.y, b = blockIdx.z;
   const int R = a.G * a.B, S = a.n_splits;
-  if (rho >= R) return;
-  const int rg = rho / 64, q = rho % 64;
-  const size_t unit = ((size_t)b * a.Hkv + kvh) * a.n_rg + rg;
-  const float* pr = a.part + unit * S * 64 * PSTRIDE + (size_t)q * PSTRIDE;
   const size_t ss = 64 * PSTRIDE;
+  // (m, l) of every (split, row) of this workgroup
+  for (int idx = threadIdx.x; idx < S * 8; idx += 256) {
+    const int sp = idx >> 3, row = idx & 7, rho = min(rho0 + row, R - 1);
+    const size_t unit = ((size_t)b * a.Hkv + kvh) * a.n_rg + rho / 64;
+    const float* pr = a.part + (unit * S + sp) * ss + (size_t)(rho % 64) * PSTRIDE;
+    wsh[row][sp] = pr[AD];
+    lsh[row][sp] = pr[AD + 1];
+  }
+  __syncthreads();
+  const int rho = rho0 + rl;
+  // weights: the row's 32 threads split the splits, then combine through lane shuffles
   float ms = -INFINITY;
-  for (int sp = 0; sp < S; ++sp) ms = fmaxf(ms, pr[sp * ss + AD]);
+  for (int sp = t; sp < S; sp += 32) ms = fmaxf(ms, wsh[rl][sp]);
+#pragma unroll
+  for (int o = 16; o > 0; o >>= 1) ms = fmaxf(ms, __shfl_xor(ms, o, 64));
   float lt = 0.f;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll 4
-  for (int sp = 0; sp < S; ++sp) {
-    const float mv = pr[sp * ss + AD];
+  for (int sp = t; sp < S; sp += 32) {
+    const float mv = wsh[rl][sp];
     const float wgt = mv == -INFINITY ? 0.f : exp2f(mv - ms);
-    lt += pr[sp * ss + AD + 1] * wgt;
-    const float4 x = *(const float4*)(pr + sp * ss + 4 * t);
+    lt += lsh[rl][sp] * wgt;
+    wsh[rl][sp] = wgt;
+  }
+#pragma unroll
+  for (int o = 16; o > 0; o >>= 1) lt += __shfl_xor(lt, o, 64);
+  __syncthreads();
+  if (rho >= R) return;
+  const size_t unit = ((size_t)b * a.Hkv + kvh) * a.n_rg + rho / 64;
+  const float* pr = a.part + unit * S * ss + (size_t)(rho % 64) * PSTRIDE + 4 * t;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 16
+  for (int sp = 0; sp < S; ++sp) {
+    const float wgt = wsh[rl][sp];
+    const float4 x = *(const float4*)(pr + sp * ss);
     acc.x += x.x * wgt;
     acc.y += x.y * wgt;
     acc.z += x.z * wgt;
@@ -478,6 +503,8 @@ AttnPlan attn_plan(int dt, int batch, int Hkv, int G, int B, int ctx_cap) {
   static const int forced = env_int("DFLASH_ATTN_SPLIT_LEN", 0);
   if (forced >= 128) len = (forced + 127) / 128 * 128;
   if (len > 64 * ATTN_MAX_SPLIT_PAGES) len = 64 * ATTN_MAX_SPLIT_PAGES;
+  if ((cap + len - 1) / len > MERGE_MAX_SPLITS) len = (cap + MERGE_MAX_SPLITS - 1) / MERGE_MAX_SPLITS;
+  len = (len + 127) / 128 * 128;
   p.split_len = len;
   p.n_ctx_splits = (cap + len - 1) / len;
   return p;
@@ -517,6 +544,9 @@ hipError_t launch_attention(int dt, const AttnPlan& p, const float* q, const voi
     a.part = part;
     a.out = o;
     a.out_afrag = o_afrag;
+    // the split's page list and the merge's weights live in fixed LDS arrays
+    if (p.split_len > 64 * ATTN_MAX_SPLIT_PAGES || p.n_ctx_splits > MERGE_MAX_SPLITS)
+      return hipErrorInvalidValue;
     dim3 grid(p.n_ctx_splits, Hkv * p.n_rg, batch);
     hipLaunchKernelGGL(attn_splitk_bf16, grid, dim3(ATTN_THREADS), 0, st, a);
     hipError_t e = hipGetLastError();
