@@ -63,6 +63,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-reps", type=int, default=3)
+    ap.add_argument("--no-workload-sweep", action="store_true",
+                    help="skip the batch-16, 512-row injection and batch-8 cycle measurements")
     ap.add_argument("--no-context-sweep", action="store_true",
                     help="skip the draft block / attention timing at 4K, 64K and 262K contexts")
     ap.add_argument("--probe-copy", type=int, default=0, metavar="MB",
@@ -238,6 +240,8 @@ def main():
     }
     if not args.no_context_sweep:
         out["context_sweep"] = context_sweep(draft, D, B, dev)
+    if not args.no_workload_sweep:
+        out["workload_sweep"] = workload_sweep(draft, target, D, T, B, dev)
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, dw, shared, feats0, anchor, args.cpu_reps, draft_tok_s)
@@ -249,6 +253,143 @@ def main():
         torch.neg(src, out=dst)      # reads and writes exactly probe_copy MiB each
         torch.cuda.synchronize()
         log(f"probe copy: {args.probe_copy} MiB read + {args.probe_copy} MiB written")
+
+
+def _filled_kv(rt, torch, shape, lens, cap, dev, seed):
+    """Paged cache of len(lens) sequences with synthetic N(0, 1) K/V in every page."""
+    kv = rt.PagedKV(shape, len(lens), cap, torch.bfloat16, dev)
+    gen = torch.Generator(device=dev).manual_seed(seed)
+    for t in kv.k + kv.v:
+        t.normal_(generator=gen)
+    kv.seq_len.copy_(torch.tensor(lens, dtype=torch.int32))
+    return kv
+
+
+def _timed(torch, fn, reps):
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for e0, e1 in evs:
+        e0.record()
+        fn()
+        e1.record()
+    torch.cuda.synchronize()
+    return sum(e0.elapsed_time(e1) for e0, e1 in evs) * 1e3 / reps
+
+
+def workload_sweep(draft, target, D, T, B, dev, reps=5, cycles=4):
+    """The batched workloads, timed on the same models:
+    * batch 16, contexts in [2048, 8192] in shuffled 64-token pages: draft block, and the
+      gate/up GEMMs' useful bf16 rate against the dense MFMA peak (M = 256 rows);
+    * one 512-row injection chunk (fusion + K/V of every draft layer), against MFMA peak;
+    * batch 8, 8192-token caches, full cycles under the seeded acceptance-forcing rule
+      for p in {0.3, 0.7, 1.0}: tau, T_draft = draft block, T_verify = verify + accept +
+      inject + commit, L = (T_draft + T_verify) / tau per sequence."""
+    import numpy as np
+    import torch
+    import synth
+    from block_diffusion_drafter_03_amd import _lib
+    from block_diffusion_drafter_03_amd import runtime as rt
+
+    out = {}
+    # ---- batch 16, ragged paged contexts ----
+    w3 = synth.workload("qwen3_8b_b16_paged")
+    lens = synth.ctx_lengths(w3)
+    kv = _filled_kv(rt, torch, D, lens, max(lens) + B + 64, dev, 3)
+    g = torch.Generator().manual_seed(7)
+    perm = torch.randperm(kv.block_table.numel(), generator=g).to(torch.int32)
+    kv.block_table.copy_(perm.reshape(kv.block_table.shape))
+    ws = rt.Workspace(draft.workspace_bytes(w3.batch, B, kv.capacity, w3.batch * B), dev)
+    anchor = synth.anchors(w3, dev)
+    ids = torch.zeros(w3.batch, B - 1, dtype=torch.int32, device=dev)
+    rt.draft_block(draft, kv, anchor, B, ids, ws)
+    torch.cuda.synchronize()
+    _lib.timing_arm(_lib.KERNEL_GEMM_GATE_UP, reps * D.n_layers)
+    us = _timed(torch, lambda: rt.draft_block(draft, kv, anchor, B, ids, ws), reps)
+    gu_ms = _lib.timing_read(reps * D.n_layers)
+    assert int(kv.err.item()) == 0
+    M = w3.batch * B
+    gu_tf = 2.0 * M * (2 * D.ffn) * D.hidden / (sum(gu_ms) / len(gu_ms) * 1e-3) / 1e12
+    out["qwen3_8b_b16_paged"] = {
+        "us_per_draft_block": round(us, 2), "draft_tok_s": round(w3.batch * (B - 1) / (us * 1e-6), 1),
+        "gate_up_us": round(sum(gu_ms) / len(gu_ms) * 1e3, 2),
+        "gate_up_useful_tflops": round(gu_tf, 1),
+        "gate_up_mfma_frac": round(gu_tf / MFMA_BF16_PEAK_TFLOPS, 4),
+        "note": "useful flops 2*M*N*K; the compensated activations issue twice as many MFMAs"}
+    log(f"batch 16: draft block {us:.1f} us, gate/up {gu_tf:.0f} useful TFLOP/s")
+    # ---- one 512-row injection chunk ----
+    rows = 512
+    rs = torch.zeros(rows, dtype=torch.int32, device=dev)
+    rp = torch.arange(rows, dtype=torch.int32, device=dev)
+    feats = torch.randn(rows, 5 * D.hidden, device=dev).to(torch.bfloat16)
+    kv1 = rt.PagedKV(D, 1, rows + 64, torch.bfloat16, dev)
+    ws1 = rt.Workspace(draft.workspace_bytes(1, B, kv1.capacity, rows), dev)
+    rt.inject_ctx(draft, kv1, feats, rs, rp, 0, ws1)
+    us_inj = _timed(torch, lambda: rt.inject_ctx(draft, kv1, feats, rs, rp, 0, ws1), reps)
+    flops = 2.0 * rows * (5 * D.hidden * D.hidden + D.hidden * D.n_layers * 2 * D.n_kv_heads * D.head_dim)
+    inj_tf = flops / (us_inj * 1e-6) / 1e12
+    out["inject_512_rows"] = {"us": round(us_inj, 2), "useful_tflops": round(inj_tf, 1),
+                              "mfma_frac": round(inj_tf / MFMA_BF16_PEAK_TFLOPS, 4)}
+    log(f"inject 512 rows: {us_inj:.1f} us, {inj_tf:.0f} useful TFLOP/s")
+    del kv, ws, kv1, ws1
+    torch.cuda.empty_cache()
+    # ---- batch 8 cycles with forced acceptance ----
+    w5 = synth.workload("qwen3_8b_cycle_b8")
+    lens5 = synth.ctx_lengths(w5)
+    nb = w5.batch
+    cap = max(lens5) + B * (3 * cycles + 2) + 64
+    k = len(w5.taps)
+    res = {}
+    for pi, p_acc in enumerate(w5.accept_p):
+        tkv = _filled_kv(rt, torch, T, lens5, cap, dev, 50 + pi)
+        dkv = _filled_kv(rt, torch, D, lens5, cap, dev, 60 + pi)
+        ws_d = rt.Workspace(draft.workspace_bytes(nb, B, dkv.capacity, nb * B), dev)
+        ws_t = rt.Workspace(target.workspace_bytes(nb, B, tkv.capacity), dev)
+        feats = torch.zeros(nb, B, k * T.hidden, dtype=torch.bfloat16, device=dev)
+        gv = torch.zeros(nb, B, dtype=torch.int32, device=dev)
+        tau = torch.zeros(nb, dtype=torch.int32, device=dev)
+        bonus = torch.zeros(nb, dtype=torch.int32, device=dev)
+        drafts = torch.zeros(nb, B - 1, dtype=torch.int32, device=dev)
+        rs = torch.arange(nb, dtype=torch.int32, device=dev).repeat_interleave(B)
+        rp = torch.arange(B, dtype=torch.int32, device=dev).repeat(nb)
+        anchor = synth.anchors(w5, dev)
+        t_draft, t_ver, taus = [], [], []
+        for c in range(cycles):
+            t_draft.append(_timed(torch, lambda: rt.draft_block(draft, dkv, anchor, B, drafts, ws_d), 1))
+            # untimed pre-pass: the target's greedy continuation g*_0 .. g*_f of every sequence
+            coins = synth.force_coins(1234 + pi, c, nb, B, p_acc)
+            own = drafts.cpu().numpy()
+            d = own.copy()
+            fmax = int(max(np.argmin(np.append(cr, False)) for cr in coins))
+            gstar = np.zeros((nb, B), dtype=np.int64)
+            for j in range(fmax + 1):
+                rt.verify_accept(target, tkv, anchor, torch.tensor(d, dtype=torch.int32, device=dev),
+                                 B, feats, gv, tau, bonus, ws_t)
+                gj = gv.cpu().numpy()
+                gstar[:, j] = gj[:, j]
+                if j < B - 1:
+                    d[:, j] = gj[:, j]
+            forced = np.stack([synth.forced_drafts(coins[b], gstar[b], own[b], T.vocab)[0] for b in range(nb)])
+            drafts.copy_(torch.tensor(forced, dtype=torch.int32))
+            torch.cuda.synchronize()
+
+            def verify_cycle():
+                rt.verify_accept(target, tkv, anchor, drafts, B, feats, gv, tau, bonus, ws_t)
+                rt.inject_ctx(draft, dkv, feats.view(nb * B, -1), rs, rp, 1, ws_d)
+                rt.kv_commit(tkv, dkv, tau, B)
+            t_ver.append(_timed(torch, verify_cycle, 1))
+            taus.append(tau.cpu().numpy().astype(float))
+            anchor = bonus.clone()
+        assert int(tkv.err.item()) == 0 and int(dkv.err.item()) == 0
+        tau_mean = float(np.mean(taus))
+        td, tv = float(np.mean(t_draft)), float(np.mean(t_ver))
+        res[str(p_acc)] = {"tau_mean": round(tau_mean, 3),
+                           "expected_tau": round(1.0 + sum(p_acc ** j for j in range(1, B)), 3),
+                           "us_draft": round(td, 2), "us_verify_inject_commit": round(tv, 2),
+                           "L_us_per_token": round((td + tv) / tau_mean, 2)}
+        log(f"batch 8, p={p_acc}: tau {tau_mean:.2f}, draft {td:.0f} us, verify+inject+commit {tv:.0f} us")
+        del tkv, dkv, ws_d, ws_t
+        torch.cuda.empty_cache()
+    out["qwen3_8b_cycle_b8"] = res
+    return out
 
 
 def context_sweep(draft, shape, B, dev, contexts=(4096, 65536, 262144), reps=5):

@@ -7,9 +7,8 @@
 // tapped features of the fusion GEMM) are row-major and enter as they are.
 //  * gemm_gemv_bf16   (M <= 16): the weight-streaming shape of a drafter step.  8 waves
 //    split K, a workgroup walks 16-column tiles; see the kernel.
-//  * gemm_tiled_bf16  (M > 16): 64x64 output tiles, 2x2 waves of 32x32, BK = 64, A and W
-//    staged through LDS with the next K tile's global loads in flight during the MFMAs;
-//    1-D grid remapped so that the M tiles sharing a W column block run on one XCD.
+//  * gemm_mfma_bf16   (M > 16): 2 x 2 waves of up to 64 x 64 outputs, A (hi, lo) and W staged
+//    through LDS in fragment order, the next K step's loads in flight during the MFMAs.
 //  * gemm_f32         (float32 models): VALU 64x64 tiles, BK = 16, row-major operands.
 //
 // MFMA: v_mfma_f32_16x16x32_bf16.  Lane l (r = l % 16, g = l / 16) supplies A[r][8g..8g+7]
@@ -312,191 +311,228 @@ static int gemv_stream_tiles() {
   static const int v = env_knob("DFLASH_GEMV_STREAM_TILES", num_cus());
   return v;
 }
+// DFLASH_GEMM_TILE forces the M > 16 workgroup tile and K staging (see launch_kind)
+static int gemm_tile_knob() {
+  static const int v = env_knob("DFLASH_GEMM_TILE", 0);
+  return v;
+}
 
 // ---------------------------------------------------------------------------------------
-#define TB 64
-#define TK 64
-#define TPAD 8
-
-// A tile (64 rows x 64 k) staging.  TA = float: 16 fragment halves of 1 KB (4 row blocks x
-// 2 steps x 2 halves); thread c, slot j covers row 16 j + c % 16, k = 32 (c / 128) +
-// 8 ((c % 64) / 16) + 4 ((c / 64) % 2) .. +3.  TA = bf16: row-major rows, 2 x 8 values.
-template <typename TA> struct ATile;
-template <> struct ATile<float> {
-  static constexpr int SLOTS = 4, VALS = 4;
-};
-template <> struct ATile<bf16> {
-  static constexpr int SLOTS = 2, VALS = 8;
-};
-
-template <typename TA, bool NORM, int KIND>
-__global__ __launch_bounds__(256) void gemm_tiled_bf16(GemmArgs ga) {
+// M > 16: WGM x WGN waves, each wave TM x TN MFMA tiles (16 x 16), so a workgroup covers
+// (16 TM WGM) x (16 TN WGN) outputs.  An LDS stage holds KSUB MFMA k-steps (BK = 32 KSUB),
+// double-buffered; DEPTH stages of global loads are in flight in registers while one is
+// computed (the loads are unconditional, the stage index clamped, so the compiler counts
+// them and never drains the ring).  LDS holds the operands in fragment order - A as (hi,
+// lo) bf16 pairs split from the float32 activations on the way in, W as it is stored - so
+// every MFMA operand read is one contiguous, conflict-free 1 KB per wave.  Grid: tiles
+// M-fastest, remapped so the M tiles of one W column block run on one XCD (one L2).
+template <typename TA, int WGM, int WGN, int TM, int TN, int KSUB, int DEPTH, bool NORM, int KIND>
+__global__ __launch_bounds__(64 * WGM * WGN) void gemm_mfma_bf16(GemmArgs ga) {
   constexpr bool TWO = AIsFloat<TA>::value;
-  constexpr int SLOTS = ATile<TA>::SLOTS, VALS = ATile<TA>::VALS;
-  __shared__ __attribute__((aligned(16))) bf16 As[TWO ? 2 : 1][TB][TK + TPAD];
-  __shared__ __attribute__((aligned(16))) bf16 Bs[TB][TK + TPAD];
-  __shared__ float ss_part[NORM ? TB : 1][NORM ? 17 : 1];
-  __shared__ float rstd_s[TB];
+  constexpr int NT_ = 64 * WGM * WGN;             // threads
+  constexpr int BM = 16 * TM * WGM, BN = 16 * TN * WGN;   // workgroup tile
+  constexpr int RB = BM / 16, NB = BN / 16;       // 16-row A blocks, 16-column W tiles
+  constexpr int NP = TWO ? 2 : 1;                 // A planes in LDS: hi (, lo)
+  // staging slots per thread and k-step: A float32: RB x 2 halves x 64 lanes float4;
+  // A bf16 (row-major rows): RB x 64 lanes x 16 B; W: NB x 64 lanes x 16 B
+  constexpr int AS = TWO ? RB * 2 * 64 / NT_ : RB * 64 / NT_;
+  constexpr int WS = NB * 64 / NT_;
+  static_assert(AS >= 1 && WS >= 1 && AS * NT_ == (TWO ? RB * 128 : RB * 64) && WS * NT_ == NB * 64,
+                "tile does not split evenly over the threads");
+  static_assert(DEPTH == 2 || DEPTH == 3, "ring depth");
+  __shared__ __attribute__((aligned(16))) bf16x8 As[2][NP][KSUB][RB][64];
+  __shared__ __attribute__((aligned(16))) bf16x8 Ws[2][KSUB][NB][64];
+  __shared__ float ss_part[NORM ? BM : 1][NORM ? 9 : 1];
+  __shared__ float rstd_s[NORM ? BM : 1];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int r = lane & 15, g = lane >> 4;
-  const int wm = w >> 1, wn = w & 1;
+  const int wm = w / WGN, wn = w % WGN;
   const int M = ga.M, N = ga.N, K = ga.K, KS = K >> 5;
+  const int NST = KS / KSUB;                      // stages (K % (32 KSUB) == 0)
   const int MB = (M + 15) >> 4, NT = (N + 15) >> 4;
-  const int mt_n = (M + TB - 1) / TB, nt_n = (N + TB - 1) / TB;
+  const int mt_n = (M + BM - 1) / BM, nt_n = (N + BN - 1) / BN;
   const int T = mt_n * nt_n;
-  // tiles ordered M-fastest; give each XCD (WG id mod 8) a contiguous run of tiles so the
-  // M tiles that read the same W columns share an L2
   int t = blockIdx.x;
   if ((T & 7) == 0) t = (blockIdx.x & 7) * (T >> 3) + (blockIdx.x >> 3);
-  const int m0 = (t % mt_n) * TB, n0 = (t / mt_n) * TB;
+  const int m0 = (t % mt_n) * BM, n0 = (t / mt_n) * BN;
 
-  // ---- this thread's A slots ----
-  int arow[SLOTS], acol[SLOTS];
-  const TA* ap[SLOTS];
+  // ---- staging slots ----
+  const TA* ap[AS];
+  int a_rb[AS], a_lane[AS], a_h[AS];
 #pragma unroll
-  for (int j = 0; j < SLOTS; ++j) {
+  for (int j = 0; j < AS; ++j) {
+    const int q = tid + NT_ * j;
     if constexpr (TWO) {
-      arow[j] = 16 * j + r;
-      acol[j] = 32 * (tid >> 7) + 8 * g + 4 * ((tid >> 6) & 1);
-      const int mb = min((m0 >> 4) + j, MB - 1);
-      ap[j] = (const TA*)ga.A + ((size_t)(mb * KS + (tid >> 7)) * 2 + ((tid >> 6) & 1)) * 256 + lane * 4;
+      a_rb[j] = q >> 7;
+      a_h[j] = (q >> 6) & 1;
+      a_lane[j] = q & 63;
+      const int mb = min((m0 >> 4) + a_rb[j], MB - 1);
+      ap[j] = (const TA*)ga.A + ((size_t)mb * KS * 2 + a_h[j]) * 256 + a_lane[j] * 4;
     } else {
-      const int c = tid + 256 * j;
-      arow[j] = c >> 3;
-      acol[j] = (c & 7) * 8;
-      ap[j] = (const TA*)ga.A + (size_t)min(m0 + arow[j], M - 1) * ga.lda + acol[j];
+      a_rb[j] = q >> 6;
+      a_h[j] = 0;
+      a_lane[j] = q & 63;
+      const int row = min(m0 + a_rb[j] * 16 + (a_lane[j] & 15), M - 1);
+      ap[j] = (const TA*)ga.A + (size_t)row * ga.lda + (a_lane[j] >> 4) * 8;
     }
   }
-  // A slot loads of the K tile at k0 (float: the step advances by 2 per K tile)
-  auto load_as = [&](int k0, float (*ra)[VALS]) {
+  const bf16* wp[WS];
+  int w_nt[WS], w_lane[WS];
 #pragma unroll
-    for (int j = 0; j < SLOTS; ++j) {
-      if constexpr (TWO) {
-        const float4 x = *(const float4*)(ap[j] + (size_t)(k0 >> 5) * 512);
-        ra[j][0] = x.x; ra[j][1] = x.y; ra[j][2] = x.z; ra[j][3] = x.w;
-      } else {
-        load8(ap[j] + k0, ra[j]);
+  for (int j = 0; j < WS; ++j) {
+    const int q = tid + NT_ * j;
+    w_nt[j] = q >> 6;
+    w_lane[j] = q & 63;
+    wp[j] = wblock(ga.B, min((n0 >> 4) + w_nt[j], NT - 1), 0, KS) + w_lane[j] * 8;
+  }
+  const bf16* gk = NORM ? (const bf16*)ga.norm_g : nullptr;
+  float ss[AS];
+#pragma unroll
+  for (int j = 0; j < AS; ++j) ss[j] = 0.f;
+
+  struct Stage {
+    float ra[KSUB][AS][TWO ? 4 : 8];
+    bf16x8 rw[KSUB][WS];
+  };
+  Stage s0, s1, s2;
+  auto gload = [&](Stage& st, int stage) {
+#pragma unroll
+    for (int u = 0; u < KSUB; ++u) {
+      const int ks = stage * KSUB + u;
+#pragma unroll
+      for (int j = 0; j < AS; ++j) {
+        if constexpr (TWO) {
+          const float4 x = *(const float4*)(ap[j] + (size_t)ks * 512);
+          st.ra[u][j][0] = x.x; st.ra[u][j][1] = x.y; st.ra[u][j][2] = x.z; st.ra[u][j][3] = x.w;
+        } else {
+          load8(ap[j] + (size_t)ks * 32, st.ra[u][j]);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < WS; ++j) st.rw[u][j] = *(const bf16x8*)(wp[j] + (size_t)ks * 512);
+    }
+  };
+  // staged stage -> LDS buffer `buf` (RMSNorm statistics and gain on the way)
+  auto lstore = [&](Stage& st, int buf, int stage) {
+#pragma unroll
+    for (int u = 0; u < KSUB; ++u) {
+      const int ks = stage * KSUB + u;
+#pragma unroll
+      for (int j = 0; j < AS; ++j) {
+        if constexpr (TWO) {
+          float v[8];
+          const int k0 = ks * 32 + 8 * (a_lane[j] >> 4) + 4 * a_h[j];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float x = st.ra[u][j][e];
+            if (NORM) {
+              ss[j] += x * x;
+              x *= (float)gk[k0 + e];
+            }
+            v[e] = x;
+            v[4 + e] = 0.f;
+          }
+          bf16x8 hi, lo;
+          split8(v, hi, lo);
+          bf16x4* dh = (bf16x4*)&As[buf][0][u][a_rb[j]][a_lane[j]] + a_h[j];
+          bf16x4* dl = (bf16x4*)&As[buf][NP - 1][u][a_rb[j]][a_lane[j]] + a_h[j];
+          *dh = bf16x4{hi[0], hi[1], hi[2], hi[3]};
+          *dl = bf16x4{lo[0], lo[1], lo[2], lo[3]};
+        } else {
+          bf16x8 hi, lo;
+          split8(st.ra[u][j], hi, lo);
+          As[buf][0][u][a_rb[j]][a_lane[j]] = hi;
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < WS; ++j) Ws[buf][u][w_nt[j]][w_lane[j]] = st.rw[u][j];
+    }
+  };
+
+  f32x4 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < KSUB; ++u) {
+      bf16x8 wf[TN];
+#pragma unroll
+      for (int j = 0; j < TN; ++j) wf[j] = Ws[buf][u][wn * TN + j][lane];
+#pragma unroll
+      for (int p = 0; p < NP; ++p) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+          const bf16x8 af = As[buf][p][u][wm * TM + i][lane];
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, wf[j], acc[i][j], 0, 0, 0);
+        }
       }
     }
   };
-  // ---- this thread's W slots: 2 x 16 B of the 8 fragment blocks of the tile ----
-  const bf16* bp[2];
-  int brow_[2], bcol[2];
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int q = tid + 256 * j, blk = q >> 6, bl = q & 63;
-    brow_[j] = 16 * (blk >> 1) + (bl & 15);
-    bcol[j] = 32 * (blk & 1) + 8 * (bl >> 4);
-    bp[j] = wblock(ga.B, min((n0 >> 4) + (blk >> 1), NT - 1), blk & 1, KS) + bl * 8;
-  }
-  const bf16* gk = NORM ? (const bf16*)ga.norm_g : nullptr;
-  float ra[SLOTS][VALS];
-  bf16x8 rb[2];
-  float ss[SLOTS];
-#pragma unroll
-  for (int j = 0; j < SLOTS; ++j) ss[j] = 0.f;
-  load_as(0, ra);
-#pragma unroll
-  for (int j = 0; j < 2; ++j) rb[j] = *(const bf16x8*)bp[j];
-  f32x4 acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  for (int k0 = 0; k0 < K; k0 += TK) {
-#pragma unroll
-    for (int j = 0; j < SLOTS; ++j) {
-      float v[8];
-#pragma unroll
-      for (int e = 0; e < VALS; ++e) {
-        float x = ra[j][e];
-        if (NORM) {
-          ss[j] += x * x;
-          x *= (float)gk[k0 + acol[j] + e];
-        }
-        v[e] = x;
-      }
-#pragma unroll
-      for (int e = VALS; e < 8; ++e) v[e] = 0.f;
-      bf16x8 hi, lo;
-      split8(v, hi, lo);
-      if constexpr (TWO) {
-        bf16x4 h4 = {hi[0], hi[1], hi[2], hi[3]}, l4 = {lo[0], lo[1], lo[2], lo[3]};
-        *(bf16x4*)&As[0][arow[j]][acol[j]] = h4;
-        *(bf16x4*)&As[TWO ? 1 : 0][arow[j]][acol[j]] = l4;
-      } else {
-        *(bf16x8*)&As[0][arow[j]][acol[j]] = hi;
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < 2; ++j) *(bf16x8*)&Bs[brow_[j]][bcol[j]] = rb[j];
+  // ring: stage q is computed from LDS buffer q % 2 while the next DEPTH stages are in
+  // flight; then stage q+1 moves to the other buffer.  Past the last stage the loads still
+  // run (clamped, harmless) so that every slot issues the same instructions.
+  const int last = NST - 1;
+  gload(s0, 0);
+  gload(s1, min(1, last));
+  if constexpr (DEPTH == 3) gload(s2, min(2, last));
+  lstore(s0, 0, 0);
+  __syncthreads();
+  auto body = [&](int q, Stage& ld, Stage& nx) {
+    gload(ld, min(q + DEPTH, last));
+    if (q < NST) compute(q & 1);
+    if (q + 1 < NST) lstore(nx, (q + 1) & 1, q + 1);
     __syncthreads();
-    if (k0 + TK < K) {
-      load_as(k0 + TK, ra);
-#pragma unroll
-      for (int j = 0; j < 2; ++j) rb[j] = *(const bf16x8*)(bp[j] + (size_t)((k0 + TK) >> 5) * 512);
+  };
+  if constexpr (DEPTH == 3) {
+    for (int q = 0; q < NST; q += 3) {
+      body(q, s0, s1);
+      body(q + 1, s1, s2);
+      body(q + 2, s2, s0);
     }
-#pragma unroll
-    for (int kk = 0; kk < TK; kk += 32) {
-      bf16x8 bfr[2];
-#pragma unroll
-      for (int j = 0; j < 2; ++j) bfr[j] = *(const bf16x8*)&Bs[wn * 32 + j * 16 + r][kk + g * 8];
-#pragma unroll
-      for (int p = 0; p < (TWO ? 2 : 1); ++p) {
-        bf16x8 af[2];
-#pragma unroll
-        for (int i = 0; i < 2; ++i) af[i] = *(const bf16x8*)&As[p][wm * 32 + i * 16 + r][kk + g * 8];
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-          for (int j = 0; j < 2; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-      }
+  } else {
+    for (int q = 0; q < NST; q += 2) {
+      body(q, s0, s1);
+      body(q + 1, s1, s0);
     }
-    __syncthreads();
   }
   if (NORM) {
-    if constexpr (TWO) {
-      // row 16 j + r collects its 16 contributors (tid / 16) in a fixed order
+    // row rb*16 + (lane & 15) collects its 8 contributors (lane >> 4, half) in a fixed order
 #pragma unroll
-      for (int j = 0; j < SLOTS; ++j) ss_part[arow[j]][tid >> 4] = ss[j];
-      __syncthreads();
-      if (tid < TB) {
-        float s = 0.f;
-        for (int i = 0; i < 16; ++i) s += ss_part[tid][i];
-        rstd_s[tid] = 1.0f / sqrtf(s / (float)K + ga.eps);
-      }
-    } else {
-      // the 8 threads loading one A row are consecutive lanes
+    for (int j = 0; j < AS; ++j) ss_part[a_rb[j] * 16 + (a_lane[j] & 15)][(a_lane[j] >> 4) * 2 + a_h[j]] = ss[j];
+    __syncthreads();
+    if (tid < BM) {
+      float s = 0.f;
 #pragma unroll
-      for (int j = 0; j < SLOTS; ++j) {
-        float s = ss[j];
-        s += __shfl_xor(s, 1, 64);
-        s += __shfl_xor(s, 2, 64);
-        s += __shfl_xor(s, 4, 64);
-        if ((tid & 7) == 0) rstd_s[arow[j]] = 1.0f / sqrtf(s / (float)K + ga.eps);
-      }
+      for (int i = 0; i < 8; ++i) s += ss_part[tid][i];
+      rstd_s[tid] = 1.0f / sqrtf(s / (float)K + ga.eps);
     }
     __syncthreads();
   }
-  unsigned long long best[2][4] = {{0ull, 0ull, 0ull, 0ull}, {0ull, 0ull, 0ull, 0ull}};
+  unsigned long long best[TM][4];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int lr0 = wm * 32 + i * 16 + g * 4;
+    for (int e = 0; e < 4; ++e) best[i][e] = 0ull;
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int lr0 = (wm * TM + i) * 16 + g * 4;
       float v[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) v[e] = NORM ? acc[i][j][e] * rstd_s[lr0 + e] : acc[i][j][e];
-      tile_epilogue<bf16, KIND>(ga, m0 + lr0, n0 + wn * 32 + j * 16 + r, v, r, best[i]);
+      tile_epilogue<bf16, KIND>(ga, m0 + lr0, n0 + (wn * TN + j) * 16 + r, v, r, best[i]);
     }
   if (KIND == EPI_ARGMAX && r == 0) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int row = m0 + wm * 32 + i * 16 + g * 4 + e;
+        const int row = m0 + (wm * TM + i) * 16 + g * 4 + e;
         if (row < M && best[i][e]) atomicMax(&ga.e.keys[row], best[i][e]);
       }
   }
@@ -628,8 +664,30 @@ static hipError_t launch_kind(int dt, const GemmArgs& ga, hipStream_t st) {
     }
     return hipGetLastError();
   }
-  const int tiles = ((M + TB - 1) / TB) * ((N + TB - 1) / TB);
-  hipLaunchKernelGGL((gemm_tiled_bf16<TA, NORM, KIND>), dim3(tiles), dim3(256), 0, st, ga);
+  // the largest workgroup tile that still gives every CU work
+  auto wgs = [&](int bm, int bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
+  const int tile = gemm_tile_knob();
+#define MFMA_LAUNCH(WGM, WGN, TM, TN, KSUB, DEPTH)                                             \
+  hipLaunchKernelGGL((gemm_mfma_bf16<TA, WGM, WGN, TM, TN, KSUB, DEPTH, NORM, KIND>),         \
+                     dim3(wgs(16 * TM * WGM, 16 * TN * WGN)), dim3(64 * WGM * WGN), 0, st, ga)
+  // (8-wave tiles need float32 A: row-major bf16 A rows do not split over 512 threads; a
+  // stage of KSUB k-steps needs K % (32 KSUB) == 0, else one k-step per stage)
+  const int ks = ga.K >> 5;
+  const bool f = AIsFloat<TA>::value;
+  switch ((f || tile < 4) && ks % 4 == 0 ? tile : 0) {
+    case 1: MFMA_LAUNCH(2, 2, 2, 2, 2, 3); break;   //  64 x  64, 4 waves, BK  64
+    case 2: MFMA_LAUNCH(2, 2, 2, 2, 4, 2); break;   //  64 x  64, 4 waves, BK 128
+    case 3: MFMA_LAUNCH(2, 2, 2, 4, 2, 3); break;   //  64 x 128, 4 waves, BK  64
+    case 4: if constexpr (AIsFloat<TA>::value) MFMA_LAUNCH(2, 4, 2, 4, 2, 2); break;  //  64 x 256, 8 waves
+    case 5: if constexpr (AIsFloat<TA>::value && KIND != EPI_ARGMAX) MFMA_LAUNCH(2, 4, 4, 4, 2, 2); break;  // 128 x 256, 8 waves
+    case 6: if constexpr (AIsFloat<TA>::value) MFMA_LAUNCH(2, 2, 4, 4, 2, 2); break;  // 128 x 128, 4 waves
+    case 7: if constexpr (AIsFloat<TA>::value) MFMA_LAUNCH(2, 4, 2, 2, 4, 2); break;  //  64 x 128, 8 waves
+    default:
+      if (ks % 2) MFMA_LAUNCH(2, 2, 2, 2, 1, 3);
+      else if (wgs(64, 128) >= num_cus()) MFMA_LAUNCH(2, 2, 2, 4, 2, 3);
+      else MFMA_LAUNCH(2, 2, 2, 2, 2, 3);
+  }
+#undef MFMA_LAUNCH
   return hipGetLastError();
 }
 
