@@ -35,9 +35,10 @@ def log(msg):
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "gemv_gate_up.qwen3_8b_b1_ctx4k.pmc_traffic.txt")
 
 
-def measured_traffic():
-    """HBM bytes per launch of the roofline kernel from the committed FETCH_SIZE/WRITE_SIZE
-    summary, or None when the kernel's sources have changed since the counters were taken."""
+def measured_profile():
+    """(HBM bytes per launch, rocprofv3 kernel-trace average duration in us) of the roofline
+    kernel from the committed FETCH_SIZE/WRITE_SIZE summary, or (None, None) when the
+    kernel's sources have changed since the counters were taken."""
     import hashlib
     try:
         fields = {}
@@ -50,10 +51,11 @@ def measured_traffic():
             with open(os.path.join(ROOT, src), "rb") as f:
                 h.update(f.read())
         if h.hexdigest() != fields["kernel_sources_sha256"]:
-            return None
-        return int(fields["traffic_bytes_per_launch"])
-    except (OSError, KeyError, ValueError):
-        return None
+            return None, None
+        trace = fields.get("kernel-trace average duration (same command without counters)", "")
+        return int(fields["traffic_bytes_per_launch"]), (float(trace.split()[0]) if trace else None)
+    except (OSError, KeyError, ValueError, IndexError):
+        return None, None
 
 
 def main():
@@ -72,8 +74,8 @@ def main():
                          "(calibrates HBM byte counters of profiler runs)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: the drafter step is data-parallel over sequences "
-              "and this build runs no collectives (see DESIGN.md for how it would shard).",
+        print("bench.py measures one GPU only: the drafter step is data-parallel over sequences, "
+              "each GPU serving its own sequences with its own cache, and no collectives are run.",
               file=sys.stderr)
         sys.exit(2)
 
@@ -205,6 +207,7 @@ def main():
                                      + D.hidden * D.n_q_heads * D.head_dim + 3 * D.ffn * D.hidden) * 2
                        + D.vocab * D.hidden * 2 + D.n_layers * n * D.n_kv_heads * D.head_dim * 2 * 2)
 
+    traffic, prof_us = measured_profile()
     out = {
         "metric": METRIC,
         "value": round(draft_tok_s, 1),
@@ -233,9 +236,12 @@ def main():
         "draft_block_hbm_frac": round(hbm_bytes_draft / (us_draft * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
         "roofline": {"kernel": "gemm_gemv_bf16 (gate/up projection + SwiGLU, M=16)", "bound": "hbm",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "bytes_per_launch": int(avg_bytes), "avg_launch_us": round(avg_us, 2),
-                     "launches": len(gu_ms)},
+                     "launches": len(gu_ms),
+                     # the rocprofv3 kernel-trace average of the committed profile (kernel only;
+                     # the event pair above also holds the dispatch of the kernel, a few us)
+                     "profile_avg_kernel_us": prof_us},
         "kernels": breakdown,
     }
     if not args.no_context_sweep:

@@ -162,14 +162,19 @@ struct TimingState {
 };
 TimingState g_timing;
 
+// event pair of the next launch of `kernel` when that class is armed, else -1
+int timing_slot(int kernel) {
+  if (g_timing.kernel == kernel && g_timing.count < g_timing.capacity) return g_timing.count++;
+  return -1;
+}
+// events recorded around the launches of one kernel class; created without the
+// system-scope fence (hipEventDisableSystemFence), so that recording them writes back and
+// invalidates no caches and the pair brackets the kernels with the least added time
 struct Timed {
   hipStream_t st;
-  int slot = -1;
-  Timed(int kernel, hipStream_t s) : st(s) {
-    if (g_timing.kernel == kernel && g_timing.count < g_timing.capacity) {
-      slot = g_timing.count++;
-      hipEventRecord(g_timing.ev[2 * slot], st);
-    }
+  int slot;
+  Timed(int kernel, hipStream_t s) : st(s), slot(timing_slot(kernel)) {
+    if (slot >= 0) hipEventRecord(g_timing.ev[2 * slot], st);
   }
   ~Timed() {
     if (slot >= 0) hipEventRecord(g_timing.ev[2 * slot + 1], st);
@@ -502,7 +507,7 @@ int dflash_timing_arm(int32_t kernel, int32_t capacity) {
   for (hipEvent_t e : g_timing.ev) hipEventDestroy(e);
   g_timing.ev.assign(2 * (size_t)capacity, nullptr);
   for (auto& e : g_timing.ev)
-    if (hipEventCreate(&e) != hipSuccess) return DFLASH_E_HIP;
+    if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return DFLASH_E_HIP;
   g_timing.kernel = kernel;
   g_timing.capacity = capacity;
   g_timing.count = 0;

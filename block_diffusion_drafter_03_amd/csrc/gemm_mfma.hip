@@ -1,0 +1,272 @@
+// Tiled MFMA GEMM for M > 16 rows (batched drafter blocks, verification of a batch, long
+// injections): acc[m][n] = sum_k A[m][k] W[n][k] with optional A-side RMSNorm and a fused
+// epilogue (epilogue.h).  Operand layouts as in the GEMV: W (bf16) in B-fragment order,
+// float32 activations in A-fragment order, caller-supplied bf16 rows (the tapped features
+// of the fusion GEMM) row-major.
+#include "gemm_common.h"
+
+namespace dflash {
+
+// ---------------------------------------------------------------------------------------
+// M > 16: WGM x WGN waves, each wave TM x TN MFMA tiles (16 x 16), so a workgroup covers
+// (16 TM WGM) x (16 TN WGN) outputs.  An LDS stage holds KSUB MFMA k-steps (BK = 32 KSUB),
+// double-buffered; DEPTH stages of global loads are in flight in registers while one is
+// computed (the loads are unconditional, the stage index clamped, so the compiler counts
+// them and never drains the ring).  LDS holds the operands in fragment order - A as (hi,
+// lo) bf16 pairs split from the float32 activations on the way in, W as it is stored - so
+// every MFMA operand read is one contiguous, conflict-free 1 KB per wave.  Grid: tiles
+// M-fastest, remapped so the M tiles of one W column block run on one XCD (one L2).
+template <typename TA, int WGM, int WGN, int TM, int TN, int KSUB, int DEPTH, bool NORM, int KIND>
+__global__ __launch_bounds__(64 * WGM * WGN) void gemm_mfma_bf16(GemmArgs ga) {
+  constexpr bool TWO = AIsFloat<TA>::value;
+  constexpr int NT_ = 64 * WGM * WGN;             // threads
+  constexpr int BM = 16 * TM * WGM, BN = 16 * TN * WGN;   // workgroup tile
+  constexpr int RB = BM / 16, NB = BN / 16;       // 16-row A blocks, 16-column W tiles
+  constexpr int NP = TWO ? 2 : 1;                 // A planes in LDS: hi (, lo)
+  // staging slots per thread and k-step: A float32: RB x 2 halves x 64 lanes float4;
+  // A bf16 (row-major rows): RB x 64 lanes x 16 B; W: NB x 64 lanes x 16 B
+  constexpr int AS = TWO ? RB * 2 * 64 / NT_ : RB * 64 / NT_;
+  constexpr int WS = NB * 64 / NT_;
+  static_assert(AS >= 1 && WS >= 1 && AS * NT_ == (TWO ? RB * 128 : RB * 64) && WS * NT_ == NB * 64,
+                "tile does not split evenly over the threads");
+  static_assert(DEPTH == 2 || DEPTH == 3, "ring depth");
+  __shared__ __attribute__((aligned(16))) bf16x8 As[2][NP][KSUB][RB][64];
+  __shared__ __attribute__((aligned(16))) bf16x8 Ws[2][KSUB][NB][64];
+  __shared__ float ss_part[NORM ? BM : 1][NORM ? 9 : 1];
+  __shared__ float rstd_s[NORM ? BM : 1];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int r = lane & 15, g = lane >> 4;
+  const int wm = w / WGN, wn = w % WGN;
+  const int M = ga.M, N = ga.N, K = ga.K, KS = K >> 5;
+  const int NST = KS / KSUB;                      // stages (K % (32 KSUB) == 0)
+  const int MB = (M + 15) >> 4, NT = (N + 15) >> 4;
+  const int mt_n = (M + BM - 1) / BM, nt_n = (N + BN - 1) / BN;
+  const int T = mt_n * nt_n;
+  int t = blockIdx.x;
+  if ((T & 7) == 0) t = (blockIdx.x & 7) * (T >> 3) + (blockIdx.x >> 3);
+  const int m0 = (t % mt_n) * BM, n0 = (t / mt_n) * BN;
+
+  // ---- staging slots ----
+  const TA* ap[AS];
+  int a_rb[AS], a_lane[AS], a_h[AS];
+#pragma unroll
+  for (int j = 0; j < AS; ++j) {
+    const int q = tid + NT_ * j;
+    if constexpr (TWO) {
+      a_rb[j] = q >> 7;
+      a_h[j] = (q >> 6) & 1;
+      a_lane[j] = q & 63;
+      const int mb = min((m0 >> 4) + a_rb[j], MB - 1);
+      ap[j] = (const TA*)ga.A + ((size_t)mb * KS * 2 + a_h[j]) * 256 + a_lane[j] * 4;
+    } else {
+      a_rb[j] = q >> 6;
+      a_h[j] = 0;
+      a_lane[j] = q & 63;
+      const int row = min(m0 + a_rb[j] * 16 + (a_lane[j] & 15), M - 1);
+      ap[j] = (const TA*)ga.A + (size_t)row * ga.lda + (a_lane[j] >> 4) * 8;
+    }
+  }
+  const bf16* wp[WS];
+  int w_nt[WS], w_lane[WS];
+#pragma unroll
+  for (int j = 0; j < WS; ++j) {
+    const int q = tid + NT_ * j;
+    w_nt[j] = q >> 6;
+    w_lane[j] = q & 63;
+    wp[j] = wblock(ga.B, min((n0 >> 4) + w_nt[j], NT - 1), 0, KS) + w_lane[j] * 8;
+  }
+  const bf16* gk = NORM ? (const bf16*)ga.norm_g : nullptr;
+  float ss[AS];
+#pragma unroll
+  for (int j = 0; j < AS; ++j) ss[j] = 0.f;
+
+  struct Stage {
+    float ra[KSUB][AS][TWO ? 4 : 8];
+    bf16x8 rw[KSUB][WS];
+  };
+  Stage s0, s1, s2;
+  auto gload = [&](Stage& st, int stage) {
+#pragma unroll
+    for (int u = 0; u < KSUB; ++u) {
+      const int ks = stage * KSUB + u;
+#pragma unroll
+      for (int j = 0; j < AS; ++j) {
+        if constexpr (TWO) {
+          const float4 x = *(const float4*)(ap[j] + (size_t)ks * 512);
+          st.ra[u][j][0] = x.x; st.ra[u][j][1] = x.y; st.ra[u][j][2] = x.z; st.ra[u][j][3] = x.w;
+        } else {
+          load8(ap[j] + (size_t)ks * 32, st.ra[u][j]);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < WS; ++j) st.rw[u][j] = *(const bf16x8*)(wp[j] + (size_t)ks * 512);
+    }
+  };
+  // staged stage -> LDS buffer `buf` (RMSNorm statistics and gain on the way)
+  auto lstore = [&](Stage& st, int buf, int stage) {
+#pragma unroll
+    for (int u = 0; u < KSUB; ++u) {
+      const int ks = stage * KSUB + u;
+#pragma unroll
+      for (int j = 0; j < AS; ++j) {
+        if constexpr (TWO) {
+          float v[8];
+          const int k0 = ks * 32 + 8 * (a_lane[j] >> 4) + 4 * a_h[j];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float x = st.ra[u][j][e];
+            if (NORM) {
+              ss[j] += x * x;
+              x *= (float)gk[k0 + e];
+            }
+            v[e] = x;
+            v[4 + e] = 0.f;
+          }
+          bf16x8 hi, lo;
+          split8(v, hi, lo);
+          bf16x4* dh = (bf16x4*)&As[buf][0][u][a_rb[j]][a_lane[j]] + a_h[j];
+          bf16x4* dl = (bf16x4*)&As[buf][NP - 1][u][a_rb[j]][a_lane[j]] + a_h[j];
+          *dh = bf16x4{hi[0], hi[1], hi[2], hi[3]};
+          *dl = bf16x4{lo[0], lo[1], lo[2], lo[3]};
+        } else {
+          bf16x8 hi, lo;
+          split8(st.ra[u][j], hi, lo);
+          As[buf][0][u][a_rb[j]][a_lane[j]] = hi;
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < WS; ++j) Ws[buf][u][w_nt[j]][w_lane[j]] = st.rw[u][j];
+    }
+  };
+
+  f32x4 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < KSUB; ++u) {
+      bf16x8 wf[TN];
+#pragma unroll
+      for (int j = 0; j < TN; ++j) wf[j] = Ws[buf][u][wn * TN + j][lane];
+#pragma unroll
+      for (int p = 0; p < NP; ++p) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+          const bf16x8 af = As[buf][p][u][wm * TM + i][lane];
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, wf[j], acc[i][j], 0, 0, 0);
+        }
+      }
+    }
+  };
+  // ring: stage q is computed from LDS buffer q % 2 while the next DEPTH stages are in
+  // flight; then stage q+1 moves to the other buffer.  Past the last stage the loads still
+  // run (clamped, harmless) so that every slot issues the same instructions.
+  const int last = NST - 1;
+  gload(s0, 0);
+  gload(s1, min(1, last));
+  if constexpr (DEPTH == 3) gload(s2, min(2, last));
+  lstore(s0, 0, 0);
+  __syncthreads();
+  auto body = [&](int q, Stage& ld, Stage& nx) {
+    gload(ld, min(q + DEPTH, last));
+    if (q < NST) compute(q & 1);
+    if (q + 1 < NST) lstore(nx, (q + 1) & 1, q + 1);
+    __syncthreads();
+  };
+  if constexpr (DEPTH == 3) {
+    for (int q = 0; q < NST; q += 3) {
+      body(q, s0, s1);
+      body(q + 1, s1, s2);
+      body(q + 2, s2, s0);
+    }
+  } else {
+    for (int q = 0; q < NST; q += 2) {
+      body(q, s0, s1);
+      body(q + 1, s1, s0);
+    }
+  }
+  if (NORM) {
+    // row rb*16 + (lane & 15) collects its 8 contributors (lane >> 4, half) in a fixed order
+#pragma unroll
+    for (int j = 0; j < AS; ++j) ss_part[a_rb[j] * 16 + (a_lane[j] & 15)][(a_lane[j] >> 4) * 2 + a_h[j]] = ss[j];
+    __syncthreads();
+    if (tid < BM) {
+      float s = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) s += ss_part[tid][i];
+      rstd_s[tid] = 1.0f / sqrtf(s / (float)K + ga.eps);
+    }
+    __syncthreads();
+  }
+  unsigned long long best[TM][4];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) best[i][e] = 0ull;
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int lr0 = (wm * TM + i) * 16 + g * 4;
+      float v[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = NORM ? acc[i][j][e] * rstd_s[lr0 + e] : acc[i][j][e];
+      tile_epilogue<bf16, KIND>(ga, m0 + lr0, n0 + (wn * TN + j) * 16 + r, v, r, best[i]);
+    }
+  if (KIND == EPI_ARGMAX && r == 0) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = m0 + (wm * TM + i) * 16 + g * 4 + e;
+        if (row < M && best[i][e]) atomicMax(&ga.e.keys[row], best[i][e]);
+      }
+  }
+}
+
+// DFLASH_GEMM_TILE forces the workgroup tile and K staging (benchmark sweeps; see below)
+static int gemm_tile_knob() {
+  static const int v = env_knob("DFLASH_GEMM_TILE", 0);
+  return v;
+}
+
+struct MfmaLaunch {
+  template <typename TA, bool NORM, int KIND>
+  static hipError_t run(const GemmArgs& ga, hipStream_t st) {
+    const int M = ga.M, N = ga.N;
+    // the largest workgroup tile that still gives every CU work
+    auto wgs = [&](int bm, int bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
+    const int tile = gemm_tile_knob();
+#define MFMA_LAUNCH(WGM, WGN, TM, TN, KSUB, DEPTH)                                             \
+  return launch1(gemm_mfma_bf16<TA, WGM, WGN, TM, TN, KSUB, DEPTH, NORM, KIND>,               \
+                 dim3(wgs(16 * TM * WGM, 16 * TN * WGN)), dim3(64 * WGM * WGN), st, ga)
+    // (8-wave tiles need float32 A: row-major bf16 A rows do not split over 512 threads; a
+    // stage of KSUB k-steps needs K % (32 KSUB) == 0, else one k-step per stage)
+    const int ks = ga.K >> 5;
+    const bool f = AIsFloat<TA>::value;
+    switch ((f || tile < 4) && ks % 4 == 0 ? tile : 0) {
+      case 1: MFMA_LAUNCH(2, 2, 2, 2, 2, 3); break;   //  64 x  64, 4 waves, BK  64
+      case 2: MFMA_LAUNCH(2, 2, 2, 2, 4, 2); break;   //  64 x  64, 4 waves, BK 128
+      case 3: MFMA_LAUNCH(2, 2, 2, 4, 2, 3); break;   //  64 x 128, 4 waves, BK  64
+      case 4: if constexpr (AIsFloat<TA>::value) MFMA_LAUNCH(2, 4, 2, 4, 2, 2); break;  //  64 x 256, 8 waves
+      case 5: if constexpr (AIsFloat<TA>::value && KIND != EPI_ARGMAX) MFMA_LAUNCH(2, 4, 4, 4, 2, 2); break;  // 128 x 256, 8 waves
+      case 6: if constexpr (AIsFloat<TA>::value) MFMA_LAUNCH(2, 2, 4, 4, 2, 2); break;  // 128 x 128, 4 waves
+      case 7: if constexpr (AIsFloat<TA>::value) MFMA_LAUNCH(2, 4, 2, 2, 4, 2); break;  //  64 x 128, 8 waves
+      default:
+        if (ks % 2) MFMA_LAUNCH(2, 2, 2, 2, 1, 3);
+        else if (wgs(64, 128) >= num_cus()) MFMA_LAUNCH(2, 2, 2, 4, 2, 3);
+        else MFMA_LAUNCH(2, 2, 2, 2, 2, 3);
+    }
+#undef MFMA_LAUNCH
+    return hipErrorInvalidValue;
+  }
+};
+
+// bf16 models, K a multiple of 32
+hipError_t launch_gemm_mfma(const GemmArgs& ga, hipStream_t st) { return dispatch_gemm<MfmaLaunch>(ga, st); }
+
+}  // namespace dflash

@@ -1,0 +1,221 @@
+// Weight-streaming GEMM for M <= 16 rows (one drafter block of one sequence, or a short
+// injection): acc[m][n] = sum_k A[m][k] W[n][k] with optional A-side RMSNorm and a fused
+// epilogue (epilogue.h).  W (bf16) is in B-fragment order and the float32 activations in
+// A-fragment order (common.h), so every operand load of a wave is one contiguous 1 KB
+// burst; activations enter the MFMAs as compensated (hi, lo) bf16 pairs.
+#include "gemm_common.h"
+
+namespace dflash {
+
+// M <= 16: NW waves split K, one 32-wide step per MFMA (pair).
+//  * ASTAT (many tiles, K <= 4096): one workgroup per CU walks the tiles; each wave keeps
+//    its K-slice of the A rows for all of them, already multiplied by the RMSNorm gain and
+//    split into (hi, lo) (rstd is applied in the epilogue): hi in registers, lo in LDS
+//    (128 KB: the workgroup owns the CU), so the vector memory path carries only W: a wave
+//    issues all of its W loads of a tile at once (CH steps, 1 KB each) and the next tile's
+//    loads go out right after the MFMAs, in flight across the reduction.
+//  * streamed (few tiles, or K > 4096): A and W are loaded together in chunks of CHS
+//    steps; no LDS for A, so several workgroups share a CU and every tile is in flight.
+// 8 waves of 512 threads leave each wave 256 registers, so the stationary A, a full tile
+// of W in flight and the epilogue never spill.
+#define GEMV_MAX_TILES 8   // tiles per workgroup whose epilogue is deferred (non-argmax kinds)
+
+template <typename TA, int NW, bool NORM, bool ASTAT, int KIND>
+__global__ __launch_bounds__(NW * 64) void gemm_gemv_bf16(GemmArgs ga) {
+  constexpr bool TWO = AIsFloat<TA>::value;
+  constexpr int CH = 128 / NW;       // stationary steps per wave (K <= 4096)
+  constexpr int CHS = 8;             // streamed chunk
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int r = lane & 15, g = lane >> 4;
+  const int M = ga.M, N = ga.N, K = ga.K;
+  const int KS = K >> 5;
+  const int spw = KS / NW;                       // K % (32 NW) == 0
+  const int ks0 = w * spw;
+  const int n_tiles = (N + 15) >> 4;
+  __shared__ f32x4 red[NW][64];
+  __shared__ f32x4 done[GEMV_MAX_TILES][64];
+  __shared__ float ss_red[NW][16];
+  __shared__ float rstd[16];
+  __shared__ bf16x8 alo[ASTAT && TWO ? NW : 1][ASTAT && TWO ? CH : 1][64];
+  // running argmax keys of wave 0's lanes (kept out of the main loop's registers)
+  __shared__ unsigned long long bsh[KIND == EPI_ARGMAX ? 4 : 1][64];
+  const bf16* gk = NORM ? (const bf16*)ga.norm_g + g * 8 : nullptr;
+  // this lane's 8 A values of step ks (row r)
+  auto load_a = [&](int ks, float v[8]) {
+    if constexpr (TWO)
+      afrag_load8((const float*)ga.A, 0, ks, KS, lane, v);
+    else
+      load8((const bf16*)ga.A + (size_t)min(r, M - 1) * ga.lda + (size_t)ks * 32 + g * 8, v);
+  };
+  int nbuf = 0;
+  bool first = true;
+  if (KIND == EPI_ARGMAX && w == 0)
+#pragma unroll
+    for (int i = 0; i < (KIND == EPI_ARGMAX ? 4 : 1); ++i) bsh[i][lane] = 0ull;
+
+  bf16x8 ah[ASTAT ? CH : 1];
+  // W loads of this workgroup's first tile go out before the A prologue (independent)
+  bf16x8 wn[ASTAT ? CH : 1];
+  auto load_w = [&](int t) {
+#pragma unroll
+    for (int s = 0; s < CH; ++s)
+      if (s < spw) wn[s] = *(const bf16x8*)(wblock(ga.B, t, ks0 + s, KS) + lane * 8);
+  };
+  if constexpr (ASTAT) {
+    if (blockIdx.x < n_tiles) load_w(blockIdx.x);
+    float ss = 0.f;
+#pragma unroll
+    for (int s = 0; s < CH; ++s) {
+      if (s < spw) {
+        float v[8];
+        load_a(ks0 + s, v);
+        bf16x8 lo;
+        a_operand<NORM, true>(v, gk + (size_t)(ks0 + s) * 32, &ss, ah[s], lo);
+        if constexpr (TWO) alo[w][s][lane] = lo;
+      }
+    }
+    if (NORM) {
+      ss += __shfl_xor(ss, 16, 64);
+      ss += __shfl_xor(ss, 32, 64);
+      if (g == 0) ss_red[w][r] = ss;
+      __syncthreads();
+      if (threadIdx.x < 16) {
+        float s = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < NW; ++ww) s += ss_red[ww][threadIdx.x];
+        rstd[threadIdx.x] = 1.0f / sqrtf(s / (float)K + ga.eps);
+      }
+      __syncthreads();
+    }
+  }
+
+  for (int t = blockIdx.x; t < n_tiles; t += gridDim.x) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc2 = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (ASTAT) {
+#pragma unroll
+      for (int s = 0; s < CH; ++s)
+        if (s < spw) {
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[s], wn[s], acc, 0, 0, 0);
+          if constexpr (TWO) acc2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo[w][s][lane], wn[s], acc2, 0, 0, 0);
+        }
+      // the next tile's W loads are in flight across the barrier and the reduction
+      if (t + gridDim.x < n_tiles) load_w(t + gridDim.x);
+    } else {
+      float ss = 0.f;
+      for (int c0 = 0; c0 < spw; c0 += CHS) {
+        bf16x8 wf[CHS];
+        float av[CHS][8];
+#pragma unroll
+        for (int s = 0; s < CHS; ++s) {
+          const int k = ks0 + min(c0 + s, spw - 1);
+          wf[s] = *(const bf16x8*)(wblock(ga.B, t, k, KS) + lane * 8);
+          load_a(k, av[s]);
+        }
+#pragma unroll
+        for (int s = 0; s < CHS; ++s)
+          if (c0 + s < spw) {
+            bf16x8 hi, lo;
+            if (first)
+              a_operand<NORM, true>(av[s], gk + (size_t)(ks0 + c0 + s) * 32, &ss, hi, lo);
+            else
+              a_operand<NORM, false>(av[s], gk + (size_t)(ks0 + c0 + s) * 32, &ss, hi, lo);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, wf[s], acc, 0, 0, 0);
+            if constexpr (TWO) acc2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, wf[s], acc2, 0, 0, 0);
+          }
+      }
+      if (NORM && first) {
+        ss += __shfl_xor(ss, 16, 64);
+        ss += __shfl_xor(ss, 32, 64);
+        if (g == 0) ss_red[w][r] = ss;
+      }
+    }
+    red[w][lane] = acc + acc2;
+    __syncthreads();
+    if (NORM && !ASTAT && first) {
+      if (threadIdx.x < 16) {
+        float s = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < NW; ++ww) s += ss_red[ww][threadIdx.x];
+        rstd[threadIdx.x] = 1.0f / sqrtf(s / (float)K + ga.eps);
+      }
+      __syncthreads();
+    }
+    first = false;
+    if (w == 0) {
+      f32x4 s = red[0][lane];
+#pragma unroll
+      for (int ww = 1; ww < NW; ++ww) s += red[ww][lane];
+      if constexpr (KIND == EPI_ARGMAX) {
+        float v[4];
+        unsigned long long best[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          v[i] = NORM ? s[i] * rstd[g * 4 + i] : s[i];
+          best[i] = bsh[i][lane];
+        }
+        tile_epilogue<bf16, KIND>(ga, g * 4, t * 16 + r, v, r, best);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) bsh[i][lane] = best[i];
+      } else {
+        done[nbuf][lane] = s;   // epilogue deferred until the A registers are dead
+      }
+    }
+    ++nbuf;
+    __syncthreads();
+  }
+  if constexpr (KIND != EPI_ARGMAX) {
+    // every wave takes buffered tiles: the epilogues run in parallel, off the main loop's
+    // register budget
+    unsigned long long best[4];
+    for (int i = w; i < nbuf; i += NW) {
+      const f32x4 s = done[i][lane];
+      float v[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = NORM ? s[e] * rstd[g * 4 + e] : s[e];
+      tile_epilogue<bf16, KIND>(ga, g * 4, (blockIdx.x + i * gridDim.x) * 16 + r, v, r, best);
+    }
+  }
+  if (KIND == EPI_ARGMAX && w == 0 && r == 0) {
+#pragma unroll
+    for (int i = 0; i < (KIND == EPI_ARGMAX ? 4 : 1); ++i) {
+      const int row = g * 4 + i;
+      const unsigned long long k = bsh[i][lane];
+      if (row < M && k) atomicMax(&ga.e.keys[row], k);
+    }
+  }
+}
+
+// Tuning knobs (benchmark sweeps): DFLASH_GEMV_STREAM_TILES sets the largest tile count
+// that uses the streamed-A form (default: one tile per CU).
+static int gemv_stream_tiles() {
+  static const int v = env_knob("DFLASH_GEMV_STREAM_TILES", num_cus());
+  return v;
+}
+
+struct GemvLaunch {
+  template <typename TA, bool NORM, int KIND>
+  static hipError_t run(const GemmArgs& ga, hipStream_t st) {
+    const int n_tiles = (ga.N + 15) / 16;
+    // few tiles (up to gemv_stream_tiles(), default one per CU) or K > 4096: one workgroup
+    // per tile, A streamed with W, so that several workgroups may share a CU and every tile
+    // is in flight at once; otherwise one workgroup per CU with the A slice stationary,
+    // walking the tiles (the deferred epilogue buffer bounds the tiles per workgroup)
+    if (n_tiles <= gemv_stream_tiles() || ga.K > 4096) {
+      int grid = n_tiles;
+      if (grid > 8 * num_cus()) grid = 8 * num_cus();
+      if (KIND != EPI_ARGMAX && grid * GEMV_MAX_TILES < n_tiles)
+        grid = (n_tiles + GEMV_MAX_TILES - 1) / GEMV_MAX_TILES;
+      return launch1(gemm_gemv_bf16<TA, GEMV_NW, NORM, false, KIND>, dim3(grid), dim3(GEMV_NW * 64), st, ga);
+    } else {
+      int grid = n_tiles < num_cus() ? n_tiles : num_cus();
+      if (KIND != EPI_ARGMAX && grid * GEMV_MAX_TILES < n_tiles)
+        grid = (n_tiles + GEMV_MAX_TILES - 1) / GEMV_MAX_TILES;
+      return launch1(gemm_gemv_bf16<TA, GEMV_NW, NORM, true, KIND>, dim3(grid), dim3(GEMV_NW * 64), st, ga);
+    }
+  }
+};
+
+// bf16 models, M <= 16, K a multiple of 32 * GEMV_NW (checked by launch_gemm)
+hipError_t launch_gemv(const GemmArgs& ga, hipStream_t st) { return dispatch_gemm<GemvLaunch>(ga, st); }
+
+}  // namespace dflash

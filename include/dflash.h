@@ -226,7 +226,8 @@ int dflash_kv_commit(dflash_kv* target_kv, dflash_kv* draft_ctx, const int32_t* 
 /*
  * Measurement hook (benchmarks only; not thread-safe).  dflash_timing_arm(kernel, n)
  * makes the library record a HIP event pair on the launching stream around each of the
- * next n launches of one kernel class; dflash_timing_read(ms, n) waits for those events,
+ * next n launches of one kernel class (events created with hipEventDisableSystemFence, so
+ * that recording them flushes no caches); dflash_timing_read(ms, n) waits for those events,
  * writes each launch's duration in milliseconds, disarms, and returns the number of
  * launches recorded (or a negative dflash_status).  Events are host-side HIP objects;
  * no device memory is allocated.
