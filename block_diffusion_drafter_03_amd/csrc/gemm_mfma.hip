@@ -80,8 +80,12 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_mfma_bf16(GemmArgs ga) {
 #pragma unroll
   for (int j = 0; j < AS; ++j) ss[j] = 0.f;
 
+  // a stage's activations, their RMSNorm gains and its weights, loaded together (a gain
+  // loaded only when the stage is copied to LDS would be waited for at once and drain the
+  // load ring)
   struct Stage {
     float ra[KSUB][AS][TWO ? 4 : 8];
+    bf16x4 rg[NORM ? KSUB : 1][NORM ? AS : 1];
     bf16x8 rw[KSUB][WS];
   };
   Stage s0, s1, s2;
@@ -94,6 +98,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_mfma_bf16(GemmArgs ga) {
         if constexpr (TWO) {
           const float4 x = *(const float4*)(ap[j] + (size_t)ks * 512);
           st.ra[u][j][0] = x.x; st.ra[u][j][1] = x.y; st.ra[u][j][2] = x.z; st.ra[u][j][3] = x.w;
+          if constexpr (NORM)
+            st.rg[u][j] = *(const bf16x4*)(gk + ks * 32 + 8 * (a_lane[j] >> 4) + 4 * a_h[j]);
         } else {
           load8(ap[j] + (size_t)ks * 32, st.ra[u][j]);
         }
@@ -111,13 +117,12 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_mfma_bf16(GemmArgs ga) {
       for (int j = 0; j < AS; ++j) {
         if constexpr (TWO) {
           float v[8];
-          const int k0 = ks * 32 + 8 * (a_lane[j] >> 4) + 4 * a_h[j];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             float x = st.ra[u][j][e];
-            if (NORM) {
+            if constexpr (NORM) {
               ss[j] += x * x;
-              x *= (float)gk[k0 + e];
+              x *= (float)st.rg[u][j][e];
             }
             v[e] = x;
             v[4 + e] = 0.f;
@@ -228,7 +233,253 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_mfma_bf16(GemmArgs ga) {
   }
 }
 
-// DFLASH_GEMM_TILE forces the workgroup tile and K staging (benchmark sweeps; see below)
+// ---------------------------------------------------------------------------------------
+// M > 16 with the weights going straight to registers.  4 waves; wave w owns the TN 16-column
+// tiles n0/16 + w TN + j (j < TN) of the workgroup's BN = 64 TN columns for all BM rows, so
+// every weight fragment is loaded from HBM by exactly one wave, into its registers, and used
+// there: no LDS traffic for W.  The BM activation rows are shared by the 4 waves through a
+// double-buffered LDS stage of KSUB k-steps (fragment order; float32 rows split into (hi,
+// lo) bf16 pairs on the way in, RMSNorm statistics gathered there).  Per k-step a wave reads
+// BM/16 A fragments (per plane) from LDS and issues TN MFMAs on each, so LDS reads take
+// 1/TN of the MFMA time.  Weights run three stages ahead in a register ring, the
+// activations one stage ahead.  Grid: tiles M-fastest, remapped so the row tiles of one weight column
+// block run on one XCD (their second weight read hits that XCD's L2).
+template <typename TA, int BM, int TN, int KSUB, bool NORM, int KIND>
+__global__ __launch_bounds__(256) void gemm_wdirect_bf16(GemmArgs ga) {
+  constexpr bool TWO = AIsFloat<TA>::value;
+  constexpr int NT_ = 256;
+  constexpr int RB = BM / 16, BN = 64 * TN;
+  constexpr int NP = TWO ? 2 : 1;
+  // activation staging slots per thread and k-step: float32: RB x 2 halves x 64 lanes of
+  // float4; bf16 (row-major rows): RB x 64 lanes x 16 B
+  constexpr int AS = TWO ? RB * 2 * 64 / NT_ : RB * 64 / NT_;
+  static_assert(AS >= 1 && AS * NT_ == (TWO ? RB * 128 : RB * 64), "row tile does not split over the threads");
+  
+  // epilogue chunk: EPC row blocks of accumulators per wave go through LDS at a time
+  constexpr int EPC = RB * TN * 4 <= 128 ? RB : RB / 2;
+  constexpr int AS_BYTES = 2 * NP * KSUB * RB * 1024, EP_BYTES = 4 * EPC * TN * 1024;
+  __shared__ __attribute__((aligned(16))) char smem[AS_BYTES > EP_BYTES ? AS_BYTES : EP_BYTES];
+  bf16x8 (*As)[NP][KSUB][RB][64] = (bf16x8 (*)[NP][KSUB][RB][64])smem;
+  __shared__ float ss_part[NORM ? BM : 1][NORM ? 9 : 1];
+  __shared__ float rstd_s[NORM ? BM : 1];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int r = lane & 15, g = lane >> 4;
+  const int M = ga.M, N = ga.N, K = ga.K, KS = K >> 5;
+  const int NST = KS / KSUB;                      // K % (32 KSUB) == 0 (checked by the launcher)
+  const int MB = (M + 15) >> 4, NTl = (N + 15) >> 4;
+  const int mt_n = (M + BM - 1) / BM, nt_n = (N + BN - 1) / BN;
+  const int T = mt_n * nt_n;
+  int t = blockIdx.x;
+  if ((T & 7) == 0) t = (blockIdx.x & 7) * (T >> 3) + (blockIdx.x >> 3);
+  const int m0 = (t % mt_n) * BM, n0 = (t / mt_n) * BN;
+
+  // ---- activation staging slots ----
+  const TA* ap[AS];
+  int a_rb[AS], a_lane[AS], a_h[AS];
+#pragma unroll
+  for (int j = 0; j < AS; ++j) {
+    const int q = tid + NT_ * j;
+    if constexpr (TWO) {
+      a_rb[j] = q >> 7;
+      a_h[j] = (q >> 6) & 1;
+      a_lane[j] = q & 63;
+      const int mb = min((m0 >> 4) + a_rb[j], MB - 1);
+      ap[j] = (const TA*)ga.A + ((size_t)mb * KS * 2 + a_h[j]) * 256 + a_lane[j] * 4;
+    } else {
+      a_rb[j] = q >> 6;
+      a_h[j] = 0;
+      a_lane[j] = q & 63;
+      const int row = min(m0 + a_rb[j] * 16 + (a_lane[j] & 15), M - 1);
+      ap[j] = (const TA*)ga.A + (size_t)row * ga.lda + (a_lane[j] >> 4) * 8;
+    }
+  }
+  // ---- this wave's weight tiles (clamped: columns past N are computed and discarded) ----
+  const bf16* wp[TN];
+#pragma unroll
+  for (int j = 0; j < TN; ++j)
+    wp[j] = wblock(ga.B, min((n0 >> 4) + w * TN + j, NTl - 1), 0, KS) + lane * 8;
+  const bf16* gk = NORM ? (const bf16*)ga.norm_g : nullptr;
+  float ss[AS];
+#pragma unroll
+  for (int j = 0; j < AS; ++j) ss[j] = 0.f;
+
+  // activations of a stage with their RMSNorm gains, loaded together one body ahead of
+  // their copy to LDS (a load waited for right after it is issued would drain the weight
+  // ring)
+  struct AStage {
+    float ra[KSUB][AS][TWO ? 4 : 8];
+    bf16x4 rg[NORM ? KSUB : 1][NORM ? AS : 1];
+  };
+  auto gload_a = [&](AStage& sa, int stage) {
+    auto& ra = sa.ra;
+    auto& rg = sa.rg;
+#pragma unroll
+    for (int u = 0; u < KSUB; ++u) {
+      const int ks = stage * KSUB + u;
+#pragma unroll
+      for (int j = 0; j < AS; ++j) {
+        if constexpr (TWO) {
+          const float4 x = *(const float4*)(ap[j] + (size_t)ks * 512);
+          ra[u][j][0] = x.x; ra[u][j][1] = x.y; ra[u][j][2] = x.z; ra[u][j][3] = x.w;
+          if constexpr (NORM)
+            rg[u][j] = *(const bf16x4*)(gk + ks * 32 + 8 * (a_lane[j] >> 4) + 4 * a_h[j]);
+        } else {
+          load8(ap[j] + (size_t)ks * 32, ra[u][j]);
+        }
+      }
+    }
+  };
+  // staged activations of `stage` -> LDS buffer `buf` (RMSNorm statistics and gain on the
+  // way; a clamped repeat of the last stage is stored but not counted)
+  auto lstore_a = [&](const AStage& sa, int buf, int stage, bool count) {
+    const auto& ra = sa.ra;
+    const auto& rg = sa.rg;
+#pragma unroll
+    for (int u = 0; u < KSUB; ++u) {
+      const int ks = stage * KSUB + u;
+#pragma unroll
+      for (int j = 0; j < AS; ++j) {
+        if constexpr (TWO) {
+          float v[8];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float x = ra[u][j][e];
+            if constexpr (NORM) {
+              ss[j] += count ? x * x : 0.f;
+              x *= (float)rg[u][j][e];
+            }
+            v[e] = x;
+            v[4 + e] = 0.f;
+          }
+          bf16x8 hi, lo;
+          split8(v, hi, lo);
+          bf16x4* dh = (bf16x4*)&As[buf][0][u][a_rb[j]][a_lane[j]] + a_h[j];
+          bf16x4* dl = (bf16x4*)&As[buf][NP - 1][u][a_rb[j]][a_lane[j]] + a_h[j];
+          *dh = bf16x4{hi[0], hi[1], hi[2], hi[3]};
+          *dl = bf16x4{lo[0], lo[1], lo[2], lo[3]};
+        } else {
+          bf16x8 hi, lo;
+          split8(ra[u][j], hi, lo);
+          As[buf][0][u][a_rb[j]][a_lane[j]] = hi;
+        }
+      }
+    }
+  };
+  typedef bf16x8 WStage[KSUB][TN];
+  auto gload_w = [&](WStage& wr, int stage) {
+#pragma unroll
+    for (int u = 0; u < KSUB; ++u)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        wr[u][j] = *(const bf16x8*)(wp[j] + (size_t)(stage * KSUB + u) * 512);
+  };
+
+  f32x4 acc[RB][TN];
+#pragma unroll
+  for (int i = 0; i < RB; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // the RB fragments of the next (k-step, plane) group are read from LDS while the MFMAs of
+  // the current group issue, so one wave per SIMD does not wait on LDS latency
+  auto compute = [&](int buf, const WStage& wr) {
+    constexpr int NG = KSUB * NP;
+    bf16x8 fa[2][RB];
+#pragma unroll
+    for (int i = 0; i < RB; ++i) fa[0][i] = As[buf][0][0][i][lane];
+#pragma unroll
+    for (int q = 0; q < NG; ++q) {
+      const int u = q / NP;
+      if (q + 1 < NG) {
+#pragma unroll
+        for (int i = 0; i < RB; ++i) fa[(q + 1) & 1][i] = As[buf][(q + 1) % NP][(q + 1) / NP][i][lane];
+      }
+#pragma unroll
+      for (int i = 0; i < RB; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[q & 1][i], wr[u][j], acc[i][j], 0, 0, 0);
+    }
+  };
+
+  // ring: stage q is computed with its weights from ring slot q % 3 and its activations
+  // from LDS buffer q % 2; then the activations of stage q + 1 (loaded one body earlier) go
+  // to the other buffer, and the freed slots reload stage q + 2 (activations) and q + 3
+  // (weights).  Loads past the last stage are clamped to it (L2 hits), so every body issues
+  // the same instructions and the compiler keeps the ring in flight.  (A deeper ring - four
+  // weight stages, two activation stages - measured slower: it leaves the compiler too few
+  // registers to schedule the MFMAs.)
+  const int last = NST - 1;
+  WStage w0, w1, w2;
+  AStage an;
+  gload_w(w0, 0);
+  gload_w(w1, min(1, last));
+  gload_w(w2, min(2, last));
+  gload_a(an, 0);
+  lstore_a(an, 0, 0, true);
+  gload_a(an, min(1, last));
+  __syncthreads();
+  auto body = [&](int q, WStage& wr) {
+    if (q < NST) compute(q & 1, wr);
+    lstore_a(an, (q + 1) & 1, min(q + 1, last), q + 1 < NST);
+    gload_a(an, min(q + 2, last));
+    gload_w(wr, min(q + 3, last));
+    __syncthreads();
+  };
+  for (int q = 0; q < NST; q += 3) {
+    body(q, w0);
+    body(q + 1, w1);
+    body(q + 2, w2);
+  }
+  if (NORM) {
+    // row rb*16 + (lane & 15) collects its 8 contributors (lane >> 4, half) in a fixed order
+#pragma unroll
+    for (int j = 0; j < AS; ++j) ss_part[a_rb[j] * 16 + (a_lane[j] & 15)][(a_lane[j] >> 4) * 2 + a_h[j]] = ss[j];
+    __syncthreads();
+    if (tid < BM) {
+      float s = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) s += ss_part[tid][i];
+      rstd_s[tid] = 1.0f / sqrtf(s / (float)K + ga.eps);
+    }
+    __syncthreads();
+  }
+  // Epilogue: the accumulators of EPC row blocks at a time go to this wave's LDS region and
+  // a runtime loop walks them, so the accumulator array is only ever indexed statically
+  // (the epilogue code is too large to unroll RB x TN times).
+  f32x4* ep = (f32x4*)smem + (size_t)w * EPC * TN * 64;
+#pragma unroll
+  for (int c = 0; c < RB / EPC; ++c) {
+    __syncthreads();   // LDS stage buffers / previous chunk no longer read
+#pragma unroll
+    for (int i = 0; i < EPC; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) ep[(i * TN + j) * 64 + lane] = acc[c * EPC + i][j];
+    __syncthreads();
+#pragma unroll 1
+    for (int i = 0; i < EPC; ++i) {
+      const int lr0 = (c * EPC + i) * 16 + g * 4;
+      unsigned long long best[4] = {0ull, 0ull, 0ull, 0ull};
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const f32x4 a = ep[(i * TN + j) * 64 + lane];
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = NORM ? a[e] * rstd_s[lr0 + e] : a[e];
+        tile_epilogue<bf16, KIND>(ga, m0 + lr0, n0 + (w * TN + j) * 16 + r, v, r, best);
+      }
+      if (KIND == EPI_ARGMAX && r == 0) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int row = m0 + lr0 + e;
+          if (row < M && best[e]) atomicMax(&ga.e.keys[row], best[e]);
+        }
+      }
+    }
+  }
+}
+
+// DFLASH_GEMM_TILE forces a kernel and tile (benchmark sweeps): 1-3 the LDS-staged
+// configurations, 10 / 11 the weight-direct kernel, 0 automatic
 static int gemm_tile_knob() {
   static const int v = env_knob("DFLASH_GEMM_TILE", 0);
   return v;
@@ -238,30 +489,48 @@ struct MfmaLaunch {
   template <typename TA, bool NORM, int KIND>
   static hipError_t run(const GemmArgs& ga, hipStream_t st) {
     const int M = ga.M, N = ga.N;
-    // the largest workgroup tile that still gives every CU work
     auto wgs = [&](int bm, int bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
     const int tile = gemm_tile_knob();
+    const int ks = ga.K >> 5;
+#define WD_LAUNCH(BM, TN)                                                                     \
+  return launch1(gemm_wdirect_bf16<TA, BM, TN, 2, NORM, KIND>, dim3(wgs(BM, 64 * TN)),     \
+                 dim3(256), st, ga)
 #define MFMA_LAUNCH(WGM, WGN, TM, TN, KSUB, DEPTH)                                             \
   return launch1(gemm_mfma_bf16<TA, WGM, WGN, TM, TN, KSUB, DEPTH, NORM, KIND>,               \
                  dim3(wgs(16 * TM * WGM, 16 * TN * WGN)), dim3(64 * WGM * WGN), st, ga)
-    // (8-wave tiles need float32 A: row-major bf16 A rows do not split over 512 threads; a
-    // stage of KSUB k-steps needs K % (32 KSUB) == 0, else one k-step per stage)
-    const int ks = ga.K >> 5;
-    const bool f = AIsFloat<TA>::value;
-    switch ((f || tile < 4) && ks % 4 == 0 ? tile : 0) {
-      case 1: MFMA_LAUNCH(2, 2, 2, 2, 2, 3); break;   //  64 x  64, 4 waves, BK  64
-      case 2: MFMA_LAUNCH(2, 2, 2, 2, 4, 2); break;   //  64 x  64, 4 waves, BK 128
-      case 3: MFMA_LAUNCH(2, 2, 2, 4, 2, 3); break;   //  64 x 128, 4 waves, BK  64
-      case 4: if constexpr (AIsFloat<TA>::value) MFMA_LAUNCH(2, 4, 2, 4, 2, 2); break;  //  64 x 256, 8 waves
-      case 5: if constexpr (AIsFloat<TA>::value && KIND != EPI_ARGMAX) MFMA_LAUNCH(2, 4, 4, 4, 2, 2); break;  // 128 x 256, 8 waves
-      case 6: if constexpr (AIsFloat<TA>::value) MFMA_LAUNCH(2, 2, 4, 4, 2, 2); break;  // 128 x 128, 4 waves
-      case 7: if constexpr (AIsFloat<TA>::value) MFMA_LAUNCH(2, 4, 2, 2, 4, 2); break;  //  64 x 128, 8 waves
+    // Automatic choice (measured on the Qwen3-8B shapes at M = 256): when 64 x 128 tiles give
+    // every CU work (gate/up, LM head, injection K/V), the weight-direct kernel, with 4 weight
+    // tiles per wave once there are two workgroups per CU of them; otherwise (QKV, O, down)
+    // 64 x 64 LDS-staged tiles, which keep the most CUs busy.
+    if (tile == 0 && ks % 4 == 0) {
+      if (wgs(64, 128) >= num_cus()) {
+        if constexpr (AIsFloat<TA>::value) {
+          if (wgs(64, 256) >= 2 * num_cus()) WD_LAUNCH(64, 4);
+          WD_LAUNCH(64, 2);
+        } else {
+          WD_LAUNCH(64, 4);
+        }
+      }
+      MFMA_LAUNCH(2, 2, 2, 2, 2, 3);
+    }
+    // forced choices (sweeps): 10 / 11 weight-direct 64 x 128 / 64 x 256; 1-3 LDS-staged
+    if (ks % 4 == 0) {
+      if constexpr (AIsFloat<TA>::value) {
+        if (tile == 10) WD_LAUNCH(64, 2);
+      }
+      if (tile == 11) WD_LAUNCH(64, 4);
+    }
+    // (a stage of KSUB k-steps needs K % (32 KSUB) == 0, else one k-step per stage)
+    switch (ks % 4 == 0 && tile < 10 ? tile : 0) {
+      case 1: MFMA_LAUNCH(2, 2, 2, 2, 2, 3);   //  64 x  64, BK  64
+      case 2: MFMA_LAUNCH(2, 2, 2, 2, 4, 2);   //  64 x  64, BK 128
+      case 3: MFMA_LAUNCH(2, 2, 2, 4, 2, 3);   //  64 x 128, BK  64
       default:
         if (ks % 2) MFMA_LAUNCH(2, 2, 2, 2, 1, 3);
-        else if (wgs(64, 128) >= num_cus()) MFMA_LAUNCH(2, 2, 2, 4, 2, 3);
-        else MFMA_LAUNCH(2, 2, 2, 2, 2, 3);
+        MFMA_LAUNCH(2, 2, 2, 2, 2, 3);
     }
 #undef MFMA_LAUNCH
+#undef WD_LAUNCH
     return hipErrorInvalidValue;
   }
 };
