@@ -8,7 +8,8 @@
 #include <stdlib.h>
 #include "epilogue.h"
 
-#define GEMV_NW 8   // waves per workgroup of the M <= 16 GEMV (K must be a multiple of 32 GEMV_NW)
+#define GEMV_NW 8    // waves per workgroup of the M <= 16 GEMV (K must be a multiple of 32 GEMV_NW)
+#define GEMV_CH 16   // 32-wide steps per wave of its stationary-A form (K = 32 GEMV_NW GEMV_CH)
 
 namespace dflash {
 
@@ -96,15 +97,14 @@ DF_DEV void tile_epilogue(const GemmArgs& ga, int row0, int col, const float v[4
 template <typename TA> struct AIsFloat { static constexpr bool value = false; };
 template <> struct AIsFloat<float> { static constexpr bool value = true; };
 
-// v (8 raw A values) -> operand pair; with NORM, sum of squares of the raw values is added
-// to *ss and v is multiplied by the gain slice gp[0..7] first.
-template <bool NORM, bool ACC_SS>
-DF_DEV void a_operand(float v[8], const bf16* gp, float* ss, bf16x8& hi, bf16x8& lo) {
+// v (8 raw A values) -> operand pair; with NORM, the sum of squares of the raw values is
+// added to *ss and v is multiplied by the gain slice gv first.
+template <bool NORM>
+DF_DEV void a_operand(float v[8], const bf16x8 gv, float* ss, bf16x8& hi, bf16x8& lo) {
   if (NORM) {
-    const bf16x8 gv = *(const bf16x8*)gp;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      if (ACC_SS) *ss += v[e] * v[e];
+      *ss += v[e] * v[e];
       v[e] *= (float)gv[e];
     }
   }

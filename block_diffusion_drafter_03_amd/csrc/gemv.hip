@@ -23,13 +23,14 @@ namespace dflash {
 template <typename TA, int NW, bool NORM, bool ASTAT, int KIND>
 __global__ __launch_bounds__(NW * 64) void gemm_gemv_bf16(GemmArgs ga) {
   constexpr bool TWO = AIsFloat<TA>::value;
-  constexpr int CH = 128 / NW;       // stationary steps per wave (K <= 4096)
+  constexpr int CH = GEMV_CH;        // stationary steps per wave (K = 32 NW CH = 4096)
   constexpr int CHS = 8;             // streamed chunk
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int r = lane & 15, g = lane >> 4;
   const int M = ga.M, N = ga.N, K = ga.K;
   const int KS = K >> 5;
-  const int spw = KS / NW;                       // K % (32 NW) == 0
+  // steps per wave: K % (32 NW) == 0; the stationary form takes exactly K = 32 NW CH
+  const int spw = ASTAT ? CH : KS / NW;
   const int ks0 = w * spw;
   const int n_tiles = (N + 15) >> 4;
   __shared__ f32x4 red[NW][64];
@@ -54,25 +55,32 @@ __global__ __launch_bounds__(NW * 64) void gemm_gemv_bf16(GemmArgs ga) {
     for (int i = 0; i < (KIND == EPI_ARGMAX ? 4 : 1); ++i) bsh[i][lane] = 0ull;
 
   bf16x8 ah[ASTAT ? CH : 1];
-  // W loads of this workgroup's first tile go out before the A prologue (independent)
-  bf16x8 wn[ASTAT ? CH : 1];
-  auto load_w = [&](int t) {
+  // stationary form: one tile of W per wave in registers, reloaded step by step with the
+  // next tile of the walk right after each step's MFMAs, so that about CH loads stay in
+  // flight at every moment (a whole next tile is in flight across the reduction).  Past
+  // the walk the reload is clamped to its last tile (an L2 hit), keeping every load
+  // unconditional.  The first tile's loads go out before the A prologue (independent).
+  bf16x8 wa[ASTAT ? CH : 1];
+  // every step's load is issued unconditionally, so the compiler can count the loads and
+  // never drains the ring with a full wait
+  auto load_w = [&](bf16x8 (&wn)[ASTAT ? CH : 1], int t) {
 #pragma unroll
-    for (int s = 0; s < CH; ++s)
-      if (s < spw) wn[s] = *(const bf16x8*)(wblock(ga.B, t, ks0 + s, KS) + lane * 8);
+    for (int s = 0; s < CH; ++s) wn[s] = *(const bf16x8*)(wblock(ga.B, t, ks0 + s, KS) + lane * 8);
   };
+  const int G = gridDim.x;
+  const int t_last = blockIdx.x < n_tiles ? blockIdx.x + (n_tiles - 1 - blockIdx.x) / G * G : 0;
   if constexpr (ASTAT) {
-    if (blockIdx.x < n_tiles) load_w(blockIdx.x);
+    if (blockIdx.x < n_tiles) load_w(wa, blockIdx.x);
     float ss = 0.f;
 #pragma unroll
     for (int s = 0; s < CH; ++s) {
-      if (s < spw) {
-        float v[8];
-        load_a(ks0 + s, v);
-        bf16x8 lo;
-        a_operand<NORM, true>(v, gk + (size_t)(ks0 + s) * 32, &ss, ah[s], lo);
-        if constexpr (TWO) alo[w][s][lane] = lo;
-      }
+      const int k = ks0 + s;
+      float v[8];
+      load_a(k, v);
+      const bf16x8 gv = NORM ? *(const bf16x8*)(gk + (size_t)k * 32) : bf16x8{};
+      bf16x8 lo;
+      a_operand<NORM>(v, gv, &ss, ah[s], lo);
+      if constexpr (TWO) alo[w][s][lane] = lo;
     }
     if (NORM) {
       ss += __shfl_xor(ss, 16, 64);
@@ -89,46 +97,8 @@ __global__ __launch_bounds__(NW * 64) void gemm_gemv_bf16(GemmArgs ga) {
     }
   }
 
-  for (int t = blockIdx.x; t < n_tiles; t += gridDim.x) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc2 = {0.f, 0.f, 0.f, 0.f};
-    if constexpr (ASTAT) {
-#pragma unroll
-      for (int s = 0; s < CH; ++s)
-        if (s < spw) {
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[s], wn[s], acc, 0, 0, 0);
-          if constexpr (TWO) acc2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo[w][s][lane], wn[s], acc2, 0, 0, 0);
-        }
-      // the next tile's W loads are in flight across the barrier and the reduction
-      if (t + gridDim.x < n_tiles) load_w(t + gridDim.x);
-    } else {
-      float ss = 0.f;
-      for (int c0 = 0; c0 < spw; c0 += CHS) {
-        bf16x8 wf[CHS];
-        float av[CHS][8];
-#pragma unroll
-        for (int s = 0; s < CHS; ++s) {
-          const int k = ks0 + min(c0 + s, spw - 1);
-          wf[s] = *(const bf16x8*)(wblock(ga.B, t, k, KS) + lane * 8);
-          load_a(k, av[s]);
-        }
-#pragma unroll
-        for (int s = 0; s < CHS; ++s)
-          if (c0 + s < spw) {
-            bf16x8 hi, lo;
-            if (first)
-              a_operand<NORM, true>(av[s], gk + (size_t)(ks0 + c0 + s) * 32, &ss, hi, lo);
-            else
-              a_operand<NORM, false>(av[s], gk + (size_t)(ks0 + c0 + s) * 32, &ss, hi, lo);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, wf[s], acc, 0, 0, 0);
-            if constexpr (TWO) acc2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, wf[s], acc2, 0, 0, 0);
-          }
-      }
-      if (NORM && first) {
-        ss += __shfl_xor(ss, 16, 64);
-        ss += __shfl_xor(ss, 32, 64);
-        if (g == 0) ss_red[w][r] = ss;
-      }
-    }
+  // reduction of a tile's 8 wave partials, then its epilogue (argmax) or a deferred slot
+  auto finish = [&](int t, f32x4 acc, f32x4 acc2) {
     red[w][lane] = acc + acc2;
     __syncthreads();
     if (NORM && !ASTAT && first) {
@@ -162,6 +132,53 @@ __global__ __launch_bounds__(NW * 64) void gemm_gemv_bf16(GemmArgs ga) {
     }
     ++nbuf;
     __syncthreads();
+  };
+
+  if constexpr (ASTAT) {
+    for (int t = blockIdx.x; t < n_tiles; t += G) {
+      const int tn = min(t + G, t_last);
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc2 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < CH; ++s) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[s], wa[s], acc, 0, 0, 0);
+        if constexpr (TWO) acc2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo[w][s][lane], wa[s], acc2, 0, 0, 0);
+        wa[s] = *(const bf16x8*)(wblock(ga.B, tn, ks0 + s, KS) + lane * 8);
+      }
+      finish(t, acc, acc2);
+    }
+  } else {
+    for (int t = blockIdx.x; t < n_tiles; t += G) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc2 = {0.f, 0.f, 0.f, 0.f};
+      float ss = 0.f;
+      for (int c0 = 0; c0 < spw; c0 += CHS) {
+        // a chunk's weights, activations and gains loaded together, unconditionally (steps
+        // past spw clamped to the last one, their activations zeroed)
+        bf16x8 wf[CHS], gv[CHS];
+        float av[CHS][8];
+#pragma unroll
+        for (int s = 0; s < CHS; ++s) {
+          const int k = ks0 + min(c0 + s, spw - 1);
+          wf[s] = *(const bf16x8*)(wblock(ga.B, t, k, KS) + lane * 8);
+          load_a(k, av[s]);
+          if constexpr (NORM) gv[s] = *(const bf16x8*)(gk + (size_t)k * 32);
+        }
+#pragma unroll
+        for (int s = 0; s < CHS; ++s) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) av[s][e] = c0 + s < spw ? av[s][e] : 0.f;
+          bf16x8 hi, lo;
+          a_operand<NORM>(av[s], gv[s], &ss, hi, lo);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, wf[s], acc, 0, 0, 0);
+          if constexpr (TWO) acc2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, wf[s], acc2, 0, 0, 0);
+        }
+      }
+      if (NORM && first) {
+        ss += __shfl_xor(ss, 16, 64);
+        ss += __shfl_xor(ss, 32, 64);
+        if (g == 0) ss_red[w][r] = ss;
+      }
+      finish(t, acc, acc2);
+    }
   }
   if constexpr (KIND != EPI_ARGMAX) {
     // every wave takes buffered tiles: the epilogues run in parallel, off the main loop's
@@ -196,11 +213,11 @@ struct GemvLaunch {
   template <typename TA, bool NORM, int KIND>
   static hipError_t run(const GemmArgs& ga, hipStream_t st) {
     const int n_tiles = (ga.N + 15) / 16;
-    // few tiles (up to gemv_stream_tiles(), default one per CU) or K > 4096: one workgroup
+    // few tiles (up to gemv_stream_tiles(), default one per CU) or K != 4096: one workgroup
     // per tile, A streamed with W, so that several workgroups may share a CU and every tile
     // is in flight at once; otherwise one workgroup per CU with the A slice stationary,
     // walking the tiles (the deferred epilogue buffer bounds the tiles per workgroup)
-    if (n_tiles <= gemv_stream_tiles() || ga.K > 4096) {
+    if (n_tiles <= gemv_stream_tiles() || ga.K != 32 * GEMV_NW * GEMV_CH) {
       int grid = n_tiles;
       if (grid > 8 * num_cus()) grid = 8 * num_cus();
       if (KIND != EPI_ARGMAX && grid * GEMV_MAX_TILES < n_tiles)
