@@ -385,10 +385,12 @@ size_t dflash_workspace_bytes(const dflash_model* m, int32_t batch, int32_t bloc
 int dflash_inject_ctx(const dflash_model* m, dflash_kv* kv, const void* feats, int32_t n_rows,
                       const int32_t* row_seq, const int32_t* row_pos, int32_t pos_relative,
                       void* ws, size_t ws_bytes, void* stream) {
-  if (!m || !feats || !row_seq || !row_pos || n_rows < 1) return DFLASH_E_ARG;
+  if (!m || n_rows < 0) return DFLASH_E_ARG;
   if (!m->d.w_c) return DFLASH_E_ARG;
   int e = check_kv(m, kv);
   if (e) return e;
+  if (n_rows == 0) return DFLASH_OK;   // nothing to inject (the row arrays may be empty)
+  if (!feats || !row_seq || !row_pos) return DFLASH_E_ARG;
   float* x = nullptr;
   float2* rope = nullptr;
   const size_t need = inject_ws(m, n_rows, ws, &x, &rope);

@@ -164,7 +164,9 @@ size_t dflash_workspace_bytes(const dflash_model* model, int32_t batch, int32_t 
  *   row_seq  device int32 [n_rows]: sequence of each row.
  *   row_pos  device int32 [n_rows]: position of each row, absolute when pos_relative = 0,
  *            else added to seq_len[row_seq[r]].
- * seq_len is not changed (kv_commit advances it).
+ * seq_len is not changed (kv_commit advances it).  n_rows = 0 is a no-op (the row
+ * arrays are then not read and may be NULL); n_rows < 0 is DFLASH_E_ARG.  A row whose
+ * sequence or position has no mapped page is skipped and DFLASH_DEVERR_PAGE flagged.
  */
 int dflash_inject_ctx(const dflash_model* draft, dflash_kv* draft_ctx, const void* feats,
                       int32_t n_rows, const int32_t* row_seq, const int32_t* row_pos,

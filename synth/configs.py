@@ -94,8 +94,20 @@ MID = Workload(
     ctx=(200, 333, 64), target=_MID_TARGET, taps=(1, 3),
     note="test-only bf16 model: ragged vocab / contexts, GQA 4, 6-layer target")
 
-WORKLOADS = {w.cid: w for w in (TINY, CFG2, CFG3, CFG4, CFG5, MID)}
-WORKLOADS.update({w.name: w for w in (TINY, CFG2, CFG3, CFG4, CFG5, MID)})
+# Test-only: a wide vocabulary (LM-head GEMM of 80 block rows over 40000 columns: the
+# wide-N MFMA GEMM path, with ragged row and column tails) and degenerate contexts (empty,
+# one row, exactly one page, one page plus one row).
+_WIDE_DRAFT = ModelShape(n_layers=1, hidden=512, n_q_heads=8, n_kv_heads=2, head_dim=128,
+                         ffn=1536, vocab=40000)
+_WIDE_TARGET = ModelShape(n_layers=2, hidden=512, n_q_heads=8, n_kv_heads=2, head_dim=128,
+                          ffn=1536, vocab=40000)
+WIDE = Workload(
+    cid=102, name="wide_bf16", dtype="bf16", draft=_WIDE_DRAFT, n_taps=2, block=16, batch=5,
+    ctx=(130, 0, 257, 1, 64), target=_WIDE_TARGET, taps=(0, 1),
+    note="test-only bf16 model: vocab 40000, batch 5, contexts 130 / 0 / 257 / 1 / 64")
+
+WORKLOADS = {w.cid: w for w in (TINY, CFG2, CFG3, CFG4, CFG5, MID, WIDE)}
+WORKLOADS.update({w.name: w for w in (TINY, CFG2, CFG3, CFG4, CFG5, MID, WIDE)})
 
 
 def workload(key) -> Workload:

@@ -17,6 +17,9 @@ NEAR_TIE = 1e-2                        # oracle top-2 logit gap below which ids 
 def maxrel(x, y):
     x = np.asarray(x, dtype=np.float64)
     y = np.asarray(y, dtype=np.float64)
+    assert x.shape == y.shape, f"shape {x.shape} != {y.shape}"
+    if y.size == 0:   # e.g. the cache rows of an empty context
+        return 0.0
     den = np.max(np.abs(y))
     return float(np.max(np.abs(x - y)) / den) if den > 0 else float(np.max(np.abs(x)))
 

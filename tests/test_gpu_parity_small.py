@@ -1,6 +1,7 @@
-"""GPU vs oracle parity at sizes the oracle finishes in seconds: the tiny fp32 drafter and
-a small bf16 GQA model whose shapes span several tiles and leave ragged tails (vocab 3000,
-contexts 200 / 333 / 64, pages handed out in shuffled order)."""
+"""GPU vs oracle parity at sizes the oracle finishes in seconds: the tiny fp32 drafter, a
+small bf16 GQA model whose shapes span several tiles and leave ragged tails (vocab 3000,
+contexts 200 / 333 / 64, pages handed out in shuffled order), and a wide-vocabulary bf16
+model (80 block rows x 40000 LM-head columns; contexts 130 / 0 / 257 / 1 / 64)."""
 import numpy as np
 import pytest
 import torch
@@ -15,13 +16,15 @@ from harness import (DEV, TOL, Setup, assert_accept, assert_close, assert_ids, a
 pytestmark = pytest.mark.gpu
 
 WORKLOADS = ["tiny_f32", "mid_bf16"]
+# plus a wide-vocabulary model with empty and one-row contexts for the draft / verify checks
+WITH_WIDE = WORKLOADS + ["wide_bf16"]
 
 
 def _feats(w, lens):
     return [synth.features(w, n, DEV, tag=f"feats.b{b}") for b, n in enumerate(lens)]
 
 
-@pytest.mark.parametrize("name", WORKLOADS)
+@pytest.mark.parametrize("name", WITH_WIDE)
 def test_inject_and_draft_block(name):
     w = synth.workload(name)
     S = Setup(w)
@@ -80,7 +83,7 @@ def _forced_block(S, np_cache, n, anchor, B, f, rng):
     return toks
 
 
-@pytest.mark.parametrize("name", WORKLOADS)
+@pytest.mark.parametrize("name", WITH_WIDE)
 def test_verify_accept(name):
     w = synth.workload(name)
     S = Setup(w, target=True)
