@@ -64,7 +64,7 @@ def main():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-reps", type=int, default=3)
+    ap.add_argument("--cpu-reps", type=int, default=30)
     ap.add_argument("--no-workload-sweep", action="store_true",
                     help="skip the batch-16, 512-row injection and batch-8 cycle measurements")
     ap.add_argument("--no-context-sweep", action="store_true",
