@@ -203,6 +203,22 @@ def main():
         ms = _lib.timing_read(64)
         breakdown[name] = {"launches_per_cycle": len(ms) / 3,
                            "us_per_cycle": sum(ms) * 1e3 / 3}
+
+    # the block size is a runtime argument: draft blocks of 8, 10 and 16 on the same cache
+    block_sweep = {}
+    for Bs in (8, 10, 16):
+        ids_s = torch.zeros(1, Bs - 1, dtype=torch.int32, device=dev)
+        for _ in range(2):
+            rt.draft_block(draft, dkv, state["anchor"], Bs, ids_s, ws_d)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            rt.draft_block(draft, dkv, state["anchor"], Bs, ids_s, ws_d)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / 10
+        block_sweep[str(Bs)] = {"us_per_draft_block": round(us, 2),
+                                "draft_tok_s": round((Bs - 1) / (us * 1e-6), 1)}
     hbm_bytes_draft = (D.n_layers * ((D.n_q_heads + 2 * D.n_kv_heads) * D.head_dim * D.hidden
                                      + D.hidden * D.n_q_heads * D.head_dim + 3 * D.ffn * D.hidden) * 2
                        + D.vocab * D.hidden * 2 + D.n_layers * n * D.n_kv_heads * D.head_dim * 2 * 2)
@@ -243,6 +259,7 @@ def main():
                      # the event pair above also holds the dispatch of the kernel, a few us)
                      "profile_avg_kernel_us": prof_us},
         "kernels": breakdown,
+        "block_sweep": block_sweep,
     }
     if not args.no_context_sweep:
         out["context_sweep"] = context_sweep(draft, D, B, dev)

@@ -1,0 +1,139 @@
+"""The block size B as a runtime schedule: the kernels take B per call, so a drafter and
+target built around B = 16 run blocks of 8 and 10 (the smaller-B inference and the B = 10
+variant the DFlash notes page reports), and a decoding loop may change B from one cycle to
+the next.  Parity with the oracle at each B, and losslessness of a mixed schedule."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synth
+from block_diffusion_drafter_03_amd import runtime as rt
+
+from harness import (DEV, TOL, Setup, assert_accept, assert_ids, assert_rows_close, inject_all)
+
+pytestmark = pytest.mark.gpu
+
+NAME = "mid_bf16"
+SIZES = (16, 8, 10)
+
+
+def test_draft_and_verify_at_each_block_size():
+    w = synth.workload(NAME)
+    S = Setup(w, target=True)
+    lens = synth.ctx_lengths(w)
+    Bmax, tol = max(SIZES), TOL[w.dtype]
+    kv = S.kv(w.draft, max(lens) + Bmax + 70)
+    ws = S.workspace(S.draft, Bmax, kv.capacity, inject_rows=sum(lens))
+    feats = [synth.features(w, n, DEV, tag=f"feats.b{b}") for b, n in enumerate(lens)]
+    inject_all(S, kv, feats, ws)
+    anchor = synth.anchors(w, DEV)
+    ctxs = [O.inject(synth.to_numpy(feats[b]), np.arange(n), S.np_dw, w.draft, store=S.store)
+            for b, n in enumerate(lens)]
+    for B in SIZES:
+        ids = torch.zeros(w.batch, B - 1, dtype=torch.int32, device=DEV)
+        logits = torch.zeros(w.batch, B - 1, w.draft.vocab, device=DEV)
+        rt.draft_block(S.draft, kv, anchor, B, ids, ws, logits)
+        torch.cuda.synchronize()
+        assert kv.err.item() == 0
+        for b, n in enumerate(lens):
+            o_ids, o_z, _ = O.draft_block(S.np_dw, S.np_shared, w.draft, ctxs[b], int(anchor[b]), n, B,
+                                          store=S.store)
+            assert_rows_close(logits[b].cpu().numpy(), o_z, tol, f"B={B} logits seq {b}")
+            assert_ids(ids[b].cpu().numpy(), o_ids, o_z, f"B={B} draft ids seq {b}")
+    # verify at each B on a fresh target cache (the block's K/V are written at n .. n+B-1)
+    T = w.target
+    for B in SIZES:
+        tkv = S.kv(T, max(lens) + Bmax + 70, seed=1)
+        dense = synth.synthetic_ctx_kv(w, "target", lens, DEV)
+        for l in range(T.n_layers):
+            for b, n in enumerate(lens):
+                tkv.write_dense(l, b, dense[l][b][0], dense[l][b][1])
+        tkv.seq_len.copy_(torch.tensor(lens, dtype=torch.int32))
+        np_cache = [[(synth.to_numpy(dense[l][b][0]), synth.to_numpy(dense[l][b][1]))
+                     for l in range(T.n_layers)] for b in range(len(lens))]
+        rng = np.random.default_rng(B)
+        blocks = [[int(anchor[b])] + [int(x) for x in rng.integers(0, T.vocab, B - 1)]
+                  for b in range(w.batch)]
+        bt = torch.tensor(blocks, dtype=torch.int32, device=DEV)
+        k = len(w.taps)
+        fo = torch.zeros(w.batch, B, k * T.hidden, dtype=S.st, device=DEV)
+        g = torch.zeros(w.batch, B, dtype=torch.int32, device=DEV)
+        tau = torch.zeros(w.batch, dtype=torch.int32, device=DEV)
+        bonus = torch.zeros(w.batch, dtype=torch.int32, device=DEV)
+        logits = torch.zeros(w.batch, B, T.vocab, device=DEV)
+        wst = S.workspace(S.target, Bmax, tkv.capacity)
+        rt.verify_accept(S.target, tkv, bt[:, 0].contiguous(), bt[:, 1:].contiguous(), B, fo, g, tau,
+                         bonus, wst, logits)
+        torch.cuda.synchronize()
+        assert tkv.err.item() == 0
+        for b, n in enumerate(lens):
+            og, oz, _, _, _ = O.verify(S.np_tw, S.np_shared, T, np_cache[b], blocks[b], n, w.taps,
+                                       store=S.store)
+            assert_rows_close(logits[b].cpu().numpy(), oz, tol, f"B={B} verify logits seq {b}")
+            assert_ids(g[b].cpu().numpy(), og, oz, f"B={B} target argmax seq {b}")
+            assert_accept(tau[b], bonus[b], g[b].cpu().numpy(), blocks[b][1:], og, oz, f"B={B} accept seq {b}")
+
+
+def test_mixed_block_schedule_reproduces_greedy_decoding():
+    """Cycles whose block size follows 16, 8, 10, 8, 16, ... emit the target's greedy stream
+    (up to the first oracle near-tie): speculative decoding stays lossless under any B
+    schedule, and the caches stay in step through blocks of different sizes."""
+    w = synth.workload(NAME)
+    S = Setup(w, target=True)
+    T, D = w.target, w.draft
+    schedule = [16, 8, 10, 8, 16, 10, 8, 10]
+    Bmax, n0, n_new = max(schedule), 40, 40
+    prompts = [synth.prompt_tokens(w, n0, "cpu", tag=f"prompt{b}").numpy() for b in range(w.batch)]
+    cap = n0 + n_new + 2 * Bmax * len(schedule) + 64
+    tkv = S.kv(T, cap, seed=2)
+    dkv = S.kv(D, cap, seed=3)
+    k = len(w.taps)
+    ws_t = S.workspace(S.target, max(Bmax, n0), tkv.capacity)
+    ws_d = S.workspace(S.draft, Bmax, dkv.capacity, inject_rows=w.batch * max(Bmax, n0))
+    batch = w.batch
+
+    def verify(anchor, drafts, blk):
+        feats = torch.zeros(batch, blk, k * T.hidden, dtype=S.st, device=DEV)
+        g = torch.zeros(batch, blk, dtype=torch.int32, device=DEV)
+        tau = torch.zeros(batch, dtype=torch.int32, device=DEV)
+        bonus = torch.zeros(batch, dtype=torch.int32, device=DEV)
+        rt.verify_accept(S.target, tkv, anchor, drafts, blk, feats, g, tau, bonus, ws_t)
+        return feats, g, tau, bonus
+
+    def inject_rel(feats, blk):
+        rs = torch.arange(batch, dtype=torch.int32, device=DEV).repeat_interleave(blk)
+        rp = torch.arange(blk, dtype=torch.int32, device=DEV).repeat(batch)
+        rt.inject_ctx(S.draft, dkv, feats.reshape(batch * blk, -1).contiguous(), rs, rp, 1, ws_d)
+
+    ids = torch.tensor(np.stack(prompts), dtype=torch.int32, device=DEV)
+    feats, g, _, _ = verify(ids[:, 0].contiguous(), ids[:, 1:].contiguous(), n0)
+    inject_rel(feats, n0)
+    rt.kv_commit(tkv, dkv, torch.full((batch,), n0, dtype=torch.int32, device=DEV), n0)
+    anchor = g[:, -1].contiguous()
+    emitted = [[int(a)] for a in anchor.cpu()]
+    cycle = 0
+    while min(len(e) for e in emitted) < n_new:
+        B = schedule[cycle % len(schedule)]
+        cycle += 1
+        drafts = torch.zeros(batch, B - 1, dtype=torch.int32, device=DEV)
+        rt.draft_block(S.draft, dkv, anchor, B, drafts, ws_d)
+        feats, g, tau, bonus = verify(anchor, drafts, B)
+        inject_rel(feats, B)
+        rt.kv_commit(tkv, dkv, tau, B)
+        t, bo, d = tau.cpu().numpy(), bonus.cpu().numpy(), drafts.cpu().numpy()
+        for b in range(batch):
+            assert 1 <= t[b] <= B
+            emitted[b] += [int(x) for x in d[b, : t[b] - 1]] + [int(bo[b])]
+        anchor = bonus.clone()
+    torch.cuda.synchronize()
+    assert tkv.err.item() == 0 and dkv.err.item() == 0
+    assert torch.equal(tkv.seq_len, dkv.seq_len)
+    for b in range(batch):
+        ref = O.greedy_decode(S.np_tw, S.np_shared, T, prompts[b], n_new, store=S.store)
+        got = emitted[b][:n_new]
+        if got != ref:
+            i = next(i for i in range(n_new) if got[i] != ref[i])
+            _, z, _, _, _ = O.target_forward(S.np_tw, S.np_shared, T, None,
+                                             np.concatenate([prompts[b], ref[:i]]), 0, (), store=S.store)
+            assert O.top2_gap(z[-1]) < 1e-2, f"seq {b}: stream differs at {i}"

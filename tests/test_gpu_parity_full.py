@@ -2,7 +2,8 @@
 configuration the bench uses.
 
  * Qwen3-8B-shaped drafter, batch 1, 4096 injected rows (512-row injection chunks):
-   every cache row, every hidden state, every logit, every draft id.
+   every cache row, every hidden state, every logit, every draft id; then blocks of 8 and
+   10 on the same cache (the block size is a runtime argument).
  * batch 16, contexts in [2048, 8192], 64-token pages in shuffled order: the M = 256 tiled
    GEMM path and the ragged paged attention; injection of the 16 block rows of every
    sequence at its own position.
@@ -45,10 +46,10 @@ def _draft_outputs(S, kv, B, batch):
     return ids, logits, hid
 
 
-def _check_draft(S, b, ctx_np, n, anchor, ids, logits, hid, what):
+def _check_draft(S, b, ctx_np, n, anchor, ids, logits, hid, what, block=None):
     m = S.w.draft
-    o_ids, o_z, o_hid = O.draft_block(S.np_dw, S.np_shared, m, ctx_np, int(anchor), n, S.w.block,
-                                      store=S.store)
+    o_ids, o_z, o_hid = O.draft_block(S.np_dw, S.np_shared, m, ctx_np, int(anchor), n,
+                                      block or S.w.block, store=S.store)
     for l in range(m.n_layers + 1):
         assert_close(hid[l, b].cpu().numpy(), o_hid[l], TOLB, f"{what} hidden layer {l}")
     assert_rows_close(logits[b].cpu().numpy(), o_z, TOLB, f"{what} logits")
@@ -79,6 +80,15 @@ def test_qwen3_8b_batch1_ctx4k():
         assert_close(V, ctx[l][1], TOLB, f"cfg 4k ctx V layer {l}")
     checked = _check_draft(S, 0, ctx, n, anchor[0], ids, logits, hid, "cfg 4k")
     assert checked >= 10    # the near-tie exclusion leaves most positions checked
+    # the block size is a runtime argument: blocks of 8 and 10 on the same cache and
+    # workspace (the schedule of a B = 16 design run at smaller B)
+    for Bs in (8, 10):
+        ids, logits, hid = _draft_outputs(S, kv, Bs, 1)
+        rt.draft_block(S.draft, kv, anchor, Bs, ids, ws, logits, hid)
+        torch.cuda.synchronize()
+        assert kv.err.item() == 0
+        checked = _check_draft(S, 0, ctx, n, anchor[0], ids, logits, hid, f"cfg 4k B={Bs}", block=Bs)
+        assert checked >= Bs - 4
 
 
 def test_qwen3_8b_batch16_paged_ragged():
