@@ -352,6 +352,148 @@ def spec_decode(target_w, draft_w, shared, tshape, dshape, prompt, n_new, block,
 
 
 # ----------------------------------------------------------------------------------------
+# Temperature sampling and lossless rejection-sampling verification  [DF §6.2: sampling at
+# temperature 1 keeps the method lossless; the DFlash 2 notes (§7.2) name "lossless rejection
+# sampling" as the verifier under sampling].  The pages give no further detail, so the
+# readings are the standard speculative-sampling rule:
+#   * the drafter samples each masked position i independently from q_i = softmax(z^d_i / T);
+#   * the target's row j gives p_j = softmax(z^t_j / T) for the token at position j+1, so draft
+#     d_i is checked against p_{i-1}: accepted when u_i < p_{i-1}(d_i) / q_i(d_i);
+#   * at the first rejection i the cycle emits a token drawn from norm(max(0, p_{i-1} - q_i));
+#     when all B-1 drafts pass it emits a token drawn from p_{B-1};
+#   * tau = accepted + 1 as in the greedy rule; the emitted token is the next anchor.
+# Random numbers come from a counter-based generator (splitmix64, Vigna's published mixing
+# function over a Weyl sequence): stream number `index` of seed s is mix(s + (index + 1) *
+# 0x9E3779B97F4A7C15), index = (((counter * 4 + purpose) * 4096 + b) * 128 + i) * 262144 + v.
+# A uniform in (0, 1) takes the top 24 bits: u = ((r >> 40) + 0.5) / 2^24 (exact in float32).
+# Purposes: 0 = drafter Gumbel noise (b, position i, vocab id v), 1 = acceptance uniforms
+# (b, position i, v = 0), 2 = Gumbel noise of the emitted token (b, target row, v).  Sampling
+# from softmax(x) is argmax(x + G) with G = -log(-log(u)) (the Gumbel-max identity), keys
+# formed in float32 as the kernels do: x = float32(z) / float32(T).
+
+_GOLDEN = np.uint64(0x9E3779B97F4A7C15)
+
+
+def splitmix64_mix(z):
+    """Vigna's splitmix64 output function on uint64 arrays."""
+    z = np.asarray(z, dtype=np.uint64)
+    with np.errstate(over="ignore"):
+        z = (z ^ (z >> np.uint64(30))) * np.uint64(0xBF58476D1CE4E5B9)
+        z = (z ^ (z >> np.uint64(27))) * np.uint64(0x94D049BB133111EB)
+    return z ^ (z >> np.uint64(31))
+
+
+def rng_index(counter, purpose, b, i, v):
+    """64-bit stream index of draw (counter, purpose, b, i, v) - fields of 25, 2, 12, 7 and 18
+    bits (v < 262144 covers every vocabulary here)."""
+    with np.errstate(over="ignore"):
+        c = np.uint64(counter) * np.uint64(4) + np.uint64(purpose)
+        c = c * np.uint64(4096) + np.uint64(b)
+        c = c * np.uint64(128) + np.uint64(i)
+        return c * np.uint64(262144) + np.asarray(v, dtype=np.uint64)
+
+
+def uniform01(seed, counter, purpose, b, i, v):
+    """Counter-based uniforms in (0, 1), float32 (24-bit), for an array of vocab ids v."""
+    with np.errstate(over="ignore"):
+        st = np.uint64(seed) + (rng_index(counter, purpose, b, i, v) + np.uint64(1)) * _GOLDEN
+    r = splitmix64_mix(st)
+    return ((r >> np.uint64(40)).astype(np.float32) + np.float32(0.5)) * np.float32(2.0 ** -24)
+
+
+def gumbel(seed, counter, purpose, b, i, v):
+    u = uniform01(seed, counter, purpose, b, i, v)
+    return -np.log(-np.log(u))   # float32 throughout
+
+
+def sample_keys(z, temperature, seed, counter, purpose, b, i):
+    """float32 keys z / T + G of one logits row; their argmax (lowest index on ties) is a
+    sample of softmax(z / T)."""
+    z = np.asarray(z, dtype=np.float32)
+    v = np.arange(z.shape[-1])
+    return z / np.float32(temperature) + gumbel(seed, counter, purpose, b, i, v)
+
+
+def log_softmax_t(z, temperature):
+    """log softmax(z / T) in float64."""
+    x = np.asarray(z, dtype=np.float64) / float(temperature)
+    m = np.max(x, axis=-1, keepdims=True)
+    return x - (m + np.log(np.sum(np.exp(x - m), axis=-1, keepdims=True)))
+
+
+def draft_block_sampled(w, shared, shape, ctx, anchor, n, block, temperature, seed, counter, b=0,
+                        dt=np.float32, store=None):
+    """The drafter pass of draft_block, with each masked position i = 1 .. B-1 sampled from
+    softmax(z_i / T) by the Gumbel-max identity (purpose 0, position i).  Returns
+    (draft_ids [B-1], logits [B-1, V], keys [B-1, V])."""
+    _, z, _ = draft_block(w, shared, shape, ctx, anchor, n, block, dt, store)
+    keys = np.stack([sample_keys(z[i - 1], temperature, seed, counter, 0, b, i) for i in range(1, block)]) \
+        if block > 1 else np.zeros((0, z.shape[-1]), np.float32)
+    return argmax_lowest(keys), z, keys
+
+
+def accept_sampled(draft_ids, draft_logits, target_logits, temperature, seed, counter, b=0):
+    """Speculative-sampling acceptance of one block (readings above).  draft_ids [B-1],
+    draft_logits [B-1, V] (rows for positions 1 .. B-1), target_logits [B, V].  Returns
+    (a, tau, token, ratios [B-1], uniforms [B-1], keys of the emitted token's draw [V])."""
+    B = target_logits.shape[0]
+    lp = log_softmax_t(target_logits, temperature)
+    lq = log_softmax_t(draft_logits, temperature) if B > 1 else np.zeros((0, lp.shape[-1]))
+    ratios = np.zeros(B - 1)
+    us = np.zeros(B - 1)
+    a = 0
+    rejected = False
+    for i in range(1, B):
+        d = int(draft_ids[i - 1])
+        ratios[i - 1] = np.exp(lp[i - 1, d] - lq[i - 1, d])
+        us[i - 1] = float(uniform01(seed, counter, 1, b, i, 0))
+        if not rejected and us[i - 1] < ratios[i - 1]:
+            a = i
+        else:
+            rejected = True
+    v = np.arange(lp.shape[-1])
+    g = gumbel(seed, counter, 2, b, a, v).astype(np.float64)
+    if a < B - 1:   # residual norm(max(0, p_a - q_{a+1})): the normaliser does not move the argmax
+        res = np.exp(lp[a]) - np.exp(lq[a])
+        with np.errstate(divide="ignore"):
+            keys = np.where(res > 0, np.log(np.maximum(res, 1e-300)), -np.inf) + g
+    else:
+        keys = lp[a] + g
+    return a, a + 1, int(argmax_lowest(keys)), ratios, us, keys
+
+
+def spec_decode_sampled(target_w, draft_w, shared, tshape, dshape, prompt, n_new, block, taps,
+                        temperature, seed, dt=np.float32, store=None):
+    """Sampling speculative decoding: drafter sampling, rejection verification, commit.
+    The first token after the prompt is drawn from the target at the prompt's last row
+    (purpose 2, row 0 of counter 0); cycle c uses counter c + 1.  Returns (tokens, taus)."""
+    prompt = np.asarray(prompt, dtype=np.int64)
+    _, z, feats, new_kv, _ = target_forward(target_w, shared, tshape, None, prompt, 0, taps, dt, store)
+    n = len(prompt)
+    tcache = append_kv(empty_cache(tshape, dt), new_kv, n)
+    dctx = inject(feats, np.arange(n), draft_w, dshape, dt, store)
+    lp = log_softmax_t(z[-1:], temperature)[0]
+    anchor = int(argmax_lowest(lp + gumbel(seed, 0, 2, 0, 0, np.arange(lp.shape[-1])).astype(np.float64)))
+    out = [anchor]
+    taus = []
+    counter = 1
+    while len(out) < n_new:
+        drafts, zd, _ = draft_block_sampled(draft_w, shared, dshape, dctx, anchor, n, block,
+                                            temperature, seed, counter, 0, dt, store)
+        block_ids = np.concatenate([[anchor], drafts])
+        _, zt, feats, new_kv, _ = verify(target_w, shared, tshape, tcache, block_ids, n, taps, dt, store)
+        a, tau, tok, _, _, _ = accept_sampled(drafts, zd, zt, temperature, seed, counter, 0)
+        tcache, dctx = commit(tcache, dctx, new_kv, feats, tau, n, draft_w, dshape, dt, store)
+        out.extend(int(t) for t in drafts[:a])
+        out.append(tok)
+        taus.append(tau)
+        n += tau
+        anchor = tok
+        counter += 1
+    return out[:n_new], taus
+
+
+# ----------------------------------------------------------------------------------------
 # Accounting  [DF §2.2 latency model; [TRY] acceptance tables and log lines]
 
 
