@@ -365,7 +365,8 @@ def spec_decode(target_w, draft_w, shared, tshape, dshape, prompt, n_new, block,
 # Random numbers come from a counter-based generator (splitmix64, Vigna's published mixing
 # function over a Weyl sequence): stream number `index` of seed s is mix(s + (index + 1) *
 # 0x9E3779B97F4A7C15), index = (((counter * 4 + purpose) * 4096 + b) * 128 + i) * 262144 + v.
-# A uniform in (0, 1) takes the top 24 bits: u = ((r >> 40) + 0.5) / 2^24 (exact in float32).
+# A uniform in (0, 1) takes the top 23 bits: u = ((r >> 41) + 0.5) / 2^23, exact in float32
+# (24 significant bits) and strictly inside (0, 1), so -log(-log(u)) is always finite.
 # Purposes: 0 = drafter Gumbel noise (b, position i, vocab id v), 1 = acceptance uniforms
 # (b, position i, v = 0), 2 = Gumbel noise of the emitted token (b, target row, v).  Sampling
 # from softmax(x) is argmax(x + G) with G = -log(-log(u)) (the Gumbel-max identity), keys
@@ -394,11 +395,11 @@ def rng_index(counter, purpose, b, i, v):
 
 
 def uniform01(seed, counter, purpose, b, i, v):
-    """Counter-based uniforms in (0, 1), float32 (24-bit), for an array of vocab ids v."""
+    """Counter-based uniforms in (0, 1), float32 (23 random bits), for an array of vocab ids v."""
     with np.errstate(over="ignore"):
         st = np.uint64(seed) + (rng_index(counter, purpose, b, i, v) + np.uint64(1)) * _GOLDEN
     r = splitmix64_mix(st)
-    return ((r >> np.uint64(40)).astype(np.float32) + np.float32(0.5)) * np.float32(2.0 ** -24)
+    return ((r >> np.uint64(41)).astype(np.float32) + np.float32(0.5)) * np.float32(2.0 ** -23)
 
 
 def gumbel(seed, counter, purpose, b, i, v):

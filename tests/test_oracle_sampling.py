@@ -20,6 +20,10 @@ def test_splitmix64_matches_published_vectors():
 def test_uniforms_are_uniform_in_the_open_interval():
     u = O.uniform01(7, 3, 0, 2, 5, np.arange(200000))
     assert u.dtype == np.float32 and u.min() > 0 and u.max() < 1
+    # the extreme draws stay strictly inside (0, 1) in float32
+    top = (np.float32(2 ** 23 - 1) + np.float32(0.5)) * np.float32(2.0 ** -23)
+    low = np.float32(0.5) * np.float32(2.0 ** -23)
+    assert 0 < low and top < 1 and np.isfinite(-np.log(-np.log(np.array([low, top], np.float32)))).all()
     counts, _ = np.histogram(u, bins=32, range=(0, 1))
     assert stats.chisquare(counts).pvalue > 1e-3
     # different fields give different streams
