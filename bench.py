@@ -98,7 +98,7 @@ def main():
     tw = synth.model_weights(wt, "target", dev)
     draft = rt.Model(D, dw, shared, n_taps=w.n_taps, draft=True)
     target = rt.Model(T, tw, shared, n_taps=len(taps), taps=taps, draft=False)
-    cap = n + B * (K + W + 3 * 8 + 4) + 64          # every cycle appends <= B rows
+    cap = n + B * (K + W + 3 * 8 + 12 + 4) + 64     # every cycle appends <= B rows
     dkv = rt.PagedKV(D, 1, cap, torch.bfloat16, dev)
     tkv = rt.PagedKV(T, 1, cap, torch.bfloat16, dev)
     chunk = 512
@@ -219,6 +219,10 @@ def main():
         us = e0.elapsed_time(e1) * 1e3 / 10
         block_sweep[str(Bs)] = {"us_per_draft_block": round(us, 2),
                                 "draft_tok_s": round((Bs - 1) / (us * 1e-6), 1)}
+
+    # temperature sampling (T = 1) with rejection-sampling verification: 12 cycles
+    sampling = sampled_cycles(draft, target, dkv, tkv, ws_d, ws_t, state["anchor"], B, w.n_taps,
+                              D, T, dev)
     hbm_bytes_draft = (D.n_layers * ((D.n_q_heads + 2 * D.n_kv_heads) * D.head_dim * D.hidden
                                      + D.hidden * D.n_q_heads * D.head_dim + 3 * D.ffn * D.hidden) * 2
                        + D.vocab * D.hidden * 2 + D.n_layers * n * D.n_kv_heads * D.head_dim * 2 * 2)
@@ -260,6 +264,7 @@ def main():
                      "profile_avg_kernel_us": prof_us},
         "kernels": breakdown,
         "block_sweep": block_sweep,
+        "sampling_t1": sampling,
     }
     if not args.no_context_sweep:
         out["context_sweep"] = context_sweep(draft, D, B, dev)
@@ -413,6 +418,43 @@ def workload_sweep(draft, target, D, T, B, dev, reps=5, cycles=4):
         torch.cuda.empty_cache()
     out["qwen3_8b_cycle_b8"] = res
     return out
+
+
+def sampled_cycles(draft, target, dkv, tkv, ws_d, ws_t, anchor, B, n_taps, D, T, dev, cycles=12):
+    """Cycles of sampled drafting (T = 1), rejection-sampling verification, injection and
+    commit on the bench's caches: µs of the drafting and verifying calls and the mean tau
+    (random synthetic weights, so the drafter and target barely agree)."""
+    import torch
+    from block_diffusion_drafter_03_amd import runtime as rt
+
+    zd = torch.zeros(1, B - 1, D.vocab, device=dev)
+    zt = torch.zeros(1, B, T.vocab, device=dev)
+    drafts = torch.zeros(1, B - 1, dtype=torch.int32, device=dev)
+    feats = torch.zeros(1, B, n_taps * D.hidden, dtype=torch.bfloat16, device=dev)
+    tau = torch.zeros(1, dtype=torch.int32, device=dev)
+    nxt = torch.zeros(1, dtype=torch.int32, device=dev)
+    rseq = torch.zeros(B, dtype=torch.int32, device=dev)
+    rpos = torch.arange(B, dtype=torch.int32, device=dev)
+    a = anchor.clone()
+    seq0 = int(tkv.seq_len.item())
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(cycles)]
+    for c in range(cycles):
+        ev = evs[c]
+        ev[0].record()
+        rt.draft_block_sampled(draft, dkv, a, B, 1.0, 2024, c, drafts, zd, ws_d)
+        ev[1].record()
+        rt.verify_sampled(target, tkv, a, drafts, zd, B, 1.0, 2024, c, feats, zt, tau, nxt, ws_t)
+        ev[2].record()
+        rt.inject_ctx(draft, dkv, feats.view(B, -1), rseq, rpos, 1, ws_d)
+        rt.kv_commit(tkv, dkv, tau, B)
+        a = nxt.clone()
+    torch.cuda.synchronize()
+    assert int(tkv.err.item()) == 0 and int(dkv.err.item()) == 0
+    us_d = sum(e[0].elapsed_time(e[1]) for e in evs[2:]) * 1e3 / (cycles - 2)
+    us_v = sum(e[1].elapsed_time(e[2]) for e in evs[2:]) * 1e3 / (cycles - 2)
+    return {"us_per_sampled_draft_block": round(us_d, 2), "us_per_sampled_verify": round(us_v, 2),
+            "tau_mean": round((int(tkv.seq_len.item()) - seq0) / cycles, 3),
+            "note": "drafter and target weights are independent random draws"}
 
 
 def context_sweep(draft, shape, B, dev, contexts=(4096, 65536, 262144), reps=5):

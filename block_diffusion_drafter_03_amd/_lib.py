@@ -20,7 +20,7 @@ DEVERR_PAGE, DEVERR_TOKEN, DEVERR_TAU = 1, 2, 4
 EXPORTS = ("dflash_model_create", "dflash_model_destroy", "dflash_status_str",
            "dflash_workspace_bytes", "dflash_inject_ctx", "dflash_draft_block",
            "dflash_verify_accept", "dflash_kv_commit", "dflash_timing_arm",
-           "dflash_timing_read")
+           "dflash_timing_read", "dflash_draft_block_sampled", "dflash_verify_sampled")
 KERNEL_LM_HEAD, KERNEL_GEMM_QKV, KERNEL_GEMM_O, KERNEL_GEMM_GATE_UP, KERNEL_GEMM_DOWN, \
     KERNEL_ATTENTION, KERNEL_INJECT_FUSE, KERNEL_INJECT_KV = range(8)
 
@@ -77,6 +77,15 @@ def lib():
                                            c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                            c_void_p, c_void_p, c_size_t, c_void_p]
         L.dflash_verify_accept.restype = c_int32
+        L.dflash_draft_block_sampled.argtypes = [c_void_p, POINTER(KV), c_void_p, c_int32, c_float,
+                                                 ctypes.c_uint64, c_int32, c_void_p, c_void_p,
+                                                 c_void_p, c_size_t, c_void_p]
+        L.dflash_draft_block_sampled.restype = c_int32
+        L.dflash_verify_sampled.argtypes = [c_void_p, POINTER(KV), c_void_p, c_void_p, c_void_p,
+                                            c_int32, c_float, ctypes.c_uint64, c_int32, c_void_p,
+                                            c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
+                                            c_void_p]
+        L.dflash_verify_sampled.restype = c_int32
         L.dflash_kv_commit.argtypes = [POINTER(KV), POINTER(KV), c_void_p, c_int32, c_void_p]
         L.dflash_kv_commit.restype = c_int32
         L.dflash_timing_arm.argtypes = [c_int32, c_int32]
@@ -127,6 +136,20 @@ def verify_accept(handle, kv: KV, anchor, draft_ids, block, feats_out, target_ar
     return lib().dflash_verify_accept(c_void_p(handle), ctypes.byref(kv), anchor, draft_ids, block,
                                       feats_out, target_argmax, tau, bonus, logits_dbg,
                                       hidden_dbg, ws, ws_bytes, stream)
+
+
+def draft_block_sampled(handle, kv: KV, anchor, block, temperature, seed, counter, draft_ids,
+                        draft_logits, ws, ws_bytes, stream) -> int:
+    return lib().dflash_draft_block_sampled(c_void_p(handle), ctypes.byref(kv), anchor, block,
+                                            temperature, seed, counter, draft_ids, draft_logits,
+                                            ws, ws_bytes, stream)
+
+
+def verify_sampled(handle, kv: KV, anchor, draft_ids, draft_logits, block, temperature, seed,
+                   counter, feats_out, target_logits, tau, next_token, ws, ws_bytes, stream) -> int:
+    return lib().dflash_verify_sampled(c_void_p(handle), ctypes.byref(kv), anchor, draft_ids,
+                                       draft_logits, block, temperature, seed, counter, feats_out,
+                                       target_logits, tau, next_token, ws, ws_bytes, stream)
 
 
 def timing_arm(kernel: int, capacity: int):

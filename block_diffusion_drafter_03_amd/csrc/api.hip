@@ -64,6 +64,7 @@ struct StepWs {
   float* act;
   unsigned long long* keys;
   float2* rope;
+  SampleWs smp;       // sampling verification scratch
   AttnPlan plan;
 };
 
@@ -83,6 +84,11 @@ size_t step_ws(const dflash_model* m, int batch, int B, int ctx_cap, void* base,
   t.act = (float*)cv.take((size_t)Mp * d.ffn * 4);
   t.keys = (unsigned long long*)cv.take((size_t)M * 8);
   t.rope = (float2*)cv.take((size_t)M * (hd / 2) * sizeof(float2));
+  const size_t srows = (size_t)batch * (2 * B - 1);
+  t.smp.part = (float2*)cv.take(srows * SAMPLE_MAX_CHUNKS * sizeof(float2));
+  t.smp.lse = (float*)cv.take(srows * 4);
+  t.smp.acc = (int32_t*)cv.take((size_t)batch * 4);
+  t.smp.keys = (unsigned long long*)cv.take((size_t)batch * SAMPLE_MAX_CHUNKS * 8);
   if (w) *w = t;
   return cv.off;
 }
@@ -295,14 +301,28 @@ int run_layers(const dflash_model* m, const dflash_kv* kv, int batch, int B, con
 // LM head with RMSNorm(g_f) on the A side and the argmax epilogue over every row of h
 // (argmax keys per row; the optional logits copy leaves out each block's anchor row when
 // skipB != 0).
+// Sampling parameters of the drafter's LM head (temperature <= 0: argmax)
+struct Sampling {
+  float temperature = 0.f;
+  unsigned long long seed = 0;
+  unsigned counter = 0;
+};
+
 int run_lm_head(const dflash_model* m, const StepWs& w, int rows, int skipB, float* logits,
-                hipStream_t st) {
+                hipStream_t st, int B = 0, const Sampling& smp = Sampling()) {
   const dflash_model_desc& d = m->d;
   GemmArgs g = gemm_args(w.h, d.hidden, one_seg(d.lm_head, d.vocab, d.hidden), rows, d.vocab,
                          d.hidden, d.final_norm, d.rms_eps, EPI_ARGMAX);
   g.e.keys = w.keys;
   g.e.logits = logits;
   g.e.skipB = skipB;
+  if (smp.temperature > 0.f) {
+    g.e.sample = 1;
+    g.e.temperature = smp.temperature;
+    g.e.seed = smp.seed;
+    g.e.counter = smp.counter;
+    g.e.B = B;
+  }
   return run_gemm(DFLASH_KERNEL_LM_HEAD, d.dtype, g, st);
 }
 
@@ -442,9 +462,9 @@ int dflash_inject_ctx(const dflash_model* m, dflash_kv* kv, const void* feats, i
   return DFLASH_OK;
 }
 
-int dflash_draft_block(const dflash_model* m, const dflash_kv* kv, const int32_t* anchor,
-                       int32_t block, int32_t* draft_ids, float* logits_dbg, float* hidden_dbg,
-                       void* ws, size_t ws_bytes, void* stream) {
+static int draft_block_impl(const dflash_model* m, const dflash_kv* kv, const int32_t* anchor,
+                            int32_t block, int32_t* draft_ids, float* logits_dbg, float* hidden_dbg,
+                            void* ws, size_t ws_bytes, void* stream, const Sampling& smp) {
   if (!m || !anchor || !draft_ids) return DFLASH_E_ARG;
   if (block < 1 || block > 64) return DFLASH_E_SHAPE;
   int e = check_kv(m, kv);
@@ -459,10 +479,33 @@ int dflash_draft_block(const dflash_model* m, const dflash_kv* kv, const int32_t
   e = run_layers(m, kv, batch, B, w, /*causal=*/0, /*write_cache=*/0, nullptr, hidden_dbg, st);
   if (e) return e;
   if (B == 1) return DFLASH_OK;   // a block of one has no masked position to draft
-  e = run_lm_head(m, w, M, B, logits_dbg, st);
+  e = run_lm_head(m, w, M, B, logits_dbg, st, B, smp);
   if (e) return e;
   HIPCHK(launch_unpack_ids(w.keys, batch, B, draft_ids, st));
   return DFLASH_OK;
+}
+
+int dflash_draft_block(const dflash_model* m, const dflash_kv* kv, const int32_t* anchor,
+                       int32_t block, int32_t* draft_ids, float* logits_dbg, float* hidden_dbg,
+                       void* ws, size_t ws_bytes, void* stream) {
+  return draft_block_impl(m, kv, anchor, block, draft_ids, logits_dbg, hidden_dbg, ws, ws_bytes,
+                          stream, Sampling());
+}
+
+int dflash_draft_block_sampled(const dflash_model* m, const dflash_kv* kv, const int32_t* anchor,
+                               int32_t block, float temperature, uint64_t seed, int32_t counter,
+                               int32_t* draft_ids, float* draft_logits, void* ws, size_t ws_bytes,
+                               void* stream) {
+  if (!(temperature > 0.f) || counter < 0 || !draft_logits) return DFLASH_E_ARG;
+  if (block < 2) return DFLASH_E_SHAPE;
+  if (kv && kv->batch > 4096) return DFLASH_E_SHAPE;   // the generator's sequence field
+  if (m && m->d.vocab > 262144) return DFLASH_E_SHAPE;  // and its vocabulary field
+  Sampling smp;
+  smp.temperature = temperature;
+  smp.seed = seed;
+  smp.counter = (unsigned)counter;
+  return draft_block_impl(m, kv, anchor, block, draft_ids, draft_logits, nullptr, ws, ws_bytes,
+                          stream, smp);
 }
 
 int dflash_verify_accept(const dflash_model* m, dflash_kv* kv, const int32_t* anchor,
@@ -487,6 +530,36 @@ int dflash_verify_accept(const dflash_model* m, dflash_kv* kv, const int32_t* an
   e = run_lm_head(m, w, M, 0, logits_dbg, st);
   if (e) return e;
   HIPCHK(launch_accept(w.keys, draft_ids, batch, B, target_argmax, tau, bonus, st));
+  return DFLASH_OK;
+}
+
+int dflash_verify_sampled(const dflash_model* m, dflash_kv* kv, const int32_t* anchor,
+                          const int32_t* draft_ids, const float* draft_logits, int32_t block,
+                          float temperature, uint64_t seed, int32_t counter, void* feats_out,
+                          float* target_logits, int32_t* tau, int32_t* next_token, void* ws,
+                          size_t ws_bytes, void* stream) {
+  if (!m || !anchor || !draft_ids || !draft_logits || !target_logits || !tau || !next_token)
+    return DFLASH_E_ARG;
+  if (!(temperature > 0.f) || counter < 0) return DFLASH_E_ARG;
+  if (block < 2 || block > 64) return DFLASH_E_SHAPE;
+  int e = check_kv(m, kv);
+  if (e) return e;
+  if (kv->batch > 4096 || m->d.vocab > 262144) return DFLASH_E_SHAPE;
+  if (feats_out && m->taps.empty()) return DFLASH_E_ARG;
+  const dflash_model_desc& d = m->d;
+  const int batch = kv->batch, B = block, M = batch * B, V = d.vocab;
+  StepWs w;
+  const size_t need = step_ws(m, batch, B, kv->max_pages_per_seq * 64, ws, &w);
+  if (!ws || ws_bytes < need) return DFLASH_E_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  HIPCHK(launch_embed(d.dtype, embed_args(m, kv, w, 1, draft_ids, anchor, B, nullptr), st));
+  e = run_layers(m, kv, batch, B, w, /*causal=*/1, /*write_cache=*/1, feats_out, nullptr, st);
+  if (e) return e;
+  e = run_lm_head(m, w, M, 0, target_logits, st);
+  if (e) return e;
+  HIPCHK(launch_verify_sampled(target_logits, draft_logits, draft_ids, batch, B, V, temperature,
+                               seed, (unsigned)counter, w.smp, tau, next_token, kv->error_flags,
+                               st));
   return DFLASH_OK;
 }
 

@@ -100,6 +100,28 @@ DF_DEV void rope_cs(int64_t p, int i, int d, double base, float* c, float* s) {
   *s = (float)sin(a);
 }
 
+// Counter-based uniforms for sampling: draw number index + 1 of a splitmix64 stream seeded
+// with `seed` (Vigna's published mixing function over the Weyl sequence of step
+// 0x9E3779B97F4A7C15), index = (((counter * 4 + purpose) * 4096 + b) * 128 + i) * 262144 + v,
+// keeping the top 23 bits: u = (r >> 41) + 1/2, over 2^23 - exact in float32 and strictly
+// inside (0, 1).  Purposes: 0 drafter noise (b, position i, id v), 1 acceptance uniforms
+// (b, position i, v = 0), 2 noise of the emitted token (b, target row i, id v).
+DF_DEV float rng_uniform(unsigned long long seed, unsigned counter, unsigned purpose, unsigned b,
+                         unsigned i, unsigned v) {
+  const unsigned long long idx =
+      ((((unsigned long long)counter * 4ull + purpose) * 4096ull + b) * 128ull + i) * 262144ull + v;
+  unsigned long long z = seed + (idx + 1ull) * 0x9E3779B97F4A7C15ull;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  z ^= z >> 31;
+  return ((float)(unsigned)(z >> 41) + 0.5f) * 1.1920928955078125e-7f;   // 2^-23
+}
+// Gumbel noise -log(-log(u)): argmax(x + noise) samples softmax(x)
+DF_DEV float gumbel_noise(unsigned long long seed, unsigned counter, unsigned purpose, unsigned b,
+                          unsigned i, unsigned v) {
+  return -logf(-logf(rng_uniform(seed, counter, purpose, b, i, v)));
+}
+
 // Device error bits (mirror of DFLASH_DEVERR_*).
 #define DEVERR_PAGE 1
 #define DEVERR_TOKEN 2

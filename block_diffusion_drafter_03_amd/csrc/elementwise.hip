@@ -1,7 +1,6 @@
 // Row kernels of the drafter / verifier step that are not GEMM epilogues: the block
 // embedding, argmax decoding, greedy acceptance and the commit of sequence lengths.
-#include "common.h"
-#include "kernels.h"
+#include "epilogue.h"
 
 namespace dflash {
 
@@ -118,6 +117,206 @@ hipError_t launch_commit(int32_t* seq_t, int32_t* seq_d, int32_t* err_t, int32_t
                          const int32_t* tau, int batch, int B, hipStream_t st) {
   hipLaunchKernelGGL(commit_kernel, dim3((batch + 63) / 64), dim3(64), 0, st, seq_t, seq_d, err_t,
                      err_d, tau, batch, B);
+  return hipGetLastError();
+}
+
+}  // namespace dflash
+
+// ---------------------------------------------------------------------------------------
+// Sampling verification ([DF] section 6.2 and the DFlash 2 notes, section 7.2: lossless
+// rejection sampling at temperature T; the standard speculative-sampling rule).
+
+namespace dflash {
+
+// Four launches, each spread over the vocabulary so that a row's V logits are scanned by
+// many workgroups at once:
+//  1. lse_partial: (max, sum exp(z/T - max)) of every chunk of every target and drafter row;
+//  2. accept_decide: one workgroup per sequence folds the chunk partials into each row's
+//     log-sum-exp, then decides the accepted prefix a and writes tau = a + 1;
+//  3. sample_chunk: the Gumbel-max key of each chunk of the row the emitted token comes from;
+//  4. sample_finish: the largest chunk key of each sequence gives the emitted token.
+// The reduction order is fixed by the chunking, so results do not depend on timing.
+#define SAMPLE_THREADS 256
+
+int sample_chunks(int V) { return std::min(SAMPLE_MAX_CHUNKS, std::max(1, (V + 4095) / 4096)); }
+
+// grid (rows, chunks): rows 0 .. nt-1 are the target's, the rest the drafter's
+__global__ __launch_bounds__(SAMPLE_THREADS) void lse_partial_kernel(const float* zt, const float* zd,
+                                                                     int nt, int V, int clen,
+                                                                     float inv_t, float2* part) {
+  __shared__ float red[SAMPLE_THREADS / 64];
+  const int row = blockIdx.x, c = blockIdx.y;
+  const float* z = row < nt ? zt + (size_t)row * V : zd + (size_t)(row - nt) * V;
+  const int v0 = c * clen, v1 = min(V, v0 + clen);
+  float m = -INFINITY;
+  for (int v = v0 + threadIdx.x; v < v1; v += 4 * SAMPLE_THREADS) {
+    float x[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) x[u] = z[min(v + u * SAMPLE_THREADS, v1 - 1)];   // v1 > v here
+#pragma unroll
+    for (int u = 0; u < 4; ++u) m = fmaxf(m, x[u] * inv_t);
+  }
+  m = wave_max(m);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  float s = 0.f;
+  if (m > -INFINITY) {   // an empty chunk keeps (-inf, 0)
+    for (int v = v0 + threadIdx.x; v < v1; v += 4 * SAMPLE_THREADS) {
+      float x[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) x[u] = z[min(v + u * SAMPLE_THREADS, v1 - 1)];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (v + u * SAMPLE_THREADS < v1) s += expf(x[u] * inv_t - m);
+    }
+  }
+  s = block_sum(s, red);
+  if (threadIdx.x == 0) part[(size_t)row * gridDim.y + c] = make_float2(m, s);
+}
+
+// one wave: lse of a row from its nch (<= 64) chunk partials
+DF_DEV float fold_lse(const float2* p, int nch) {
+  const int l = threadIdx.x & 63;
+  const float2 q = l < nch ? p[l] : make_float2(-INFINITY, 0.f);
+  const float m = wave_max(q.x);
+  const float s = wave_sum(q.x > -INFINITY ? q.y * expf(q.x - m) : 0.f);
+  return m + logf(s);
+}
+
+// grid (batch), 1024 threads.  Draft d_i (i = 1 .. B-1) is judged by target row i-1: accepted
+// while u_i < p_{i-1}(d_i) / q_i(d_i), u_i the uniform of draw (counter, 1, b, i, 0);
+// a = the accepted prefix, tau = a + 1.  lse: target rows [batch * B] then drafter rows
+// [batch * (B-1)].
+__global__ __launch_bounds__(1024) void accept_decide_kernel(
+    const float* zt, const float* zd, const float2* part, int nch, const int32_t* drafts, int B,
+    int V, float inv_t, unsigned long long seed, unsigned counter, float* lse, int32_t* acc,
+    int32_t* tau, int32_t* err) {
+  __shared__ float lt_s[64], ld_s[64];
+  const int b = blockIdx.x, batch = gridDim.x, w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  for (int r = w; r < 2 * B - 1; r += 16) {
+    const int row = r < B ? b * B + r : batch * B + b * (B - 1) + (r - B);
+    const float v = fold_lse(part + (size_t)row * nch, nch);
+    if (l == 0) {
+      lse[row] = v;
+      if (r < B) lt_s[r] = v; else ld_s[r - B] = v;
+    }
+  }
+  __syncthreads();
+  if (w == 0) {
+    bool reject = false;
+    if (l >= 1 && l < B) {
+      const int d = drafts[(size_t)b * (B - 1) + l - 1];
+      if (d < 0 || d >= V) {   // not a token: rejected, and reported
+        flag_error(err, DEVERR_TOKEN);
+        reject = true;
+      } else {
+        const float lp = zt[((size_t)b * B + l - 1) * V + d] * inv_t - lt_s[l - 1];
+        const float lq = zd[((size_t)b * (B - 1) + l - 1) * V + d] * inv_t - ld_s[l - 1];
+        reject = !(rng_uniform(seed, counter, 1, b, l, 0) < expf(lp - lq));
+      }
+    }
+    const unsigned long long rej = __ballot(reject);
+    if (l == 0) {
+      const int a = rej ? __builtin_ctzll(rej) - 1 : B - 1;
+      acc[b] = a;
+      tau[b] = a + 1;
+    }
+  }
+}
+
+// grid (batch, chunks): the emitted token is the argmax over v of key(v) + Gumbel noise of
+// draw (counter, 2, b, a, v), key = log max(0, p_a - q_{a+1}) after a rejection (the
+// residual distribution; its normaliser does not move the argmax), else log p_{B-1}.
+__global__ __launch_bounds__(SAMPLE_THREADS) void sample_chunk_kernel(
+    const float* zt, const float* zd, const float* lse, const int32_t* acc, int B, int V, int clen,
+    float inv_t, unsigned long long seed, unsigned counter, unsigned long long* keys) {
+  __shared__ unsigned long long best_s[SAMPLE_THREADS / 64];
+  const int b = blockIdx.x, c = blockIdx.y, batch = gridDim.x;
+  const int a = acc[b];
+  const bool resid = a < B - 1;
+  const float* pt = zt + ((size_t)b * B + a) * V;
+  const float lt = lse[b * B + a];
+  const float* pd = zd + ((size_t)b * (B - 1) + (resid ? a : 0)) * V;
+  const float ld = resid ? lse[batch * B + b * (B - 1) + a] : 0.f;
+  const int v0 = c * clen, v1 = min(V, v0 + clen);
+  unsigned long long best = 0ull;
+  for (int v = v0 + threadIdx.x; v < v1; v += 4 * SAMPLE_THREADS) {
+    float xt[4], xd[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int vv = min(v + u * SAMPLE_THREADS, v1 - 1);
+      xt[u] = pt[vv];
+      xd[u] = resid ? pd[vv] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int vv = v + u * SAMPLE_THREADS;
+      if (vv >= v1) continue;
+      float key;
+      if (resid) {
+        const float r = expf(xt[u] * inv_t - lt) - expf(xd[u] * inv_t - ld);
+        key = r > 0.f ? logf(r) : -INFINITY;
+      } else {
+        key = xt[u] * inv_t - lt;
+      }
+      if (key > -INFINITY) {
+        const unsigned long long k = pack_argmax_key(key + gumbel_noise(seed, counter, 2, b, a, vv), vv);
+        best = k > best ? k : best;
+      }
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const unsigned lo = __shfl_xor((unsigned)(best & 0xFFFFFFFFull), o, 64);
+    const unsigned hi = __shfl_xor((unsigned)(best >> 32), o, 64);
+    const unsigned long long k = ((unsigned long long)hi << 32) | lo;
+    best = k > best ? k : best;
+  }
+  if ((threadIdx.x & 63) == 0) best_s[threadIdx.x >> 6] = best;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    unsigned long long k = best_s[0];
+    for (int w = 1; w < SAMPLE_THREADS / 64; ++w) k = best_s[w] > k ? best_s[w] : k;
+    keys[(size_t)b * gridDim.y + c] = k;
+  }
+}
+
+// grid (batch), one wave: largest chunk key (ties in value go to the lowest id, as packed)
+__global__ __launch_bounds__(64) void sample_finish_kernel(const unsigned long long* keys, int nch,
+                                                           int32_t* next_token) {
+  const int b = blockIdx.x, l = threadIdx.x;
+  unsigned long long best = l < nch ? keys[(size_t)b * nch + l] : 0ull;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const unsigned lo = __shfl_xor((unsigned)(best & 0xFFFFFFFFull), o, 64);
+    const unsigned hi = __shfl_xor((unsigned)(best >> 32), o, 64);
+    const unsigned long long k = ((unsigned long long)hi << 32) | lo;
+    best = k > best ? k : best;
+  }
+  if (l == 0) next_token[b] = best ? unpack_argmax_idx(best) : 0;
+}
+
+hipError_t launch_verify_sampled(const float* zt, const float* zd, const int32_t* drafts, int batch,
+                                 int B, int V, float temperature, unsigned long long seed,
+                                 unsigned counter, const SampleWs& ws, int32_t* tau,
+                                 int32_t* next_token, int32_t* err, hipStream_t st) {
+  if (batch <= 0) return hipSuccess;
+  if (B < 2 || B > 64 || V < 1) return hipErrorInvalidValue;
+  const int nch = sample_chunks(V), clen = (V + nch - 1) / nch;
+  const float inv_t = 1.f / temperature;
+  const int rows = batch * B + batch * (B - 1);
+  hipLaunchKernelGGL(lse_partial_kernel, dim3(rows, nch), dim3(SAMPLE_THREADS), 0, st, zt, zd,
+                     batch * B, V, clen, inv_t, ws.part);
+  hipLaunchKernelGGL(accept_decide_kernel, dim3(batch), dim3(1024), 0, st, zt, zd,
+                     (const float2*)ws.part, nch, drafts, B, V, inv_t, seed, counter, ws.lse,
+                     ws.acc, tau, err);
+  hipLaunchKernelGGL(sample_chunk_kernel, dim3(batch, nch), dim3(SAMPLE_THREADS), 0, st, zt, zd,
+                     (const float*)ws.lse, (const int32_t*)ws.acc, B, V, clen, inv_t, seed, counter,
+                     ws.keys);
+  hipLaunchKernelGGL(sample_finish_kernel, dim3(batch), dim3(64), 0, st,
+                     (const unsigned long long*)ws.keys, nch, next_token);
   return hipGetLastError();
 }
 

@@ -69,7 +69,7 @@ __global__ __launch_bounds__(256) void gemm_f32(GemmArgs ga) {
       for (int j = 0; j < 4; ++j)
         if (row < M && col0 + j < N) {
           if (e.logits) logit_store(e, row, col0 + j, N, v[j]);
-          k = umax64(k, pack_argmax_key(v[j], col0 + j));
+          k = umax64(k, pack_argmax_key(argmax_value(e, row, col0 + j, v[j]), col0 + j));
         }
       k = umax64(k, shfl_xor_u64(k, 1));
       k = umax64(k, shfl_xor_u64(k, 2));

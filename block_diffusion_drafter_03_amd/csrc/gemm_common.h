@@ -55,6 +55,14 @@ DF_DEV void logit_store(const EpiArgs& e, int row, int col, int N, float v) {
   e.logits[(size_t)row * N + col] = v;
 }
 
+// the value whose maximum the argmax epilogue takes: the logit itself, or for sampling the
+// tempered logit plus the row's Gumbel noise at this column
+DF_DEV float argmax_value(const EpiArgs& e, int row, int col, float v) {
+  if (!e.sample) return v;
+  const int b = row / e.B, i = row - b * e.B;
+  return v / e.temperature + gumbel_noise(e.seed, e.counter, 0, b, i, col);
+}
+
 // Epilogue of one 16x16 MFMA tile held in the accumulator layout: v[i] = acc[row0+4g+i][col].
 // Pair epilogues are taken by even lanes (their odd neighbour holds column col + 1).
 template <typename T, int KIND>
@@ -68,7 +76,7 @@ DF_DEV void tile_epilogue(const GemmArgs& ga, int row0, int col, const float v[4
       const int row = row0 + i;
       const bool ok = row < M && col < N;
       if (ok && e.logits) logit_store(e, row, col, N, v[i]);
-      unsigned long long k = ok ? pack_argmax_key(v[i], col) : 0ull;
+      unsigned long long k = ok ? pack_argmax_key(argmax_value(e, row, col, v[i]), col) : 0ull;
       k = umax64(k, shfl_xor_u64(k, 1));
       k = umax64(k, shfl_xor_u64(k, 2));
       k = umax64(k, shfl_xor_u64(k, 4));

@@ -71,6 +71,12 @@ struct EpiArgs {
   unsigned long long* keys;
   float* logits;
   int skipB;
+  // sampling instead of argmax: key = logit / temperature + Gumbel noise of draw (counter,
+  // purpose 0, b = row / B, i = row % B, v = column)
+  int sample;
+  float temperature;
+  unsigned long long seed;
+  unsigned counter;
 };
 
 struct GemmArgs {
@@ -150,5 +156,20 @@ hipError_t launch_accept(const unsigned long long* keys, const int32_t* drafts, 
                          int32_t* g, int32_t* tau, int32_t* bonus, hipStream_t st);
 hipError_t launch_commit(int32_t* seq_t, int32_t* seq_d, int32_t* err_t, int32_t* err_d,
                          const int32_t* tau, int batch, int B, hipStream_t st);
+// Rejection-sampling verification of every sequence's block at temperature T.  zt: target
+// logits [batch, B, V]; zd: drafter logits of positions 1 .. B-1 [batch, B-1, V]; drafts
+// [batch, B-1].  Writes tau[b] and next_token[b].  Scratch (workspace):
+#define SAMPLE_MAX_CHUNKS 64
+struct SampleWs {
+  float2* part;              // [batch * (2B - 1)][chunks] (max, sum) partials
+  float* lse;                // [batch * (2B - 1)] row log-sum-exps
+  int32_t* acc;              // [batch] accepted prefix
+  unsigned long long* keys;  // [batch][chunks] Gumbel-max keys
+};
+int sample_chunks(int V);   // vocabulary chunks per row, 1 .. SAMPLE_MAX_CHUNKS
+hipError_t launch_verify_sampled(const float* zt, const float* zd, const int32_t* drafts, int batch,
+                                 int B, int V, float temperature, unsigned long long seed,
+                                 unsigned counter, const SampleWs& ws, int32_t* tau,
+                                 int32_t* next_token, int32_t* err, hipStream_t st);
 
 }  // namespace dflash

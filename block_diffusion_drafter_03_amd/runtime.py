@@ -210,6 +210,23 @@ def verify_accept(model: Model, kv: PagedKV, anchor, draft_ids, block, feats_out
     _lib._check(st, "dflash_verify_accept")
 
 
+def draft_block_sampled(model: Model, kv: PagedKV, anchor, block, temperature, seed, counter,
+                        draft_ids, draft_logits, ws: Workspace):
+    st = _lib.draft_block_sampled(model.handle, kv.struct, _ptr(anchor), int(block),
+                                  float(temperature), int(seed), int(counter), _ptr(draft_ids),
+                                  _ptr(draft_logits), _ptr(ws.buf), ws.nbytes, _stream())
+    _lib._check(st, "dflash_draft_block_sampled")
+
+
+def verify_sampled(model: Model, kv: PagedKV, anchor, draft_ids, draft_logits, block, temperature,
+                   seed, counter, feats_out, target_logits, tau, next_token, ws: Workspace):
+    st = _lib.verify_sampled(model.handle, kv.struct, _ptr(anchor), _ptr(draft_ids),
+                             _ptr(draft_logits), int(block), float(temperature), int(seed),
+                             int(counter), _ptr(feats_out), _ptr(target_logits), _ptr(tau),
+                             _ptr(next_token), _ptr(ws.buf), ws.nbytes, _stream())
+    _lib._check(st, "dflash_verify_sampled")
+
+
 def kv_commit(target_kv, draft_kv, tau, block):
     st = _lib.kv_commit(target_kv.struct if target_kv is not None else None,
                         draft_kv.struct if draft_kv is not None else None, _ptr(tau), int(block),

@@ -216,6 +216,47 @@ int dflash_verify_accept(const dflash_model* target, dflash_kv* target_kv,
                          void* stream);
 
 /*
+ * Sampling: temperature-T drafting and lossless rejection-sampling verification ([DF]
+ * section 6.2, sampling at temperature 1; the DFlash 2 notes, section 7.2, name lossless
+ * rejection sampling as the verifier).  The pages give no more detail; the rule is the
+ * standard speculative-sampling one:
+ *   * the drafter samples each masked position i = 1 .. block-1 from q_i = softmax(z_i / T);
+ *   * the target's row j gives p_j = softmax(z^t_j / T); draft d_i is accepted while
+ *     u_i < p_{i-1}(d_i) / q_i(d_i); a = the accepted prefix, tau = a + 1;
+ *   * the emitted token (the next anchor) is drawn from norm(max(0, p_a - q_{a+1})) after a
+ *     rejection, else from p_{block-1}.
+ * Random numbers: draw number index + 1 of a splitmix64 stream seeded with `seed` (Vigna's
+ * mixing function over the Weyl sequence of step 0x9E3779B97F4A7C15), index =
+ * (((counter * 4 + purpose) * 4096 + b) * 128 + i) * 262144 + v, u = ((r >> 41) + 1/2) / 2^23;
+ * purpose 0 = drafter noise (position i, id v), 1 = acceptance uniform (position i), 2 = noise
+ * of the emitted token (target row a, id v).  Samples use the Gumbel-max identity: argmax of
+ * x + G, G = -log(-log(u)), in float32.  A cycle passes the same (seed, counter) to both
+ * calls and a new counter to the next cycle.  batch <= 4096, vocab <= 262144, 0 <= counter
+ * < 2^25, temperature > 0, 2 <= block <= 64; the workspace is dflash_workspace_bytes'.
+ *
+ * dflash_draft_block_sampled: as dflash_draft_block, with the ids drawn as above.
+ *   draft_logits device float [batch, block-1, vocab] (out, required): the drafter's logits
+ *                of positions 1 .. block-1 (its proposal distribution, read by the verifier).
+ * dflash_verify_sampled: as dflash_verify_accept (same target pass, cache writes and taps),
+ * then the rejection rule.
+ *   draft_logits  device float [batch, block-1, vocab] (in): from the drafting call.
+ *   target_logits device float [batch, block, vocab] (out, required): the target's logits.
+ *   tau           device int32 [batch] (out): a + 1.
+ *   next_token    device int32 [batch] (out): the emitted token.
+ * A draft id outside [0, vocab) counts as rejected and flags DFLASH_DEVERR_TOKEN.
+ */
+int dflash_draft_block_sampled(const dflash_model* draft, const dflash_kv* draft_ctx,
+                               const int32_t* anchor, int32_t block, float temperature,
+                               uint64_t seed, int32_t counter, int32_t* draft_ids,
+                               float* draft_logits, void* ws, size_t ws_bytes, void* stream);
+int dflash_verify_sampled(const dflash_model* target, dflash_kv* target_kv,
+                          const int32_t* anchor, const int32_t* draft_ids,
+                          const float* draft_logits, int32_t block, float temperature,
+                          uint64_t seed, int32_t counter, void* feats_out, float* target_logits,
+                          int32_t* tau, int32_t* next_token, void* ws, size_t ws_bytes,
+                          void* stream);
+
+/*
  * Commit / rollback ([DF] section 4.5: accepted tokens are appended, the cycle repeats
  * from the updated context): seq_len[b] += tau[b] in the target cache and in the drafter
  * context (either may be NULL).  Rows written beyond the new length by verify_accept or

@@ -102,6 +102,20 @@ def test_workspace_bytes_and_entry_validation():
         assert L.dflash_inject_ctx(h, ctypes.byref(kv), one, 4, one, one, 0, one, 1 << 30, None) == -1
         assert L.dflash_kv_commit(None, None, one, 16, None) == -1
         assert L.dflash_kv_commit(ctypes.byref(kv), None, one, 0, None) == -2
+        # sampling entry points: temperature, counter, required logits buffers, block >= 2
+        ds = L.dflash_draft_block_sampled
+        assert ds(h, ctypes.byref(kv), one, 16, 0.0, 1, 0, one, one, one, 1 << 30, None) == -1
+        assert ds(h, ctypes.byref(kv), one, 16, 1.0, 1, -1, one, one, one, 1 << 30, None) == -1
+        assert ds(h, ctypes.byref(kv), one, 16, 1.0, 1, 0, one, None, one, 1 << 30, None) == -1
+        assert ds(h, ctypes.byref(kv), one, 1, 1.0, 1, 0, one, one, one, 1 << 30, None) == -2
+        assert ds(h, ctypes.byref(kv), one, 16, 1.0, 1, 0, one, one, one, 16, None) == -5
+        vs = L.dflash_verify_sampled
+        assert vs(h, ctypes.byref(kv), one, one, one, 16, -1.0, 1, 0, None, one, one, one, one,
+                  1 << 30, None) == -1
+        assert vs(h, ctypes.byref(kv), one, one, None, 16, 1.0, 1, 0, None, one, one, one, one,
+                  1 << 30, None) == -1
+        assert vs(h, ctypes.byref(kv), one, one, one, 65, 1.0, 1, 0, None, one, one, one, one,
+                  1 << 30, None) == -2
     finally:
         _lib.model_destroy(h)
 

@@ -25,8 +25,8 @@ import torch
 import oracle as O
 import synth
 
-from harness import (DEV, TOL, Setup, assert_accept, assert_close, assert_ids, assert_rows_close,
-                     read_cache)
+from harness import (DEV, NEAR_TIE, TOL, Setup, assert_accept, assert_close, assert_ids,
+                     assert_rows_close, read_cache)
 from block_diffusion_drafter_03_amd import runtime as rt
 
 pytestmark = pytest.mark.gpu
@@ -89,6 +89,19 @@ def test_qwen3_8b_batch1_ctx4k():
         assert kv.err.item() == 0
         checked = _check_draft(S, 0, ctx, n, anchor[0], ids, logits, hid, f"cfg 4k B={Bs}", block=Bs)
         assert checked >= Bs - 4
+    # temperature sampling at T = 1 (the drafter's logits and its sampled ids)
+    zd = torch.zeros(1, B - 1, w.draft.vocab, device=DEV)
+    ids = torch.zeros(1, B - 1, dtype=torch.int32, device=DEV)
+    rt.draft_block_sampled(S.draft, kv, anchor, B, 1.0, 99, 3, ids, zd, ws)
+    torch.cuda.synchronize()
+    assert kv.err.item() == 0
+    o_ids, o_z, o_keys = O.draft_block_sampled(S.np_dw, S.np_shared, w.draft, ctx, int(anchor[0]), n, B,
+                                               1.0, 99, 3, 0, store=S.store)
+    assert_rows_close(zd[0].cpu().numpy(), o_z, TOLB, "cfg 4k sampled draft logits")
+    gaps = O.top2_gap(o_keys.astype(np.float64))
+    sel = gaps >= NEAR_TIE
+    assert sel.sum() >= B - 4
+    assert np.array_equal(ids[0].cpu().numpy()[sel], o_ids[sel]), "cfg 4k sampled draft ids"
 
 
 def test_qwen3_8b_batch16_paged_ragged():
