@@ -38,6 +38,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_gemv_bf16(GemmArgs ga) {
   __shared__ float ss_red[NW][16];
   __shared__ float rstd[16];
   __shared__ bf16x8 alo[ASTAT && TWO ? NW : 1][ASTAT && TWO ? CH : 1][64];
+  __shared__ bf16x8 gsh[ASTAT && NORM ? NW * 64 : 1];   // stationary form: the K norm gains
   // running argmax keys of wave 0's lanes (kept out of the main loop's registers)
   __shared__ unsigned long long bsh[KIND == EPI_ARGMAX ? 4 : 1][64];
   const bf16* gk = NORM ? (const bf16*)ga.norm_g + g * 8 : nullptr;
@@ -63,25 +64,41 @@ __global__ __launch_bounds__(NW * 64) void gemm_gemv_bf16(GemmArgs ga) {
   bf16x8 wa[ASTAT ? CH : 1];
   // every step's load is issued unconditionally, so the compiler can count the loads and
   // never drains the ring with a full wait
+  // (the steps of one tile are consecutive 1 KB fragments: one base address per tile)
   auto load_w = [&](bf16x8 (&wn)[ASTAT ? CH : 1], int t) {
+    const bf16* p = wblock(ga.B, t, ks0, KS) + lane * 8;
 #pragma unroll
-    for (int s = 0; s < CH; ++s) wn[s] = *(const bf16x8*)(wblock(ga.B, t, ks0 + s, KS) + lane * 8);
+    for (int s = 0; s < CH; ++s) wn[s] = *(const bf16x8*)(p + (size_t)s * 512);
   };
   const int G = gridDim.x;
   const int t_last = blockIdx.x < n_tiles ? blockIdx.x + (n_tiles - 1 - blockIdx.x) / G * G : 0;
   if constexpr (ASTAT) {
-    if (blockIdx.x < n_tiles) load_w(wa, blockIdx.x);
+    // The norm gains (K = 8 per thread) and every A step of this wave are loaded at once;
+    // the first W tile goes out only when this wave's A has arrived.  W issued earlier
+    // (independent of A) floods the memory system with every workgroup's first tile and
+    // delays the A fetches by about twice their own latency.  The launch keeps
+    // gridDim.x <= n_tiles.
+    bf16x8 gl;
+    if constexpr (NORM) gl = *(const bf16x8*)((const bf16*)ga.norm_g + threadIdx.x * 8);
+    float av[CH][8];
+#pragma unroll
+    for (int s = 0; s < CH; ++s) load_a(ks0 + s, av[s]);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (NORM) {
+      gsh[threadIdx.x] = gl;
+      __syncthreads();
+    }
     float ss = 0.f;
 #pragma unroll
     for (int s = 0; s < CH; ++s) {
-      const int k = ks0 + s;
-      float v[8];
-      load_a(k, v);
-      const bf16x8 gv = NORM ? *(const bf16x8*)(gk + (size_t)k * 32) : bf16x8{};
+      const bf16x8 gv = NORM ? gsh[(ks0 + s) * 4 + g] : bf16x8{};
       bf16x8 lo;
-      a_operand<NORM>(v, gv, &ss, ah[s], lo);
+      a_operand<NORM>(av[s], gv, &ss, ah[s], lo);
       if constexpr (TWO) alo[w][s][lane] = lo;
     }
+    __builtin_amdgcn_sched_barrier(0);
+    load_w(wa, blockIdx.x);
+    __builtin_amdgcn_sched_barrier(0);
     if (NORM) {
       ss += __shfl_xor(ss, 16, 64);
       ss += __shfl_xor(ss, 32, 64);
@@ -137,17 +154,19 @@ __global__ __launch_bounds__(NW * 64) void gemm_gemv_bf16(GemmArgs ga) {
   if constexpr (ASTAT) {
     for (int t = blockIdx.x; t < n_tiles; t += G) {
       const int tn = min(t + G, t_last);
+      const bf16* pn = wblock(ga.B, tn, ks0, KS) + lane * 8;
       f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < CH; ++s) {
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[s], wa[s], acc, 0, 0, 0);
         if constexpr (TWO) acc2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo[w][s][lane], wa[s], acc2, 0, 0, 0);
-        wa[s] = *(const bf16x8*)(wblock(ga.B, tn, ks0 + s, KS) + lane * 8);
+        wa[s] = *(const bf16x8*)(pn + (size_t)s * 512);
       }
       finish(t, acc, acc2);
     }
   } else {
     for (int t = blockIdx.x; t < n_tiles; t += G) {
+      const bf16* pt = wblock(ga.B, t, 0, KS) + lane * 8;
       f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc2 = {0.f, 0.f, 0.f, 0.f};
       float ss = 0.f;
       for (int c0 = 0; c0 < spw; c0 += CHS) {
@@ -158,7 +177,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_gemv_bf16(GemmArgs ga) {
 #pragma unroll
         for (int s = 0; s < CHS; ++s) {
           const int k = ks0 + min(c0 + s, spw - 1);
-          wf[s] = *(const bf16x8*)(wblock(ga.B, t, k, KS) + lane * 8);
+          wf[s] = *(const bf16x8*)(pt + (size_t)k * 512);
           load_a(k, av[s]);
           if constexpr (NORM) gv[s] = *(const bf16x8*)(gk + (size_t)k * 32);
         }
