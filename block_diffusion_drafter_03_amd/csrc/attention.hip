@@ -88,37 +88,27 @@ __global__ __launch_bounds__(ATTN_THREADS, 1) void attn_splitk_bf16(AttnArgs a) 
   const int n_ctx_steps = kend > kbeg ? (kend - kbeg + 63) / 64 : 0;
   // split 0 also takes the block's own keys
 
-  // the split's physical pages, read and checked once (a page index used straight from
-  // global memory would make every step wait for all loads in flight)
-  __shared__ int pages_s[ATTN_MAX_SPLIT_PAGES];
-  for (int i = tid; i < n_ctx_steps; i += ATTN_THREADS) {
-    int page = a.block_table[(size_t)b * a.max_pages + (kbeg >> 6) + i];
-    if (page < 0 || page >= a.num_pages) {
-      flag_error(a.err, DEVERR_PAGE);
-      page = 0;
-    }
-    pages_s[i] = page;
-  }
-  __syncthreads();
+  // Start-up takes two memory round trips: the query rows, the block's own keys (split 0)
+  // and the split's page-table entries are fetched together, then the first context steps
+  // (their addresses need the page table), while the queries are converted.
 
   // this wave's query tile: rows rho = rg*64 + wq*16 + r as the Q^T MFMA operand, scaled
-  // into the log2 domain and split into a compensated (hi, lo) pair
+  // into the log2 domain and split into a compensated (hi, lo) pair (after the page table)
   const int rho = rg * 64 + wq * 16 + r;
   const int jq = rho < R ? rho % a.B : 0x7fffffff;
+  float qv[4][8];
   bf16x8 qh[4], ql[4];
   {
     const int gq = rho < R ? rho / a.B : 0;
     const float* src = a.q + (size_t)(b * a.B + (rho < R ? jq : 0)) * a.Hq * AD +
                        (size_t)(kvh * a.G + gq) * AD + g * 8;
 #pragma unroll
-    for (int cs = 0; cs < 4; ++cs) {
-      float v[8];
-      load8(src + cs * 32, v);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = rho < R ? v[e] * a.scale_log2 : 0.f;
-      split8(v, qh[cs], ql[cs]);
-    }
+    for (int cs = 0; cs < 4; ++cs) load8(src + cs * 32, qv[cs]);
   }
+
+  // the split's physical pages, read and checked once (a page index used straight from
+  // global memory would make every step wait for all loads in flight)
+  __shared__ int pages_s[ATTN_MAX_SPLIT_PAGES];
 
   // ---- global -> register staging of one step: 4 x 16 B per thread (K then V^T) ----
   // Every context step issues exactly these 4 loads, unconditionally and to valid
@@ -245,14 +235,39 @@ __global__ __launch_bounds__(ATTN_THREADS, 1) void attn_splitk_bf16(AttnArgs a) 
       o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pl, o[dt], 0, 0, 0);
     }
   };
-  // the block's own keys first (split 0): loaded together with the ring's first steps
+  // the block's own keys first (split 0)
   bf16x8 stb[4];
   const int last = n_ctx_steps - 1;
   if (s == 0) load_blk(stb);
+  // (every thread reads and writes its slots unconditionally - past the split's last page
+  // the index is clamped to a valid entry - so every thread waits here for its loads and
+  // the query conversion below needs no wait on the context loads issued after it)
+  constexpr int PPT = ATTN_MAX_SPLIT_PAGES / ATTN_THREADS;
+  int pg[PPT];
+#pragma unroll
+  for (int j = 0; j < PPT; ++j)
+    pg[j] = a.block_table[(size_t)b * a.max_pages + (kbeg >> 6) + min(tid + j * ATTN_THREADS, max(n_ctx_steps - 1, 0))];
+#pragma unroll
+  for (int j = 0; j < PPT; ++j) {
+    const int i = tid + j * ATTN_THREADS;
+    int page = pg[j];
+    if (page < 0 || page >= a.num_pages) {
+      if (i < n_ctx_steps) flag_error(a.err, DEVERR_PAGE);
+      page = 0;
+    }
+    pages_s[i] = page;
+  }
+  __syncthreads();
   if (n_ctx_steps > 0) {
     load_ctx(0, st0);
     load_ctx(min(1, last), st1);
     load_ctx(min(2, last), st2);
+  }
+#pragma unroll
+  for (int cs = 0; cs < 4; ++cs) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qv[cs][e] = rho < R ? qv[cs][e] * a.scale_log2 : 0.f;
+    split8(qv[cs], qh[cs], ql[cs]);
   }
   if (s == 0) {
     store_step(0, a.B, stb);
@@ -370,7 +385,7 @@ __global__ __launch_bounds__(256) void attn_merge_bf16(AttnArgs a) {
 }
 
 // Tuning knob read once from the environment (benchmark sweeps): DFLASH_ATTN_SPLIT_LEN
-// forces the keys per split (rounded up to a multiple of 128).
+// forces the largest keys per split (rounded up to a multiple of 64).
 static int env_int(const char* name, int dflt) {
   const char* s = getenv(name);
   return s && *s ? atoi(s) : dflt;
@@ -493,18 +508,20 @@ AttnPlan attn_plan(int dt, int batch, int Hkv, int G, int B, int ctx_cap) {
   const int cap = ctx_cap > 0 ? ctx_cap : 1;
   const int units = batch * Hkv * p.n_rg;
   // one workgroup per CU (register-bound): aim for one wave of workgroups over the chip,
-  // with at least 256 keys (4 steps) in a split
+  // with at least 192 keys (3 steps) in a split
   int want = attn_num_cus() / units;
-  const int max_splits = (cap + 255) / 256;
+  const int max_splits = (cap + 191) / 192;
   if (want > max_splits) want = max_splits;
   if (want < 1) want = 1;
+  // split lengths: 192 keys for short contexts, else a multiple of 128 (measured: at 64K and
+  // 256K contexts, 128-key multiples stream faster than the evener 64-key multiples)
   int len = (cap + want - 1) / want;
-  len = (len + 127) / 128 * 128;
+  len = len <= 192 ? 192 : (len + 127) / 128 * 128;
   static const int forced = env_int("DFLASH_ATTN_SPLIT_LEN", 0);
-  if (forced >= 128) len = (forced + 127) / 128 * 128;
+  if (forced >= 64) len = (forced + 63) / 64 * 64;
   if (len > 64 * ATTN_MAX_SPLIT_PAGES) len = 64 * ATTN_MAX_SPLIT_PAGES;
   if ((cap + len - 1) / len > MERGE_MAX_SPLITS) len = (cap + MERGE_MAX_SPLITS - 1) / MERGE_MAX_SPLITS;
-  len = (len + 127) / 128 * 128;
+  len = (len + 63) / 64 * 64;
   p.split_len = len;
   p.n_ctx_splits = (cap + len - 1) / len;
   return p;

@@ -106,7 +106,7 @@ struct KvLayer {
 
 struct AttnPlan {
   int n_ctx_splits;   // context splits (grid dimension, before the block split)
-  int split_len;      // keys per context split (multiple of 128)
+  int split_len;      // keys per context split (multiple of 64)
   int n_rg;           // 64-row groups of the G*B query rows of one KV head
 };
 AttnPlan attn_plan(int dt, int batch, int Hkv, int G, int B, int ctx_cap);
