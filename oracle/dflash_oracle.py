@@ -527,3 +527,56 @@ def expected_tau_forced(p, block):
     with probability p and the first unforced position is made to differ:
     tau = 1 + (length of the leading run of forced positions)."""
     return 1.0 + sum(p ** k for k in range(1, block))
+
+
+# ----------------------------------------------------------------------------------------
+# DFlash 2 path selector  [DF §7.1, "Problem 1: Selection Headroom"]: the top-16 candidates
+# of each masked position are kept and every adjacent pair (predecessor a, candidate b) is
+# scored S_t(a, b) = U_t(b) + <A(a) * H(h_t), B(b)>, U_t(b) the drafter's own logit and
+# A, B, H 256-dimensional projections; a greedy walk over the scores picks the drafts.
+# The page names the pieces but not their inputs, so the readings are:
+#   * A(a) = E[a] W_A and B(b) = E[b] W_B with E the shared token embedding, H(h) = h W_H
+#     with h the drafter's final hidden state after the final RMSNorm (the LM head's
+#     input); W_A, W_B, W_H are [D, 256] (for a 2560-wide 4B drafter, 3 x 2560 x 256 =
+#     1.97M parameters - the page's 2.0M);
+#   * U_t(b) is the raw logit z_t(b);
+#   * the walk starts at the anchor (the last verified token): position 1's predecessor is
+#     the anchor, position t's is the candidate chosen at t - 1;
+#   * candidates are the top_k logits of a position, ties to the lower id; the walk's ties
+#     go to the lower id as well.
+
+
+def topk_lowest(z, k):
+    """Ids of the k largest entries of each row of z, in descending value, ties to the lower
+    id."""
+    z = np.asarray(z)
+    if z.ndim == 1:
+        return topk_lowest(z[None], k)[0]
+    ids = np.broadcast_to(np.arange(z.shape[-1]), z.shape)
+    return np.lexsort((ids, -z), axis=-1)[:, :k]
+
+
+def select_path(z, h_final, anchor, embed, g_f, eps, w_a, w_b, w_h, top_k=16, dt=np.float32):
+    """Greedy path selection over a drafted block [DF §7.1].
+
+    z: drafter logits of the masked positions [B-1, V]; h_final: the drafter's final hidden
+    states of those positions before the final norm [B-1, D]; anchor: the block's first
+    token.  Returns (draft_ids [B-1], candidates [B-1, top_k], scores [B-1, top_k] of the
+    chosen predecessor's row at each position)."""
+    z = np.asarray(z, dtype=dt)
+    E = np.asarray(embed, dtype=dt)
+    cand = topk_lowest(z, top_k)
+    hh = rmsnorm(np.asarray(h_final, dtype=dt), g_f, eps, dt) @ np.asarray(w_h, dtype=dt)
+    wa = np.asarray(w_a, dtype=dt)
+    wb = np.asarray(w_b, dtype=dt)
+    prev = int(anchor)
+    out, rows = [], []
+    for t in range(z.shape[0]):
+        a_vec = E[prev] @ wa                               # A(a)
+        b_vec = E[cand[t]] @ wb                            # B(b) for every candidate b
+        s = z[t, cand[t]] + b_vec @ (a_vec * hh[t])        # S_t(a, b)
+        best = max(range(top_k), key=lambda j: (s[j], -int(cand[t][j])))
+        prev = int(cand[t][best])
+        out.append(prev)
+        rows.append(s)
+    return np.array(out, dtype=np.int64), cand, np.array(rows)
