@@ -223,6 +223,8 @@ def main():
     # temperature sampling (T = 1) with rejection-sampling verification: 12 cycles
     sampling = sampled_cycles(draft, target, dkv, tkv, ws_d, ws_t, state["anchor"], B, w.n_taps,
                               D, T, dev)
+    # DFlash 2 path selector (rank 256, top-16) on the same drafter and context
+    selector = selector_timing(w, draft, dkv, ws_d, state["anchor"], B, D, dev)
     hbm_bytes_draft = (D.n_layers * ((D.n_q_heads + 2 * D.n_kv_heads) * D.head_dim * D.hidden
                                      + D.hidden * D.n_q_heads * D.head_dim + 3 * D.ffn * D.hidden) * 2
                        + D.vocab * D.hidden * 2 + D.n_layers * n * D.n_kv_heads * D.head_dim * 2 * 2)
@@ -265,6 +267,7 @@ def main():
         "kernels": breakdown,
         "block_sweep": block_sweep,
         "sampling_t1": sampling,
+        "path_selector": selector,
     }
     if not args.no_context_sweep:
         out["context_sweep"] = context_sweep(draft, D, B, dev)
@@ -455,6 +458,36 @@ def sampled_cycles(draft, target, dkv, tkv, ws_d, ws_t, anchor, B, n_taps, D, T,
     return {"us_per_sampled_draft_block": round(us_d, 2), "us_per_sampled_verify": round(us_v, 2),
             "tau_mean": round((int(tkv.seq_len.item()) - seq0) / cycles, 3),
             "note": "drafter and target weights are independent random draws"}
+
+
+def selector_timing(w, draft, dkv, ws_d, anchor, B, D, dev, reps=10):
+    """µs per draft block with the DFlash 2 path selector (rank 256, top-16; synthetic
+    selector weights) against the plain greedy draft block on the same cache."""
+    import torch
+    import synth
+    from block_diffusion_drafter_03_amd import runtime as rt
+
+    sw = synth.selector_weights(w, rank=256, device=dev)
+    sel = rt.Selector(draft, sw["w_a"], sw["w_b"], sw["w_h"], top_k=16)
+    sws = rt.Workspace(sel.workspace_bytes(draft, 1, B), dev)
+    ids = torch.zeros(1, B - 1, dtype=torch.int32, device=dev)
+    zd = torch.zeros(1, B - 1, D.vocab, device=dev)
+    out = {}
+    for name, call in (("greedy", lambda: rt.draft_block(draft, dkv, anchor, B, ids, ws_d)),
+                       ("selector", lambda: rt.draft_block_select(draft, dkv, anchor, B, sel, ids, zd,
+                                                                  ws_d, sws))):
+        for _ in range(3):
+            call()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            call()
+        e1.record()
+        torch.cuda.synchronize()
+        out["us_per_draft_block_" + name] = round(e0.elapsed_time(e1) * 1e3 / reps, 2)
+    assert int(dkv.err.item()) == 0
+    out["overhead_frac"] = round(out["us_per_draft_block_selector"] / out["us_per_draft_block_greedy"] - 1, 4)
+    return out
 
 
 def context_sweep(draft, shape, B, dev, contexts=(4096, 65536, 262144), reps=5):

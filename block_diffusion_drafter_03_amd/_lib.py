@@ -20,7 +20,8 @@ DEVERR_PAGE, DEVERR_TOKEN, DEVERR_TAU = 1, 2, 4
 EXPORTS = ("dflash_model_create", "dflash_model_destroy", "dflash_status_str",
            "dflash_workspace_bytes", "dflash_inject_ctx", "dflash_draft_block",
            "dflash_verify_accept", "dflash_kv_commit", "dflash_timing_arm",
-           "dflash_timing_read", "dflash_draft_block_sampled", "dflash_verify_sampled")
+           "dflash_timing_read", "dflash_draft_block_sampled", "dflash_verify_sampled",
+           "dflash_selector_workspace_bytes", "dflash_draft_block_select")
 KERNEL_LM_HEAD, KERNEL_GEMM_QKV, KERNEL_GEMM_O, KERNEL_GEMM_GATE_UP, KERNEL_GEMM_DOWN, \
     KERNEL_ATTENTION, KERNEL_INJECT_FUSE, KERNEL_INJECT_KV = range(8)
 
@@ -41,6 +42,10 @@ class KV(ctypes.Structure):
                 ("num_pages", c_int32), ("k_pool", POINTER(c_void_p)),
                 ("v_pool", POINTER(c_void_p)), ("block_table", c_void_p),
                 ("seq_len", c_void_p), ("error_flags", c_void_p)]
+
+
+class Selector(ctypes.Structure):
+    _fields_ = [("w_ab", c_void_p), ("w_h", c_void_p), ("rank", c_int32), ("top_k", c_int32)]
 
 
 class DFlashError(RuntimeError):
@@ -86,6 +91,12 @@ def lib():
                                             c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
                                             c_void_p]
         L.dflash_verify_sampled.restype = c_int32
+        L.dflash_selector_workspace_bytes.argtypes = [c_void_p, POINTER(Selector), c_int32, c_int32]
+        L.dflash_selector_workspace_bytes.restype = c_size_t
+        L.dflash_draft_block_select.argtypes = [c_void_p, POINTER(KV), c_void_p, c_int32,
+                                                POINTER(Selector), c_void_p, c_void_p, c_void_p,
+                                                c_void_p, c_size_t, c_void_p, c_size_t, c_void_p]
+        L.dflash_draft_block_select.restype = c_int32
         L.dflash_kv_commit.argtypes = [POINTER(KV), POINTER(KV), c_void_p, c_int32, c_void_p]
         L.dflash_kv_commit.restype = c_int32
         L.dflash_timing_arm.argtypes = [c_int32, c_int32]
@@ -150,6 +161,17 @@ def verify_sampled(handle, kv: KV, anchor, draft_ids, draft_logits, block, tempe
     return lib().dflash_verify_sampled(c_void_p(handle), ctypes.byref(kv), anchor, draft_ids,
                                        draft_logits, block, temperature, seed, counter, feats_out,
                                        target_logits, tau, next_token, ws, ws_bytes, stream)
+
+
+def selector_workspace_bytes(handle, sel: Selector, batch: int, block: int) -> int:
+    return int(lib().dflash_selector_workspace_bytes(c_void_p(handle), ctypes.byref(sel), batch, block))
+
+
+def draft_block_select(handle, kv: KV, anchor, block, sel: Selector, draft_ids, draft_logits,
+                       candidates, ws, ws_bytes, sel_ws, sel_ws_bytes, stream) -> int:
+    return lib().dflash_draft_block_select(c_void_p(handle), ctypes.byref(kv), anchor, block,
+                                           ctypes.byref(sel), draft_ids, draft_logits, candidates,
+                                           ws, ws_bytes, sel_ws, sel_ws_bytes, stream)
 
 
 def timing_arm(kernel: int, capacity: int):

@@ -355,6 +355,42 @@ int validate_model(const dflash_model_desc* d) {
   return DFLASH_OK;
 }
 
+// Path-selector scratch: H of every block row, chunk top-k keys, candidate ids, the gathered
+// embedding rows (anchor, then position-major candidates, per sequence) and their [A | B]
+// projections.
+struct SelWs {
+  float* hh;
+  unsigned long long* keys;
+  int32_t* cand;
+  void* gather;
+  float* P;
+  float* S;
+};
+
+size_t sel_ws(const dflash_model* m, const dflash_selector* s, int batch, int B, void* base,
+              SelWs* w) {
+  const int D = m->d.hidden, r = s->rank, k = s->top_k;
+  const size_t rows = (size_t)batch * (B - 1);
+  const size_t msel = (size_t)batch * (1 + (size_t)(B - 1) * k);
+  Carve cv(base);
+  SelWs t;
+  t.hh = (float*)cv.take((size_t)batch * B * r * 4);
+  t.keys = (unsigned long long*)cv.take(rows * SAMPLE_MAX_CHUNKS * 16 * 8);
+  t.cand = (int32_t*)cv.take(rows * 16 * 4);
+  t.gather = cv.take(msel * D * esz(m->d.dtype));
+  t.P = (float*)cv.take(msel * 2 * r * 4);
+  t.S = (float*)cv.take(rows * 16 * 16 * 4);
+  if (w) *w = t;
+  return cv.off;
+}
+
+int check_selector(const dflash_model* m, const dflash_selector* s) {
+  if (!m || !s || !s->w_ab || !s->w_h) return DFLASH_E_ARG;
+  if (s->rank < 16 || s->rank > 512 || s->rank % 16) return DFLASH_E_SHAPE;
+  if (s->top_k < 1 || s->top_k > 16 || s->top_k > m->d.vocab) return DFLASH_E_SHAPE;
+  return DFLASH_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -506,6 +542,60 @@ int dflash_draft_block_sampled(const dflash_model* m, const dflash_kv* kv, const
   smp.counter = (unsigned)counter;
   return draft_block_impl(m, kv, anchor, block, draft_ids, draft_logits, nullptr, ws, ws_bytes,
                           stream, smp);
+}
+
+size_t dflash_selector_workspace_bytes(const dflash_model* m, const dflash_selector* sel,
+                                       int32_t batch, int32_t block) {
+  if (check_selector(m, sel) || batch < 1 || block < 2 || block > 64) return 0;
+  return sel_ws(m, sel, batch, block, nullptr, nullptr);
+}
+
+int dflash_draft_block_select(const dflash_model* m, const dflash_kv* kv, const int32_t* anchor,
+                              int32_t block, const dflash_selector* sel, int32_t* draft_ids,
+                              float* draft_logits, int32_t* candidates, void* ws, size_t ws_bytes,
+                              void* sws, size_t sws_bytes, void* stream) {
+  if (!m || !anchor || !draft_ids || !draft_logits) return DFLASH_E_ARG;
+  if (block < 2 || block > 64) return DFLASH_E_SHAPE;
+  int e = check_selector(m, sel);
+  if (e) return e;
+  e = check_kv(m, kv);
+  if (e) return e;
+  const dflash_model_desc& d = m->d;
+  const int dt = d.dtype, batch = kv->batch, B = block, D = d.hidden, V = d.vocab;
+  const int r = sel->rank, k = sel->top_k;
+  if ((size_t)batch * (1 + (size_t)(B - 1) * k) > ((size_t)1 << 20)) return DFLASH_E_SHAPE;
+  SelWs sw;
+  const size_t need = sel_ws(m, sel, batch, B, sws, &sw);
+  if (!sws || sws_bytes < need) return DFLASH_E_WORKSPACE;
+  // the drafter pass and its LM head (logits of positions 1 .. B-1)
+  e = draft_block_impl(m, kv, anchor, block, draft_ids, draft_logits, nullptr, ws, ws_bytes,
+                       stream, Sampling());
+  if (e) return e;
+  StepWs w;
+  step_ws(m, batch, B, kv->max_pages_per_seq * 64, ws, &w);
+  hipStream_t st = (hipStream_t)stream;
+  {  // H(h_t) of every block row: the final RMSNorm on the A side, then W_H
+    GemmArgs g = gemm_args(w.h, D, one_seg(sel->w_h, r, D), batch * B, r, D, d.final_norm,
+                           d.rms_eps, EPI_STORE_F32);
+    g.e.out = sw.hh;
+    g.e.ldo = r;
+    HIPCHK(launch_gemm(dt, g, st));
+  }
+  int chunks = 1;
+  HIPCHK(launch_topk(draft_logits, batch * (B - 1), V, k, sw.keys, &chunks, st));
+  HIPCHK(launch_topk_merge(sw.keys, chunks, k, batch, B, d.embed, D, (int)esz(dt), anchor,
+                           sw.cand, candidates, sw.gather, st));
+  {  // [A | B] of the gathered embedding rows
+    const int msel = batch * (1 + (B - 1) * k);
+    GemmArgs g = gemm_args(sw.gather, D, one_seg(sel->w_ab, 2 * r, D), msel, 2 * r, D, nullptr,
+                           d.rms_eps, EPI_STORE_F32);
+    g.a_bf16 = dt == DFLASH_BF16;
+    g.e.out = sw.P;
+    g.e.ldo = 2 * r;
+    HIPCHK(launch_gemm(dt, g, st));
+  }
+  HIPCHK(launch_select(sw.P, sw.hh, draft_logits, sw.cand, batch, B, k, r, V, sw.S, draft_ids, st));
+  return DFLASH_OK;
 }
 
 int dflash_verify_accept(const dflash_model* m, dflash_kv* kv, const int32_t* anchor,

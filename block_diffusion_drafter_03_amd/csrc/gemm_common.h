@@ -160,7 +160,8 @@ static hipError_t dispatch_gemm(const GemmArgs& ga, hipStream_t st) {
     case EPI_ARGMAX: return norm ? F::template run<float, true, EPI_ARGMAX>(ga, st) : hipErrorInvalidValue;
     case EPI_INJECT_KV: return norm ? F::template run<float, true, EPI_INJECT_KV>(ga, st) : hipErrorInvalidValue;
     case EPI_RESID: return norm ? hipErrorInvalidValue : F::template run<float, false, EPI_RESID>(ga, st);
-    case EPI_STORE_F32: return norm ? hipErrorInvalidValue : F::template run<float, false, EPI_STORE_F32>(ga, st);
+    case EPI_STORE_F32: return norm ? F::template run<float, true, EPI_STORE_F32>(ga, st)
+                                    : F::template run<float, false, EPI_STORE_F32>(ga, st);
     default: return hipErrorInvalidValue;
   }
 }

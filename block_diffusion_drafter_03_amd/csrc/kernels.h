@@ -172,4 +172,16 @@ hipError_t launch_verify_sampled(const float* zt, const float* zd, const int32_t
                                  unsigned counter, const SampleWs& ws, int32_t* tau,
                                  int32_t* next_token, int32_t* err, hipStream_t st);
 
+// DFlash 2 path selector (select.hip).  Top-k keys of every chunk of every logit row
+// (keys [rows][chunks][16]; *chunks returns the chunk count), their merge into candidate
+// ids with the gather of the candidates' and anchors' embedding rows, and the scoring walk.
+hipError_t launch_topk(const float* logits, int rows, int V, int k, unsigned long long* keys,
+                       int* chunks, hipStream_t st);
+hipError_t launch_topk_merge(const unsigned long long* keys, int chunks, int k, int batch, int B,
+                             const void* embed, int D, int esz, const int32_t* anchor,
+                             int32_t* cand, int32_t* cand_out, void* gather, hipStream_t st);
+hipError_t launch_select(const float* P, const float* Hh, const float* logits, const int32_t* cand,
+                         int batch, int B, int k, int r, int V, float* S, int32_t* draft_ids,
+                         hipStream_t st);
+
 }  // namespace dflash

@@ -227,6 +227,35 @@ def verify_sampled(model: Model, kv: PagedKV, anchor, draft_ids, draft_logits, b
     _lib._check(st, "dflash_verify_sampled")
 
 
+class Selector:
+    """DFlash 2 path-selector weights for a drafter: w_a, w_b, w_h [hidden, rank] (the maps
+    A, B, H of the pair score), packed as the library's [rank, hidden] weight rows in the
+    drafter's dtype and layout."""
+
+    def __init__(self, model: Model, w_a, w_b, w_h, top_k=16):
+        mat = frag_pack if model.dtype == torch.bfloat16 else (lambda t: t.contiguous())
+        self.rank = int(w_a.shape[1])
+        self.top_k = int(top_k)
+        self.w_ab = mat(torch.cat([w_a.t(), w_b.t()], 0).to(model.dtype).contiguous())
+        self.w_h = mat(w_h.t().to(model.dtype).contiguous())
+        s = _lib.Selector()
+        s.w_ab, s.w_h = self.w_ab.data_ptr(), self.w_h.data_ptr()
+        s.rank, s.top_k = self.rank, self.top_k
+        self.struct = s
+
+    def workspace_bytes(self, model: Model, batch, block) -> int:
+        return _lib.selector_workspace_bytes(model.handle, self.struct, batch, block)
+
+
+def draft_block_select(model: Model, kv: PagedKV, anchor, block, sel: Selector, draft_ids,
+                       draft_logits, ws: Workspace, sel_ws: Workspace, candidates=None):
+    st = _lib.draft_block_select(model.handle, kv.struct, _ptr(anchor), int(block), sel.struct,
+                                 _ptr(draft_ids), _ptr(draft_logits), _ptr(candidates),
+                                 _ptr(ws.buf), ws.nbytes, _ptr(sel_ws.buf), sel_ws.nbytes,
+                                 _stream())
+    _lib._check(st, "dflash_draft_block_select")
+
+
 def kv_commit(target_kv, draft_kv, tau, block):
     st = _lib.kv_commit(target_kv.struct if target_kv is not None else None,
                         draft_kv.struct if draft_kv is not None else None, _ptr(tau), int(block),

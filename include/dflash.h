@@ -257,6 +257,50 @@ int dflash_verify_sampled(const dflash_model* target, dflash_kv* target_kv,
                           void* stream);
 
 /*
+ * DFlash 2 path selector ([DF] section 7.1, "Problem 1: Selection Headroom"): the drafter
+ * keeps the top_k candidates of each masked position and scores every adjacent pair
+ * (predecessor a, candidate b) as S_t(a, b) = U_t(b) + <A(a) * H(h_t), B(b)>; a greedy walk
+ * from the anchor over the scores picks the drafts.  Readings (the page names the pieces,
+ * not their inputs): U_t(b) = the raw logit z_t(b); A(a) = E[a] W_A and B(b) = E[b] W_B with
+ * E the shared embedding; H(h_t) = RMSNorm(h_t; final norm) W_H with h_t the drafter's final
+ * hidden state (the LM head's input); position 1's predecessor is the anchor, position t's
+ * the candidate chosen at t - 1; candidates are the top_k logits (ties to the lower id), and
+ * the walk's ties go to the lower id.  All scoring is in float32.
+ *
+ * dflash_selector: caller-owned weights in the drafter's dtype and weight layout (the
+ * B-fragment order for bfloat16 models, row-major for float32 ones), K = hidden:
+ *   w_ab  [2 * rank, hidden]: rows 0 .. rank-1 are W_A^T, rows rank .. 2 rank - 1 W_B^T.
+ *   w_h   [rank, hidden]: W_H^T.
+ *   rank  multiple of 16 in [16, 512] (the page's selector uses 256); top_k in [1, 16].
+ *
+ * dflash_selector_workspace_bytes: scratch of the selection (a second workspace, beside the
+ * step workspace of dflash_workspace_bytes); 0 on invalid arguments.
+ *
+ * dflash_draft_block_select: the drafter pass of dflash_draft_block, then the selector.
+ *   draft_ids     device int32 [batch, block-1] (out): the walk's picks.
+ *   draft_logits  device float [batch, block-1, vocab] (out, required): the drafter's logits
+ *                 of positions 1 .. block-1.
+ *   candidates    device int32 [batch, block-1, top_k] (out) or NULL: each position's
+ *                 candidates in descending logit.
+ *   ws / sel_ws   the step workspace and the selector scratch.
+ * 2 <= block <= 64; batch * (1 + (block - 1) * top_k) <= 2^20.
+ */
+typedef struct dflash_selector {
+  const void* w_ab;
+  const void* w_h;
+  int32_t rank;
+  int32_t top_k;
+} dflash_selector;
+
+size_t dflash_selector_workspace_bytes(const dflash_model* draft, const dflash_selector* sel,
+                                       int32_t batch, int32_t block);
+int dflash_draft_block_select(const dflash_model* draft, const dflash_kv* draft_ctx,
+                              const int32_t* anchor, int32_t block, const dflash_selector* sel,
+                              int32_t* draft_ids, float* draft_logits, int32_t* candidates,
+                              void* ws, size_t ws_bytes, void* sel_ws, size_t sel_ws_bytes,
+                              void* stream);
+
+/*
  * Commit / rollback ([DF] section 4.5: accepted tokens are appended, the cycle repeats
  * from the updated context): seq_len[b] += tau[b] in the target cache and in the drafter
  * context (either may be NULL).  Rows written beyond the new length by verify_accept or

@@ -99,6 +99,13 @@ def model_weights(w: Workload, which: str, device="cpu") -> dict:
     return out
 
 
+def selector_weights(w: Workload, rank: int = 256, std: float = WEIGHT_STD, device="cpu") -> dict:
+    """Path-selector maps of the drafter: w_a, w_b, w_h [hidden, rank], N(0, std^2)."""
+    D = w.draft.hidden
+    return {n: normal((D, rank), std, w.cid, f"selector.{n}", device, w.dtype)
+            for n in ("w_a", "w_b", "w_h")}
+
+
 def features(w: Workload, rows: int, device="cpu", tag="feats") -> torch.Tensor:
     """Tapped target features [rows, k*D], N(0, 1)."""
     return normal((rows, w.n_taps * w.draft.hidden), 1.0, w.cid, tag, device, w.dtype)

@@ -128,3 +128,27 @@ def inject_all(setup: Setup, kv, feats_per_seq, ws, chunk=None):
 def read_cache(kv, layer, b, n):
     K, V = kv.read_dense(layer, b, n)
     return synth.to_numpy(K), synth.to_numpy(V)
+
+
+def check_selection(g_ids, g_cand, o_ids, o_cand, o_rows, z, top_k, tie, what):
+    """Path-selector outputs of one sequence against the oracle's.  Candidate sets are
+    compared where the oracle's top_k-th and next logits differ by >= tie; the walk's picks
+    in order, a difference being allowed only where the oracle decides the pick by a
+    near-tie of scores or where the candidate sets differ at a near-tie of the boundary
+    (the walk stops being compared there: later picks depend on it).  Returns (candidate
+    positions checked, picks checked)."""
+    cand_checked = walk_checked = 0
+    for t in range(len(o_ids)):
+        srt = np.sort(z[t])[::-1]
+        if srt[top_k - 1] - srt[top_k] >= tie:
+            assert set(g_cand[t]) == set(o_cand[t]), f"{what} position {t + 1} candidates"
+            cand_checked += 1
+    for t in range(len(o_ids)):
+        if g_ids[t] == o_ids[t]:
+            walk_checked += 1
+            continue
+        srt = np.sort(z[t])[::-1]
+        boundary_tie = set(g_cand[t]) != set(o_cand[t]) and srt[top_k - 1] - srt[top_k] < tie
+        assert boundary_tie or float(O.top2_gap(o_rows[t])) < tie, f"{what} position {t + 1}"
+        break
+    return cand_checked, walk_checked

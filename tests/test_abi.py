@@ -116,6 +116,27 @@ def test_workspace_bytes_and_entry_validation():
                   1 << 30, None) == -1
         assert vs(h, ctypes.byref(kv), one, one, one, 65, 1.0, 1, 0, None, one, one, one, one,
                   1 << 30, None) == -2
+        # path selector: weights, rank (multiple of 16, <= 512), top_k (1 .. 16), logits buffer,
+        # block >= 2, its own scratch
+        sel = _lib.Selector()
+        sel.w_ab, sel.w_h, sel.rank, sel.top_k = 0x5000, 0x6000, 256, 16
+        assert _lib.selector_workspace_bytes(h, sel, 1, 16) > 0
+        assert _lib.selector_workspace_bytes(h, sel, 1, 1) == 0
+        dsel = L.dflash_draft_block_select
+
+        def call(block=16, logits=one, sel_bytes=1 << 30):
+            return dsel(h, ctypes.byref(kv), one, block, ctypes.byref(sel), one, logits, None, one,
+                        1 << 30, one, sel_bytes, None)
+        assert call(logits=None) == -1
+        assert call(block=1) == -2
+        assert call(sel_bytes=16) == -5
+        for field, bad, code in (("rank", 100, -2), ("rank", 1024, -2), ("top_k", 0, -2),
+                                 ("top_k", 17, -2), ("w_h", 0, -1)):
+            keep = getattr(sel, field)
+            setattr(sel, field, bad)
+            assert call() == code, field
+            assert _lib.selector_workspace_bytes(h, sel, 1, 16) == 0
+            setattr(sel, field, keep)
     finally:
         _lib.model_destroy(h)
 

@@ -26,7 +26,7 @@ import oracle as O
 import synth
 
 from harness import (DEV, NEAR_TIE, TOL, Setup, assert_accept, assert_close, assert_ids,
-                     assert_rows_close, read_cache)
+                     assert_rows_close, check_selection, read_cache)
 from block_diffusion_drafter_03_amd import runtime as rt
 
 pytestmark = pytest.mark.gpu
@@ -102,6 +102,24 @@ def test_qwen3_8b_batch1_ctx4k():
     sel = gaps >= NEAR_TIE
     assert sel.sum() >= B - 4
     assert np.array_equal(ids[0].cpu().numpy()[sel], o_ids[sel]), "cfg 4k sampled draft ids"
+    # DFlash 2 path selector at its full size: rank 256, top-16 candidates
+    sw = synth.selector_weights(w, rank=256, device=DEV)
+    w_a, w_b = ((sw[k].float() * 50.0).to(torch.bfloat16) for k in ("w_a", "w_b"))
+    selr = rt.Selector(S.draft, w_a, w_b, sw["w_h"], top_k=16)
+    sws = rt.Workspace(selr.workspace_bytes(S.draft, 1, B), DEV)
+    ids = torch.zeros(1, B - 1, dtype=torch.int32, device=DEV)
+    cand = torch.zeros(1, B - 1, 16, dtype=torch.int32, device=DEV)
+    rt.draft_block_select(S.draft, kv, anchor, B, selr, ids, zd, ws, sws, candidates=cand)
+    torch.cuda.synchronize()
+    assert kv.err.item() == 0
+    _, o_z, o_hid = O.draft_block(S.np_dw, S.np_shared, w.draft, ctx, int(anchor[0]), n, B, store=S.store)
+    o_ids, o_cand, o_rows = O.select_path(o_z, o_hid[-1][1:], int(anchor[0]), S.np_shared["embed"],
+                                          S.np_dw["g_f"], w.draft.rms_eps, synth.to_numpy(w_a),
+                                          synth.to_numpy(w_b), synth.to_numpy(sw["w_h"]), top_k=16)
+    assert_rows_close(zd[0].cpu().numpy(), o_z, TOLB, "cfg 4k selector draft logits")
+    c, k = check_selection(ids[0].cpu().numpy(), cand[0].cpu().numpy(), o_ids, o_cand, o_rows, o_z, 16,
+                           NEAR_TIE, "cfg 4k selector")
+    assert c >= (B - 1) // 3 and k >= (B - 1) // 2, (c, k)
 
 
 def test_qwen3_8b_batch16_paged_ragged():
