@@ -149,6 +149,44 @@ def inject(feats, positions, w, shape, dt=np.float32, store=None):
 # Decoder layer shared by the drafter (bidirectional block) and the target (causal block)
 
 
+# DFlash 2 two-tap dynamic convolution  [DF §7.1, "Problem 2: Suffix Decay"]: a depthwise
+# convolution reaching one position back, Conv(x)_t = k_{t,0} * x_t + k_{t,1} * x_{t-1},
+# inserted before and after each attention and feed-forward sublayer; each coefficient is a
+# learned base kernel plus a content-dependent correction; the first position reads the last
+# verified token and every later one its predecessor.  Readings (the page gives the formula,
+# the placement and the parameter count, 16.5M for the 5-layer Qwen3.5-4B drafter):
+#   * placement: inside each sublayer's branch - on the normalised input (after the
+#     sublayer's RMSNorm, "before") and on the sublayer's output (before the residual add,
+#     "after"): h <- h + Conv_post(Sub(Conv_pre(RMSNorm(h))));
+#   * correction: linear in the convolution's own input x_t, one coefficient per tap per
+#     group of 16 channels: k_{t,j}[c] = base_j[c] + (x_t W_k)[2 (c // 16) + j], W_k [D, D/8]
+#     (columns interleave the taps of each group).  Per convolution 2D + D * D/8 parameters:
+#     for D = 2560 and 4 convolutions in each of 5 layers, 20 x 824,320 = 16.49M - the page's
+#     16.5M;
+#   * the block's first row is the anchor, the last verified token; it reads itself
+#     (x_{-1} = x_0), every later row its predecessor.
+
+
+def dconv(x, base, w_k, dt=np.float32):
+    """Two-tap dynamic convolution of the block rows x [T, D] (readings above).  base [2, D],
+    w_k [D, D/8]."""
+    x = np.asarray(x, dtype=dt)
+    T, D = x.shape
+    corr = x @ np.asarray(w_k, dtype=dt)                 # [T, 2 * D/16]
+    grp = np.arange(D) // 16
+    k0 = np.asarray(base[0], dtype=dt)[None, :] + corr[:, 2 * grp]
+    k1 = np.asarray(base[1], dtype=dt)[None, :] + corr[:, 2 * grp + 1]
+    prev = np.concatenate([x[:1], x[:-1]], axis=0)      # row 0 reads itself
+    return k0 * x + k1 * prev
+
+
+def _conv(w, i, which, x, dt):
+    key = f"L{i}.dconv_{which}"
+    if key + ".base" not in w:
+        return x
+    return dconv(x, w[key + ".base"], w[key + ".w_k"], dt)
+
+
 def decoder_layer(h, w, i, shape, positions, ctx_k, ctx_v, causal, dt=np.float32, store=None):
     """One pre-norm decoder layer over the block rows h [T, D].
 
@@ -158,11 +196,13 @@ def decoder_layer(h, w, i, shape, positions, ctx_k, ctx_v, causal, dt=np.float32
     ([TRY] Fig. 1, causal attention in the main model).  The context rows take no part
     in Q, O, the residual or the FFN ([DF §4.3]).  FFN: SwiGLU (the drafter is
     described as Qwen-style in [TRY]'s appendix).  The block's K/V enter attention as
-    stored (`store`).  Returns (h_out, k_blk, v_blk)."""
+    stored (`store`).  A DFlash 2 drafter's weights may hold the two-tap convolutions
+    (keys L{i}.dconv_{pre_attn,post_attn,pre_ffn,post_ffn}.{base,w_k}).  Returns (h_out,
+    k_blk, v_blk)."""
     T = h.shape[0]
     Hq, Hkv, d = shape.n_q_heads, shape.n_kv_heads, shape.head_dim
     G = Hq // Hkv
-    u = rmsnorm(h, w[f"L{i}.g_in"], shape.rms_eps, dt)
+    u = _conv(w, i, "pre_attn", rmsnorm(h, w[f"L{i}.g_in"], shape.rms_eps, dt), dt)
     q = (u @ np.asarray(w[f"L{i}.wq"], dtype=dt).T).reshape(T, Hq, d)
     kb = (u @ np.asarray(w[f"L{i}.wk"], dtype=dt).T).reshape(T, Hkv, d)
     vb = (u @ np.asarray(w[f"L{i}.wv"], dtype=dt).T).reshape(T, Hkv, d)
@@ -183,10 +223,10 @@ def decoder_layer(h, w, i, shape, positions, ctx_k, ctx_v, causal, dt=np.float32
             Kh, Vh = kb[:, kv, :], vb[:, kv, :]
         for j in range(kv * G, (kv + 1) * G):
             o[:, j, :] = attention(q[:, j, :], Kh, Vh, visible, dt)
-    h = h + o.reshape(T, Hq * d) @ np.asarray(w[f"L{i}.wo"], dtype=dt).T
-    u = rmsnorm(h, w[f"L{i}.g_post"], shape.rms_eps, dt)
+    h = h + _conv(w, i, "post_attn", o.reshape(T, Hq * d) @ np.asarray(w[f"L{i}.wo"], dtype=dt).T, dt)
+    u = _conv(w, i, "pre_ffn", rmsnorm(h, w[f"L{i}.g_post"], shape.rms_eps, dt), dt)
     a = silu(u @ np.asarray(w[f"L{i}.wg"], dtype=dt).T) * (u @ np.asarray(w[f"L{i}.wu"], dtype=dt).T)
-    h = h + a @ np.asarray(w[f"L{i}.wd"], dtype=dt).T
+    h = h + _conv(w, i, "post_ffn", a @ np.asarray(w[f"L{i}.wd"], dtype=dt).T, dt)
     return h, kb, vb
 
 

@@ -9,6 +9,7 @@ the very same values (the oracle receives host copies upcast to float32).
 from .configs import (ModelShape, Workload, WORKLOADS, workload, TINY, MID,
                       QWEN3_8B_DRAFT, QWEN3_8B_TARGET)
 from .fixtures import (seed_of, normal, uniform_ints, model_weights, shared_weights, selector_weights,
+                       dconv_shapes, dconv_weights, DCONV_NAMES,
                        features, anchors, ctx_lengths, synthetic_ctx_kv, to_numpy,
                        splitmix64, force_coins, forced_drafts, prompt_tokens)
 

@@ -106,6 +106,32 @@ def selector_weights(w: Workload, rank: int = 256, std: float = WEIGHT_STD, devi
             for n in ("w_a", "w_b", "w_h")}
 
 
+DCONV_NAMES = ("pre_attn", "post_attn", "pre_ffn", "post_ffn")
+
+
+def dconv_shapes(hidden: int) -> dict:
+    """Shapes of one two-tap dynamic convolution: base [2, D] and the correction map
+    W_k [D, D/8] (one coefficient per tap per group of 16 channels)."""
+    return {"base": (2, hidden), "w_k": (hidden, hidden // 8)}
+
+
+def dconv_weights(w: Workload, device="cpu", base1_std: float = 0.5, wk_scale: float = 0.3) -> dict:
+    """Two-tap convolutions of every drafter layer (keys L{i}.dconv_{name}.{base,w_k}):
+    base_0 = 1 + N(0, 0.1^2), base_1 = N(0, base1_std^2), W_k = N(0, (wk_scale^2 / D))."""
+    m = w.draft
+    D = m.hidden
+    out = {}
+    for i in range(m.n_layers):
+        for name in DCONV_NAMES:
+            key = f"L{i}.dconv_{name}"
+            b0 = 1.0 + normal((1, D), 0.1, w.cid, key + ".b0", device)
+            b1 = normal((1, D), base1_std, w.cid, key + ".b1", device)
+            out[key + ".base"] = torch.cat([b0, b1], 0).to(_storage(w.dtype))
+            out[key + ".w_k"] = normal(dconv_shapes(D)["w_k"], wk_scale / D ** 0.5, w.cid, key + ".w_k",
+                                       device, w.dtype)
+    return out
+
+
 def features(w: Workload, rows: int, device="cpu", tag="feats") -> torch.Tensor:
     """Tapped target features [rows, k*D], N(0, 1)."""
     return normal((rows, w.n_taps * w.draft.hidden), 1.0, w.cid, tag, device, w.dtype)
