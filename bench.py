@@ -225,6 +225,8 @@ def main():
                               D, T, dev)
     # DFlash 2 path selector (rank 256, top-16) on the same drafter and context
     selector = selector_timing(w, draft, dkv, ws_d, state["anchor"], B, D, dev)
+    # DFlash 2 two-tap convolutions around every sublayer: the same drafter with them
+    dconv = dconv_timing(w, dw, shared, dkv, state["anchor"], B, D, n, dev)
     hbm_bytes_draft = (D.n_layers * ((D.n_q_heads + 2 * D.n_kv_heads) * D.head_dim * D.hidden
                                      + D.hidden * D.n_q_heads * D.head_dim + 3 * D.ffn * D.hidden) * 2
                        + D.vocab * D.hidden * 2 + D.n_layers * n * D.n_kv_heads * D.head_dim * 2 * 2)
@@ -268,6 +270,7 @@ def main():
         "block_sweep": block_sweep,
         "sampling_t1": sampling,
         "path_selector": selector,
+        "dconv": dconv,
     }
     if not args.no_context_sweep:
         out["context_sweep"] = context_sweep(draft, D, B, dev)
@@ -487,6 +490,35 @@ def selector_timing(w, draft, dkv, ws_d, anchor, B, D, dev, reps=10):
         out["us_per_draft_block_" + name] = round(e0.elapsed_time(e1) * 1e3 / reps, 2)
     assert int(dkv.err.item()) == 0
     out["overhead_frac"] = round(out["us_per_draft_block_selector"] / out["us_per_draft_block_greedy"] - 1, 4)
+    return out
+
+
+def dconv_timing(w, dw, shared, dkv, anchor, B, D, n, dev, reps=10):
+    """µs per draft block of the drafter with DFlash 2 convolutions (synthetic weights)
+    against the plain drafter, on the same injected context."""
+    import torch
+    import synth
+    from block_diffusion_drafter_03_amd import runtime as rt
+
+    conv = rt.Model(D, dw, shared, n_taps=w.n_taps, draft=True, dconv=synth.dconv_weights(w, dev))
+    plain = rt.Model(D, dw, shared, n_taps=w.n_taps, draft=True)
+    ws = rt.Workspace(conv.workspace_bytes(1, B, dkv.capacity), dev)
+    ids = torch.zeros(1, B - 1, dtype=torch.int32, device=dev)
+    out = {}
+    for name, model in (("plain", plain), ("dconv", conv)):
+        for _ in range(3):
+            rt.draft_block(model, dkv, anchor, B, ids, ws)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            rt.draft_block(model, dkv, anchor, B, ids, ws)
+        e1.record()
+        torch.cuda.synchronize()
+        out["us_per_draft_block_" + name] = round(e0.elapsed_time(e1) * 1e3 / reps, 2)
+    assert int(dkv.err.item()) == 0
+    out["overhead_frac"] = round(out["us_per_draft_block_dconv"] / out["us_per_draft_block_plain"] - 1, 4)
+    conv.close()
+    plain.close()
     return out
 
 

@@ -33,7 +33,7 @@ class ModelDesc(ctypes.Structure):
                 ("rope_base", c_float), ("mask_token_id", c_int32), ("n_taps", c_int32),
                 ("tap_layers", POINTER(c_int32)), ("embed", c_void_p), ("lm_head", c_void_p),
                 ("final_norm", c_void_p), ("w_c", c_void_p), ("g_c", c_void_p),
-                ("layer_w", POINTER(c_void_p))]
+                ("layer_w", POINTER(c_void_p)), ("dconv", POINTER(c_void_p))]
 
 
 class KV(ctypes.Structure):

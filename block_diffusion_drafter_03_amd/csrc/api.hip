@@ -28,6 +28,7 @@ struct dflash_model {
   dflash_model_desc d;
   std::vector<const void*> layer_w;
   std::vector<int32_t> taps;
+  std::vector<const void*> dconv;   // empty, or [n_layers * 8] (DFlash 2 convolutions)
 };
 
 namespace {
@@ -65,6 +66,8 @@ struct StepWs {
   unsigned long long* keys;
   float2* rope;
   SampleWs smp;       // sampling verification scratch
+  float* xa;          // DFlash 2 convolutions: a convolution's input or output [Mp, D]
+  float* dk;          // and its correction coefficients [M, D / 8]
   AttnPlan plan;
 };
 
@@ -89,6 +92,9 @@ size_t step_ws(const dflash_model* m, int batch, int B, int ctx_cap, void* base,
   t.smp.lse = (float*)cv.take(srows * 4);
   t.smp.acc = (int32_t*)cv.take((size_t)batch * 4);
   t.smp.keys = (unsigned long long*)cv.take((size_t)batch * SAMPLE_MAX_CHUNKS * 8);
+  const bool dc = !m->dconv.empty();
+  t.xa = (float*)cv.take(dc ? (size_t)Mp * D * 4 : 0);
+  t.dk = (float*)cv.take(dc ? (size_t)M * (D / 8) * 4 : 0);
   if (w) *w = t;
   return cv.off;
 }
@@ -230,11 +236,42 @@ int run_layers(const dflash_model* m, const dflash_kv* kv, int batch, int B, con
   const int Nqkv = (Hq + 2 * Hkv) * hd;
   const float eps = d.rms_eps;
   const int afrag = dt == DFLASH_BF16;
+  const bool dc = !m->dconv.empty();
+  if (dc && feats_out) return DFLASH_E_ARG;   // the convolutions belong to a drafter
+  // DFlash 2 convolution `c` of layer l: its correction GEMM, then the convolution itself.
+  // pre: w.xa = Conv(RMSNorm(h; g_norm)); post: h += Conv(w.xa) (+ the hidden_dbg copy).
+  auto conv = [&](int l, int c, const void* g_norm, bool post, float* hdbg) -> int {
+    const float* x = post ? w.xa : w.h;
+    GemmArgs g = gemm_args(x, D, one_seg(m->dconv[l * 8 + 2 * c + 1], D / 8, D), M, D / 8, D,
+                           g_norm, eps, EPI_STORE_F32);
+    g.e.out = w.dk;
+    g.e.ldo = D / 8;
+    HIPCHK(launch_gemm(dt, g, st));
+    DconvArgs a;
+    a.x = x;
+    a.norm_g = g_norm;
+    a.eps = eps;
+    a.corr = w.dk;
+    a.base = m->dconv[l * 8 + 2 * c];
+    a.M = M;
+    a.D = D;
+    a.B = B;
+    a.afrag = afrag;
+    a.bf16 = dt == DFLASH_BF16;
+    a.accumulate = post;
+    a.out = post ? w.h : w.xa;
+    a.hdbg = hdbg;
+    HIPCHK(launch_dconv(a, st));
+    return DFLASH_OK;
+  };
   for (int l = 0; l < d.n_layers; ++l) {
     const KvLayer kvl = layer_view(kv, l);
-    {  // QKV projection with RMSNorm(g_in) on the A side; RoPE / layout epilogue
-      GemmArgs g = gemm_args(w.h, D, one_seg(W(m, l, DFLASH_W_QKV), Nqkv, D), M, Nqkv, D,
-                             W(m, l, DFLASH_W_G_IN), eps, EPI_QKV);
+    if (dc)
+      if (int s = conv(l, DFLASH_DCONV_PRE_ATTN, W(m, l, DFLASH_W_G_IN), false, nullptr)) return s;
+    {  // QKV projection with RMSNorm(g_in) on the A side (or of the convolved input);
+       // RoPE / layout epilogue
+      GemmArgs g = gemm_args(dc ? w.xa : w.h, D, one_seg(W(m, l, DFLASH_W_QKV), Nqkv, D), M, Nqkv, D,
+                             dc ? nullptr : W(m, l, DFLASH_W_G_IN), eps, EPI_QKV);
       EpiArgs& e = g.e;
       e.B = B;
       e.Bp = Bp;
@@ -261,29 +298,39 @@ int run_layers(const dflash_model* m, const dflash_kv* kv, int batch, int B, con
       HIPCHK(launch_attention(dt, w.plan, w.q, w.kblk, w.vblkT, kvl, batch, B, Bp, Hq, Hkv, hd,
                               causal, w.part, w.o, afrag, st));
     }
-    {  // O projection + residual
+    {  // O projection + residual (with the convolutions: the output, convolved below)
       GemmArgs g = gemm_args(w.o, Hq * hd, one_seg(W(m, l, DFLASH_W_O), D, Hq * hd), M, D,
-                             Hq * hd, nullptr, eps, EPI_RESID);
+                             Hq * hd, nullptr, eps, dc ? EPI_STORE_F32 : EPI_RESID);
       g.e.h = w.h;
       g.e.ldh = D;
+      g.e.out = w.xa;
+      g.e.ldo = D;
       g.e.afrag = afrag;
       if (int s = run_gemm(DFLASH_KERNEL_GEMM_O, dt, g, st)) return s;
     }
-    {  // gate/up with RMSNorm(g_post) on the A side; SwiGLU epilogue
-      GemmArgs g = gemm_args(w.h, D, one_seg(W(m, l, DFLASH_W_GATE_UP), 2 * F, D), M, 2 * F, D,
-                             W(m, l, DFLASH_W_G_POST), eps, EPI_SWIGLU);
+    if (dc) {
+      if (int s = conv(l, DFLASH_DCONV_POST_ATTN, nullptr, true, nullptr)) return s;
+      if (int s = conv(l, DFLASH_DCONV_PRE_FFN, W(m, l, DFLASH_W_G_POST), false, nullptr)) return s;
+    }
+    {  // gate/up with RMSNorm(g_post) on the A side (or of the convolved input); SwiGLU
+      GemmArgs g = gemm_args(dc ? w.xa : w.h, D, one_seg(W(m, l, DFLASH_W_GATE_UP), 2 * F, D), M,
+                             2 * F, D, dc ? nullptr : W(m, l, DFLASH_W_G_POST), eps, EPI_SWIGLU);
       g.e.act = w.act;
       g.e.F = F;
       g.e.afrag = afrag;
       if (int s = run_gemm(DFLASH_KERNEL_GEMM_GATE_UP, dt, g, st)) return s;
     }
-    {  // down projection + residual (+ tap / debug copies)
+    float* hdbg_l = hidden_dbg ? hidden_dbg + (size_t)(l + 1) * M * D : nullptr;
+    {  // down projection + residual (+ tap / debug copies; with the convolutions: the output,
+       // convolved below)
       GemmArgs g = gemm_args(w.act, F, one_seg(W(m, l, DFLASH_W_DOWN), D, F), M, D, F, nullptr, eps,
-                             EPI_RESID);
+                             dc ? EPI_STORE_F32 : EPI_RESID);
       g.e.h = w.h;
       g.e.ldh = D;
+      g.e.out = w.xa;
+      g.e.ldo = D;
       g.e.afrag = afrag;
-      g.e.hdbg = hidden_dbg ? hidden_dbg + (size_t)(l + 1) * M * D : nullptr;
+      g.e.hdbg = dc ? nullptr : hdbg_l;
       if (feats_out) {
         for (size_t t = 0; t < m->taps.size(); ++t)
           if (m->taps[t] == l) {
@@ -294,6 +341,8 @@ int run_layers(const dflash_model* m, const dflash_kv* kv, int batch, int B, con
       }
       if (int s = run_gemm(DFLASH_KERNEL_GEMM_DOWN, dt, g, st)) return s;
     }
+    if (dc)
+      if (int s = conv(l, DFLASH_DCONV_POST_FFN, nullptr, true, hdbg_l)) return s;
   }
   return DFLASH_OK;
 }
@@ -352,6 +401,11 @@ int validate_model(const dflash_model_desc* d) {
   if (d->tap_layers)
     for (int t = 0; t < d->n_taps; ++t)
       if (d->tap_layers[t] < 0 || d->tap_layers[t] >= d->n_layers) return DFLASH_E_ARG;
+  if (d->dconv) {
+    if (d->tap_layers || d->hidden % 128) return DFLASH_E_SHAPE;   // drafter only
+    for (int i = 0; i < d->n_layers * 8; ++i)
+      if (!d->dconv[i]) return DFLASH_E_ARG;
+  }
   return DFLASH_OK;
 }
 
@@ -418,8 +472,10 @@ int dflash_model_create(const dflash_model_desc* desc, dflash_model** out) {
   m->d = *desc;
   m->layer_w.assign(desc->layer_w, desc->layer_w + (size_t)desc->n_layers * DFLASH_LAYER_TENSORS);
   if (desc->tap_layers) m->taps.assign(desc->tap_layers, desc->tap_layers + desc->n_taps);
+  if (desc->dconv) m->dconv.assign(desc->dconv, desc->dconv + (size_t)desc->n_layers * 8);
   m->d.layer_w = nullptr;
   m->d.tap_layers = nullptr;
+  m->d.dconv = nullptr;
   *out = m;
   return DFLASH_OK;
 }

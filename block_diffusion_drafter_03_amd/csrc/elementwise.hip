@@ -320,4 +320,75 @@ hipError_t launch_verify_sampled(const float* zt, const float* zd, const int32_t
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------------------
+// DFlash 2 two-tap dynamic convolution ([DF] section 7.1, Problem 2): grid (rows, D / 256),
+// one channel per thread; with the norm each workgroup first sums the squares of its row
+// and of the row it reads (16 loads per thread in flight at once).
+#define DCONV_CH 256
+__global__ __launch_bounds__(DCONV_CH) void dconv_kernel(DconvArgs a) {
+  __shared__ float red[8];
+  const int r = blockIdx.x, D = a.D, j = r % a.B;
+  const int p = j == 0 ? r : r - 1;
+  auto at = [&](int row, int c) -> size_t {
+    return a.afrag ? afrag_off(row, c, D >> 5) : (size_t)row * D + c;
+  };
+  float sr = 1.f, sp = 1.f;
+  if (a.norm_g) {
+    float s0 = 0.f, s1 = 0.f;
+    for (int c0 = threadIdx.x; c0 < D; c0 += DCONV_CH * 8) {
+      float x0[8], x1[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int c = min(c0 + u * DCONV_CH, D - 1);
+        x0[u] = a.x[at(r, c)];
+        x1[u] = a.x[at(p, c)];
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (c0 + u * DCONV_CH < D) {
+          s0 += x0[u] * x0[u];
+          s1 += x1[u] * x1[u];
+        }
+    }
+    s0 = block_sum(s0, red);
+    s1 = block_sum(s1, red + 4);
+    sr = 1.0f / sqrtf(s0 / (float)D + a.eps);
+    sp = 1.0f / sqrtf(s1 / (float)D + a.eps);
+  }
+  const int c = blockIdx.y * DCONV_CH + threadIdx.x;
+  if (c >= D) return;
+  float xr = a.x[at(r, c)] * sr, xp = a.x[at(p, c)] * sp;
+  float b0, b1;
+  if (a.bf16) {
+    b0 = (float)((const bf16*)a.base)[c];
+    b1 = (float)((const bf16*)a.base)[D + c];
+    if (a.norm_g) {
+      const float g = (float)((const bf16*)a.norm_g)[c];
+      xr *= g;
+      xp *= g;
+    }
+  } else {
+    b0 = ((const float*)a.base)[c];
+    b1 = ((const float*)a.base)[D + c];
+    if (a.norm_g) {
+      const float g = ((const float*)a.norm_g)[c];
+      xr *= g;
+      xp *= g;
+    }
+  }
+  const float* cr = a.corr + (size_t)r * (D >> 3) + 2 * (c >> 4);
+  const float y = (b0 + cr[0]) * xr + (b1 + cr[1]) * xp;
+  const size_t o = at(r, c);
+  const float v = a.accumulate ? a.out[o] + y : y;
+  a.out[o] = v;
+  if (a.hdbg) a.hdbg[(size_t)r * D + c] = v;
+}
+
+hipError_t launch_dconv(const DconvArgs& a, hipStream_t st) {
+  if (a.M <= 0) return hipSuccess;
+  if (a.D % 16 || a.B < 1) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(dconv_kernel, dim3(a.M, (a.D + DCONV_CH - 1) / DCONV_CH), dim3(DCONV_CH), 0, st, a);
+  return hipGetLastError();
+}
+
 }  // namespace dflash

@@ -155,8 +155,10 @@ static hipError_t dispatch_gemm(const GemmArgs& ga, hipStream_t st) {
     return F::template run<bf16, false, EPI_STORE_F32>(ga, st);
   }
   switch (ga.e.kind) {
-    case EPI_QKV: return norm ? F::template run<float, true, EPI_QKV>(ga, st) : hipErrorInvalidValue;
-    case EPI_SWIGLU: return norm ? F::template run<float, true, EPI_SWIGLU>(ga, st) : hipErrorInvalidValue;
+    case EPI_QKV: return norm ? F::template run<float, true, EPI_QKV>(ga, st)
+                              : F::template run<float, false, EPI_QKV>(ga, st);
+    case EPI_SWIGLU: return norm ? F::template run<float, true, EPI_SWIGLU>(ga, st)
+                                 : F::template run<float, false, EPI_SWIGLU>(ga, st);
     case EPI_ARGMAX: return norm ? F::template run<float, true, EPI_ARGMAX>(ga, st) : hipErrorInvalidValue;
     case EPI_INJECT_KV: return norm ? F::template run<float, true, EPI_INJECT_KV>(ga, st) : hipErrorInvalidValue;
     case EPI_RESID: return norm ? hipErrorInvalidValue : F::template run<float, false, EPI_RESID>(ga, st);

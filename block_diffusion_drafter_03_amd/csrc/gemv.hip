@@ -237,6 +237,10 @@ struct GemvLaunch {
     // is in flight at once; otherwise one workgroup per CU with the A slice stationary,
     // walking the tiles (the deferred epilogue buffer bounds the tiles per workgroup)
     if (n_tiles <= gemv_stream_tiles() || ga.K != 32 * GEMV_NW * GEMV_CH) {
+      // very few tiles (a quarter of the CUs or fewer, e.g. the 512-column correction maps
+      // of the convolutions): 16 waves split K, so each wave's share is one chunk in flight
+      if (n_tiles * 4 <= num_cus() && ga.K % (32 * 16) == 0)
+        return launch1(gemm_gemv_bf16<TA, 16, NORM, false, KIND>, dim3(n_tiles), dim3(16 * 64), st, ga);
       int grid = n_tiles;
       if (grid > 8 * num_cus()) grid = 8 * num_cus();
       if (KIND != EPI_ARGMAX && grid * GEMV_MAX_TILES < n_tiles)

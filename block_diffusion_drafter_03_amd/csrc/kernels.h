@@ -172,6 +172,23 @@ hipError_t launch_verify_sampled(const float* zt, const float* zd, const int32_t
                                  unsigned counter, const SampleWs& ws, int32_t* tau,
                                  int32_t* next_token, int32_t* err, hipStream_t st);
 
+// DFlash 2 two-tap dynamic convolution of M block rows (B rows per sequence):
+// out[r] (=, or += when accumulate) k0 * x_r + k1 * x_p, p = r - 1 (the sequence's first row:
+// p = r), k_j[c] = base[j][c] + corr[r][2 (c / 16) + j].  With norm_g, x = RMSNorm(x; norm_g)
+// (each row's own rstd).  x, out: float [M, D], A-fragment order when afrag, else row-major;
+// hdbg: optional row-major copy of out after the add.
+struct DconvArgs {
+  const float* x;
+  const void* norm_g;
+  float eps;
+  const float* corr;   // [M, D / 8] row-major
+  const void* base;    // [2, D] (model dtype)
+  int M, D, B, afrag, bf16, accumulate;
+  float* out;
+  float* hdbg;
+};
+hipError_t launch_dconv(const DconvArgs& a, hipStream_t st);
+
 // DFlash 2 path selector (select.hip).  Top-k keys of every chunk of every logit row
 // (keys [rows][chunks][16]; *chunks returns the chunk count), their merge into candidate
 // ids with the gather of the candidates' and anchors' embedding rows, and the scoring walk.

@@ -61,7 +61,8 @@ def frag_pack(w):
 
 
 class Model:
-    """A drafter (``draft=True``: needs W_c and g_c) or a target model.
+    """A drafter (``draft=True``: needs W_c and g_c) or a target model; a DFlash 2 drafter
+    also takes its two-tap convolutions (``dconv``: keys L{i}.dconv_{name}.{base,w_k}).
 
     ``weights`` uses the per-layer names L{i}.{g_in,wq,wk,wv,wo,g_post,wg,wu,wd}, plus g_f
     and (drafter) w_c, g_c; ``shared`` holds embed and lm_head.  Q/K/V and gate/up are
@@ -69,7 +70,7 @@ class Model:
     every matrix but the embedding into the B-fragment order (see include/dflash.h)."""
 
     def __init__(self, shape, weights: dict, shared: dict, n_taps: int, taps=None,
-                 draft: bool = True):
+                 draft: bool = True, dconv: dict = None):
         self.shape = shape
         dtype = shared["embed"].dtype
         self.dtype = dtype
@@ -108,6 +109,18 @@ class Model:
             d.w_c = w_c.data_ptr()
             d.g_c = weights["g_c"].data_ptr()
         d.layer_w = ctypes.cast(self._lw, POINTER(c_void_p))
+        if dconv is not None:
+            # DFlash 2 convolutions: base [2, D] as is, W_k [D, D/8] as weight rows [D/8, D]
+            cp = []
+            for i in range(shape.n_layers):
+                for name in ("pre_attn", "post_attn", "pre_ffn", "post_ffn"):
+                    key = f"L{i}.dconv_{name}"
+                    base = dconv[key + ".base"].to(dtype).contiguous()
+                    w_k = mat(dconv[key + ".w_k"].t().to(dtype).contiguous())
+                    self._keep += [base, w_k]
+                    cp += [base.data_ptr(), w_k.data_ptr()]
+            self._dc = (c_void_p * len(cp))(*cp)
+            d.dconv = ctypes.cast(self._dc, POINTER(c_void_p))
         self.desc = d
         self.handle = _lib.model_create(d)
         self.n_taps = n_taps

@@ -112,7 +112,30 @@ typedef struct dflash_model_desc {
   const void* w_c;              /* drafter: fusion weight W_c [hidden, n_taps * hidden]       */
   const void* g_c;              /* drafter: gain of the RMSNorm after W_c [hidden]            */
   const void* const* layer_w;   /* host array [n_layers * DFLASH_LAYER_TENSORS]               */
+  const void* const* dconv;     /* NULL, or a DFlash 2 drafter's two-tap convolutions: host
+                                   array [n_layers * 8], see DFLASH_DCONV_* below            */
 } dflash_model_desc;
+
+/*
+ * DFlash 2 two-tap dynamic convolution ([DF] section 7.1, "Problem 2: Suffix Decay"):
+ * Conv(x)_t = k_{t,0} * x_t + k_{t,1} * x_{t-1}, depthwise, before and after each attention
+ * and feed-forward sublayer; each coefficient is a base kernel plus a content-dependent
+ * correction.  Readings: "before" acts on the sublayer's normalised input, "after" on its
+ * output ahead of the residual add (h <- h + Conv_post(Sub(Conv_pre(RMSNorm(h))))); the
+ * correction is linear in the convolution's input, one coefficient per tap per group of 16
+ * channels: k_{t,j}[c] = base[j][c] + (x_t W_k^T)[2 (c / 16) + j]; the block's first row
+ * (the anchor) reads itself, every later row its predecessor in the block.
+ * dconv[l * 8 + 2 * conv] = base [2, hidden] (model dtype, row j = tap j) and
+ * dconv[l * 8 + 2 * conv + 1] = W_k [hidden / 8, hidden] in the weight layout (row 2g + j =
+ * tap j of channel group g), conv = DFLASH_DCONV_*.  Drafter only (no taps): hidden must be a
+ * multiple of 128.
+ */
+enum {
+  DFLASH_DCONV_PRE_ATTN = 0,
+  DFLASH_DCONV_POST_ATTN = 1,
+  DFLASH_DCONV_PRE_FFN = 2,
+  DFLASH_DCONV_POST_FFN = 3
+};
 
 /*
  * Paged KV cache (the target's cache, or the drafter's own injected-context cache -

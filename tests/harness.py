@@ -68,12 +68,16 @@ def assert_accept(tau, bonus, gpu_g, drafts, og, oz, what):
 class Setup:
     """Drafter (+ target) of a workload on the GPU, with numpy float32 copies for the oracle."""
 
-    def __init__(self, w: synth.Workload, target=False, device=DEV):
+    def __init__(self, w: synth.Workload, target=False, device=DEV, dconv=None):
+        """dconv: None, or the DFlash 2 convolution weights of the drafter (a dict as from
+        synth.dconv_weights)."""
         self.w = w
         self.device = device
         self.dw = synth.model_weights(w, "draft", device)
         self.shared = synth.shared_weights(w, device)
-        self.draft = rt.Model(w.draft, self.dw, self.shared, n_taps=w.n_taps, draft=True)
+        self.draft = rt.Model(w.draft, self.dw, self.shared, n_taps=w.n_taps, draft=True, dconv=dconv)
+        if dconv is not None:
+            self.dw = {**self.dw, **dconv}
         self.np_dw = {k: synth.to_numpy(v) for k, v in self.dw.items()}
         self.np_shared = {k: synth.to_numpy(v) for k, v in self.shared.items()}
         self.target = None

@@ -69,6 +69,21 @@ def test_model_create_validates():
     assert st == 0
 
 
+def test_model_create_validates_convolutions():
+    ptrs = (ctypes.c_void_p * 8)(*([0x7000] * 8))
+    d = _desc()
+    d.dconv = ctypes.cast(ptrs, ctypes.POINTER(ctypes.c_void_p))
+    st, h = _create(d)
+    assert st == 0
+    _lib.model_destroy(h)
+    ptrs[5] = None                       # a missing convolution tensor
+    assert _create(d)[0] == -1
+    ptrs[5] = 0x7000
+    taps = (ctypes.c_int32 * 1)(0)       # a target (tapped layers) cannot hold convolutions
+    d.n_taps, d.tap_layers = 1, ctypes.cast(taps, ctypes.POINTER(ctypes.c_int32))
+    assert _create(d)[0] == -2
+
+
 def test_workspace_bytes_and_entry_validation():
     st, h = _create(_desc())
     assert st == 0

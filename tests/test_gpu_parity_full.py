@@ -120,6 +120,20 @@ def test_qwen3_8b_batch1_ctx4k():
     c, k = check_selection(ids[0].cpu().numpy(), cand[0].cpu().numpy(), o_ids, o_cand, o_rows, o_z, 16,
                            NEAR_TIE, "cfg 4k selector")
     assert c >= (B - 1) // 3 and k >= (B - 1) // 2, (c, k)
+    # DFlash 2 two-tap convolutions around every sublayer of the full-size drafter
+    dconv = synth.dconv_weights(w, DEV)
+    conv = rt.Model(w.draft, S.dw, S.shared, n_taps=w.n_taps, draft=True, dconv=dconv)
+    ids, logits, hid = _draft_outputs(S, kv, B, 1)
+    rt.draft_block(conv, kv, anchor, B, ids, ws, logits, hid)
+    torch.cuda.synchronize()
+    assert kv.err.item() == 0
+    np_conv = {**S.np_dw, **{k: synth.to_numpy(v) for k, v in dconv.items()}}
+    o_ids, o_z, o_hid = O.draft_block(np_conv, S.np_shared, w.draft, ctx, int(anchor[0]), n, B, store=S.store)
+    for l in range(w.draft.n_layers + 1):
+        assert_close(hid[l, 0].cpu().numpy(), o_hid[l], TOLB, f"cfg 4k dconv hidden layer {l}")
+    assert_rows_close(logits[0].cpu().numpy(), o_z, TOLB, "cfg 4k dconv logits")
+    assert assert_ids(ids[0].cpu().numpy(), o_ids, o_z, "cfg 4k dconv draft ids") >= 10
+    conv.close()
 
 
 def test_qwen3_8b_batch16_paged_ragged():
