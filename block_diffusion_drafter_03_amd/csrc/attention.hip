@@ -205,12 +205,17 @@ __global__ __launch_bounds__(ATTN_THREADS, 1) void attn_splitk_bf16(AttnArgs a) 
           mx = fmaxf(mx, x);
         }
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    // the reference max moves only when a step's max exceeds it by more than 8 (log2
-    // domain): probabilities relative to it stay <= 256, the softmax is the same for any
-    // reference, and deep into a context the O rescale is mostly skipped
-    const float mnew = mx > m + 8.f ? mx : m;
+    // the reference max moves only when a step's column max exceeds it by more than 8
+    // (log2 domain): probabilities relative to it stay <= 256, the softmax is the same for
+    // any reference, and deep into a context the O rescale is mostly skipped.  No column
+    // max can exceed it unless some lane's own max does, so the cross-lane max is formed
+    // only then (the same reference values, with no lane exchange in the common case).
+    float mnew = m;
+    if (__any(mx > m + 8.f)) {
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      mnew = mx > m + 8.f ? mx : m;
+    }
     const float alpha = mnew == m ? 1.f : (m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mnew));
     const float msub = mnew == -INFINITY ? 0.f : mnew;   // all scores -inf: p = 0
     float ps = 0.f;
