@@ -169,18 +169,26 @@ __global__ __launch_bounds__(ATTN_THREADS, 1) void attn_splitk_bf16(AttnArgs a) 
   auto compute = [&](int buf, bool blk, int lim) {
     const bf16* K = kt[buf];
     const bf16* VT = vt[buf];
+    // every K and V^T fragment of the step is read from LDS up front, so the V^T reads are
+    // in flight across the score MFMAs and the softmax instead of waited for pair by pair
+    bf16x8 kf[2][4], vf[8];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int cs = 0; cs < 4; ++cs)   // key kh*32 + 8(r>>2) + (r&3) + 4t
+        kf[t][cs] = *(const bf16x8*)(K + (kh * 32 + 16 * t + r) * KROW + g * 8 + cs * 32);
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) vf[dt] = *(const bf16x8*)(VT + (dt * 16 + r) * VROW + kh * 32 + g * 8);
     f32x4 sc[2];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      sc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const bf16* kr = K + (kh * 32 + 16 * t + r) * KROW + g * 8;   // key kh*32 + 8(r>>2) + (r&3) + 4t
+    for (int t = 0; t < 2; ++t) sc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int cs = 0; cs < 4; ++cs) {
-        const bf16x8 kf = *(const bf16x8*)(kr + cs * 32);
-        sc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qh[cs], sc[t], 0, 0, 0);
-        sc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, ql[cs], sc[t], 0, 0, 0);
+    for (int cs = 0; cs < 4; ++cs)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        sc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[t][cs], qh[cs], sc[t], 0, 0, 0);
+        sc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[t][cs], ql[cs], sc[t], 0, 0, 0);
       }
-    }
     // lane holds keys kh*32 + 8g + 4t + e (e < 4) of the step for query column r
     float p[8];
     float mx = -INFINITY;
@@ -235,9 +243,8 @@ __global__ __launch_bounds__(ATTN_THREADS, 1) void attn_splitk_bf16(AttnArgs a) 
     }
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
-      const bf16x8 vf = *(const bf16x8*)(VT + (dt * 16 + r) * VROW + kh * 32 + g * 8);
-      o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, ph, o[dt], 0, 0, 0);
-      o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pl, o[dt], 0, 0, 0);
+      o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[dt], ph, o[dt], 0, 0, 0);
+      o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[dt], pl, o[dt], 0, 0, 0);
     }
   };
   // the block's own keys first (split 0)
