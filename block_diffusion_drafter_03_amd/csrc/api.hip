@@ -242,6 +242,19 @@ int run_layers(const dflash_model* m, const dflash_kv* kv, int batch, int B, con
   // pre: w.xa = Conv(RMSNorm(h; g_norm)); post: h += Conv(w.xa) (+ the hidden_dbg copy).
   auto conv = [&](int l, int c, const void* g_norm, bool post, float* hdbg) -> int {
     const float* x = post ? w.xa : w.h;
+    if (dt == DFLASH_BF16 && gemv_dconv_supported(M, D)) {
+      // one launch: the correction GEMV with the convolution as its epilogue
+      GemmArgs g = gemm_args(x, D, one_seg(m->dconv[l * 8 + 2 * c + 1], D / 8, D), M, D / 8, D,
+                             g_norm, eps, EPI_DCONV);
+      g.e.out = post ? w.h : w.xa;
+      g.e.afrag = 1;
+      g.e.B = B;
+      g.e.hdbg = hdbg;
+      g.e.dconv_base = m->dconv[l * 8 + 2 * c];
+      g.e.dconv_accumulate = post;
+      HIPCHK(launch_gemv_dconv(g, st));
+      return DFLASH_OK;
+    }
     GemmArgs g = gemm_args(x, D, one_seg(m->dconv[l * 8 + 2 * c + 1], D / 8, D), M, D / 8, D,
                            g_norm, eps, EPI_STORE_F32);
     g.e.out = w.dk;

@@ -199,7 +199,40 @@ __global__ __launch_bounds__(NW * 64) void gemm_gemv_bf16(GemmArgs ga) {
       finish(t, acc, acc2);
     }
   }
-  if constexpr (KIND != EPI_ARGMAX) {
+  if constexpr (KIND == EPI_DCONV) {
+    // the convolution of the tile's 128 channels for every row, from the tile's 16
+    // correction columns (two per 16-channel group) held in `done`, by all threads
+    const EpiArgs& e = ga.e;
+    const float* x = (const float*)ga.A;
+    const bf16* base = (const bf16*)e.dconv_base;
+    const int KS2 = K >> 5;
+    for (int i = 0; i < nbuf; ++i) {
+      const int t = blockIdx.x + i * gridDim.x;
+      for (int q = threadIdx.x; q < 16 * 128; q += NW * 64) {
+        const int m = q >> 7, c = t * 128 + (q & 127);
+        if (m >= M || c >= K) continue;
+        const int p = m % e.B == 0 ? m : m - 1;
+        const int pair = 2 * ((c >> 4) - 8 * t);        // the channel group's two columns
+        float k0 = done[i][(m >> 2) * 16 + pair][m & 3];
+        float k1 = done[i][(m >> 2) * 16 + pair + 1][m & 3];
+        float xr = x[afrag_off(m, c, KS2)], xp = x[afrag_off(p, c, KS2)];
+        if constexpr (NORM) {
+          const float gc = (float)((const bf16*)ga.norm_g)[c];
+          k0 *= rstd[m];
+          k1 *= rstd[m];
+          xr *= rstd[m] * gc;
+          xp *= rstd[p] * gc;
+        }
+        k0 += (float)base[c];
+        k1 += (float)base[K + c];
+        const float y = k0 * xr + k1 * xp;
+        float* o = (float*)e.out + afrag_off(m, c, KS2);
+        const float v = e.dconv_accumulate ? *o + y : y;
+        *o = v;
+        if (e.hdbg) e.hdbg[(size_t)m * K + c] = v;
+      }
+    }
+  } else if constexpr (KIND != EPI_ARGMAX) {
     // every wave takes buffered tiles: the epilogues run in parallel, off the main loop's
     // register budget
     unsigned long long best[4];
@@ -257,5 +290,22 @@ struct GemvLaunch {
 
 // bf16 models, M <= 16, K a multiple of 32 * GEMV_NW (checked by launch_gemm)
 hipError_t launch_gemv(const GemmArgs& ga, hipStream_t st) { return dispatch_gemm<GemvLaunch>(ga, st); }
+
+// The convolution's correction GEMM with the convolution as its epilogue: the 16-wave
+// streamed form, one workgroup per 16-column tile (128 channels).
+bool gemv_dconv_supported(int M, int K) {
+  const int n_tiles = (K / 8 + 15) / 16;
+  return M >= 1 && M <= 16 && K % (32 * 16) == 0 && n_tiles * 4 <= num_cus();
+}
+
+hipError_t launch_gemv_dconv(const GemmArgs& ga, hipStream_t st) {
+  if (ga.a_bf16 || ga.N * 8 != ga.K || !gemv_dconv_supported(ga.M, ga.K) || !ga.e.dconv_base ||
+      !ga.e.out || ga.e.B < 1)
+    return hipErrorInvalidValue;
+  const int n_tiles = (ga.N + 15) / 16;
+  if (ga.norm_g)
+    return launch1(gemm_gemv_bf16<float, 16, true, false, EPI_DCONV>, dim3(n_tiles), dim3(16 * 64), st, ga);
+  return launch1(gemm_gemv_bf16<float, 16, false, false, EPI_DCONV>, dim3(n_tiles), dim3(16 * 64), st, ga);
+}
 
 }  // namespace dflash

@@ -30,7 +30,8 @@ enum EpiKind {
   EPI_QKV,            // RoPE q, k; write q (float), k_blk, v_blk^T (and the block K/V into a cache)
   EPI_SWIGLU,         // act = SiLU(gate) * up (float)
   EPI_INJECT_KV,      // RoPE K, scatter K and V of every draft layer into the paged cache
-  EPI_ARGMAX          // per-row argmax (packed 64-bit atomic max); optional float logits
+  EPI_ARGMAX,         // per-row argmax (packed 64-bit atomic max); optional float logits
+  EPI_DCONV           // DFlash 2 convolution from its correction coefficients (M <= 16 GEMV only)
 };
 
 struct EpiArgs {
@@ -77,6 +78,13 @@ struct EpiArgs {
   float temperature;
   unsigned long long seed;
   unsigned counter;
+  // EPI_DCONV: the GEMM's outputs are the correction coefficients of a two-tap convolution
+  // of its own A rows x (normalised by the A-side RMSNorm when there is one):
+  // y[m][c] = (base[c] + acc[m][2(c/16)]) x[m][c] + (base[D + c] + acc[m][2(c/16) + 1]) x[p][c]
+  // with p = m - 1 inside a B-row block (p = m for its first row); out (A-fragment order,
+  // row length D = K) = y, or += y when dconv_accumulate; hdbg (row-major) gets the result
+  const void* dconv_base;   // [2, D] (bf16)
+  int dconv_accumulate;
 };
 
 struct GemmArgs {
@@ -93,6 +101,10 @@ struct GemmArgs {
 
 // acc = A x W^T over the full K, then the epilogue.
 hipError_t launch_gemm(int dt, const GemmArgs& g, hipStream_t st);
+// The DFlash 2 convolution fused into its correction GEMM (EPI_DCONV): bf16 models, M <= 16,
+// N = K / 8 with K a multiple of 512 and at most one 16-column tile per four CUs.
+bool gemv_dconv_supported(int M, int K);
+hipError_t launch_gemv_dconv(const GemmArgs& g, hipStream_t st);
 
 // Paged-cache view of one layer.
 struct KvLayer {

@@ -1,6 +1,8 @@
 """DFlash 2 two-tap dynamic convolution in the drafter on the GPU ([DF] section 7.1, Problem
 2) against the oracle: every layer's output, the logits and the draft ids of a drafter with
 convolutions, on the same seeded weights and context."""
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -33,7 +35,19 @@ def _draft(S, w):
 
 @pytest.mark.parametrize("name", ["tiny_f32", "mid_bf16"])
 def test_convolved_drafter_matches_oracle(name):
-    w = synth.workload(name)
+    _check_against_oracle(synth.workload(name), name)
+
+
+def test_convolution_fused_into_its_correction_gemv_matches_oracle():
+    """One bf16 sequence of B = 16 rows (M = 16): every convolution runs as the epilogue of
+    its correction GEMV instead of a separate launch (the batch-3 case above, M = 48, keeps
+    the separate convolution kernel)."""
+    w = dataclasses.replace(synth.workload("mid_bf16"), batch=1, ctx=(333,))
+    assert w.batch * w.block <= 16
+    _check_against_oracle(w, "mid_bf16 batch 1")
+
+
+def _check_against_oracle(w, name):
     S = Setup(w, dconv=synth.dconv_weights(w, DEV))
     B, m, tol = w.block, w.draft, TOL[w.dtype]
     lens, feats, anchor, ids, logits, hid = _draft(S, w)
