@@ -83,8 +83,12 @@ __global__ __launch_bounds__(ATTN_THREADS, 1) void attn_splitk_bf16(AttnArgs a) 
 
   int n_ctx = a.seq_len[b];
   n_ctx = max(0, min(n_ctx, a.max_pages * 64));
-  const int kbeg = s * a.split_len;                  // multiple of 64
-  const int kend = min(kbeg + a.split_len, n_ctx);
+  // keys per split: this sequence's context spread evenly over the splits in whole pages
+  // (never more than the planned split length, which sizes the page list), so a grid sized
+  // for the cache capacity stays balanced at any context length
+  const int slen = min(a.split_len, ((n_ctx + a.n_splits - 1) / a.n_splits + 63) / 64 * 64);
+  const int kbeg = s * slen;                         // multiple of 64
+  const int kend = min(kbeg + slen, n_ctx);
   const int n_ctx_steps = kend > kbeg ? (kend - kbeg + 63) / 64 : 0;
   // split 0 also takes the block's own keys
 
@@ -525,10 +529,10 @@ AttnPlan attn_plan(int dt, int batch, int Hkv, int G, int B, int ctx_cap) {
   const int max_splits = (cap + 191) / 192;
   if (want > max_splits) want = max_splits;
   if (want < 1) want = 1;
-  // split lengths: 192 keys for short contexts, else a multiple of 128 (measured: at 64K and
-  // 256K contexts, 128-key multiples stream faster than the evener 64-key multiples)
+  // planned split length: the capacity over `want` splits in whole pages, at least 192 keys
+  // (the kernel then spreads each sequence's actual context evenly over the splits)
   int len = (cap + want - 1) / want;
-  len = len <= 192 ? 192 : (len + 127) / 128 * 128;
+  len = len <= 192 ? 192 : (len + 63) / 64 * 64;
   static const int forced = env_int("DFLASH_ATTN_SPLIT_LEN", 0);
   if (forced >= 64) len = (forced + 63) / 64 * 64;
   if (len > 64 * ATTN_MAX_SPLIT_PAGES) len = 64 * ATTN_MAX_SPLIT_PAGES;
