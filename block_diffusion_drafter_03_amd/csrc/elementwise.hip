@@ -16,10 +16,32 @@ __global__ __launch_bounds__(256) void embed_kernel(EmbedArgs a) {
     tok = 0;
   }
   const T* e = (const T*)a.E + (size_t)tok * D;
-  for (int c = threadIdx.x; c < D; c += 256) {
-    const float x = to_f(e[c]);
-    a.h[a.afrag ? afrag_off(row, c, D >> 5) : (size_t)row * D + c] = x;
-    if (a.hdbg) a.hdbg[(size_t)row * D + c] = x;
+  bool done = false;
+  if constexpr (sizeof(T) == 2) {
+    if (a.afrag && D % 8 == 0) {
+      // bf16 rows into the A-fragment order: 8 channels per thread, one 16-byte load and
+      // two float4 stores (channels 8q .. 8q+3 and 8q+4 .. 8q+7 are contiguous in the two
+      // halves of their fragment)
+      for (int c = threadIdx.x * 8; c < D; c += 256 * 8) {
+        const bf16x8 v = *(const bf16x8*)(e + c);
+        const float4 lo = make_float4((float)v[0], (float)v[1], (float)v[2], (float)v[3]);
+        const float4 hi = make_float4((float)v[4], (float)v[5], (float)v[6], (float)v[7]);
+        *(float4*)(a.h + afrag_off(row, c, D >> 5)) = lo;
+        *(float4*)(a.h + afrag_off(row, c + 4, D >> 5)) = hi;
+        if (a.hdbg) {
+          *(float4*)(a.hdbg + (size_t)row * D + c) = lo;
+          *(float4*)(a.hdbg + (size_t)row * D + c + 4) = hi;
+        }
+      }
+      done = true;
+    }
+  }
+  if (!done) {
+    for (int c = threadIdx.x; c < D; c += 256) {
+      const float x = to_f(e[c]);
+      a.h[a.afrag ? afrag_off(row, c, D >> 5) : (size_t)row * D + c] = x;
+      if (a.hdbg) a.hdbg[(size_t)row * D + c] = x;
+    }
   }
   // RoPE angles of this row's position (float64, rounded to float32)
   const int pos = a.seq_len[b] + j;
