@@ -347,6 +347,7 @@ __global__ __launch_bounds__(ATTN_THREADS, 1) void attn_splitk_bf16(AttnArgs a) 
 // log-sum-exp weights are formed there, and each thread then sums its 4 columns over the
 // splits with independent loads.
 #define MERGE_MAX_SPLITS 512
+#define MERGE_REG_SPLITS 32
 __global__ __launch_bounds__(256) void attn_merge_bf16(AttnArgs a) {
   __shared__ float wsh[8][MERGE_MAX_SPLITS];
   __shared__ float lsh[8][MERGE_MAX_SPLITS];
@@ -355,6 +356,19 @@ __global__ __launch_bounds__(256) void attn_merge_bf16(AttnArgs a) {
   const int kvh = blockIdx.y, b = blockIdx.z;
   const int R = a.G * a.B, S = a.n_splits;
   const size_t ss = 64 * PSTRIDE;
+  const int rho = rho0 + rl;
+  // up to MERGE_REG_SPLITS splits: this thread's 4 columns of every split are loaded now,
+  // together with the (m, l) of the workgroup's rows below, instead of after the weights
+  // (one memory round trip less; the sum runs in the same split order either way)
+  constexpr int SR = MERGE_REG_SPLITS;
+  const int rho_c = min(rho, R - 1);
+  const float* prc = a.part + (((size_t)b * a.Hkv + kvh) * a.n_rg + rho_c / 64) * S * ss +
+                     (size_t)(rho_c % 64) * PSTRIDE + 4 * t;
+  float4 xr[SR];
+  if (S <= SR) {
+#pragma unroll
+    for (int sp = 0; sp < SR; ++sp) xr[sp] = *(const float4*)(prc + min(sp, S - 1) * ss);
+  }
   // (m, l) of every (split, row) of this workgroup
   for (int idx = threadIdx.x; idx < S * 8; idx += 256) {
     const int sp = idx >> 3, row = idx & 7, rho = min(rho0 + row, R - 1);
@@ -364,7 +378,6 @@ __global__ __launch_bounds__(256) void attn_merge_bf16(AttnArgs a) {
     lsh[row][sp] = pr[AD + 1];
   }
   __syncthreads();
-  const int rho = rho0 + rl;
   // weights: the row's 32 threads split the splits, then combine through lane shuffles
   float ms = -INFINITY;
   for (int sp = t; sp < S; sp += 32) ms = fmaxf(ms, wsh[rl][sp]);
@@ -381,17 +394,28 @@ __global__ __launch_bounds__(256) void attn_merge_bf16(AttnArgs a) {
   for (int o = 16; o > 0; o >>= 1) lt += __shfl_xor(lt, o, 64);
   __syncthreads();
   if (rho >= R) return;
-  const size_t unit = ((size_t)b * a.Hkv + kvh) * a.n_rg + rho / 64;
-  const float* pr = a.part + unit * S * ss + (size_t)(rho % 64) * PSTRIDE + 4 * t;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (S <= SR) {
+#pragma unroll
+    for (int sp = 0; sp < SR; ++sp) {
+      if (sp < S) {
+        const float wgt = wsh[rl][sp];
+        acc.x += xr[sp].x * wgt;
+        acc.y += xr[sp].y * wgt;
+        acc.z += xr[sp].z * wgt;
+        acc.w += xr[sp].w * wgt;
+      }
+    }
+  } else {
 #pragma unroll 16
-  for (int sp = 0; sp < S; ++sp) {
-    const float wgt = wsh[rl][sp];
-    const float4 x = *(const float4*)(pr + sp * ss);
-    acc.x += x.x * wgt;
-    acc.y += x.y * wgt;
-    acc.z += x.z * wgt;
-    acc.w += x.w * wgt;
+    for (int sp = 0; sp < S; ++sp) {
+      const float wgt = wsh[rl][sp];
+      const float4 x = *(const float4*)(prc + sp * ss);
+      acc.x += x.x * wgt;
+      acc.y += x.y * wgt;
+      acc.z += x.z * wgt;
+      acc.w += x.w * wgt;
+    }
   }
   const float inv = 1.f / lt;
   const int gq = rho / a.B, j = rho % a.B;
