@@ -498,26 +498,21 @@ struct MfmaLaunch {
 #define MFMA_LAUNCH(WGM, WGN, TM, TN, KSUB, DEPTH)                                             \
   return launch1(gemm_mfma_bf16<TA, WGM, WGN, TM, TN, KSUB, DEPTH, NORM, KIND>,               \
                  dim3(wgs(16 * TM * WGM, 16 * TN * WGN)), dim3(64 * WGM * WGN), st, ga)
-    // Automatic choice (measured on the Qwen3-8B shapes at M = 256): when 64 x 128 tiles give
-    // every CU work (gate/up, LM head, injection K/V), the weight-direct kernel, with 4 weight
-    // tiles per wave once there are two workgroups per CU of them; otherwise (QKV, O, down)
-    // 64 x 64 LDS-staged tiles, which keep the most CUs busy.
+    // Automatic choice (measured on the Qwen3-8B shapes at M = 256 and the 512-row injection):
+    // when 64 x 128 tiles give every CU work (gate/up, LM head, injection K/V, the fusion
+    // GEMM over 512 feature rows), the weight-direct kernel, with 4 weight tiles per wave once
+    // there are two workgroups per CU of them; otherwise (QKV, O, down) 64 x 64 LDS-staged
+    // tiles, which keep the most CUs busy.
     if (tile == 0 && ks % 4 == 0) {
       if (wgs(64, 128) >= num_cus()) {
-        if constexpr (AIsFloat<TA>::value) {
-          if (wgs(64, 256) >= 2 * num_cus()) WD_LAUNCH(64, 4);
-          WD_LAUNCH(64, 2);
-        } else {
-          WD_LAUNCH(64, 4);
-        }
+        if (wgs(64, 256) >= 2 * num_cus()) WD_LAUNCH(64, 4);
+        WD_LAUNCH(64, 2);
       }
       MFMA_LAUNCH(2, 2, 2, 2, 2, 3);
     }
     // forced choices (sweeps): 10 / 11 weight-direct 64 x 128 / 64 x 256; 1-3 LDS-staged
     if (ks % 4 == 0) {
-      if constexpr (AIsFloat<TA>::value) {
-        if (tile == 10) WD_LAUNCH(64, 2);
-      }
+      if (tile == 10) WD_LAUNCH(64, 2);
       if (tile == 11) WD_LAUNCH(64, 4);
     }
     // (a stage of KSUB k-steps needs K % (32 KSUB) == 0, else one k-step per stage)
