@@ -508,6 +508,10 @@ struct MfmaLaunch {
         if (wgs(64, 256) >= 2 * num_cus()) WD_LAUNCH(64, 4);
         WD_LAUNCH(64, 2);
       }
+      // (32 x 64 tiles when 64 x 64 ones would leave CUs idle, e.g. O and down at 128 rows)
+      if constexpr (AIsFloat<TA>::value) {
+        if (wgs(64, 64) < num_cus()) MFMA_LAUNCH(2, 2, 1, 2, 2, 3);
+      }
       MFMA_LAUNCH(2, 2, 2, 2, 2, 3);
     }
     // forced choices (sweeps): 10 / 11 weight-direct 64 x 128 / 64 x 256; 1-3 LDS-staged
