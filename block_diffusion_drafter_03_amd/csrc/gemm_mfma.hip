@@ -479,7 +479,7 @@ __global__ __launch_bounds__(256) void gemm_wdirect_bf16(GemmArgs ga) {
 }
 
 // DFLASH_GEMM_TILE forces a kernel and tile (benchmark sweeps): 1-3 the LDS-staged
-// configurations, 10 / 11 the weight-direct kernel, 0 automatic
+// configurations, 10 / 11 / 13 the weight-direct kernel, 0 automatic
 static int gemm_tile_knob() {
   static const int v = env_knob("DFLASH_GEMM_TILE", 0);
   return v;
@@ -505,7 +505,19 @@ struct MfmaLaunch {
     // tiles, which keep the most CUs busy.
     if (tile == 0 && ks % 4 == 0) {
       if (wgs(64, 128) >= num_cus()) {
-        if (wgs(64, 256) >= 2 * num_cus()) WD_LAUNCH(64, 4);
+        // two workgroups are resident per CU: 64 x 192 tiles when their grid fills whole
+        // rounds of those slots clearly better (gate/up at 256 rows: 512 workgroups in one
+        // round instead of 768 in one and a half)
+        const int slots = 2 * num_cus();
+        auto fill = [&](int tn) {
+          const int n = wgs(64, 64 * tn);
+          return (double)n / ((double)((n + slots - 1) / slots) * slots);
+        };
+        const int tn = wgs(64, 256) >= slots ? 4 : 2;
+        if constexpr (AIsFloat<TA>::value) {
+          if (wgs(64, 192) >= num_cus() && fill(3) > fill(tn) + 0.1) WD_LAUNCH(64, 3);
+        }
+        if (tn == 4) WD_LAUNCH(64, 4);
         WD_LAUNCH(64, 2);
       }
       // (32 x 64 tiles when 64 x 64 ones would leave CUs idle, e.g. O and down at 128 rows)
@@ -514,10 +526,13 @@ struct MfmaLaunch {
       }
       MFMA_LAUNCH(2, 2, 2, 2, 2, 3);
     }
-    // forced choices (sweeps): 10 / 11 weight-direct 64 x 128 / 64 x 256; 1-3 LDS-staged
+    // forced choices (sweeps): 10 / 11 / 13 weight-direct 64 x 128 / 64 x 256 / 64 x 192; 1-3 LDS-staged
     if (ks % 4 == 0) {
       if (tile == 10) WD_LAUNCH(64, 2);
       if (tile == 11) WD_LAUNCH(64, 4);
+      if constexpr (AIsFloat<TA>::value) {
+        if (tile == 13) WD_LAUNCH(64, 3);   // 64 x 192
+      }
     }
     // (a stage of KSUB k-steps needs K % (32 KSUB) == 0, else one k-step per stage)
     switch (ks % 4 == 0 && tile < 10 ? tile : 0) {
