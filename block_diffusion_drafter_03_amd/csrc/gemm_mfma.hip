@@ -520,9 +520,12 @@ struct MfmaLaunch {
         if (tn == 4) WD_LAUNCH(64, 4);
         WD_LAUNCH(64, 2);
       }
-      // (32 x 64 tiles when 64 x 64 ones would leave CUs idle, e.g. O and down at 128 rows)
-      if constexpr (AIsFloat<TA>::value) {
-        if (wgs(64, 64) < num_cus()) MFMA_LAUNCH(2, 2, 1, 2, 2, 3);
+      // (32 x 64 tiles when 64 x 64 ones would leave CUs idle, e.g. O and down at 128 rows;
+      // bf16 rows - the fusion GEMM over the tapped features - as two-wave workgroups, whose
+      // 128 threads split that tile's staging evenly)
+      if (wgs(64, 64) < num_cus()) {
+        if constexpr (AIsFloat<TA>::value) MFMA_LAUNCH(2, 2, 1, 2, 2, 3);
+        else MFMA_LAUNCH(1, 2, 2, 2, 2, 3);
       }
       MFMA_LAUNCH(2, 2, 2, 2, 2, 3);
     }
