@@ -113,15 +113,15 @@ def main():
         pos = torch.arange(a, a + chunk, dtype=torch.int32, device=dev)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
-        rt.inject_ctx(draft, dkv, feats0[a:a + chunk].contiguous(), seq0, pos, 0, ws_d)
+        rt.inject_ctx(draft, dkv, feats0[a:a + chunk].contiguous(), seq0, pos, 0, a + chunk, ws_d)
         e1.record()
         inj_ms.append((e0, e1))
-    dkv.seq_len.fill_(n)
+    dkv.set_seq_len(n)
     tctx = synth.synthetic_ctx_kv(wt, "target", [n], dev)
     for l in range(T.n_layers):
         tkv.write_dense(l, 0, tctx[l][0][0], tctx[l][0][1])
     del tctx
-    tkv.seq_len.fill_(n)
+    tkv.set_seq_len(n)
     torch.cuda.synchronize()
     chunk_us = [a.elapsed_time(b) * 1e3 for a, b in inj_ms]
 
@@ -143,7 +143,7 @@ def main():
         if ev: ev[1].record()
         rt.verify_accept(target, tkv, a, drafts, B, feats, g, tau, bo, ws_t)
         if ev: ev[2].record()
-        rt.inject_ctx(draft, dkv, feats2d, rseq, rpos, 1, ws_d)
+        rt.inject_ctx(draft, dkv, feats2d, rseq, rpos, 1, B, ws_d)
         if ev: ev[3].record()
         rt.kv_commit(tkv, dkv, tau, B)
         if ev: ev[4].record()
@@ -295,7 +295,7 @@ def _filled_kv(rt, torch, shape, lens, cap, dev, seed):
     gen = torch.Generator(device=dev).manual_seed(seed)
     for t in kv.k + kv.v:
         t.normal_(generator=gen)
-    kv.seq_len.copy_(torch.tensor(lens, dtype=torch.int32))
+    kv.set_seq_len(lens)
     return kv
 
 
@@ -356,8 +356,8 @@ def workload_sweep(draft, target, D, T, B, dev, reps=5, cycles=4):
     feats = torch.randn(rows, 5 * D.hidden, device=dev).to(torch.bfloat16)
     kv1 = rt.PagedKV(D, 1, rows + 64, torch.bfloat16, dev)
     ws1 = rt.Workspace(draft.workspace_bytes(1, B, kv1.capacity, rows), dev)
-    rt.inject_ctx(draft, kv1, feats, rs, rp, 0, ws1)
-    us_inj = _timed(torch, lambda: rt.inject_ctx(draft, kv1, feats, rs, rp, 0, ws1), reps)
+    rt.inject_ctx(draft, kv1, feats, rs, rp, 0, rows, ws1)
+    us_inj = _timed(torch, lambda: rt.inject_ctx(draft, kv1, feats, rs, rp, 0, rows, ws1), reps)
     flops = 2.0 * rows * (5 * D.hidden * D.hidden + D.hidden * D.n_layers * 2 * D.n_kv_heads * D.head_dim)
     inj_tf = flops / (us_inj * 1e-6) / 1e12
     out["inject_512_rows"] = {"us": round(us_inj, 2), "useful_tflops": round(inj_tf, 1),
@@ -407,7 +407,7 @@ def workload_sweep(draft, target, D, T, B, dev, reps=5, cycles=4):
 
             def verify_cycle():
                 rt.verify_accept(target, tkv, anchor, drafts, B, feats, gv, tau, bonus, ws_t)
-                rt.inject_ctx(draft, dkv, feats.view(nb * B, -1), rs, rp, 1, ws_d)
+                rt.inject_ctx(draft, dkv, feats.view(nb * B, -1), rs, rp, 1, B, ws_d)
                 rt.kv_commit(tkv, dkv, tau, B)
             t_ver.append(_timed(torch, verify_cycle, 1))
             taus.append(tau.cpu().numpy().astype(float))
@@ -451,7 +451,7 @@ def sampled_cycles(draft, target, dkv, tkv, ws_d, ws_t, anchor, B, n_taps, D, T,
         ev[1].record()
         rt.verify_sampled(target, tkv, a, drafts, zd, B, 1.0, 2024, c, feats, zt, tau, nxt, ws_t)
         ev[2].record()
-        rt.inject_ctx(draft, dkv, feats.view(B, -1), rseq, rpos, 1, ws_d)
+        rt.inject_ctx(draft, dkv, feats.view(B, -1), rseq, rpos, 1, B, ws_d)
         rt.kv_commit(tkv, dkv, tau, B)
         a = nxt.clone()
     torch.cuda.synchronize()
@@ -538,7 +538,7 @@ def context_sweep(draft, shape, B, dev, contexts=(4096, 65536, 262144), reps=5):
         gen = torch.Generator(device=dev).manual_seed(n)
         for t in kv.k + kv.v:
             t.normal_(generator=gen)
-        kv.seq_len.fill_(n)
+        kv.set_seq_len(n)
         ws = rt.Workspace(draft.workspace_bytes(1, B, kv.capacity), dev)
         anchor = torch.zeros(1, dtype=torch.int32, device=dev)
         ids = torch.zeros(1, B - 1, dtype=torch.int32, device=dev)

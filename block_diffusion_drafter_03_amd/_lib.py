@@ -41,7 +41,8 @@ class KV(ctypes.Structure):
                 ("page_size", c_int32), ("batch", c_int32), ("max_pages_per_seq", c_int32),
                 ("num_pages", c_int32), ("k_pool", POINTER(c_void_p)),
                 ("v_pool", POINTER(c_void_p)), ("block_table", c_void_p),
-                ("seq_len", c_void_p), ("error_flags", c_void_p)]
+                ("seq_len", c_void_p), ("error_flags", c_void_p),
+                ("capacity_tokens", c_int32), ("len_bound", c_int32)]
 
 
 class Selector(ctypes.Structure):
@@ -73,7 +74,7 @@ def lib():
         L.dflash_workspace_bytes.argtypes = [c_void_p, c_int32, c_int32, c_int32, c_int32]
         L.dflash_workspace_bytes.restype = c_size_t
         L.dflash_inject_ctx.argtypes = [c_void_p, POINTER(KV), c_void_p, c_int32, c_void_p,
-                                        c_void_p, c_int32, c_void_p, c_size_t, c_void_p]
+                                        c_void_p, c_int32, c_int32, c_void_p, c_size_t, c_void_p]
         L.dflash_inject_ctx.restype = c_int32
         L.dflash_draft_block.argtypes = [c_void_p, POINTER(KV), c_void_p, c_int32, c_void_p,
                                          c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
@@ -130,10 +131,10 @@ def workspace_bytes(handle: int, batch: int, block: int, max_ctx: int, max_injec
     return int(lib().dflash_workspace_bytes(c_void_p(handle), batch, block, max_ctx, max_inject_rows))
 
 
-def inject_ctx(handle, kv: KV, feats, n_rows, row_seq, row_pos, pos_relative, ws, ws_bytes,
-               stream) -> int:
+def inject_ctx(handle, kv: KV, feats, n_rows, row_seq, row_pos, pos_relative, pos_limit, ws,
+               ws_bytes, stream) -> int:
     return lib().dflash_inject_ctx(c_void_p(handle), ctypes.byref(kv), feats, n_rows, row_seq,
-                                   row_pos, pos_relative, ws, ws_bytes, stream)
+                                   row_pos, pos_relative, pos_limit, ws, ws_bytes, stream)
 
 
 def draft_block(handle, kv: KV, anchor, block, draft_ids, logits_dbg, hidden_dbg, ws, ws_bytes,

@@ -60,6 +60,8 @@ struct StepWs {
   float* q;
   void* kblk;
   void* vblkT;
+  void* kblk_lo;      // bf16 models: the low parts of the block's own K / V^T
+  void* vblkT_lo;
   float* part;
   float* o;
   float* act;
@@ -82,6 +84,8 @@ size_t step_ws(const dflash_model* m, int batch, int B, int ctx_cap, void* base,
   t.q = (float*)cv.take((size_t)M * Hq * hd * 4);
   t.kblk = cv.take((size_t)M * Hkv * hd * esz(dt));
   t.vblkT = cv.take((size_t)batch * Hkv * hd * Bp * esz(dt));
+  t.kblk_lo = cv.take(dt == DFLASH_BF16 ? (size_t)M * Hkv * hd * 2 : 0);
+  t.vblkT_lo = cv.take(dt == DFLASH_BF16 ? (size_t)batch * Hkv * hd * Bp * 2 : 0);
   t.part = (float*)cv.take(dt == DFLASH_BF16 ? attn_partial_floats(t.plan, batch, Hkv, hd) * 4 : 0);
   t.o = (float*)cv.take((size_t)Mp * Hq * hd * 4);
   t.act = (float*)cv.take((size_t)Mp * d.ffn * 4);
@@ -144,7 +148,16 @@ int check_kv(const dflash_model* m, const dflash_kv* kv) {
     return DFLASH_E_SHAPE;
   for (int l = 0; l < kv->n_layers; ++l)
     if (!kv->k_pool[l] || !kv->v_pool[l]) return DFLASH_E_ARG;
+  if (kv->capacity_tokens < 0 || kv->len_bound < 0 ||
+      (int64_t)kv->capacity_tokens > (int64_t)kv->max_pages_per_seq * kv->page_size)
+    return DFLASH_E_ARG;
   return DFLASH_OK;
+}
+
+// Host-side capacity rule: the positions a call touches end before `end` (exclusive),
+// which must not pass the positions mapped for every sequence.
+int check_capacity(const dflash_kv* kv, int64_t end) {
+  return end > (int64_t)kv->capacity_tokens ? DFLASH_E_CAPACITY : DFLASH_OK;
 }
 
 KvLayer layer_view(const dflash_kv* kv, int l) {
@@ -296,6 +309,8 @@ int run_layers(const dflash_model* m, const dflash_kv* kv, int batch, int B, con
       e.q = w.q;
       e.kblk = w.kblk;
       e.vblkT = w.vblkT;
+      e.kblk_lo = w.kblk_lo;
+      e.vblkT_lo = w.vblkT_lo;
       e.has_cache = write_cache;
       e.kp[0] = kvl.k;
       e.vp[0] = kvl.v;
@@ -308,8 +323,8 @@ int run_layers(const dflash_model* m, const dflash_kv* kv, int batch, int B, con
     }
     {
       Timed t(DFLASH_KERNEL_ATTENTION, st);
-      HIPCHK(launch_attention(dt, w.plan, w.q, w.kblk, w.vblkT, kvl, batch, B, Bp, Hq, Hkv, hd,
-                              causal, w.part, w.o, afrag, st));
+      HIPCHK(launch_attention(dt, w.plan, w.q, w.kblk, w.vblkT, w.kblk_lo, w.vblkT_lo, kvl, batch,
+                              B, Bp, Hq, Hkv, hd, causal, w.part, w.o, afrag, st));
     }
     {  // O projection + residual (with the convolutions: the output, convolved below)
       GemmArgs g = gemm_args(w.o, Hq * hd, one_seg(W(m, l, DFLASH_W_O), D, Hq * hd), M, D,
@@ -509,10 +524,12 @@ size_t dflash_workspace_bytes(const dflash_model* m, int32_t batch, int32_t bloc
 
 int dflash_inject_ctx(const dflash_model* m, dflash_kv* kv, const void* feats, int32_t n_rows,
                       const int32_t* row_seq, const int32_t* row_pos, int32_t pos_relative,
-                      void* ws, size_t ws_bytes, void* stream) {
-  if (!m || n_rows < 0) return DFLASH_E_ARG;
+                      int32_t pos_limit, void* ws, size_t ws_bytes, void* stream) {
+  if (!m || n_rows < 0 || pos_limit < 1) return DFLASH_E_ARG;
   if (!m->d.w_c) return DFLASH_E_ARG;
   int e = check_kv(m, kv);
+  if (e) return e;
+  e = check_capacity(kv, (pos_relative ? (int64_t)kv->len_bound : 0) + pos_limit);
   if (e) return e;
   if (n_rows == 0) return DFLASH_OK;   // nothing to inject (the row arrays may be empty)
   if (!feats || !row_seq || !row_pos) return DFLASH_E_ARG;
@@ -562,6 +579,7 @@ int dflash_inject_ctx(const dflash_model* m, dflash_kv* kv, const void* feats, i
     ep.row_seq = row_seq;
     ep.row_pos = row_pos;
     ep.pos_relative = pos_relative;
+    ep.pos_limit = pos_limit;
     if (int s = run_gemm(DFLASH_KERNEL_INJECT_KV, dt, g, st)) return s;
   }
   return DFLASH_OK;
@@ -573,6 +591,8 @@ static int draft_block_impl(const dflash_model* m, const dflash_kv* kv, const in
   if (!m || !anchor || !draft_ids) return DFLASH_E_ARG;
   if (block < 1 || block > 64) return DFLASH_E_SHAPE;
   int e = check_kv(m, kv);
+  if (e) return e;
+  e = check_capacity(kv, kv->len_bound);   // the context is read, nothing is written
   if (e) return e;
   const dflash_model_desc& d = m->d;
   const int batch = kv->batch, B = block, M = batch * B;
@@ -652,8 +672,8 @@ int dflash_draft_block_select(const dflash_model* m, const dflash_kv* kv, const 
   }
   int chunks = 1;
   HIPCHK(launch_topk(draft_logits, batch * (B - 1), V, k, sw.keys, &chunks, st));
-  HIPCHK(launch_topk_merge(sw.keys, chunks, k, batch, B, d.embed, D, (int)esz(dt), anchor,
-                           sw.cand, candidates, sw.gather, st));
+  HIPCHK(launch_topk_merge(sw.keys, chunks, k, batch, B, d.embed, D, (int)esz(dt), anchor, V,
+                           kv->error_flags, sw.cand, candidates, sw.gather, st));
   {  // [A | B] of the gathered embedding rows
     const int msel = batch * (1 + (B - 1) * k);
     GemmArgs g = gemm_args(sw.gather, D, one_seg(sel->w_ab, 2 * r, D), msel, 2 * r, D, nullptr,
@@ -675,6 +695,8 @@ int dflash_verify_accept(const dflash_model* m, dflash_kv* kv, const int32_t* an
   if (block < 1 || block > 64) return DFLASH_E_SHAPE;
   if (block > 1 && !draft_ids) return DFLASH_E_ARG;
   int e = check_kv(m, kv);
+  if (e) return e;
+  e = check_capacity(kv, (int64_t)kv->len_bound + block);   // the block's K/V are written
   if (e) return e;
   if (feats_out && m->taps.empty()) return DFLASH_E_ARG;
   const dflash_model_desc& d = m->d;
@@ -703,6 +725,8 @@ int dflash_verify_sampled(const dflash_model* m, dflash_kv* kv, const int32_t* a
   if (block < 2 || block > 64) return DFLASH_E_SHAPE;
   int e = check_kv(m, kv);
   if (e) return e;
+  e = check_capacity(kv, (int64_t)kv->len_bound + block);   // the block's K/V are written
+  if (e) return e;
   if (kv->batch > 4096 || m->d.vocab > 262144) return DFLASH_E_SHAPE;
   if (feats_out && m->taps.empty()) return DFLASH_E_ARG;
   const dflash_model_desc& d = m->d;
@@ -729,10 +753,18 @@ int dflash_kv_commit(dflash_kv* tkv, dflash_kv* dkv, const int32_t* tau, int32_t
   if (tkv && (!tkv->seq_len || tkv->batch < 1)) return DFLASH_E_ARG;
   if (dkv && (!dkv->seq_len || dkv->batch < 1)) return DFLASH_E_ARG;
   if (tkv && dkv && tkv->batch != dkv->batch) return DFLASH_E_SHAPE;
+  for (const dflash_kv* kv : {(const dflash_kv*)tkv, (const dflash_kv*)dkv}) {
+    if (!kv) continue;
+    if (kv->capacity_tokens < 0 || kv->len_bound < 0) return DFLASH_E_ARG;
+    if (int e = check_capacity(kv, (int64_t)kv->len_bound + block)) return e;
+  }
   const int batch = tkv ? tkv->batch : dkv->batch;
   HIPCHK(launch_commit(tkv ? tkv->seq_len : nullptr, dkv ? dkv->seq_len : nullptr,
                        tkv ? tkv->error_flags : nullptr, dkv ? dkv->error_flags : nullptr, tau,
                        batch, block, (hipStream_t)stream));
+  // tau <= block: the host-side bounds stay upper bounds of the new lengths
+  if (tkv) tkv->len_bound += block;
+  if (dkv) dkv->len_bound += block;
   return DFLASH_OK;
 }
 

@@ -33,6 +33,8 @@ struct AttnArgs {
   const float* q;      // [batch*B, Hq*AD]
   const bf16* kblk;    // [batch*B, Hkv*AD]
   const bf16* vblkT;   // [batch, Hkv, AD, Bp]
+  const bf16* kblk_lo;    // low parts of the block's own K / V^T (same layouts): the block
+  const bf16* vblkT_lo;   // keys enter as compensated (hi, lo) pairs; zero when stored
   const bf16* kpool;   // [num_pages, Hkv, 64, AD]
   const bf16* vpool;   // [num_pages, Hkv, AD, 64]
   const int32_t* block_table;
@@ -132,15 +134,16 @@ __global__ __launch_bounds__(ATTN_THREADS, 1) void attn_splitk_bf16(AttnArgs a) 
     }
   };
   // the block's own keys (split 0 only): K rows from k_blk, V^T columns from v_blk^T
-  // (B <= 64); rows and columns past B are read from valid places and masked at the copy
-  auto load_blk = [&](bf16x8 (&st)[4]) {
+  // (B <= 64), high or low parts; rows and columns past B are read from valid places and
+  // masked at the copy
+  auto load_blk = [&](bf16x8 (&st)[4], const bf16* kb, const bf16* vb) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int idx = tid + ATTN_THREADS * j;
       const int key = min(idx >> 4, a.B - 1);
       const int k8 = min((idx & 7) * 8, a.Bp - 8);
-      st[j] = *(const bf16x8*)(a.kblk + (size_t)(b * a.B + key) * a.Hkv * AD + (size_t)kvh * AD + (idx & 15) * 8);
-      st[2 + j] = *(const bf16x8*)(a.vblkT + ((size_t)(b * a.Hkv + kvh) * AD + (idx >> 3)) * a.Bp + k8);
+      st[j] = *(const bf16x8*)(kb + (size_t)(b * a.B + key) * a.Hkv * AD + (size_t)kvh * AD + (idx & 15) * 8);
+      st[2 + j] = *(const bf16x8*)(vb + ((size_t)(b * a.Hkv + kvh) * AD + (idx >> 3)) * a.Bp + k8);
     }
   };
   // keys at or past `lim` (a partial last page, the block's padding): their V^T columns are
@@ -169,7 +172,10 @@ __global__ __launch_bounds__(ATTN_THREADS, 1) void attn_splitk_bf16(AttnArgs a) 
   for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // this wave's half (keys kh*32 .. kh*32+31) of the step in LDS buffer `buf` (keys >= lim
-  // masked; the block's own step is causal for the verifier)
+  // masked; the block's own step is causal for the verifier).  The block's own step (blk)
+  // holds the low parts of its K / V^T in the other buffer: scores K_hi q_hi + K_hi q_lo +
+  // K_lo q_hi, outputs V_hi p_hi + V_hi p_lo + V_lo p_hi (the lo x lo terms are below
+  // float32 resolution).
   auto compute = [&](int buf, bool blk, int lim) {
     const bf16* K = kt[buf];
     const bf16* VT = vt[buf];
@@ -193,6 +199,16 @@ __global__ __launch_bounds__(ATTN_THREADS, 1) void attn_splitk_bf16(AttnArgs a) 
         sc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[t][cs], qh[cs], sc[t], 0, 0, 0);
         sc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[t][cs], ql[cs], sc[t], 0, 0, 0);
       }
+    if (blk) {
+      const bf16* KL = kt[buf ^ 1];
+#pragma unroll
+      for (int cs = 0; cs < 4; ++cs)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const bf16x8 kl = *(const bf16x8*)(KL + (kh * 32 + 16 * t + r) * KROW + g * 8 + cs * 32);
+          sc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kl, qh[cs], sc[t], 0, 0, 0);
+        }
+    }
     // lane holds keys kh*32 + 8g + 4t + e (e < 4) of the step for query column r
     float p[8];
     float mx = -INFINITY;
@@ -250,11 +266,22 @@ __global__ __launch_bounds__(ATTN_THREADS, 1) void attn_splitk_bf16(AttnArgs a) 
       o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[dt], ph, o[dt], 0, 0, 0);
       o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[dt], pl, o[dt], 0, 0, 0);
     }
+    if (blk) {
+      const bf16* VL = vt[buf ^ 1];
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        const bf16x8 vl = *(const bf16x8*)(VL + (dt * 16 + r) * VROW + kh * 32 + g * 8);
+        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vl, ph, o[dt], 0, 0, 0);
+      }
+    }
   };
-  // the block's own keys first (split 0)
-  bf16x8 stb[4];
+  // the block's own keys first (split 0), high and low parts
+  bf16x8 stb[4], stl[4];
   const int last = n_ctx_steps - 1;
-  if (s == 0) load_blk(stb);
+  if (s == 0) {
+    load_blk(stb, a.kblk, a.vblkT);
+    load_blk(stl, a.kblk_lo, a.vblkT_lo);
+  }
   // (every thread reads and writes its slots unconditionally - past the split's last page
   // the index is clamped to a valid entry - so every thread waits here for its loads and
   // the query conversion below needs no wait on the context loads issued after it)
@@ -287,6 +314,7 @@ __global__ __launch_bounds__(ATTN_THREADS, 1) void attn_splitk_bf16(AttnArgs a) 
   }
   if (s == 0) {
     store_step(0, a.B, stb);
+    store_step(1, a.B, stl);
     __syncthreads();
     compute(0, true, a.B);
     __syncthreads();
@@ -424,13 +452,6 @@ __global__ __launch_bounds__(256) void attn_merge_bf16(AttnArgs a) {
   *(float4*)out = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
 }
 
-// Tuning knob read once from the environment (benchmark sweeps): DFLASH_ATTN_SPLIT_LEN
-// forces the largest keys per split (rounded up to a multiple of 64).
-static int env_int(const char* name, int dflt) {
-  const char* s = getenv(name);
-  return s && *s ? atoi(s) : dflt;
-}
-
 // ---------------------------------------------------------------------------------------
 // float32 path: one workgroup per (sequence, block row, query head), keys in chunks of
 // 256 with an online softmax; plain VALU.
@@ -557,8 +578,6 @@ AttnPlan attn_plan(int dt, int batch, int Hkv, int G, int B, int ctx_cap) {
   // (the kernel then spreads each sequence's actual context evenly over the splits)
   int len = (cap + want - 1) / want;
   len = len <= 192 ? 192 : (len + 63) / 64 * 64;
-  static const int forced = env_int("DFLASH_ATTN_SPLIT_LEN", 0);
-  if (forced >= 64) len = (forced + 63) / 64 * 64;
   if (len > 64 * ATTN_MAX_SPLIT_PAGES) len = 64 * ATTN_MAX_SPLIT_PAGES;
   if ((cap + len - 1) / len > MERGE_MAX_SPLITS) len = (cap + MERGE_MAX_SPLITS - 1) / MERGE_MAX_SPLITS;
   len = (len + 63) / 64 * 64;
@@ -572,15 +591,18 @@ size_t attn_partial_floats(const AttnPlan& p, int batch, int Hkv, int d) {
 }
 
 hipError_t launch_attention(int dt, const AttnPlan& p, const float* q, const void* kblk,
-                            const void* vblkT, const KvLayer& kv, int batch, int B, int Bp,
-                            int Hq, int Hkv, int d, int causal, float* part, float* o,
-                            int o_afrag, hipStream_t st) {
+                            const void* vblkT, const void* kblk_lo, const void* vblkT_lo,
+                            const KvLayer& kv, int batch, int B, int Bp, int Hq, int Hkv, int d,
+                            int causal, float* part, float* o, int o_afrag, hipStream_t st) {
   const int G = Hq / Hkv;
   if (dt == BF16) {
     AttnArgs a;
     a.q = q;
     a.kblk = (const bf16*)kblk;
     a.vblkT = (const bf16*)vblkT;
+    a.kblk_lo = (const bf16*)kblk_lo;
+    a.vblkT_lo = (const bf16*)vblkT_lo;
+    if (!kblk_lo || !vblkT_lo) return hipErrorInvalidValue;
     a.kpool = (const bf16*)kv.k;
     a.vpool = (const bf16*)kv.v;
     a.block_table = kv.block_table;

@@ -86,9 +86,16 @@ DF_DEV void epi_pair(const EpiArgs& e, int row, int col, float v0, float v1) {
           dst[i + hd / 2] = y2;
         } else {
           const int kh = head - e.Hq;
-          T* dst = (T*)e.kblk + (size_t)row * e.Hkv * hd + (size_t)kh * hd;
-          dst[i] = from_f<T>(y1);
-          dst[i + hd / 2] = from_f<T>(y2);
+          const size_t o = (size_t)row * e.Hkv * hd + (size_t)kh * hd;
+          T* dst = (T*)e.kblk + o;
+          const T k1 = from_f<T>(y1), k2 = from_f<T>(y2);
+          dst[i] = k1;
+          dst[i + hd / 2] = k2;
+          if constexpr (sizeof(T) == 2) {   // low parts: zero when the rows are stored
+            bf16* lo = (bf16*)e.kblk_lo + o;
+            lo[i] = e.has_cache ? (bf16)0.f : (bf16)(y1 - (float)k1);
+            lo[i + hd / 2] = e.has_cache ? (bf16)0.f : (bf16)(y2 - (float)k2);
+          }
           if (cache) {
             T* kc = (T*)e.kp[0] + (((size_t)page * e.Hkv + kh) * 64 + slot) * hd;
             kc[i] = from_f<T>(y1);
@@ -97,9 +104,16 @@ DF_DEV void epi_pair(const EpiArgs& e, int row, int col, float v0, float v1) {
         }
       } else {
         const int vh = head - e.Hq - e.Hkv;
-        T* vt = (T*)e.vblkT + ((size_t)(b * e.Hkv + vh) * hd + el) * e.Bp + j;
-        vt[0] = from_f<T>(v0);
-        vt[e.Bp] = from_f<T>(v1);
+        const size_t o = ((size_t)(b * e.Hkv + vh) * hd + el) * e.Bp + j;
+        T* vt = (T*)e.vblkT + o;
+        const T u0 = from_f<T>(v0), u1 = from_f<T>(v1);
+        vt[0] = u0;
+        vt[e.Bp] = u1;
+        if constexpr (sizeof(T) == 2) {
+          bf16* lo = (bf16*)e.vblkT_lo + o;
+          lo[0] = e.has_cache ? (bf16)0.f : (bf16)(v0 - (float)u0);
+          lo[e.Bp] = e.has_cache ? (bf16)0.f : (bf16)(v1 - (float)u1);
+        }
         if (cache) {
           T* vc = (T*)e.vp[0] + (((size_t)page * e.Hkv + vh) * hd + el) * 64 + slot;
           vc[0] = from_f<T>(v0);
@@ -110,7 +124,12 @@ DF_DEV void epi_pair(const EpiArgs& e, int row, int col, float v0, float v1) {
     }
     case EPI_INJECT_KV: {
       const int b = e.row_seq[row];
-      const int pos = e.row_pos[row] + ((e.pos_relative && b >= 0 && b < e.batch) ? e.seq_len[b] : 0);
+      const int rp = e.row_pos[row];
+      if (rp < 0 || rp >= e.pos_limit) {   // outside the range the host checked
+        flag_error(e.err, DEVERR_PAGE);
+        break;
+      }
+      const int pos = rp + ((e.pos_relative && b >= 0 && b < e.batch) ? e.seq_len[b] : 0);
       int page;
       if (!cache_slot(e, b, pos, &page)) break;
       const int slot = pos & 63, hd = e.hd;

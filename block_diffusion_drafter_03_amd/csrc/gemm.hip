@@ -104,16 +104,10 @@ struct F32Launch {
 hipError_t launch_gemv(const GemmArgs& ga, hipStream_t st);
 hipError_t launch_gemm_mfma(const GemmArgs& ga, hipStream_t st);
 
-// DFLASH_GEMV=1 forces the tiled kernel for M <= 16 (benchmark sweeps)
-static int gemv_variant() {
-  static const int v = env_knob("DFLASH_GEMV", 0);
-  return v;
-}
-
 hipError_t launch_gemm(int dt, const GemmArgs& ga, hipStream_t st) {
   if (ga.M <= 0 || ga.N <= 0) return hipSuccess;
   if (dt == F32) return dispatch_gemm<F32Launch>(ga, st);
-  if (ga.M <= 16 && ga.K % (32 * GEMV_NW) == 0 && gemv_variant() != 1) return launch_gemv(ga, st);
+  if (ga.M <= 16 && ga.K % (32 * GEMV_NW) == 0) return launch_gemv(ga, st);
   return launch_gemm_mfma(ga, st);
 }
 

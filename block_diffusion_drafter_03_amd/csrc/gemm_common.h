@@ -5,7 +5,6 @@
 // MFMA: v_mfma_f32_16x16x32_bf16.  Lane l (r = l % 16, g = l / 16) supplies A[r][8g..8g+7]
 // and W row r's k-slice 8g..8g+7; the accumulator holds D[4g + i][r], i = 0..3.
 #pragma once
-#include <stdlib.h>
 #include "epilogue.h"
 
 #define GEMV_NW 8    // waves per workgroup of the M <= 16 GEMV (K must be a multiple of 32 GEMV_NW)
@@ -121,11 +120,7 @@ DF_DEV void a_operand(float v[8], const bf16x8 gv, float* ss, bf16x8& hi, bf16x8
 
 
 // ---------------------------------------------------------------------------------------
-// Host side.  Tuning knobs are read once from the environment (benchmark sweeps).
-static inline int env_knob(const char* name, int dflt) {
-  const char* s = getenv(name);
-  return s && *s ? atoi(s) : dflt;
-}
+// Host side.
 static inline int num_cus() {
   static int n = 0;
   if (!n) {

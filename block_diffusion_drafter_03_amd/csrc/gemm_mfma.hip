@@ -478,19 +478,11 @@ __global__ __launch_bounds__(256) void gemm_wdirect_bf16(GemmArgs ga) {
   }
 }
 
-// DFLASH_GEMM_TILE forces a kernel and tile (benchmark sweeps): 1-3 the LDS-staged
-// configurations, 10 / 11 / 13 the weight-direct kernel, 0 automatic
-static int gemm_tile_knob() {
-  static const int v = env_knob("DFLASH_GEMM_TILE", 0);
-  return v;
-}
-
 struct MfmaLaunch {
   template <typename TA, bool NORM, int KIND>
   static hipError_t run(const GemmArgs& ga, hipStream_t st) {
     const int M = ga.M, N = ga.N;
     auto wgs = [&](int bm, int bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
-    const int tile = gemm_tile_knob();
     const int ks = ga.K >> 5;
 #define WD_LAUNCH(BM, TN)                                                                     \
   return launch1(gemm_wdirect_bf16<TA, BM, TN, 2, NORM, KIND>, dim3(wgs(BM, 64 * TN)),     \
@@ -498,12 +490,13 @@ struct MfmaLaunch {
 #define MFMA_LAUNCH(WGM, WGN, TM, TN, KSUB, DEPTH)                                             \
   return launch1(gemm_mfma_bf16<TA, WGM, WGN, TM, TN, KSUB, DEPTH, NORM, KIND>,               \
                  dim3(wgs(16 * TM * WGM, 16 * TN * WGN)), dim3(64 * WGM * WGN), st, ga)
-    // Automatic choice (measured on the Qwen3-8B shapes at M = 256 and the 512-row injection):
-    // when 64 x 128 tiles give every CU work (gate/up, LM head, injection K/V, the fusion
-    // GEMM over 512 feature rows), the weight-direct kernel, with 4 weight tiles per wave once
-    // there are two workgroups per CU of them; otherwise (QKV, O, down) 64 x 64 LDS-staged
-    // tiles, which keep the most CUs busy.
-    if (tile == 0 && ks % 4 == 0) {
+    // Choice measured on the Qwen3-8B shapes at M = 256 and the 512-row injection: when
+    // 64 x 128 tiles give every CU work (gate/up, LM head, injection K/V, the fusion GEMM over
+    // 512 feature rows), the weight-direct kernel, with 4 weight tiles per wave once there
+    // are two workgroups per CU of them; otherwise (QKV, O, down) 64 x 64 LDS-staged tiles,
+    // which keep the most CUs busy.  (A stage of two k-steps needs K % 64 == 0 - the
+    // weight-direct kernel K % 128 == 0 - else one k-step per stage.)
+    if (ks % 4 == 0) {
       if (wgs(64, 128) >= num_cus()) {
         // two workgroups are resident per CU: 64 x 192 tiles when their grid fills whole
         // rounds of those slots clearly better (gate/up at 256 rows: 512 workgroups in one
@@ -529,26 +522,10 @@ struct MfmaLaunch {
       }
       MFMA_LAUNCH(2, 2, 2, 2, 2, 3);
     }
-    // forced choices (sweeps): 10 / 11 / 13 weight-direct 64 x 128 / 64 x 256 / 64 x 192; 1-3 LDS-staged
-    if (ks % 4 == 0) {
-      if (tile == 10) WD_LAUNCH(64, 2);
-      if (tile == 11) WD_LAUNCH(64, 4);
-      if constexpr (AIsFloat<TA>::value) {
-        if (tile == 13) WD_LAUNCH(64, 3);   // 64 x 192
-      }
-    }
-    // (a stage of KSUB k-steps needs K % (32 KSUB) == 0, else one k-step per stage)
-    switch (ks % 4 == 0 && tile < 10 ? tile : 0) {
-      case 1: MFMA_LAUNCH(2, 2, 2, 2, 2, 3);   //  64 x  64, BK  64
-      case 2: MFMA_LAUNCH(2, 2, 2, 2, 4, 2);   //  64 x  64, BK 128
-      case 3: MFMA_LAUNCH(2, 2, 2, 4, 2, 3);   //  64 x 128, BK  64
-      default:
-        if (ks % 2) MFMA_LAUNCH(2, 2, 2, 2, 1, 3);
-        MFMA_LAUNCH(2, 2, 2, 2, 2, 3);
-    }
+    if (ks % 2) MFMA_LAUNCH(2, 2, 2, 2, 1, 3);
+    MFMA_LAUNCH(2, 2, 2, 2, 2, 3);
 #undef MFMA_LAUNCH
 #undef WD_LAUNCH
-    return hipErrorInvalidValue;
   }
 };
 

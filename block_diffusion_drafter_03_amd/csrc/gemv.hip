@@ -254,22 +254,15 @@ __global__ __launch_bounds__(NW * 64) void gemm_gemv_bf16(GemmArgs ga) {
   }
 }
 
-// Tuning knobs (benchmark sweeps): DFLASH_GEMV_STREAM_TILES sets the largest tile count
-// that uses the streamed-A form (default: one tile per CU).
-static int gemv_stream_tiles() {
-  static const int v = env_knob("DFLASH_GEMV_STREAM_TILES", num_cus());
-  return v;
-}
-
 struct GemvLaunch {
   template <typename TA, bool NORM, int KIND>
   static hipError_t run(const GemmArgs& ga, hipStream_t st) {
     const int n_tiles = (ga.N + 15) / 16;
-    // few tiles (up to gemv_stream_tiles(), default one per CU) or K != 4096: one workgroup
+    // few tiles (up to one per CU) or K != 4096: one workgroup
     // per tile, A streamed with W, so that several workgroups may share a CU and every tile
     // is in flight at once; otherwise one workgroup per CU with the A slice stationary,
     // walking the tiles (the deferred epilogue buffer bounds the tiles per workgroup)
-    if (n_tiles <= gemv_stream_tiles() || ga.K != 32 * GEMV_NW * GEMV_CH) {
+    if (n_tiles <= num_cus() || ga.K != 32 * GEMV_NW * GEMV_CH) {
       // very few tiles (a quarter of the CUs or fewer, e.g. the 512-column correction maps
       // of the convolutions): 16 waves split K, so each wave's share is one chunk in flight
       if (n_tiles * 4 <= num_cus() && ga.K % (32 * 16) == 0)

@@ -53,6 +53,8 @@ struct EpiArgs {
   float* q;
   void* kblk;
   void* vblkT;
+  void* kblk_lo;            // bf16 models: low parts (x - bf16(x)) of k_blk / v_blk^T, zero
+  void* vblkT_lo;           // when the block is written into a cache (verification)
   // paged cache: per-layer pools (EPI_QKV uses slot 0), block table, bounds
   void* kp[8];
   void* vp[8];
@@ -64,6 +66,7 @@ struct EpiArgs {
   const int32_t* row_seq;
   const int32_t* row_pos;
   int pos_relative;
+  int pos_limit;            // rows with row_pos outside [0, pos_limit) are skipped (flagged)
   // EPI_SWIGLU
   float* act;
   int F;
@@ -126,11 +129,12 @@ size_t attn_partial_floats(const AttnPlan& p, int batch, int Hkv, int d);
 
 // o[M, Hq d] = softmax(q k^T / sqrt(d)) v over [context ; block] (causal inside the block
 // when `causal`), one query row per (sequence, block position, head).  `part` holds the
-// per-split partials (attn_partial_floats floats).
+// per-split partials (attn_partial_floats floats).  bf16 models take the block's own K/V as
+// (kblk + kblk_lo, vblkT + vblkT_lo).
 hipError_t launch_attention(int dt, const AttnPlan& p, const float* q, const void* kblk,
-                            const void* vblkT, const KvLayer& kv, int batch, int B, int Bp,
-                            int Hq, int Hkv, int d, int causal, float* part, float* o,
-                            int o_afrag, hipStream_t st);
+                            const void* vblkT, const void* kblk_lo, const void* vblkT_lo,
+                            const KvLayer& kv, int batch, int B, int Bp, int Hq, int Hkv, int d,
+                            int causal, float* part, float* o, int o_afrag, hipStream_t st);
 
 // ---- row kernels (elementwise.hip) ----
 struct EmbedArgs {
@@ -207,8 +211,9 @@ hipError_t launch_dconv(const DconvArgs& a, hipStream_t st);
 hipError_t launch_topk(const float* logits, int rows, int V, int k, unsigned long long* keys,
                        int* chunks, hipStream_t st);
 hipError_t launch_topk_merge(const unsigned long long* keys, int chunks, int k, int batch, int B,
-                             const void* embed, int D, int esz, const int32_t* anchor,
-                             int32_t* cand, int32_t* cand_out, void* gather, hipStream_t st);
+                             const void* embed, int D, int esz, const int32_t* anchor, int V,
+                             int32_t* err, int32_t* cand, int32_t* cand_out, void* gather,
+                             hipStream_t st);
 hipError_t launch_select(const float* P, const float* Hh, const float* logits, const int32_t* cand,
                          int batch, int B, int k, int r, int V, float* S, int32_t* draft_ids,
                          hipStream_t st);

@@ -97,6 +97,8 @@ struct TopkMergeArgs {
   const void* embed;                // [V, D] model dtype
   int D, esz;
   const int32_t* anchor;            // [batch]
+  int V;                            // vocabulary: an anchor outside [0, V) reads row 0
+  int32_t* err;                     // device error word or NULL
   int32_t* cand;                    // [rows][TOPK_MAX] (workspace)
   int32_t* cand_out;                // [rows][k] or NULL
   void* gather;                     // [batch * (1 + (B - 1) k)][D] model dtype
@@ -133,7 +135,12 @@ __global__ __launch_bounds__(256) void topk_merge_kernel(TopkMergeArgs a) {
   char* g = (char*)a.gather;
   const int nrow = a.k + (t == 1 ? 1 : 0);
   const int n16i = (int)n16, total = nrow * n16i;
-  const int aid = a.anchor[b];
+  // an anchor id outside the vocabulary is read as row 0 and flagged (as the embedding does)
+  int aid = a.anchor[b];
+  if (aid < 0 || aid >= a.V) {
+    if (threadIdx.x == 0 && t == 1) flag_error(a.err, DEVERR_TOKEN);
+    aid = 0;
+  }
   // 8 independent 16-byte copies per thread in flight at a time (named registers: an array
   // here ends up in scratch)
   auto src = [&](int idx) {
@@ -262,11 +269,12 @@ hipError_t launch_topk(const float* logits, int rows, int V, int k, unsigned lon
 }
 
 hipError_t launch_topk_merge(const unsigned long long* keys, int chunks, int k, int batch, int B,
-                             const void* embed, int D, int esz, const int32_t* anchor,
-                             int32_t* cand, int32_t* cand_out, void* gather, hipStream_t st) {
+                             const void* embed, int D, int esz, const int32_t* anchor, int V,
+                             int32_t* err, int32_t* cand, int32_t* cand_out, void* gather,
+                             hipStream_t st) {
   if (batch <= 0 || B < 2) return hipSuccess;
   if ((D * esz) % 16) return hipErrorInvalidValue;
-  TopkMergeArgs a{keys, chunks, k, B, embed, D, esz, anchor, cand, cand_out, gather};
+  TopkMergeArgs a{keys, chunks, k, B, embed, D, esz, anchor, V, err, cand, cand_out, gather};
   hipLaunchKernelGGL(topk_merge_kernel, dim3(batch * (B - 1)), dim3(256), 0, st, a);
   return hipGetLastError();
 }

@@ -144,7 +144,9 @@ class PagedKV:
     """Paged K/V pools of one model for `batch` sequences of up to `capacity` positions.
 
     K pool per layer [num_pages, Hkv, 64, d]; V pool [num_pages, Hkv, d, 64] (transposed
-    pages).  ``page_order`` may permute the physical pages handed to the sequences."""
+    pages).  ``page_order`` may permute the physical pages handed to the sequences.  Every
+    page of the block table is mapped, so the struct's capacity_tokens is the capacity;
+    its host-side len_bound follows ``set_seq_len`` and each commit."""
 
     def __init__(self, shape, batch, capacity, dtype, device, page_order=None, spare_pages=0):
         self.shape = shape
@@ -171,7 +173,26 @@ class PagedKV:
         s.block_table = self.block_table.data_ptr()
         s.seq_len = self.seq_len.data_ptr()
         s.error_flags = self.err.data_ptr()
+        s.capacity_tokens = self.capacity
+        s.len_bound = 0
         self.struct = s
+
+    def set_seq_len(self, lens):
+        """Committed lengths: an int for every sequence, or one per sequence.  Sets the
+        device seq_len and the host-side upper bound the library checks capacity with."""
+        if isinstance(lens, int):
+            lens = [lens] * self.batch
+        lens = [int(x) for x in lens]
+        self.seq_len.copy_(torch.tensor(lens, dtype=torch.int32))
+        self.struct.len_bound = max(lens)
+
+    def refresh_len_bound(self):
+        """Tighten the host-side bound to the device lengths (synchronises the stream)."""
+        self.struct.len_bound = int(self.seq_len.max().item())
+
+    @property
+    def len_bound(self) -> int:
+        return int(self.struct.len_bound)
 
     # --- plumbing used to load a synthetic context and to read a cache back ---------------
     def _slots(self, b, start, n):
@@ -200,9 +221,13 @@ class Workspace:
 
 # --- entry points (torch tensors in, status checked) --------------------------------------
 
-def inject_ctx(model: Model, kv: PagedKV, feats, row_seq, row_pos, pos_relative, ws: Workspace):
+def inject_ctx(model: Model, kv: PagedKV, feats, row_seq, row_pos, pos_relative, pos_limit,
+               ws: Workspace):
+    """pos_limit: every row_pos lies in [0, pos_limit) (absolute positions, or offsets from
+    the sequence's length when pos_relative)."""
     st = _lib.inject_ctx(model.handle, kv.struct, _ptr(feats), int(feats.shape[0]), _ptr(row_seq),
-                         _ptr(row_pos), int(pos_relative), _ptr(ws.buf), ws.nbytes, _stream())
+                         _ptr(row_pos), int(pos_relative), int(pos_limit), _ptr(ws.buf), ws.nbytes,
+                         _stream())
     _lib._check(st, "dflash_inject_ctx")
 
 

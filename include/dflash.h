@@ -20,9 +20,14 @@
  *  - Host-side arguments (descriptors, pointer tables, sizes) are read during the call
  *    only and may be freed when it returns.
  *  - Return value: DFLASH_OK (0) or a negative dflash_status.  Argument, shape, dtype,
- *    capacity and workspace errors are detected before anything is enqueued, so no cache
- *    or sequence length has been touched; DFLASH_E_HIP (a failed launch) may leave the
- *    call's earlier kernels enqueued.
+ *    capacity and workspace errors are detected on the host before anything is enqueued,
+ *    so no cache or sequence length has been touched; DFLASH_E_HIP (a failed launch) may
+ *    leave the call's earlier kernels enqueued.
+ *  - Capacity is checked on the host against two host-side fields of dflash_kv:
+ *    capacity_tokens (positions mapped for every sequence) and len_bound (an upper bound
+ *    on every seq_len[b], kept by the caller and advanced by dflash_kv_commit), so a call
+ *    that could write or read past the mapped pages returns DFLASH_E_CAPACITY instead of
+ *    launching.
  *  - The workspace `ws` is scratch for the duration of the call's kernels: calls that may
  *    overlap on the device (different streams) need separate workspaces.
  *  - Errors the host cannot see (an unmapped page, an out-of-range token id or tau) are
@@ -60,7 +65,7 @@ typedef enum {
   DFLASH_E_ARG = -1,        /* NULL pointer, non-positive size, bad enum            */
   DFLASH_E_SHAPE = -2,      /* shape the kernels do not support, or inconsistent    */
   DFLASH_E_DTYPE = -3,      /* unknown dtype or mismatch between model and cache    */
-  DFLASH_E_CAPACITY = -4,   /* cache cannot hold the rows the call would write      */
+  DFLASH_E_CAPACITY = -4,   /* the rows the call would touch pass capacity_tokens   */
   DFLASH_E_WORKSPACE = -5,  /* workspace NULL or smaller than dflash_workspace_bytes */
   DFLASH_E_HIP = -6         /* a HIP launch failed                                   */
 } dflash_status;
@@ -145,6 +150,20 @@ enum {
  *   V pool [num_pages, n_kv_heads, head_dim, page_size]   (V stored transposed per page)
  * Position p of sequence b lives in page block_table[b * max_pages_per_seq + p / page_size]
  * at slot p % page_size.  seq_len[b] is the committed length n_b.
+ *
+ * Capacity ([DF] section 4.5: verification writes the block's K/V at n .. n+B-1 before
+ * acceptance is known, so those positions must be mapped first).  The host cannot read
+ * seq_len without a synchronisation, so the caller states two host-side bounds:
+ *   capacity_tokens  positions 0 .. capacity_tokens-1 are mapped for every sequence
+ *                    (0 <= capacity_tokens <= max_pages_per_seq * page_size);
+ *   len_bound        an upper bound on every seq_len[b], set by the caller together with
+ *                    seq_len; dflash_kv_commit adds `block` to it (tau <= block), and the
+ *                    caller may lower it again after reading seq_len back.
+ * draft_block needs len_bound <= capacity_tokens; verify_accept / verify_sampled and
+ * kv_commit need len_bound + block <= capacity_tokens; inject_ctx needs its rows'
+ * positions (pos_limit below) to fit.  Otherwise the call returns DFLASH_E_CAPACITY and
+ * launches nothing.  The device checks every row again against the block table (a row
+ * that still lands on an unmapped page is skipped and DFLASH_DEVERR_PAGE flagged).
  */
 typedef struct dflash_kv {
   int32_t n_layers, n_kv_heads, head_dim;
@@ -157,6 +176,8 @@ typedef struct dflash_kv {
   const int32_t* block_table;   /* device [batch, max_pages_per_seq]; -1 = unmapped          */
   int32_t* seq_len;             /* device [batch]                                             */
   int32_t* error_flags;         /* device [1] or NULL: DFLASH_DEVERR_* bits are OR-ed in      */
+  int32_t capacity_tokens;      /* host: positions mapped for every sequence                  */
+  int32_t len_bound;            /* host: upper bound on every seq_len[b]; kv_commit adds block */
 } dflash_kv;
 
 typedef struct dflash_model dflash_model;   /* opaque: shapes + non-owning weight pointers */
@@ -187,13 +208,20 @@ size_t dflash_workspace_bytes(const dflash_model* model, int32_t batch, int32_t 
  *   row_seq  device int32 [n_rows]: sequence of each row.
  *   row_pos  device int32 [n_rows]: position of each row, absolute when pos_relative = 0,
  *            else added to seq_len[row_seq[r]].
+ *   pos_limit host int32: every row_pos[r] lies in [0, pos_limit).  The rows' positions
+ *            then end before pos_limit (absolute) or len_bound + pos_limit (relative),
+ *            which must not pass capacity_tokens (else DFLASH_E_CAPACITY, nothing
+ *            launched).  A row outside [0, pos_limit) is skipped on the device and
+ *            DFLASH_DEVERR_PAGE flagged.
  * seq_len is not changed (kv_commit advances it).  n_rows = 0 is a no-op (the row
- * arrays are then not read and may be NULL); n_rows < 0 is DFLASH_E_ARG.  A row whose
- * sequence or position has no mapped page is skipped and DFLASH_DEVERR_PAGE flagged.
+ * arrays are then not read and may be NULL); n_rows < 0 or pos_limit < 1 is DFLASH_E_ARG.
+ * A row whose sequence or position has no mapped page is skipped and DFLASH_DEVERR_PAGE
+ * flagged.
  */
 int dflash_inject_ctx(const dflash_model* draft, dflash_kv* draft_ctx, const void* feats,
                       int32_t n_rows, const int32_t* row_seq, const int32_t* row_pos,
-                      int32_t pos_relative, void* ws, size_t ws_bytes, void* stream);
+                      int32_t pos_relative, int32_t pos_limit, void* ws, size_t ws_bytes,
+                      void* stream);
 
 /*
  * One drafter step ([DF] section 4.4, parallel diffusion drafting; [TRY] appendix on the
@@ -206,7 +234,7 @@ int dflash_inject_ctx(const dflash_model* draft, dflash_kv* draft_ctx, const voi
  *   logits_dbg device float [batch, block-1, vocab] or NULL (out)
  *   hidden_dbg device float [n_layers+1, batch, block, hidden] or NULL (out): residual
  *              stream after the embedding and after each layer.
- * 1 <= block <= 64; the cache must hold >= seq_len[b] context rows (it is only read).
+ * 1 <= block <= 64; the cache is only read (len_bound <= capacity_tokens).
  */
 int dflash_draft_block(const dflash_model* draft, const dflash_kv* draft_ctx,
                        const int32_t* anchor, int32_t block, int32_t* draft_ids,
@@ -229,8 +257,8 @@ int dflash_draft_block(const dflash_model* draft, const dflash_kv* draft_ctx,
  *   tau, bonus    device int32 [batch] (out): a = leading j with d_j == g_{j-1},
  *                 tau = a + 1 in [1, block], bonus = g_a (the next anchor).
  *   logits_dbg    device float [batch, block, vocab] or NULL; hidden_dbg as in draft_block.
- * The cache must map positions up to seq_len[b] + block - 1 (else the row is skipped and
- * DFLASH_DEVERR_PAGE is flagged).
+ * The cache must map positions up to seq_len[b] + block - 1: len_bound + block <=
+ * capacity_tokens, else DFLASH_E_CAPACITY before any launch.
  */
 int dflash_verify_accept(const dflash_model* target, dflash_kv* target_kv,
                          const int32_t* anchor, const int32_t* draft_ids, int32_t block,
@@ -328,7 +356,9 @@ int dflash_draft_block_select(const dflash_model* draft, const dflash_kv* draft_
  * from the updated context): seq_len[b] += tau[b] in the target cache and in the drafter
  * context (either may be NULL).  Rows written beyond the new length by verify_accept or
  * inject_ctx are left in place and are overwritten by later calls: rollback is a length
- * truncation.  tau outside [1, block] is clamped and flagged DFLASH_DEVERR_TAU.
+ * truncation.  tau outside [1, block] is clamped and flagged DFLASH_DEVERR_TAU.  Each
+ * given cache needs len_bound + block <= capacity_tokens (else DFLASH_E_CAPACITY, nothing
+ * changed); on success its len_bound grows by block.
  */
 int dflash_kv_commit(dflash_kv* target_kv, dflash_kv* draft_ctx, const int32_t* tau,
                      int32_t block, void* stream);

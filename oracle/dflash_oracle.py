@@ -16,11 +16,13 @@ no blocking, fusion or reordering.  Readings taken where the pages are silent ar
 listed beside the function that takes them.
 
 Storage type (reading): the models the pages measure are held in bfloat16, so the
-buffers that carry values between passes - the K/V cache and the tapped features the
+buffers that carry values between passes - the K/V caches and the tapped features the
 target hands to the drafter - hold bfloat16 values for such a model.  With
 ``store="bf16"`` K/V are rounded to bfloat16 (nearest, ties to even) where they are
-written, attention reads every key and value as stored (the block's own included) and
-tapped features are rounded where they are handed over; all arithmetic stays in the
+written into a cache (the drafter's context by injection, the target's cache by the
+verification pass, whose block rows then attend to their own keys as stored) and tapped
+features are rounded where they are handed over.  The drafter's own block K/V live only
+for its pass and are never stored, so they are not rounded.  All arithmetic stays in the
 working float type.  ``store=None`` (float32 models) rounds nothing.
 
 Conventions: a model's weights are a dict (keys as produced by ``synth.model_weights``),
@@ -195,8 +197,11 @@ def decoder_layer(h, w, i, shape, positions, ctx_k, ctx_v, causal, dt=np.float32
     masked-diffusion block), keys j' <= j for the target's verification pass
     ([TRY] Fig. 1, causal attention in the main model).  The context rows take no part
     in Q, O, the residual or the FFN ([DF §4.3]).  FFN: SwiGLU (the drafter is
-    described as Qwen-style in [TRY]'s appendix).  The block's K/V enter attention as
-    stored (`store`).  A DFlash 2 drafter's weights may hold the two-tap convolutions
+    described as Qwen-style in [TRY]'s appendix).  The verification pass writes the
+    block's K/V into the target's cache, so there they enter attention as stored
+    (`store`); the drafter's block K/V are never stored ([DF §4.3]: the draft block's
+    keys are not part of the injected context) and enter unrounded.  The returned k_blk,
+    v_blk are the stored rows when causal.  A DFlash 2 drafter's weights may hold the two-tap convolutions
     (keys L{i}.dconv_{pre_attn,post_attn,pre_ffn,post_ffn}.{base,w_k}).  Returns (h_out,
     k_blk, v_blk)."""
     T = h.shape[0]
@@ -207,8 +212,9 @@ def decoder_layer(h, w, i, shape, positions, ctx_k, ctx_v, causal, dt=np.float32
     kb = (u @ np.asarray(w[f"L{i}.wk"], dtype=dt).T).reshape(T, Hkv, d)
     vb = (u @ np.asarray(w[f"L{i}.wv"], dtype=dt).T).reshape(T, Hkv, d)
     q = rope(q, positions, shape.rope_base, dt)
-    kb = to_storage(rope(kb, positions, shape.rope_base, dt), store)
-    vb = to_storage(vb, store)
+    kb = rope(kb, positions, shape.rope_base, dt)
+    if causal:   # written into the target's cache
+        kb, vb = to_storage(kb, store), to_storage(vb, store)
 
     n = 0 if ctx_k is None else ctx_k.shape[0]
     visible = np.ones((T, n + T), dtype=bool)

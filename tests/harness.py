@@ -125,8 +125,8 @@ def inject_all(setup: Setup, kv, feats_per_seq, ws, chunk=None):
     for a in range(0, R, step):
         e = min(R, a + step)
         rt.inject_ctx(setup.draft, kv, F[a:e].contiguous(), rs[a:e].contiguous(),
-                      rp[a:e].contiguous(), 0, ws)
-    kv.seq_len.copy_(torch.tensor([f.shape[0] for f in feats_per_seq], dtype=torch.int32))
+                      rp[a:e].contiguous(), 0, max(f.shape[0] for f in feats_per_seq), ws)
+    kv.set_seq_len([f.shape[0] for f in feats_per_seq])
 
 
 def read_cache(kv, layer, b, n):

@@ -97,6 +97,7 @@ def test_workspace_bytes_and_entry_validation():
         pools = (ctypes.c_void_p * 1)(0x2000)
         kv.k_pool = kv.v_pool = ctypes.cast(pools, ctypes.POINTER(ctypes.c_void_p))
         kv.block_table = kv.seq_len = 0x3000
+        kv.capacity_tokens, kv.len_bound = 256, 0
         L = _lib.lib()
         one = ctypes.c_void_p(0x4000)
         # every rejection below happens on the host, before any kernel launch
@@ -114,7 +115,7 @@ def test_workspace_bytes_and_entry_validation():
                                       None, one, 1 << 30, None) == -1
         kv.head_dim = 128
         # drafter-only call on a model without W_c
-        assert L.dflash_inject_ctx(h, ctypes.byref(kv), one, 4, one, one, 0, one, 1 << 30, None) == -1
+        assert L.dflash_inject_ctx(h, ctypes.byref(kv), one, 4, one, one, 0, 1, one, 1 << 30, None) == -1
         assert L.dflash_kv_commit(None, None, one, 16, None) == -1
         assert L.dflash_kv_commit(ctypes.byref(kv), None, one, 0, None) == -2
         # sampling entry points: temperature, counter, required logits buffers, block >= 2
@@ -152,6 +153,58 @@ def test_workspace_bytes_and_entry_validation():
             assert call() == code, field
             assert _lib.selector_workspace_bytes(h, sel, 1, 16) == 0
             setattr(sel, field, keep)
+    finally:
+        _lib.model_destroy(h)
+
+
+def _kv(capacity_tokens, len_bound, max_pages=4):
+    kv = _lib.KV()
+    kv.n_layers, kv.n_kv_heads, kv.head_dim, kv.page_size = 1, 2, 128, 64
+    kv.batch, kv.max_pages_per_seq, kv.num_pages = 2, max_pages, 2 * max_pages
+    pools = (ctypes.c_void_p * 1)(0x2000)
+    kv._pools = pools
+    kv.k_pool = kv.v_pool = ctypes.cast(pools, ctypes.POINTER(ctypes.c_void_p))
+    kv.block_table = kv.seq_len = 0x3000
+    kv.capacity_tokens, kv.len_bound = capacity_tokens, len_bound
+    return kv
+
+
+def test_capacity_is_refused_on_the_host_before_any_launch():
+    """[DF] section 4.5: verification writes the block's K/V at n .. n+B-1 before acceptance
+    is known.  A call whose rows could pass the mapped positions (capacity_tokens, with the
+    host-side bound len_bound on every sequence length) returns DFLASH_E_CAPACITY (-4)
+    without launching anything (no GPU here: a launch would fail differently)."""
+    ptrs = (ctypes.c_void_p * 2)(0x1000, 0x1000)
+    st, h = _create(_desc(w_c=ptrs[0], g_c=ptrs[1], n_taps=1))
+    assert st == 0
+    L = _lib.lib()
+    one = ctypes.c_void_p(0x4000)
+    big = 1 << 34
+    try:
+        kv = _kv(capacity_tokens=256, len_bound=250)
+        # verify writes 16 rows at positions up to 250 + 15 >= 256
+        assert L.dflash_verify_accept(h, ctypes.byref(kv), one, one, 16, None, one, one, one, None,
+                                      None, one, big, None) == -4
+        assert L.dflash_verify_sampled(h, ctypes.byref(kv), one, one, one, 16, 1.0, 1, 0, None, one,
+                                       one, one, one, big, None) == -4
+        # commit could advance a length past the mapped pages; the bound is left unchanged
+        assert L.dflash_kv_commit(ctypes.byref(kv), None, one, 16, None) == -4
+        assert L.dflash_kv_commit(None, ctypes.byref(kv), one, 16, None) == -4
+        assert kv.len_bound == 250
+        # injection: absolute rows up to pos_limit, relative rows up to len_bound + pos_limit
+        assert L.dflash_inject_ctx(h, ctypes.byref(kv), one, 4, one, one, 0, 257, one, big, None) == -4
+        assert L.dflash_inject_ctx(h, ctypes.byref(kv), one, 4, one, one, 1, 16, one, big, None) == -4
+        assert L.dflash_inject_ctx(h, ctypes.byref(kv), one, 4, one, one, 1, 0, one, big, None) == -1
+        # the drafter only reads its context, which must lie inside the mapped pages
+        kv.len_bound = 257
+        assert L.dflash_draft_block(h, ctypes.byref(kv), one, 16, one, None, None, one, big, None) == -4
+        assert L.dflash_draft_block_sampled(h, ctypes.byref(kv), one, 16, 1.0, 1, 0, one, one, one,
+                                            big, None) == -4
+        # inconsistent host fields are argument errors
+        for cap, bound in ((257, 0), (-1, 0), (256, -1)):
+            kv = _kv(capacity_tokens=cap, len_bound=bound)
+            assert L.dflash_verify_accept(h, ctypes.byref(kv), one, one, 16, None, one, one, one,
+                                          None, None, one, big, None) == -1, (cap, bound)
     finally:
         _lib.model_destroy(h)
 

@@ -49,7 +49,7 @@ def test_draft_and_verify_at_each_block_size():
         for l in range(T.n_layers):
             for b, n in enumerate(lens):
                 tkv.write_dense(l, b, dense[l][b][0], dense[l][b][1])
-        tkv.seq_len.copy_(torch.tensor(lens, dtype=torch.int32))
+        tkv.set_seq_len(lens)
         np_cache = [[(synth.to_numpy(dense[l][b][0]), synth.to_numpy(dense[l][b][1]))
                      for l in range(T.n_layers)] for b in range(len(lens))]
         rng = np.random.default_rng(B)
@@ -104,7 +104,7 @@ def test_mixed_block_schedule_reproduces_greedy_decoding():
     def inject_rel(feats, blk):
         rs = torch.arange(batch, dtype=torch.int32, device=DEV).repeat_interleave(blk)
         rp = torch.arange(blk, dtype=torch.int32, device=DEV).repeat(batch)
-        rt.inject_ctx(S.draft, dkv, feats.reshape(batch * blk, -1).contiguous(), rs, rp, 1, ws_d)
+        rt.inject_ctx(S.draft, dkv, feats.reshape(batch * blk, -1).contiguous(), rs, rp, 1, blk, ws_d)
 
     ids = torch.tensor(np.stack(prompts), dtype=torch.int32, device=DEV)
     feats, g, _, _ = verify(ids[:, 0].contiguous(), ids[:, 1:].contiguous(), n0)
@@ -121,6 +121,8 @@ def test_mixed_block_schedule_reproduces_greedy_decoding():
         feats, g, tau, bonus = verify(anchor, drafts, B)
         inject_rel(feats, B)
         rt.kv_commit(tkv, dkv, tau, B)
+        tkv.refresh_len_bound()
+        dkv.refresh_len_bound()
         t, bo, d = tau.cpu().numpy(), bonus.cpu().numpy(), drafts.cpu().numpy()
         for b in range(batch):
             assert 1 <= t[b] <= B

@@ -62,7 +62,7 @@ def test_injection_outside_the_pages_is_flagged_and_writes_nothing():
     f = synth.features(w, 2, DEV, tag="feats.extra")
     row_seq = torch.tensor([0, w.batch], dtype=torch.int32, device=DEV)   # 2nd: no such sequence
     row_pos = torch.tensor([kv.capacity + 5, 0], dtype=torch.int32, device=DEV)
-    rt.inject_ctx(S.draft, kv, f, row_seq, row_pos, 0, ws)
+    rt.inject_ctx(S.draft, kv, f, row_seq, row_pos, 0, kv.capacity, ws)   # row 0 past pos_limit
     torch.cuda.synchronize()
     assert kv.err.item() & _lib.DEVERR_PAGE
     for a, b in zip(before, kv.k + kv.v):
@@ -74,7 +74,7 @@ def test_empty_injection_is_a_no_op():
     before = [t.clone() for t in kv.k + kv.v]
     f = synth.features(w, 0, DEV, tag="feats.none")
     empty = torch.zeros(0, dtype=torch.int32, device=DEV)
-    rt.inject_ctx(S.draft, kv, f, empty, empty, 0, ws)
+    rt.inject_ctx(S.draft, kv, f, empty, empty, 0, 1, ws)
     torch.cuda.synchronize()
     assert kv.err.item() == 0
     for a, b in zip(before, kv.k + kv.v):
@@ -88,3 +88,33 @@ def test_commit_clamps_and_flags_tau():
     torch.cuda.synchronize()
     assert kv.err.item() & _lib.DEVERR_TAU
     assert kv.seq_len.cpu().tolist() == [lens[0] + 1, lens[1] + w.block, lens[2] + 2]
+
+
+def test_selector_with_out_of_range_anchor_is_flagged():
+    """The path selector gathers the anchor's embedding row for its first pair scores: an
+    anchor outside the vocabulary is read as row 0 and flagged, like the embedding does,
+    and the other sequences' picks are unaffected."""
+    w, S, kv, ws, lens = _drafter()
+    sw = synth.selector_weights(w, rank=64, device=DEV)
+    sel = rt.Selector(S.draft, sw["w_a"].to(torch.bfloat16), sw["w_b"].to(torch.bfloat16),
+                      sw["w_h"].to(torch.bfloat16), top_k=8)
+    sws = rt.Workspace(sel.workspace_bytes(S.draft, w.batch, w.block), DEV)
+    B, V = w.block, w.draft.vocab
+
+    def run(anchor):
+        ids = torch.zeros(w.batch, B - 1, dtype=torch.int32, device=DEV)
+        zd = torch.zeros(w.batch, B - 1, V, device=DEV)
+        rt.draft_block_select(S.draft, kv, anchor, B, sel, ids, zd, ws, sws)
+        torch.cuda.synchronize()
+        return ids.cpu()
+
+    anchor = synth.anchors(w, DEV)
+    clean = run(anchor)
+    assert kv.err.item() == 0
+    for bad_id in (V + 1000, -5):
+        bad = anchor.clone()
+        bad[1] = bad_id
+        kv.err.zero_()
+        ids = run(bad)
+        assert kv.err.item() & _lib.DEVERR_TOKEN
+        assert torch.equal(ids[0], clean[0]) and torch.equal(ids[2], clean[2])

@@ -66,8 +66,8 @@ def test_qwen3_8b_batch1_ctx4k():
     seq = torch.zeros(512, dtype=torch.int32, device=DEV)
     for a in range(0, n, 512):
         rt.inject_ctx(S.draft, kv, feats[a:a + 512].contiguous(), seq,
-                      torch.arange(a, a + 512, dtype=torch.int32, device=DEV), 0, ws)
-    kv.seq_len.fill_(n)
+                      torch.arange(a, a + 512, dtype=torch.int32, device=DEV), 0, a + 512, ws)
+    kv.set_seq_len(n)
     anchor = synth.anchors(w, DEV)
     ids, logits, hid = _draft_outputs(S, kv, B, 1)
     rt.draft_block(S.draft, kv, anchor, B, ids, ws, logits, hid)
@@ -146,7 +146,7 @@ def test_qwen3_8b_batch16_paged_ragged():
     for l in range(w.draft.n_layers):
         for b in range(batch):
             kv.write_dense(l, b, dense[l][b][0], dense[l][b][1])
-    kv.seq_len.copy_(torch.tensor(lens, dtype=torch.int32))
+    kv.set_seq_len(lens)
     ctx_np = [[(synth.to_numpy(dense[l][b][0]), synth.to_numpy(dense[l][b][1]))
                for l in range(w.draft.n_layers)] for b in range(batch)]
     del dense
@@ -165,7 +165,7 @@ def test_qwen3_8b_batch16_paged_ragged():
     feats = synth.features(w, batch * B, DEV, tag="cycle.feats")
     rs = torch.arange(batch, dtype=torch.int32, device=DEV).repeat_interleave(B)
     rp = torch.arange(B, dtype=torch.int32, device=DEV).repeat(batch)
-    rt.inject_ctx(S.draft, kv, feats, rs, rp, 1, ws)
+    rt.inject_ctx(S.draft, kv, feats, rs, rp, 1, B, ws)
     torch.cuda.synchronize()
     assert kv.err.item() == 0
     f_np = synth.to_numpy(feats)
@@ -190,14 +190,15 @@ def test_qwen3_8b_batch1_ctx256k():
         ctx_np.append([synth.to_numpy(k), synth.to_numpy(v)])
         del k, v
     _free()
-    kv.seq_len.fill_(n)
+    kv.set_seq_len(n)
     # two 512-row injection chunks overwrite context rows, one at the far end of the context
     chunk = w.inject_chunk
     ws = S.workspace(S.draft, B, kv.capacity, inject_rows=chunk)
     seq = torch.zeros(chunk, dtype=torch.int32, device=DEV)
     for p0 in (4096, n - chunk):
         feats = synth.features(w, chunk, DEV, tag=f"chunk.{p0}")
-        rt.inject_ctx(S.draft, kv, feats, seq, torch.arange(p0, p0 + chunk, dtype=torch.int32, device=DEV), 0, ws)
+        rt.inject_ctx(S.draft, kv, feats, seq, torch.arange(p0, p0 + chunk, dtype=torch.int32, device=DEV), 0,
+                      p0 + chunk, ws)
         inj = O.inject(synth.to_numpy(feats), p0 + np.arange(chunk), S.np_dw, w.draft, store=S.store)
         torch.cuda.synchronize()
         for l in range(w.draft.n_layers):
@@ -229,7 +230,7 @@ def test_qwen3_8b_cycle_batch8_target8():
         for l in range(L):
             for b in range(batch):
                 kvc.write_dense(l, b, dense[l][b][0], dense[l][b][1])
-        kvc.seq_len.copy_(torch.tensor(lens, dtype=torch.int32))
+        kvc.set_seq_len(lens)
     t_np = [[(synth.to_numpy(tctx[l][b][0]), synth.to_numpy(tctx[l][b][1])) for l in range(T.n_layers)]
             for b in range(batch)]
     d_np = [[(synth.to_numpy(dctx[l][b][0]), synth.to_numpy(dctx[l][b][1])) for l in range(D.n_layers)]
@@ -295,7 +296,7 @@ def test_qwen3_8b_cycle_batch8_target8():
     # inject all B verified rows at the old lengths, then commit tau
     rs = torch.arange(batch, dtype=torch.int32, device=DEV).repeat_interleave(B)
     rp = torch.arange(B, dtype=torch.int32, device=DEV).repeat(batch)
-    rt.inject_ctx(S.draft, dkv, feats.reshape(batch * B, -1).contiguous(), rs, rp, 1, ws_d)
+    rt.inject_ctx(S.draft, dkv, feats.reshape(batch * B, -1).contiguous(), rs, rp, 1, B, ws_d)
     rt.kv_commit(tkv, dkv, tau, B)
     torch.cuda.synchronize()
     assert dkv.err.item() == 0 and tkv.err.item() == 0

@@ -63,7 +63,7 @@ def _target_cache(S, lens, B):
     for l in range(w.target.n_layers):
         for b, n in enumerate(lens):
             kv.write_dense(l, b, dense[l][b][0], dense[l][b][1])
-    kv.seq_len.copy_(torch.tensor(lens, dtype=torch.int32))
+    kv.set_seq_len(lens)
     np_cache = [[(synth.to_numpy(dense[l][b][0]), synth.to_numpy(dense[l][b][1]))
                  for l in range(w.target.n_layers)] for b in range(len(lens))]
     return kv, np_cache
@@ -243,7 +243,7 @@ def test_speculative_cycles_reproduce_greedy_decoding(name):
     def inject_rel(feats, blk):
         rs = torch.arange(batch, dtype=torch.int32, device=DEV).repeat_interleave(blk)
         rp = torch.arange(blk, dtype=torch.int32, device=DEV).repeat(batch)
-        rt.inject_ctx(S.draft, dkv, feats.reshape(batch * blk, -1).contiguous(), rs, rp, 1, ws_d)
+        rt.inject_ctx(S.draft, dkv, feats.reshape(batch * blk, -1).contiguous(), rs, rp, 1, blk, ws_d)
 
     # prefill: one causal pass over the prompt, inject its features, advance both caches
     ids = torch.tensor(np.stack(prompts), dtype=torch.int32, device=DEV)
@@ -258,6 +258,8 @@ def test_speculative_cycles_reproduce_greedy_decoding(name):
         feats, g, tau, bonus = verify(anchor, drafts, B)
         inject_rel(feats, B)
         rt.kv_commit(tkv, dkv, tau, B)
+        tkv.refresh_len_bound()
+        dkv.refresh_len_bound()
         t, bo, d = tau.cpu().numpy(), bonus.cpu().numpy(), drafts.cpu().numpy()
         for b in range(batch):
             emitted[b] += [int(x) for x in d[b, : t[b] - 1]] + [int(bo[b])]

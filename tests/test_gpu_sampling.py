@@ -66,7 +66,7 @@ def _target_cache(S, lens, B):
     for l in range(w.target.n_layers):
         for b, n in enumerate(lens):
             kv.write_dense(l, b, dense[l][b][0], dense[l][b][1])
-    kv.seq_len.copy_(torch.tensor(lens, dtype=torch.int32))
+    kv.set_seq_len(lens)
     np_cache = [[(synth.to_numpy(dense[l][b][0]), synth.to_numpy(dense[l][b][1]))
                  for l in range(w.target.n_layers)] for b in range(len(lens))]
     return kv, np_cache
@@ -171,7 +171,7 @@ def test_sampled_cycles_keep_the_caches_in_step():
                      bonus, ws_t)
     rs = torch.arange(batch, dtype=torch.int32, device=DEV).repeat_interleave(n0)
     rp = torch.arange(n0, dtype=torch.int32, device=DEV).repeat(batch)
-    rt.inject_ctx(S.draft, dkv, feats.reshape(batch * n0, -1).contiguous(), rs, rp, 1, ws_d)
+    rt.inject_ctx(S.draft, dkv, feats.reshape(batch * n0, -1).contiguous(), rs, rp, 1, n0, ws_d)
     rt.kv_commit(tkv, dkv, torch.full((batch,), n0, dtype=torch.int32, device=DEV), n0)
     anchor = g[:, -1].contiguous()
     drafts = torch.zeros(batch, B - 1, dtype=torch.int32, device=DEV)
@@ -184,8 +184,10 @@ def test_sampled_cycles_keep_the_caches_in_step():
     for c in range(4):
         rt.draft_block_sampled(S.draft, dkv, anchor, B, 1.0, SEED, c, drafts, zd, ws_d)
         rt.verify_sampled(S.target, tkv, anchor, drafts, zd, B, 1.0, SEED, c, fo, zt, tau, nxt, ws_t)
-        rt.inject_ctx(S.draft, dkv, fo.reshape(batch * B, -1).contiguous(), rs, rp, 1, ws_d)
+        rt.inject_ctx(S.draft, dkv, fo.reshape(batch * B, -1).contiguous(), rs, rp, 1, B, ws_d)
         rt.kv_commit(tkv, dkv, tau, B)
+        tkv.refresh_len_bound()
+        dkv.refresh_len_bound()
         t = tau.cpu().numpy()
         assert ((1 <= t) & (t <= B)).all()
         anchor = nxt.clone()

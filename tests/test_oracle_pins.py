@@ -556,3 +556,21 @@ def test_bf16_storage_applies_to_cache_rows_and_taps():
     g0, z0, f0, _, hid0 = O.target_forward(tw, sh, TINY_TGT, None, [3, 5, 7], 0, (0, 2), F64)
     assert np.array_equal(hid[0], hid0[0])
     assert 0 < np.max(np.abs(hid[1] - hid0[1])) < 1e-2 * np.max(np.abs(hid0[1]))
+
+
+def test_drafter_block_keys_are_not_stored_but_verified_rows_are():
+    """Storage rounding applies where a cache is written, nothing else.  The drafter's own
+    block K/V live only for its pass ([DF] section 4.3: the draft block's keys are not part
+    of the injected context), so with an empty context a bf16-storage drafter computes
+    exactly what an unrounded one does; the target's verification pass writes the block
+    into its cache, so its block rows attend to rounded keys and return rounded K/V."""
+    wl, dw, tw, sh = _models(933)
+    ids_r, z_r, hid_r = O.draft_block(dw, sh, TINY_SHAPE, None, 5, 0, 4, F64, store="bf16")
+    ids_p, z_p, hid_p = O.draft_block(dw, sh, TINY_SHAPE, None, 5, 0, 4, F64)
+    assert np.array_equal(z_r, z_p) and np.array_equal(hid_r, hid_p)
+    # a plain decoder layer call: the non-causal (drafter) pass returns unrounded rows
+    h = np.asarray(sh["embed"], dtype=F64)[[5, 9, 9, 9]]
+    _, kb, vb = O.decoder_layer(h, dw, 0, TINY_SHAPE, np.arange(4), None, None, False, F64, "bf16")
+    assert not np.array_equal(kb, O.to_storage(kb, "bf16"))
+    _, kb, vb = O.decoder_layer(h, dw, 0, TINY_SHAPE, np.arange(4), None, None, True, F64, "bf16")
+    assert np.array_equal(kb, O.to_storage(kb, "bf16")) and np.array_equal(vb, O.to_storage(vb, "bf16"))
