@@ -21,7 +21,9 @@ EXPORTS = ("dflash_model_create", "dflash_model_destroy", "dflash_status_str",
            "dflash_workspace_bytes", "dflash_inject_ctx", "dflash_draft_block",
            "dflash_verify_accept", "dflash_kv_commit", "dflash_timing_arm",
            "dflash_timing_read", "dflash_draft_block_sampled", "dflash_verify_sampled",
-           "dflash_selector_workspace_bytes", "dflash_draft_block_select")
+           "dflash_selector_workspace_bytes", "dflash_draft_block_select",
+           "dflash_draft_block_noalloc")
+NOALLOC_SCRATCH_BYTES = 64 << 20
 KERNEL_LM_HEAD, KERNEL_GEMM_QKV, KERNEL_GEMM_O, KERNEL_GEMM_GATE_UP, KERNEL_GEMM_DOWN, \
     KERNEL_ATTENTION, KERNEL_INJECT_FUSE, KERNEL_INJECT_KV = range(8)
 
@@ -79,6 +81,9 @@ def lib():
         L.dflash_draft_block.argtypes = [c_void_p, POINTER(KV), c_void_p, c_int32, c_void_p,
                                          c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
         L.dflash_draft_block.restype = c_int32
+        L.dflash_draft_block_noalloc.argtypes = [c_void_p, POINTER(KV), c_void_p, c_int32, c_void_p,
+                                                 c_void_p, c_void_p, c_void_p]
+        L.dflash_draft_block_noalloc.restype = c_int32
         L.dflash_verify_accept.argtypes = [c_void_p, POINTER(KV), c_void_p, c_void_p, c_int32,
                                            c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                            c_void_p, c_void_p, c_size_t, c_void_p]
@@ -141,6 +146,12 @@ def draft_block(handle, kv: KV, anchor, block, draft_ids, logits_dbg, hidden_dbg
                 stream) -> int:
     return lib().dflash_draft_block(c_void_p(handle), ctypes.byref(kv), anchor, block, draft_ids,
                                     logits_dbg, hidden_dbg, ws, ws_bytes, stream)
+
+
+def draft_block_noalloc(handle, kv: KV, anchor, block, draft_ids, logits_dbg, hidden_dbg,
+                        stream) -> int:
+    return lib().dflash_draft_block_noalloc(c_void_p(handle), ctypes.byref(kv), anchor, block,
+                                            draft_ids, logits_dbg, hidden_dbg, stream)
 
 
 def verify_accept(handle, kv: KV, anchor, draft_ids, block, feats_out, target_argmax, tau, bonus,

@@ -16,6 +16,7 @@
 // and the LM head is one GEMM with RMSNorm(g_f) on the A side and an argmax epilogue.
 #include <string.h>
 
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -475,6 +476,31 @@ int check_selector(const dflash_model* m, const dflash_selector* s) {
 
 }  // namespace
 
+// Scratch of dflash_draft_block_noalloc: one array per GPU, part of the library's code
+// object.  Host code must not use the symbol itself as a device address (in host code it
+// names a host-side stand-in): the address comes from hipGetSymbolAddress, per device.
+static __device__ __align__(256) char scratch[DFLASH_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+#define NOALLOC_MAX_DEVICES 64
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[NOALLOC_MAX_DEVICES] = {};
+
+// device address of the current device's scratch (looked up once per device)
+int scratch_for_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= NOALLOC_MAX_DEVICES) return DFLASH_E_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return DFLASH_E_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return DFLASH_OK;
+}
+}  // namespace
+
 extern "C" {
 
 const char* dflash_status_str(int s) {
@@ -615,6 +641,22 @@ int dflash_draft_block(const dflash_model* m, const dflash_kv* kv, const int32_t
                        void* ws, size_t ws_bytes, void* stream) {
   return draft_block_impl(m, kv, anchor, block, draft_ids, logits_dbg, hidden_dbg, ws, ws_bytes,
                           stream, Sampling());
+}
+
+int dflash_draft_block_noalloc(const dflash_model* m, const dflash_kv* kv, const int32_t* anchor,
+                               int32_t block, int32_t* draft_ids, float* logits_dbg,
+                               float* hidden_dbg, void* stream) {
+  if (!m || !anchor || !draft_ids) return DFLASH_E_ARG;
+  if (block < 1 || block > 64) return DFLASH_E_SHAPE;
+  int e = check_kv(m, kv);
+  if (e) return e;
+  const size_t need = step_ws(m, kv->batch, block, kv->max_pages_per_seq * 64, nullptr, nullptr);
+  if (need > DFLASH_NOALLOC_SCRATCH_BYTES) return DFLASH_E_WORKSPACE;
+  void* ws = nullptr;
+  e = scratch_for_current_device(&ws);
+  if (e) return e;
+  return draft_block_impl(m, kv, anchor, block, draft_ids, logits_dbg, hidden_dbg, ws, need, stream,
+                          Sampling());
 }
 
 int dflash_draft_block_sampled(const dflash_model* m, const dflash_kv* kv, const int32_t* anchor,

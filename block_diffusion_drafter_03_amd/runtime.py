@@ -238,6 +238,14 @@ def draft_block(model: Model, kv: PagedKV, anchor, block, draft_ids, ws: Workspa
     _lib._check(st, "dflash_draft_block")
 
 
+def draft_block_noalloc(model: Model, kv: PagedKV, anchor, block, draft_ids, logits_dbg=None,
+                        hidden_dbg=None):
+    """draft_block with the library's own per-GPU scratch instead of a workspace."""
+    st = _lib.draft_block_noalloc(model.handle, kv.struct, _ptr(anchor), int(block), _ptr(draft_ids),
+                                  _ptr(logits_dbg), _ptr(hidden_dbg), _stream())
+    _lib._check(st, "dflash_draft_block_noalloc")
+
+
 def verify_accept(model: Model, kv: PagedKV, anchor, draft_ids, block, feats_out, target_argmax,
                   tau, bonus, ws: Workspace, logits_dbg=None, hidden_dbg=None):
     """anchor [batch] and draft_ids [batch, block-1] (contiguous int32) form the block."""

@@ -242,6 +242,27 @@ int dflash_draft_block(const dflash_model* draft, const dflash_kv* draft_ctx,
                        void* stream);
 
 /*
+ * dflash_draft_block without a workspace argument, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation).  It runs the same kernels as dflash_draft_block; their scratch lives in one
+ * array of DFLASH_NOALLOC_SCRATCH_BYTES bytes compiled into the library, one copy per GPU,
+ * held until the process ends.  Its device address is looked up once per device on the
+ * first call made with that device current; nothing is allocated, then or later.
+ *   Limit: the scratch the call needs (dflash_workspace_bytes(draft, batch, block,
+ *   max_pages_per_seq * page_size, 0)) must fit DFLASH_NOALLOC_SCRATCH_BYTES, else
+ *   DFLASH_E_WORKSPACE before any launch.  64 MiB holds e.g. a Qwen3-8B-shaped drafter
+ *   step of 16 sequences x 16 rows over 8K-token caches.
+ *   Sharing: every call on one GPU uses that GPU's single array, which keeps the last
+ *   call's contents (the kernels initialise what they read).  Calls that may overlap on
+ *   one GPU (different streams or threads) race on it: serialise them.
+ * Other arguments, outputs and errors as dflash_draft_block.
+ */
+#define DFLASH_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int dflash_draft_block_noalloc(const dflash_model* draft, const dflash_kv* draft_ctx,
+                               const int32_t* anchor, int32_t block, int32_t* draft_ids,
+                               float* logits_dbg, float* hidden_dbg, void* stream);
+
+/*
  * Block verification and greedy acceptance ([DF] section 4.5 steps 2-3; [TRY] Fig. 1:
  * the main model checks the block with causal attention in one parallel pass).
  * The target runs the block y = [x, d_1 .. d_{block-1}] (x = anchor[b], d = draft_ids[b])

@@ -209,6 +209,24 @@ def test_capacity_is_refused_on_the_host_before_any_launch():
         _lib.model_destroy(h)
 
 
+def test_noalloc_draft_block_refuses_steps_past_its_scratch():
+    """dflash_draft_block_noalloc runs only steps whose scratch fits the library's array:
+    a larger one is DFLASH_E_WORKSPACE (-5) on the host, before any launch or lookup."""
+    st, h = _create(_desc())
+    assert st == 0
+    L = _lib.lib()
+    one = ctypes.c_void_p(0x4000)
+    try:
+        kv = _kv(capacity_tokens=256, len_bound=0)
+        kv.batch = 1024                       # 1024 x 64 rows of 256 floats: 64 MiB of h alone
+        assert _lib.workspace_bytes(h, 1024, 64, 256, 0) > _lib.NOALLOC_SCRATCH_BYTES
+        assert L.dflash_draft_block_noalloc(h, ctypes.byref(kv), one, 64, one, None, None, None) == -5
+        assert L.dflash_draft_block_noalloc(h, ctypes.byref(kv), one, 65, one, None, None, None) == -2
+        assert L.dflash_draft_block_noalloc(h, ctypes.byref(kv), None, 16, one, None, None, None) == -1
+    finally:
+        _lib.model_destroy(h)
+
+
 def test_product_path_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "_lib", None)
     monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
