@@ -7,10 +7,13 @@ configuration the bench uses.
  * batch 16, contexts in [2048, 8192], 64-token pages in shuffled order: the M = 256 tiled
    GEMM path and the ragged paged attention; injection of the 16 block rows of every
    sequence at its own position.
- * batch 1, 262144-row context: split-K attention over the whole context, plus two
-   512-row injection chunks at positions up to 262143 (RoPE at large positions).
- * batch 8 with an 8-layer target over 8192-token caches: draft, verify (forced and random
-   drafts), accept, inject of the verified rows, commit.
+ * batch 1, 262144-row context: split-K attention over the whole context, plus nine
+   512-row injection chunks (8 at seeded random places and the last one, positions up to
+   262143: RoPE at large positions).
+ * batch 8 with an 8-layer target over 8192-token caches: two full cycles of every
+   sequence under the seeded p = 0.7 acceptance-forcing rule - draft, verify, accept,
+   inject of the verified rows, commit - with both caches' committed rows checked.
+ * the 4K, batch-16 and 262K draft blocks run twice with bitwise identical results.
 
 The oracle cannot afford to inject 80K-262K context rows (20-66 TFLOP on the host), so
 for the long contexts both sides read the same synthetic context K/V (N(0, 1), taken as
@@ -56,6 +59,17 @@ def _check_draft(S, b, ctx_np, n, anchor, ids, logits, hid, what, block=None):
     return assert_ids(ids[b].cpu().numpy(), o_ids, o_z, f"{what} draft ids")
 
 
+def _repeat_is_bitwise(S, kv, anchor, B, batch, ws, first, what):
+    """The same draft block run again: ids, logits and hidden states bit for bit (the
+    argmax's 64-bit atomic maxima and the split-K merge run across many workgroups, so
+    this checks that no result depends on their timing)."""
+    again = _draft_outputs(S, kv, B, batch)
+    rt.draft_block(S.draft, kv, anchor, B, again[0], ws, again[1], again[2])
+    torch.cuda.synchronize()
+    for x, y, name in zip(first, again, ("ids", "logits", "hidden")):
+        assert torch.equal(x, y), f"{what}: repeated {name} differ"
+
+
 def test_qwen3_8b_batch1_ctx4k():
     w = synth.workload("qwen3_8b_b1_ctx4k")
     S = Setup(w)
@@ -80,6 +94,7 @@ def test_qwen3_8b_batch1_ctx4k():
         assert_close(V, ctx[l][1], TOLB, f"cfg 4k ctx V layer {l}")
     checked = _check_draft(S, 0, ctx, n, anchor[0], ids, logits, hid, "cfg 4k")
     assert checked >= 10    # the near-tie exclusion leaves most positions checked
+    _repeat_is_bitwise(S, kv, anchor, B, 1, ws, (ids, logits, hid), "cfg 4k")
     # the block size is a runtime argument: blocks of 8 and 10 on the same cache and
     # workspace (the schedule of a B = 16 design run at smaller B)
     for Bs in (8, 10):
@@ -161,6 +176,7 @@ def test_qwen3_8b_batch16_paged_ragged():
     for b, n in enumerate(lens):
         checked += _check_draft(S, b, ctx_np[b], n, anchor[b], ids, logits, hid, f"cfg b16 seq {b}")
     assert checked >= 10 * batch
+    _repeat_is_bitwise(S, kv, anchor, B, batch, ws, (ids, logits, hid), "cfg b16")
     # injection of every sequence's 16 block rows at its own (ragged) position, M = 256
     feats = synth.features(w, batch * B, DEV, tag="cycle.feats")
     rs = torch.arange(batch, dtype=torch.int32, device=DEV).repeat_interleave(B)
@@ -191,11 +207,14 @@ def test_qwen3_8b_batch1_ctx256k():
         del k, v
     _free()
     kv.set_seq_len(n)
-    # two 512-row injection chunks overwrite context rows, one at the far end of the context
+    # 512-row injection chunks overwrite context rows: 8 seeded random chunks (whole
+    # chunks of the context) plus the last one, at the far end of the context
     chunk = w.inject_chunk
     ws = S.workspace(S.draft, B, kv.capacity, inject_rows=chunk)
     seq = torch.zeros(chunk, dtype=torch.int32, device=DEV)
-    for p0 in (4096, n - chunk):
+    rng = np.random.Generator(np.random.PCG64(4096))
+    starts = sorted(int(x) * chunk for x in rng.choice(n // chunk - 1, size=8, replace=False))
+    for p0 in starts + [n - chunk]:
         feats = synth.features(w, chunk, DEV, tag=f"chunk.{p0}")
         rt.inject_ctx(S.draft, kv, feats, seq, torch.arange(p0, p0 + chunk, dtype=torch.int32, device=DEV), 0,
                       p0 + chunk, ws)
@@ -214,14 +233,39 @@ def test_qwen3_8b_batch1_ctx256k():
     assert kv.err.item() == 0
     checked = _check_draft(S, 0, [tuple(c) for c in ctx_np], n, anchor[0], ids, logits, hid, "cfg 256k")
     assert checked >= 10
+    _repeat_is_bitwise(S, kv, anchor, B, 1, ws, (ids, logits, hid), "cfg 256k")
+
+
+P_FORCE = 0.7          # the forcing rule's probability for the full-size cycle test
+FORCE_SEED = 4321
+CYCLES = 2
+
+
+def _greedy_continuation(S, T, cache, anchor, n, count):
+    """The oracle target's greedy tokens g*_0 .. g*_{count-1} after `anchor` at position n
+    (one causal pass per token over the growing block)."""
+    toks = [int(anchor)]
+    for _ in range(count):
+        g, _, _, _, _ = O.verify(S.np_tw, S.np_shared, T, cache, toks, n, (), store=S.store)
+        toks.append(int(g[-1]))
+    return toks[1:]
 
 
 def test_qwen3_8b_cycle_batch8_target8():
+    """Full speculative cycles of the batch-8 workload, every sequence against the oracle:
+    draft (hidden states, logits, ids), the seeded p = 0.7 forcing rule (drafts taken from
+    the oracle's own greedy continuation of the target, a forced mismatch after the run of
+    heads), verify (hidden states, logits, argmax, tapped features, the block's K/V in every
+    target layer), acceptance (tau, bonus; tau = f + 1 under the rule), injection and commit
+    (the committed rows of every layer of both caches), then the next cycle from the bonus
+    token.  A sequence whose (tau, bonus) differs from the oracle's - allowed only where
+    the oracle decides them by a near-tie - leaves the comparison from there on (the two
+    sides then hold different lengths)."""
     w = synth.workload("qwen3_8b_cycle_b8")
     S = Setup(w, target=True)
     lens = synth.ctx_lengths(w)
     B, batch, T, D = w.block, w.batch, w.target, w.draft
-    cap = max(lens) + 2 * B + 64
+    cap = max(lens) + (CYCLES + 1) * B + 64
     tkv = S.kv(T, cap, seed=11)
     dkv = S.kv(D, cap, seed=12)
     tctx = synth.synthetic_ctx_kv(w, "target", lens, DEV)
@@ -239,73 +283,107 @@ def test_qwen3_8b_cycle_batch8_target8():
     _free()
     ws_d = S.workspace(S.draft, B, dkv.capacity, inject_rows=batch * B)
     ws_t = S.workspace(S.target, B, tkv.capacity)
-    anchor = synth.anchors(w, DEV)
-    # draft (M = 128: tiled GEMMs) checked against the oracle
-    ids, logits, hid = _draft_outputs(S, dkv, B, batch)
-    rt.draft_block(S.draft, dkv, anchor, B, ids, ws_d, logits, hid)
-    torch.cuda.synchronize()
-    a_np = anchor.cpu().numpy()
-    for b in (0, 5):
-        _check_draft(S, b, d_np[b], lens[b], a_np[b], ids, logits, hid, f"cycle draft seq {b}")
-    # verify input: sequence 0 drafts the target's own greedy continuation for 3 positions
-    # (oracle pre-pass) and then a forced mismatch; the other sequences take seeded random
-    # ids (mostly rejected at once)
-    drafts = synth.uniform_ints((batch, B - 1), 0, T.vocab - 1, w.cid, "cycle.drafts").numpy().astype(np.int64)
-    toks = [int(a_np[0])]
-    for _ in range(4):
-        g0, _, _, _, _ = O.verify(S.np_tw, S.np_shared, T, t_np[0], toks, lens[0], w.taps, store=S.store)
-        toks.append(int(g0[-1]))
-    drafts[0, :3] = toks[1:4]
-    if drafts[0, 3] == toks[4]:
-        drafts[0, 3] = (toks[4] + 1) % T.vocab
-    d_dev = torch.tensor(drafts, dtype=torch.int32, device=DEV)
     k = len(w.taps)
-    feats = torch.zeros(batch, B, k * T.hidden, dtype=torch.bfloat16, device=DEV)
-    g = torch.zeros(batch, B, dtype=torch.int32, device=DEV)
-    tau = torch.zeros(batch, dtype=torch.int32, device=DEV)
-    bonus = torch.zeros(batch, dtype=torch.int32, device=DEV)
-    vlog = torch.zeros(batch, B, T.vocab, device=DEV)
-    vhid = torch.zeros(T.n_layers + 1, batch, B, T.hidden, device=DEV)
-    rt.verify_accept(S.target, tkv, anchor, d_dev, B, feats, g, tau, bonus, ws_t, vlog, vhid)
-    torch.cuda.synchronize()
-    assert tkv.err.item() == 0
-    tau_np, bonus_np, g_np = tau.cpu().numpy(), bonus.cpu().numpy(), g.cpu().numpy()
-    oracle_rows = {}
-    for b in (0, 3):
-        block = [int(a_np[b])] + [int(x) for x in drafts[b]]
-        og, oz, of, onew, ohid = O.verify(S.np_tw, S.np_shared, T, t_np[b], block, lens[b], w.taps,
-                                          store=S.store)
-        for l in range(T.n_layers + 1):
-            assert_close(vhid[l, b].cpu().numpy(), ohid[l], TOLB, f"cycle verify hidden {l} seq {b}")
-        assert_rows_close(vlog[b].cpu().numpy(), oz, TOLB, f"cycle verify logits seq {b}")
-        assert_close(synth.to_numpy(feats[b]), of, TOLB, f"cycle tapped feats seq {b}")
-        assert_ids(g_np[b], og, oz, f"cycle target argmax seq {b}")
-        for l in (0, T.n_layers - 1):
-            K, V = read_cache(tkv, l, b, lens[b] + B)
-            assert_close(K[lens[b]:], onew[l][0], TOLB, f"cycle new target K seq {b} layer {l}")
-            assert_close(V[lens[b]:], onew[l][1], TOLB, f"cycle new target V seq {b} layer {l}")
-        if assert_accept(tau_np[b], bonus_np[b], g_np[b], drafts[b], og, oz, f"cycle accept seq {b}"):
-            oracle_rows[b] = (O.accept(drafts[b], og)[1], of)
-        if b == 0 and np.all(O.top2_gap(oz[:5]) >= 1e-2):
-            assert int(tau_np[0]) == 4 and int(bonus_np[0]) == int(og[3])
-    for b in range(batch):   # every sequence: the greedy rule on the kernel's own argmax
-        a2 = 0
-        while a2 < B - 1 and int(drafts[b, a2]) == int(g_np[b, a2]):
-            a2 += 1
-        assert (int(tau_np[b]), int(bonus_np[b])) == (a2 + 1, int(g_np[b, a2]))
-    # inject all B verified rows at the old lengths, then commit tau
+    anchor = synth.anchors(w, "cpu").numpy().astype(np.int64)
+    n = list(lens)
+    active = set(range(batch))
     rs = torch.arange(batch, dtype=torch.int32, device=DEV).repeat_interleave(B)
     rp = torch.arange(B, dtype=torch.int32, device=DEV).repeat(batch)
-    rt.inject_ctx(S.draft, dkv, feats.reshape(batch * B, -1).contiguous(), rs, rp, 1, B, ws_d)
-    rt.kv_commit(tkv, dkv, tau, B)
-    torch.cuda.synchronize()
-    assert dkv.err.item() == 0 and tkv.err.item() == 0
-    assert tkv.seq_len.cpu().tolist() == [n + int(t) for n, t in zip(lens, tau_np)]
-    assert dkv.seq_len.cpu().tolist() == tkv.seq_len.cpu().tolist()
-    # the drafter's committed rows: the oracle injects its own tapped features
-    for b, (t, of) in oracle_rows.items():
-        n = lens[b]
-        inj = O.inject(of[:t], n + np.arange(t), S.np_dw, D, store=S.store)
-        K, V = read_cache(dkv, 0, b, n + t)
-        assert_close(K[n:], inj[0][0], TOLB, f"cycle committed draft K seq {b}")
-        assert_close(V[n:], inj[0][1], TOLB, f"cycle committed draft V seq {b}")
+    compared_tau = 0
+    for c in range(CYCLES):
+        a_dev = torch.tensor(anchor, dtype=torch.int32, device=DEV)
+        # ---- draft (M = 128: tiled GEMMs), every active sequence against the oracle ----
+        ids, logits, hid = _draft_outputs(S, dkv, B, batch)
+        rt.draft_block(S.draft, dkv, a_dev, B, ids, ws_d, logits, hid)
+        torch.cuda.synchronize()
+        assert dkv.err.item() == 0
+        own = {}
+        for b in sorted(active):
+            o_ids, o_z, o_hid = O.draft_block(S.np_dw, S.np_shared, D, d_np[b], int(anchor[b]), n[b], B,
+                                              store=S.store)
+            for l in range(D.n_layers + 1):
+                assert_close(hid[l, b].cpu().numpy(), o_hid[l], TOLB, f"cycle {c} draft hidden {l} seq {b}")
+            assert_rows_close(logits[b].cpu().numpy(), o_z, TOLB, f"cycle {c} draft logits seq {b}")
+            assert_ids(ids[b].cpu().numpy(), o_ids, o_z, f"cycle {c} draft ids seq {b}")
+            own[b] = o_ids
+        # ---- seeded forcing rule on the oracle's greedy continuation ----
+        coins = synth.force_coins(FORCE_SEED, c, batch, B, P_FORCE)
+        drafts = synth.uniform_ints((batch, B - 1), 0, T.vocab - 1, w.cid, f"cycle{c}.drafts").numpy()
+        drafts = drafts.astype(np.int64)
+        runs = {}
+        for b in sorted(active):
+            f = int(np.argmin(np.append(coins[b], False)))
+            gstar = _greedy_continuation(S, T, t_np[b], anchor[b], n[b], f + 1)
+            drafts[b], runs[b] = synth.forced_drafts(coins[b], gstar, own[b], T.vocab)
+        d_dev = torch.tensor(drafts, dtype=torch.int32, device=DEV)
+        # ---- verify + accept ----
+        feats = torch.zeros(batch, B, k * T.hidden, dtype=torch.bfloat16, device=DEV)
+        g = torch.zeros(batch, B, dtype=torch.int32, device=DEV)
+        tau = torch.zeros(batch, dtype=torch.int32, device=DEV)
+        bonus = torch.zeros(batch, dtype=torch.int32, device=DEV)
+        vlog = torch.zeros(batch, B, T.vocab, device=DEV)
+        vhid = torch.zeros(T.n_layers + 1, batch, B, T.hidden, device=DEV)
+        rt.verify_accept(S.target, tkv, a_dev, d_dev, B, feats, g, tau, bonus, ws_t, vlog, vhid)
+        torch.cuda.synchronize()
+        assert tkv.err.item() == 0
+        tau_np, bonus_np, g_np = tau.cpu().numpy(), bonus.cpu().numpy(), g.cpu().numpy()
+        for b in range(batch):   # every sequence: the greedy rule on the kernel's own argmax
+            a2 = 0
+            while a2 < B - 1 and int(drafts[b, a2]) == int(g_np[b, a2]):
+                a2 += 1
+            assert (int(tau_np[b]), int(bonus_np[b])) == (a2 + 1, int(g_np[b, a2]))
+        oracle_commit = {}
+        for b in sorted(active):
+            block = [int(anchor[b])] + [int(x) for x in drafts[b]]
+            og, oz, of, onew, ohid = O.verify(S.np_tw, S.np_shared, T, t_np[b], block, n[b], w.taps,
+                                              store=S.store)
+            what = f"cycle {c} verify seq {b}"
+            for l in range(T.n_layers + 1):
+                assert_close(vhid[l, b].cpu().numpy(), ohid[l], TOLB, f"{what} hidden {l}")
+            assert_rows_close(vlog[b].cpu().numpy(), oz, TOLB, f"{what} logits")
+            assert_close(synth.to_numpy(feats[b]), of, TOLB, f"{what} tapped feats")
+            assert_ids(g_np[b], og, oz, f"{what} target argmax")
+            for l in range(T.n_layers):
+                K, V = read_cache(tkv, l, b, n[b] + B)
+                assert_close(K[n[b]:], onew[l][0], TOLB, f"{what} block K layer {l}")
+                assert_close(V[n[b]:], onew[l][1], TOLB, f"{what} block V layer {l}")
+            assert_accept(tau_np[b], bonus_np[b], g_np[b], drafts[b], og, oz, what)
+            a, t_o, bo = O.accept(drafts[b], og)
+            if (int(tau_np[b]), int(bonus_np[b])) == (t_o, bo):   # both sides in the same state
+                # the rule fixes tau = f + 1 (B after a full run of heads), unless one of the
+                # rows deciding it is an oracle near-tie (the continuation came from shorter
+                # passes, whose float32 rounding may order such a pair differently)
+                expect = min(runs[b] + 1, B)
+                if np.all(O.top2_gap(np.asarray(oz[:expect], dtype=np.float64)) >= NEAR_TIE):
+                    assert t_o == expect, f"{what}: tau {t_o} under a run of {runs[b]} heads"
+                compared_tau += 1
+                oracle_commit[b] = (t_o, bo, onew, of)
+            else:
+                active.discard(b)    # differs at a near-tie (allowed above): states now differ
+        # ---- inject all B verified rows at the old lengths, commit tau ----
+        rt.inject_ctx(S.draft, dkv, feats.reshape(batch * B, -1).contiguous(), rs, rp, 1, B, ws_d)
+        rt.kv_commit(tkv, dkv, tau, B)
+        torch.cuda.synchronize()
+        assert dkv.err.item() == 0 and tkv.err.item() == 0
+        seq_t, seq_d = tkv.seq_len.cpu().tolist(), dkv.seq_len.cpu().tolist()
+        assert seq_t == seq_d
+        for b in range(batch):
+            assert seq_t[b] == n[b] + int(tau_np[b])
+        # ---- the committed rows of both caches, every layer, against the oracle's own ----
+        for b, (t, bo, onew, of) in oracle_commit.items():
+            t_np[b] = O.append_kv(t_np[b], onew, t)
+            inj = O.inject(of[:t], n[b] + np.arange(t), S.np_dw, D, store=S.store)
+            d_np[b] = O.append_kv(d_np[b], inj, t)
+            for l in range(T.n_layers):
+                K, V = read_cache(tkv, l, b, n[b] + t)
+                assert_close(K, t_np[b][l][0], TOLB, f"cycle {c} committed target K seq {b} layer {l}")
+                assert_close(V, t_np[b][l][1], TOLB, f"cycle {c} committed target V seq {b} layer {l}")
+            for l in range(D.n_layers):
+                K, V = read_cache(dkv, l, b, n[b] + t)
+                assert_close(K[n[b]:], inj[l][0], TOLB, f"cycle {c} committed draft K seq {b} layer {l}")
+                assert_close(V[n[b]:], inj[l][1], TOLB, f"cycle {c} committed draft V seq {b} layer {l}")
+        n = [n[b] + int(tau_np[b]) for b in range(batch)]
+        anchor = bonus_np.astype(np.int64)
+    # near-ties take a sequence out rarely: most sequences are compared through every cycle
+    assert compared_tau >= CYCLES * batch - 3, (compared_tau, sorted(active))
+    print(f"cycle test: {compared_tau} accepts compared, {len(active)} sequences through every cycle")
