@@ -16,7 +16,7 @@ LIB = os.path.join(HERE, "libdflash.so")
 BUILD = os.path.join(ROOT, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
-SOURCES = ["gemm.hip", "gemv.hip", "gemm_mfma.hip", "attention.hip", "elementwise.hip", "select.hip",
+SOURCES = ["gemm.hip", "gemv.hip", "gemm_rows.hip", "gemm_mfma.hip", "attention.hip", "elementwise.hip", "select.hip",
            "api.hip"]
 FLAGS = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}",
          # packed-fp32 VALU forms are kept out of every kernel on this hardware

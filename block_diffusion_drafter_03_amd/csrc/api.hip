@@ -71,8 +71,22 @@ struct StepWs {
   SampleWs smp;       // sampling verification scratch
   float* xa;          // DFlash 2 convolutions: a convolution's input or output [Mp, D]
   float* dk;          // and its correction coefficients [M, D / 8]
+  SplitArgs split;    // K-split scratch of the M > 16 GEMMs
   AttnPlan plan;
 };
+
+// K-split scratch for GEMMs of `rows` rows whose column count is at most max_n (bf16 models
+// with more than 16 rows; otherwise none)
+SplitArgs carve_split(Carve& cv, int dt, int rows, int max_n) {
+  SplitArgs s;
+  memset(&s, 0, sizeof(s));
+  const bool use = dt == DFLASH_BF16 && rows > 16;
+  s.part_bytes = use ? rows_split_bytes(rows, max_n) : 0;
+  s.part = (float*)cv.take(s.part_bytes);
+  s.ss = (float*)cv.take(use ? rows_split_ss_bytes(rows) : 0);
+  if (!use) s.part = nullptr;
+  return s;
+}
 
 size_t step_ws(const dflash_model* m, int batch, int B, int ctx_cap, void* base, StepWs* w) {
   const dflash_model_desc& d = m->d;
@@ -100,16 +114,20 @@ size_t step_ws(const dflash_model* m, int batch, int B, int ctx_cap, void* base,
   const bool dc = !m->dconv.empty();
   t.xa = (float*)cv.take(dc ? (size_t)Mp * D * 4 : 0);
   t.dk = (float*)cv.take(dc ? (size_t)M * (D / 8) * 4 : 0);
+  t.split = carve_split(cv, dt, M, (Hq + 2 * Hkv) * hd > D ? (Hq + 2 * Hkv) * hd : D);
   if (w) *w = t;
   return cv.off;
 }
 
-size_t inject_ws(const dflash_model* m, int rows, void* base, float** x, float2** rope) {
+size_t inject_ws(const dflash_model* m, int rows, void* base, float** x, float2** rope,
+                 SplitArgs* split = nullptr) {
   Carve cv(base);
   float* p = (float*)cv.take((size_t)round_up(rows, 16) * m->d.hidden * 4);
   float2* r = (float2*)cv.take((size_t)rows * (m->d.head_dim / 2) * sizeof(float2));
+  const SplitArgs s = carve_split(cv, m->d.dtype, rows, m->d.hidden);
   if (x) *x = p;
   if (rope) *rope = r;
+  if (split) *split = s;
   return cv.off;
 }
 
@@ -320,6 +338,7 @@ int run_layers(const dflash_model* m, const dflash_kv* kv, int batch, int B, con
       e.num_pages = kv->num_pages;
       e.batch = kv->batch;
       e.err = kv->error_flags;
+      g.split = w.split;
       if (int s = run_gemm(DFLASH_KERNEL_GEMM_QKV, dt, g, st)) return s;
     }
     {
@@ -335,6 +354,7 @@ int run_layers(const dflash_model* m, const dflash_kv* kv, int batch, int B, con
       g.e.out = w.xa;
       g.e.ldo = D;
       g.e.afrag = afrag;
+      g.split = w.split;
       if (int s = run_gemm(DFLASH_KERNEL_GEMM_O, dt, g, st)) return s;
     }
     if (dc) {
@@ -347,6 +367,7 @@ int run_layers(const dflash_model* m, const dflash_kv* kv, int batch, int B, con
       g.e.act = w.act;
       g.e.F = F;
       g.e.afrag = afrag;
+      g.split = w.split;
       if (int s = run_gemm(DFLASH_KERNEL_GEMM_GATE_UP, dt, g, st)) return s;
     }
     float* hdbg_l = hidden_dbg ? hidden_dbg + (size_t)(l + 1) * M * D : nullptr;
@@ -368,6 +389,7 @@ int run_layers(const dflash_model* m, const dflash_kv* kv, int batch, int B, con
             g.e.tap_col = (int)t * D;
           }
       }
+      g.split = w.split;
       if (int s = run_gemm(DFLASH_KERNEL_GEMM_DOWN, dt, g, st)) return s;
     }
     if (dc)
@@ -561,7 +583,8 @@ int dflash_inject_ctx(const dflash_model* m, dflash_kv* kv, const void* feats, i
   if (!feats || !row_seq || !row_pos) return DFLASH_E_ARG;
   float* x = nullptr;
   float2* rope = nullptr;
-  const size_t need = inject_ws(m, n_rows, ws, &x, &rope);
+  SplitArgs split;
+  const size_t need = inject_ws(m, n_rows, ws, &x, &rope, &split);
   if (!ws || ws_bytes < need) return DFLASH_E_WORKSPACE;
   const dflash_model_desc& d = m->d;
   const int dt = d.dtype, D = d.hidden, L = d.n_layers, Hkv = d.n_kv_heads, hd = d.head_dim;
@@ -574,6 +597,7 @@ int dflash_inject_ctx(const dflash_model* m, dflash_kv* kv, const void* feats, i
     g.e.afrag = dt == DFLASH_BF16;
     g.e.out = x;
     g.e.ldo = D;
+    g.split = split;
     if (int s = run_gemm(DFLASH_KERNEL_INJECT_FUSE, dt, g, st)) return s;
   }
   HIPCHK(launch_rope_rows(row_seq, row_pos, pos_relative, kv->seq_len, kv->batch, n_rows, hd,
@@ -606,6 +630,7 @@ int dflash_inject_ctx(const dflash_model* m, dflash_kv* kv, const void* feats, i
     ep.row_pos = row_pos;
     ep.pos_relative = pos_relative;
     ep.pos_limit = pos_limit;
+    g.split = split;
     if (int s = run_gemm(DFLASH_KERNEL_INJECT_KV, dt, g, st)) return s;
   }
   return DFLASH_OK;

@@ -1,7 +1,8 @@
 // GEMM entry point and the float32-model kernel.  acc[m][n] = sum_k A[m][k] W[n][k]
 // (y = x W^T), optional A-side RMSNorm, then one of the epilogues of epilogue.h.
 //  * gemm_gemv_bf16 (gemv.hip, M <= 16): the weight-streaming shape of a drafter step.
-//  * gemm_mfma_bf16 (gemm_mfma.hip, M > 16): LDS-tiled MFMA GEMM.
+//  * gemm_rows_bf16 (gemm_rows.hip, M > 16, few column tiles): row-resident K-split MFMA
+//    GEMM + reduce; gemm_mfma_bf16 / gemm_wdirect_bf16 (gemm_mfma.hip, M > 16, many tiles).
 //  * gemm_f32 (here, float32 models): VALU 64 x 64 tiles, BK = 16, row-major operands.
 #include "gemm_common.h"
 
@@ -102,13 +103,13 @@ struct F32Launch {
 };
 
 hipError_t launch_gemv(const GemmArgs& ga, hipStream_t st);
-hipError_t launch_gemm_mfma(const GemmArgs& ga, hipStream_t st);
+hipError_t launch_gemm_rows(const GemmArgs& ga, hipStream_t st);
 
 hipError_t launch_gemm(int dt, const GemmArgs& ga, hipStream_t st) {
   if (ga.M <= 0 || ga.N <= 0) return hipSuccess;
   if (dt == F32) return dispatch_gemm<F32Launch>(ga, st);
   if (ga.M <= 16 && ga.K % (32 * GEMV_NW) == 0) return launch_gemv(ga, st);
-  return launch_gemm_mfma(ga, st);
+  return launch_gemm_rows(ga, st);
 }
 
 }  // namespace dflash

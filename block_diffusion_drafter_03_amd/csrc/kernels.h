@@ -90,6 +90,19 @@ struct EpiArgs {
   int dconv_accumulate;
 };
 
+// K-split scratch of the row-resident GEMM (gemm_rows.hip): raw partial accumulators of
+// every split in fragment order, [splits][16-row blocks][16-column tiles][256] floats, and
+// partial sums of squares [splits][row blocks * 16].  part == NULL: never split.
+struct SplitArgs {
+  float* part;
+  float* ss;
+  size_t part_bytes;   // capacity of `part`
+  int splits, mb_pad, nt_pad;
+};
+#define ROWS_MAX_SPLITS 8
+#define ROWS_MAX_NORM_K 16384          // A-side norm gains held in LDS
+#define ROWS_SPLIT_BYTES ((size_t)32 << 20)
+
 struct GemmArgs {
   const void* A;        // [M, K]: float32 activations (A-fragment order for bf16 models), or
                         // caller-supplied bf16 rows (row-major, stride lda) when a_bf16
@@ -100,7 +113,11 @@ struct GemmArgs {
   const void* norm_g;   // A-side RMSNorm gain [K] (model dtype) or NULL
   float eps;
   EpiArgs e;
+  SplitArgs split;      // bf16 models, M > 16: K-split scratch (or part = NULL)
 };
+// split scratch bytes for GEMMs of up to `rows` rows and `max_n` columns: (part, ss)
+size_t rows_split_bytes(int rows, int max_n);
+size_t rows_split_ss_bytes(int rows);
 
 // acc = A x W^T over the full K, then the epilogue.
 hipError_t launch_gemm(int dt, const GemmArgs& g, hipStream_t st);
