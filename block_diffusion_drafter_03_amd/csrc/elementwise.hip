@@ -101,23 +101,31 @@ hipError_t launch_unpack_ids(const unsigned long long* keys, int batch, int B, i
   return hipGetLastError();
 }
 
-// g = argmax of every verify row; a = leading drafts that equal the target's choice at
-// the previous row; tau = a + 1; bonus = g_a.
-__global__ void accept_kernel(const unsigned long long* keys, const int32_t* drafts, int batch,
-                              int B, int32_t* g, int32_t* tau, int32_t* bonus) {
-  const int b = blockIdx.x * blockDim.x + threadIdx.x;
-  if (b >= batch) return;
-  for (int j = 0; j < B; ++j) g[(size_t)b * B + j] = key_index(keys[(size_t)b * B + j]);
-  int a = 0;
-  while (a < B - 1 && drafts[(size_t)b * (B - 1) + a] == key_index(keys[(size_t)b * B + a])) ++a;
-  tau[b] = a + 1;
-  bonus[b] = key_index(keys[(size_t)b * B + a]);
+// Greedy acceptance, one wavefront per sequence (B <= 64): lane j decodes g_j, the target's
+// argmax after row j, from its packed key; lane j >= 1 compares draft d_j with g_{j-1} (its
+// neighbour's id); a ballot of the mismatches gives the leading run of matches a by a bit
+// scan; tau = a + 1 and bonus = g_a.
+__global__ __launch_bounds__(64) void accept_kernel(const unsigned long long* keys, const int32_t* drafts,
+                                                    int B, int32_t* g, int32_t* tau, int32_t* bonus) {
+  const int b = blockIdx.x, j = threadIdx.x;
+  const int gj = j < B ? key_index(keys[(size_t)b * B + j]) : -1;
+  if (j < B) g[(size_t)b * B + j] = gj;
+  const int gprev = __shfl_up(gj, 1, 64);
+  const bool miss = j >= 1 && j < B && drafts[(size_t)b * (B - 1) + j - 1] != gprev;
+  const unsigned long long mask = __ballot(miss);
+  // drafts 1 .. a match, draft a + 1 (if any) does not: a = (lowest mismatching lane) - 1
+  const int a = mask ? __ffsll((long long)mask) - 2 : B - 1;
+  const int ga = __shfl(gj, a, 64);
+  if (j == 0) {
+    tau[b] = a + 1;
+    bonus[b] = ga;
+  }
 }
 
 hipError_t launch_accept(const unsigned long long* keys, const int32_t* drafts, int batch, int B,
                          int32_t* g, int32_t* tau, int32_t* bonus, hipStream_t st) {
-  hipLaunchKernelGGL(accept_kernel, dim3((batch + 63) / 64), dim3(64), 0, st, keys, drafts, batch,
-                     B, g, tau, bonus);
+  if (B < 1 || B > 64) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(accept_kernel, dim3(batch), dim3(64), 0, st, keys, drafts, B, g, tau, bonus);
   return hipGetLastError();
 }
 
