@@ -8,9 +8,13 @@ context with blocks of 16: draft_block, verify_accept by an 8-layer Qwen3-8B-sha
 All inputs are seeded synthetic tensors already resident in HBM.
 
 Prints one JSON line: draft tokens/s of the draft block (b * (B-1) / T_draft_block) as
-`value`, the cycle time as `ms_per_step`, per-call microseconds, the roofline of the
-dominant kernel (the weight-streaming GEMV of the gate/up projections with its SwiGLU
-epilogue) timed with HIP events inside the timed region, and the CPU oracle timed on the host on a small sample.
+`value`, the cycle time as `ms_per_step`, per-call microseconds (means of the timed steps,
+and medians with p10 / p90 over 50 more cycles), the roofline of the dominant kernel (the
+weight-streaming GEMV of the gate/up projections with its SwiGLU epilogue) timed with HIP
+events inside the timed region, the float32 tiny workload, the attention roofline at 64K
+and 262K contexts, the M = 256 GEMMs against the bf16 MFMA peak, the batch-8 cycles under
+the acceptance-forcing rule (tau, alpha, L), and the CPU oracle timed on the host on a
+bounded sample (every call of the cycle).
 """
 from __future__ import annotations
 
@@ -30,6 +34,20 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def stats(values):
+    """median / p10 / p90 / mean of a list of timings (nearest rank)."""
+    a = sorted(values)
+    n = len(a)
+
+    def q(f):
+        return a[min(n - 1, max(0, int(round(f * (n - 1)))))]
+    return {"median": round(q(0.5), 2), "p10": round(q(0.1), 2), "p90": round(q(0.9), 2),
+            "mean": round(sum(a) / n, 2), "reps": n}
+
+
+STATS_REPS = 50
 
 
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "gemv_gate_up.qwen3_8b_b1_ctx4k.pmc_traffic.txt")
@@ -64,7 +82,7 @@ def main():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-reps", type=int, default=30)
+    ap.add_argument("--cpu-reps", type=int, default=20)
     ap.add_argument("--no-workload-sweep", action="store_true",
                     help="skip the batch-16, 512-row injection and batch-8 cycle measurements")
     ap.add_argument("--no-context-sweep", action="store_true",
@@ -98,7 +116,7 @@ def main():
     tw = synth.model_weights(wt, "target", dev)
     draft = rt.Model(D, dw, shared, n_taps=w.n_taps, draft=True)
     target = rt.Model(T, tw, shared, n_taps=len(taps), taps=taps, draft=False)
-    cap = n + B * (K + W + 3 * 8 + 12 + 4) + 64     # every cycle appends <= B rows
+    cap = n + B * (K + W + 3 * 8 + 12 + 4 + STATS_REPS) + 64     # every cycle appends <= B rows
     dkv = rt.PagedKV(D, 1, cap, torch.bfloat16, dev)
     tkv = rt.PagedKV(T, 1, cap, torch.bfloat16, dev)
     chunk = 512
@@ -204,6 +222,15 @@ def main():
         breakdown[name] = {"launches_per_cycle": len(ms) / 3,
                            "us_per_cycle": sum(ms) * 1e3 / 3}
 
+    # per-call latency distribution: STATS_REPS more cycles, each call bracketed by events
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(STATS_REPS)]
+    for i in range(STATS_REPS):
+        step(evs[i])
+    torch.cuda.synchronize()
+    latency = {name: stats([e[j].elapsed_time(e[j + 1]) * 1e3 for e in evs])
+               for j, name in enumerate(("draft_block", "verify_accept", "inject_16_rows", "kv_commit"))}
+    assert int(tkv.err.item()) == 0 and int(dkv.err.item()) == 0
+
     # the block size is a runtime argument: draft blocks of 8, 10 and 16 on the same cache
     block_sweep = {}
     for Bs in (8, 10, 16):
@@ -232,6 +259,7 @@ def main():
                        + D.vocab * D.hidden * 2 + D.n_layers * n * D.n_kv_heads * D.head_dim * 2 * 2)
 
     traffic, prof_us = measured_profile()
+    tiny = tiny_timing(dev)
     out = {
         "metric": METRIC,
         "value": round(draft_tok_s, 1),
@@ -265,7 +293,11 @@ def main():
                      "launches": len(gu_ms),
                      # the rocprofv3 kernel-trace average of the committed profile (kernel only;
                      # the event pair above also holds the dispatch of the kernel, a few us)
-                     "profile_avg_kernel_us": prof_us},
+                     "profile_avg_kernel_us": prof_us,
+                     "frac_profile": (round(avg_bytes / (prof_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+                                      if prof_us else None)},
+        "latency_us": latency,
+        "tiny_f32": tiny,
         "kernels": breakdown,
         "block_sweep": block_sweep,
         "sampling_t1": sampling,
@@ -274,11 +306,18 @@ def main():
     }
     if not args.no_context_sweep:
         out["context_sweep"] = context_sweep(draft, D, B, dev)
+        out["roofline_attention"] = {
+            ctx: {"bound": "hbm", "achieved": v["attention_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                  "frac": v["attention_hbm_frac"], "bytes_per_launch": v["attention_bytes_per_layer"],
+                  "median_us": v["attention_us_per_layer"]["median"]}
+            for ctx, v in out["context_sweep"].items() if int(ctx) >= 65536}
     if not args.no_workload_sweep:
         out["workload_sweep"] = workload_sweep(draft, target, D, T, B, dev)
+        out["roofline_gemm_m256"] = out["workload_sweep"]["qwen3_8b_b16_paged"]["gemms"]
 
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, dw, shared, feats0, anchor, args.cpu_reps, draft_tok_s)
+        out["cpu_baseline"] = cpu_baseline(w, wt, dw, tw, shared, feats0, anchor, tkv, args.cpu_reps,
+                                           draft_tok_s)
     print(json.dumps(out), flush=True)
     if args.probe_copy > 0:
         src = torch.ones(args.probe_copy << 18, dtype=torch.float32, device=dev)
@@ -287,6 +326,57 @@ def main():
         torch.neg(src, out=dst)      # reads and writes exactly probe_copy MiB each
         torch.cuda.synchronize()
         log(f"probe copy: {args.probe_copy} MiB read + {args.probe_copy} MiB written")
+
+
+def tiny_timing(dev, reps=STATS_REPS):
+    """The float32 tiny workload (2 layers, hidden 256, 4 heads x 64, vocab 4096, block 4,
+    128 injected context rows, batch 1): µs per draft block and per verify (2-layer target),
+    launch-latency bound; median / p10 / p90 over `reps` calls each."""
+    import torch
+    import synth
+    from block_diffusion_drafter_03_amd import runtime as rt
+
+    w = synth.TINY
+    m, t, B, n = w.draft, w.target, w.block, w.ctx[0]
+    dw = synth.model_weights(w, "draft", dev)
+    tw = synth.model_weights(w, "target", dev)
+    sh = synth.shared_weights(w, dev)
+    draft = rt.Model(m, dw, sh, n_taps=w.n_taps, draft=True)
+    target = rt.Model(t, tw, sh, n_taps=len(w.taps), taps=w.taps, draft=False)
+    dkv = rt.PagedKV(m, 1, n + B + 64, torch.float32, dev)
+    tkv = rt.PagedKV(t, 1, n + B + 64, torch.float32, dev)
+    ws = rt.Workspace(max(draft.workspace_bytes(1, B, dkv.capacity, n),
+                          target.workspace_bytes(1, B, tkv.capacity)), dev)
+    rt.inject_ctx(draft, dkv, synth.features(w, n, dev), torch.zeros(n, dtype=torch.int32, device=dev),
+                  torch.arange(n, dtype=torch.int32, device=dev), 0, n, ws)
+    dkv.set_seq_len(n)
+    tctx = synth.synthetic_ctx_kv(w, "target", [n], dev)
+    for l in range(t.n_layers):
+        tkv.write_dense(l, 0, tctx[l][0][0], tctx[l][0][1])
+    tkv.set_seq_len(n)
+    anchor = synth.anchors(w, dev)
+    ids = torch.zeros(1, B - 1, dtype=torch.int32, device=dev)
+    g = torch.zeros(1, B, dtype=torch.int32, device=dev)
+    tau = torch.zeros(1, dtype=torch.int32, device=dev)
+    bonus = torch.zeros(1, dtype=torch.int32, device=dev)
+    out = {}
+    for name, call in (("draft_block", lambda: rt.draft_block(draft, dkv, anchor, B, ids, ws)),
+                       ("verify_accept", lambda: rt.verify_accept(target, tkv, anchor, ids, B, None, g, tau,
+                                                                  bonus, ws))):
+        for _ in range(3):
+            call()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for e0, e1 in evs:
+            e0.record()
+            call()
+            e1.record()
+        torch.cuda.synchronize()
+        out["us_" + name] = stats([e0.elapsed_time(e1) * 1e3 for e0, e1 in evs])
+    assert int(dkv.err.item()) == 0 and int(tkv.err.item()) == 0
+    out["note"] = "launch-latency bound (about 11.5 MB of weights); no roofline fraction"
+    draft.close()
+    target.close()
+    return out
 
 
 def _filled_kv(rt, torch, shape, lens, cap, dev, seed):
@@ -309,7 +399,7 @@ def _timed(torch, fn, reps):
     return sum(e0.elapsed_time(e1) for e0, e1 in evs) * 1e3 / reps
 
 
-def workload_sweep(draft, target, D, T, B, dev, reps=5, cycles=4):
+def workload_sweep(draft, target, D, T, B, dev, reps=STATS_REPS, cycles=4):
     """The batched workloads, timed on the same models:
     * batch 16, contexts in [2048, 8192] in shuffled 64-token pages: draft block, and the
       gate/up GEMMs' useful bf16 rate against the dense MFMA peak (M = 256 rows);
@@ -336,19 +426,42 @@ def workload_sweep(draft, target, D, T, B, dev, reps=5, cycles=4):
     ids = torch.zeros(w3.batch, B - 1, dtype=torch.int32, device=dev)
     rt.draft_block(draft, kv, anchor, B, ids, ws)
     torch.cuda.synchronize()
-    _lib.timing_arm(_lib.KERNEL_GEMM_GATE_UP, reps * D.n_layers)
-    us = _timed(torch, lambda: rt.draft_block(draft, kv, anchor, B, ids, ws), reps)
-    gu_ms = _lib.timing_read(reps * D.n_layers)
-    assert int(kv.err.item()) == 0
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for e0, e1 in evs:
+        e0.record()
+        rt.draft_block(draft, kv, anchor, B, ids, ws)
+        e1.record()
+    torch.cuda.synchronize()
+    blk = stats([e0.elapsed_time(e1) * 1e3 for e0, e1 in evs])
+    us = blk["median"]
     M = w3.batch * B
-    gu_tf = 2.0 * M * (2 * D.ffn) * D.hidden / (sum(gu_ms) / len(gu_ms) * 1e-3) / 1e12
+    # every GEMM of the block at M = 256 rows: useful flops 2*M*N*K against the dense bf16
+    # peak, and the MFMAs actually issued (float32 activations enter as compensated hi/lo
+    # bf16 pairs: twice the useful flops)
+    Nqkv = (D.n_q_heads + 2 * D.n_kv_heads) * D.head_dim
+    shapes = {"qkv": (_lib.KERNEL_GEMM_QKV, Nqkv, D.hidden), "o": (_lib.KERNEL_GEMM_O, D.hidden, D.n_q_heads * D.head_dim),
+              "gate_up": (_lib.KERNEL_GEMM_GATE_UP, 2 * D.ffn, D.hidden),
+              "down": (_lib.KERNEL_GEMM_DOWN, D.hidden, D.ffn), "lm_head": (_lib.KERNEL_LM_HEAD, D.vocab, D.hidden)}
+    gemms = {}
+    for name, (kid, N_, K_) in shapes.items():
+        launches = D.n_layers if name != "lm_head" else 1
+        _lib.timing_arm(kid, reps * launches)
+        for _ in range(reps):
+            rt.draft_block(draft, kv, anchor, B, ids, ws)
+        ms = _lib.timing_read(reps * launches)
+        t_us = sorted(ms)[len(ms) // 2] * 1e3
+        useful = 2.0 * M * N_ * K_ / (t_us * 1e-6) / 1e12
+        gemms[name] = {"bound": "mfma", "M": M, "N": N_, "K": K_, "median_us": round(t_us, 2),
+                       "achieved": round(useful, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                       "frac": round(useful / MFMA_BF16_PEAK_TFLOPS, 4),
+                       "frac_issued": round(2 * useful / MFMA_BF16_PEAK_TFLOPS, 4)}
+    assert int(kv.err.item()) == 0
     out["qwen3_8b_b16_paged"] = {
-        "us_per_draft_block": round(us, 2), "draft_tok_s": round(w3.batch * (B - 1) / (us * 1e-6), 1),
-        "gate_up_us": round(sum(gu_ms) / len(gu_ms) * 1e3, 2),
-        "gate_up_useful_tflops": round(gu_tf, 1),
-        "gate_up_mfma_frac": round(gu_tf / MFMA_BF16_PEAK_TFLOPS, 4),
-        "note": "useful flops 2*M*N*K; the compensated activations issue twice as many MFMAs"}
-    log(f"batch 16: draft block {us:.1f} us, gate/up {gu_tf:.0f} useful TFLOP/s")
+        "us_per_draft_block": blk, "draft_tok_s": round(w3.batch * (B - 1) / (us * 1e-6), 1),
+        "gemms": gemms,
+        "note": "frac: useful 2*M*N*K flops over the dense bf16 peak; frac_issued counts the "
+                "compensated hi/lo MFMAs actually issued (twice the useful flops)"}
+    log(f"batch 16: draft block {us:.1f} us; " + ", ".join(f"{k} {v['median_us']:.0f} us" for k, v in gemms.items()))
     # ---- one 512-row injection chunk ----
     rows = 512
     rs = torch.zeros(rows, dtype=torch.int32, device=dev)
@@ -357,11 +470,19 @@ def workload_sweep(draft, target, D, T, B, dev, reps=5, cycles=4):
     kv1 = rt.PagedKV(D, 1, rows + 64, torch.bfloat16, dev)
     ws1 = rt.Workspace(draft.workspace_bytes(1, B, kv1.capacity, rows), dev)
     rt.inject_ctx(draft, kv1, feats, rs, rp, 0, rows, ws1)
-    us_inj = _timed(torch, lambda: rt.inject_ctx(draft, kv1, feats, rs, rp, 0, rows, ws1), reps)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for e0, e1 in evs:
+        e0.record()
+        rt.inject_ctx(draft, kv1, feats, rs, rp, 0, rows, ws1)
+        e1.record()
+    torch.cuda.synchronize()
+    inj = stats([e0.elapsed_time(e1) * 1e3 for e0, e1 in evs])
+    us_inj = inj["median"]
     flops = 2.0 * rows * (5 * D.hidden * D.hidden + D.hidden * D.n_layers * 2 * D.n_kv_heads * D.head_dim)
     inj_tf = flops / (us_inj * 1e-6) / 1e12
-    out["inject_512_rows"] = {"us": round(us_inj, 2), "useful_tflops": round(inj_tf, 1),
-                              "mfma_frac": round(inj_tf / MFMA_BF16_PEAK_TFLOPS, 4)}
+    out["inject_512_rows"] = {"us": inj, "useful_tflops": round(inj_tf, 1),
+                              "mfma_frac": round(inj_tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                              "note": "fusion GEMM over bf16 features (no compensation) + K/V GEMM"}
     log(f"inject 512 rows: {us_inj:.1f} us, {inj_tf:.0f} useful TFLOP/s")
     del kv, ws, kv1, ws1
     torch.cuda.empty_cache()
@@ -416,6 +537,7 @@ def workload_sweep(draft, target, D, T, B, dev, reps=5, cycles=4):
         tau_mean = float(np.mean(taus))
         td, tv = float(np.mean(t_draft)), float(np.mean(t_ver))
         res[str(p_acc)] = {"tau_mean": round(tau_mean, 3),
+                           "alpha": round((tau_mean - 1.0) / (B - 1), 4),
                            "expected_tau": round(1.0 + sum(p_acc ** j for j in range(1, B)), 3),
                            "us_draft": round(td, 2), "us_verify_inject_commit": round(tv, 2),
                            "L_us_per_token": round((td + tv) / tau_mean, 2)}
@@ -522,7 +644,7 @@ def dconv_timing(w, dw, shared, dkv, anchor, B, D, n, dev, reps=10):
     return out
 
 
-def context_sweep(draft, shape, B, dev, contexts=(4096, 65536, 262144), reps=5):
+def context_sweep(draft, shape, B, dev, contexts=(4096, 65536, 262144), reps=20):
     """Draft block at batch 1 over synthetic N(0,1) context K/V of each length: µs per draft
     block, and the attention launches (split-K kernel + merge) of every layer timed with
     the library's event hook, with their algorithmic HBM bytes (context K/V, block K/V,
@@ -554,13 +676,14 @@ def context_sweep(draft, shape, B, dev, contexts=(4096, 65536, 262144), reps=5):
         torch.cuda.synchronize()
         attn_ms = _lib.timing_read(reps * L)
         assert int(kv.err.item()) == 0
-        blk_us = sum(e0.elapsed_time(e1) for e0, e1 in evs) * 1e3 / reps
-        attn_us = sum(attn_ms) * 1e3 / len(attn_ms)
+        blk = stats([e0.elapsed_time(e1) * 1e3 for e0, e1 in evs])
+        att = stats([x * 1e3 for x in attn_ms])
+        blk_us, attn_us = blk["median"], att["median"]
         nbytes = (n + B) * Hkv * d * 2 * 2 + B * Hq * d * 4 * 2
         gbs = nbytes / (attn_us * 1e-6) / 1e9
-        out[str(n)] = {"us_per_draft_block": round(blk_us, 2),
+        out[str(n)] = {"us_per_draft_block": blk,
                        "draft_tok_s": round((B - 1) / (blk_us * 1e-6), 1),
-                       "attention_us_per_layer": round(attn_us, 2),
+                       "attention_us_per_layer": att,
                        "attention_bytes_per_layer": int(nbytes),
                        "attention_gbs": round(gbs, 1),
                        "attention_hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
@@ -570,34 +693,81 @@ def context_sweep(draft, shape, B, dev, contexts=(4096, 65536, 262144), reps=5):
     return out
 
 
-def cpu_baseline(w, dw, shared, feats0, anchor, reps, gpu_value):
-    """The oracle's draft block on the host cores (bounded sample: `reps` blocks)."""
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(w, wt, dw, tw, shared, feats0, anchor, tkv, reps, gpu_value):
+    """The oracle on the host cores, on a bounded sample of the bench workload: the drafter's
+    4096-row context injected once (timed), `reps` draft blocks, and a few of each other call
+    of the cycle (16-row and 512-row injections, verification by the 8-layer target over its
+    4096-token cache read back from the GPU, acceptance, commit)."""
     import numpy as np
     import synth
     import oracle as O
     from threadpoolctl import threadpool_info, threadpool_limits
 
     cores = len(os.sched_getaffinity(0))
+
+    def med(fn, k):
+        ts = []
+        for _ in range(k):
+            t0 = time.perf_counter()
+            r = fn()
+            ts.append(time.perf_counter() - t0)
+        return sorted(ts)[len(ts) // 2] * 1e3, r
+
     with threadpool_limits(limits=cores):
-        used = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        info = threadpool_info()
+        used = max([i.get("num_threads", 1) for i in info] or [1])
+        blas = sorted({f"{i.get('internal_api')} {i.get('version')}" for i in info if i.get("user_api") == "blas"})
         log(f"cpu baseline: copying weights to host ({cores} cores)")
         np_dw = {k: synth.to_numpy(v) for k, v in dw.items()}
         np_sh = {k: synth.to_numpy(v) for k, v in shared.items()}
-        n = w.ctx[0]
-        ctx = O.inject(synth.to_numpy(feats0), np.arange(n), np_dw, w.draft, store="bf16")
+        np_tw = {k: synth.to_numpy(v) for k, v in tw.items()}
+        D, T, B, n = w.draft, wt.target, w.block, w.ctx[0]
+        f_np = synth.to_numpy(feats0)
+        calls = {}
+        t0 = time.perf_counter()
+        ctx = O.inject(f_np, np.arange(n), np_dw, D, store="bf16")
+        calls["inject_ctx_4096_rows"] = round((time.perf_counter() - t0) * 1e3, 1)
+        calls["inject_ctx_512_rows"] = round(med(lambda: O.inject(f_np[:512], np.arange(512), np_dw, D,
+                                                                  store="bf16"), 3)[0], 1)
+        calls["inject_ctx_16_rows"] = round(med(lambda: O.inject(f_np[:16], n + np.arange(16), np_dw, D,
+                                                                 store="bf16"), 3)[0], 2)
         a = int(anchor[0])
         log(f"cpu baseline: timing {reps} oracle draft blocks")
         ts = []
+        drafts = None
         for _ in range(reps):
             t0 = time.perf_counter()
-            O.draft_block(np_dw, np_sh, w.draft, ctx, a, n, w.block, store="bf16")
+            drafts, _, _ = O.draft_block(np_dw, np_sh, D, ctx, a, n, B, store="bf16")
             ts.append(time.perf_counter() - t0)
-    t = sorted(ts)[len(ts) // 2]
-    return {"value": round((w.block - 1) / t, 2), "unit": "draft tok/s", "cores": used,
-            "kind": "oracle",
+        t_draft = sorted(ts)[len(ts) // 2]
+        calls["draft_block"] = round(t_draft * 1e3, 1)
+        tcache = []
+        for l in range(T.n_layers):
+            K, V = tkv.read_dense(l, 0, n)
+            tcache.append((synth.to_numpy(K), synth.to_numpy(V)))
+        block = [a] + [int(x) for x in drafts]
+        t_ver, (g, _, feats, new_kv, _) = med(lambda: O.verify(np_tw, np_sh, T, tcache, block, n, wt.taps,
+                                                               store="bf16"), 3)
+        calls["verify"] = round(t_ver, 1)
+        t_acc, (_, tau, _) = med(lambda: O.accept(np.asarray(drafts), g), 1001)
+        calls["accept"] = round(t_acc, 4)
+        calls["kv_commit"] = round(med(lambda: O.commit(tcache, ctx, new_kv, feats, tau, n, np_dw, D,
+                                                         store="bf16"), 3)[0], 2)
+    return {"value": round((B - 1) / t_draft, 2), "unit": "draft tok/s", "cores": used, "kind": "oracle",
             "sample": f"{reps} oracle draft blocks (float32 NumPy, same weights and injected context), "
-                      f"median {t:.3f} s",
-            "gpu_over_cpu": round(gpu_value / ((w.block - 1) / t), 1)}
+                      f"median {t_draft:.3f} s; other calls median of 3 (accept: 1001)",
+            "calls_ms": calls, "cpu_model": _cpu_model(), "blas": blas, "blas_threads": used,
+            "gpu_over_cpu": round(gpu_value / ((B - 1) / t_draft), 1)}
 
 
 if __name__ == "__main__":
