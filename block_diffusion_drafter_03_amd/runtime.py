@@ -212,6 +212,33 @@ class PagedKV:
         V = self.v[layer].permute(0, 3, 1, 2)[pages, slots]
         return K, V
 
+    # --- checkpoint / resume ----------------------------------------------------------
+    def snapshot(self) -> dict:
+        """The committed state as host tensors, independent of the page layout: seq_len and,
+        per layer and sequence, the K/V rows of positions 0 .. seq_len-1 (positions past a
+        sequence's length hold rejected draft rows and are not part of the state).
+        Synchronises the stream."""
+        lens = self.seq_len.cpu()
+        out = {"seq_len": lens.clone()}
+        for layer in range(len(self.k)):
+            for b in range(self.batch):
+                K, V = self.read_dense(layer, b, int(lens[b]))
+                out[f"k.{layer}.{b}"] = K.cpu().contiguous()
+                out[f"v.{layer}.{b}"] = V.cpu().contiguous()
+        return out
+
+    def restore(self, snap: dict):
+        """Load a snapshot of a cache of the same shape and batch (any page layout and any
+        capacity that holds the lengths)."""
+        lens = [int(x) for x in snap["seq_len"]]
+        if len(lens) != self.batch or max(lens, default=0) > self.capacity:
+            raise ValueError("snapshot does not fit this cache")
+        dev = self.block_table.device
+        for layer in range(len(self.k)):
+            for b in range(self.batch):
+                self.write_dense(layer, b, snap[f"k.{layer}.{b}"].to(dev), snap[f"v.{layer}.{b}"].to(dev))
+        self.set_seq_len(lens)
+
 
 class Workspace:
     def __init__(self, nbytes, device):

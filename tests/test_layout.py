@@ -33,3 +33,35 @@ def test_row_interleaves():
     g, u = torch.randn(5, 3), torch.randn(5, 3)
     gu = pack_gate_up(g, u)
     assert torch.equal(gu[0::2], g) and torch.equal(gu[1::2], u)
+
+
+def test_cache_snapshot_restores_into_another_page_layout():
+    """PagedKV.snapshot / restore (host tensors): the committed rows come back at the same
+    logical positions whatever the page order, capacity or the rows past seq_len."""
+    from types import SimpleNamespace
+    from block_diffusion_drafter_03_amd.runtime import PagedKV
+    shape = SimpleNamespace(n_layers=2, n_kv_heads=2, head_dim=8)
+    a = PagedKV(shape, 3, 200, torch.float32, "cpu", page_order=torch.randperm(12, generator=torch.Generator().manual_seed(1)))
+    lens = [130, 0, 64]
+    g = torch.Generator().manual_seed(2)
+    for layer in range(2):
+        for b in range(3):
+            # whole capacity written: rows past the length stand for rejected drafts
+            a.write_dense(layer, b, torch.randn(a.capacity, 2, 8, generator=g), torch.randn(a.capacity, 2, 8, generator=g))
+    a.set_seq_len(lens)
+    snap = a.snapshot()
+    assert [snap[f"k.0.{b}"].shape[0] for b in range(3)] == lens
+    c = PagedKV(shape, 3, 260, torch.float32, "cpu", page_order=torch.randperm(15, generator=torch.Generator().manual_seed(3)))
+    c.restore(snap)
+    assert c.seq_len.tolist() == lens and c.len_bound == 130
+    for layer in range(2):
+        for b in range(3):
+            ka, va = a.read_dense(layer, b, lens[b])
+            kc, vc = c.read_dense(layer, b, lens[b])
+            assert torch.equal(ka, kc) and torch.equal(va, vc)
+    small = PagedKV(shape, 3, 64, torch.float32, "cpu")
+    try:
+        small.restore(snap)
+        raise AssertionError("a snapshot longer than the capacity was accepted")
+    except ValueError:
+        pass
