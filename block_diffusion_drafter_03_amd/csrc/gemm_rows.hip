@@ -17,10 +17,14 @@
 // loads are unconditional (stage indices clamped), so the compiler counts them and never
 // drains the ring at a barrier.
 //
-// Few column tiles (QKV, O, down, the fusion GEMM): the K range is split over gridDim.y
+// Few column tiles (QKV, O, down, the fusion GEMM): the K range is split over S
 // workgroups, which write raw partial accumulators (and partial sums of squares) in
 // fragment order; gemm_rows_reduce sums the splits in a fixed order and runs the epilogue,
-// so results do not depend on timing.
+// so results do not depend on timing.  The (split, tile) work items are numbered
+// split-major and each XCD takes a contiguous range of them, so an XCD reads the A rows of
+// one or two K ranges only (all splits on every XCD would pull the whole of A from HBM
+// into each of the 8 L2s: 8 x 4 MB for 256 float32 rows of K = 4096, as much as the O
+// weights).
 #include "gemm_common.h"
 
 namespace dflash {
@@ -38,6 +42,10 @@ DF_DEV int xcd_tile(int bid, int T) {
   return (T & 7) == 0 ? (bid & 7) * (T >> 3) + (bid >> 3) : bid;
 }
 
+// launch grid of `items` work items: a multiple of 8 (the workgroups past the items exit
+// at once), so that xcd_tile always hands out contiguous ranges
+static inline int rows_grid(int items) { return (items + 7) / 8 * 8; }
+
 template <typename TA, int NW, int TM, int TN, int DEPTH, bool NORM, int KIND, bool SPLIT>
 __global__ __launch_bounds__(NW * 64, 1) void gemm_rows_bf16(GemmArgs ga, SplitArgs sp) {
   constexpr bool TWO = AIsFloat<TA>::value;
@@ -54,11 +62,13 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_rows_bf16(GemmArgs ga, SplitA
   const int M = ga.M, N = ga.N, K = ga.K, KS = K >> 5;
   const int MB = (M + 15) >> 4, NT = (N + 15) >> 4;
   const int mt_n = (M + BM - 1) / BM, nt_n = (N + BN - 1) / BN;
-  const int t = xcd_tile(blockIdx.x, mt_n * nt_n);
+  const int T = mt_n * nt_n, S = SPLIT ? sp.splits : 1;
+  const int q = xcd_tile(blockIdx.x, gridDim.x);
+  if (q >= T * S) return;   // grid padding (whole workgroup, before any barrier)
+  const int s = q / T, t = q % T;
   const int m0 = (t % mt_n) * BM, n0 = (t / mt_n) * BN;
   // this split's stages (KS % KSUB == 0, checked by the launcher)
   const int NST_ALL = KS / KSUB;
-  const int S = gridDim.y, s = blockIdx.y;
   const int st0 = (int)((long)NST_ALL * s / S), st1 = (int)((long)NST_ALL * (s + 1) / S);
   const int nst = st1 - st0;
   const int last = st1 - 1;
@@ -299,8 +309,9 @@ struct RowsLaunch {
     auto grid_of = [&](int bm_, int bn_) { return ((M + bm_ - 1) / bm_) * ((N + bn_ - 1) / bn_); };
 #define ROWS_K(NWV, TMV, TNV, DV, SPL) gemm_rows_bf16<TA, NWV, TMV, TNV, DV, NORM, KIND, SPL>
 #define ROWS_GO(NWV, TMV, TNV, DV, SPL)                                                          \
-  hipLaunchKernelGGL((ROWS_K(NWV, TMV, TNV, DV, SPL)), dim3(grid_of(NWV * 16 * TMV, 16 * TNV), SPL ? S : 1), \
-                     dim3(NWV * 64), 0, st, ga, sp)
+  hipLaunchKernelGGL((ROWS_K(NWV, TMV, TNV, DV, SPL)),                                          \
+                     dim3(rows_grid(grid_of(NWV * 16 * TMV, 16 * TNV) * (SPL ? S : 1))), dim3(NWV * 64), \
+                     0, st, ga, sp)
     if (S == 1) {
       // enough column tiles to fill the chip.  Up to 128 rows: 8 waves of 16 rows x 128
       // columns, all rows in one workgroup; beyond, the tile-parallel kernels of
