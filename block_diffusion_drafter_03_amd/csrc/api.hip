@@ -16,6 +16,7 @@
 // and the LM head is one GEMM with RMSNorm(g_f) on the A side and an argmax epilogue.
 #include <string.h>
 
+#include <algorithm>
 #include <mutex>
 #include <new>
 #include <vector>
@@ -75,16 +76,19 @@ struct StepWs {
   AttnPlan plan;
 };
 
-// K-split scratch for GEMMs of `rows` rows whose column count is at most max_n (bf16 models
-// with more than 16 rows; otherwise none)
-SplitArgs carve_split(Carve& cv, int dt, int rows, int max_n) {
+// K-split and operand-plane scratch for GEMMs of `rows` rows whose column count is at most
+// max_n and reduction length at most max_k (bf16 models with more than 16 rows; otherwise
+// none)
+SplitArgs carve_split(Carve& cv, int dt, int rows, int max_n, int max_k) {
   SplitArgs s;
   memset(&s, 0, sizeof(s));
   const bool use = dt == DFLASH_BF16 && rows > 16;
   s.part_bytes = use ? rows_split_bytes(rows, max_n) : 0;
   s.part = (float*)cv.take(s.part_bytes);
   s.ss = (float*)cv.take(use ? rows_split_ss_bytes(rows) : 0);
-  if (!use) s.part = nullptr;
+  s.pair_bytes = use ? pair_plane_bytes(rows, max_k) : 0;
+  s.pair = cv.take(s.pair_bytes);
+  if (!use) s.part = nullptr, s.pair = nullptr;
   return s;
 }
 
@@ -114,7 +118,8 @@ size_t step_ws(const dflash_model* m, int batch, int B, int ctx_cap, void* base,
   const bool dc = !m->dconv.empty();
   t.xa = (float*)cv.take(dc ? (size_t)Mp * D * 4 : 0);
   t.dk = (float*)cv.take(dc ? (size_t)M * (D / 8) * 4 : 0);
-  t.split = carve_split(cv, dt, M, (Hq + 2 * Hkv) * hd > D ? (Hq + 2 * Hkv) * hd : D);
+  const int max_k = std::max(std::max(D, Hq * hd), d.ffn);
+  t.split = carve_split(cv, dt, M, (Hq + 2 * Hkv) * hd > D ? (Hq + 2 * Hkv) * hd : D, max_k);
   if (w) *w = t;
   return cv.off;
 }
@@ -124,7 +129,7 @@ size_t inject_ws(const dflash_model* m, int rows, void* base, float** x, float2*
   Carve cv(base);
   float* p = (float*)cv.take((size_t)round_up(rows, 16) * m->d.hidden * 4);
   float2* r = (float2*)cv.take((size_t)rows * (m->d.head_dim / 2) * sizeof(float2));
-  const SplitArgs s = carve_split(cv, m->d.dtype, rows, m->d.hidden);
+  const SplitArgs s = carve_split(cv, m->d.dtype, rows, m->d.hidden, m->d.hidden);
   if (x) *x = p;
   if (rope) *rope = r;
   if (split) *split = s;
@@ -268,6 +273,9 @@ int run_layers(const dflash_model* m, const dflash_kv* kv, int batch, int B, con
   const int Nqkv = (Hq + 2 * Hkv) * hd;
   const float eps = d.rms_eps;
   const int afrag = dt == DFLASH_BF16;
+  // bf16 models beyond 16 rows: attention and SwiGLU write their outputs as compensated
+  // operand planes, which the O and down GEMMs take as they are
+  const int pairs = dt == DFLASH_BF16 && M > 16;
   const bool dc = !m->dconv.empty();
   if (dc && feats_out) return DFLASH_E_ARG;   // the convolutions belong to a drafter
   // DFlash 2 convolution `c` of layer l: its correction GEMM, then the convolution itself.
@@ -344,11 +352,12 @@ int run_layers(const dflash_model* m, const dflash_kv* kv, int batch, int B, con
     {
       Timed t(DFLASH_KERNEL_ATTENTION, st);
       HIPCHK(launch_attention(dt, w.plan, w.q, w.kblk, w.vblkT, w.kblk_lo, w.vblkT_lo, kvl, batch,
-                              B, Bp, Hq, Hkv, hd, causal, w.part, w.o, afrag, st));
+                              B, Bp, Hq, Hkv, hd, causal, w.part, w.o, pairs ? 2 : afrag, st));
     }
     {  // O projection + residual (with the convolutions: the output, convolved below)
       GemmArgs g = gemm_args(w.o, Hq * hd, one_seg(W(m, l, DFLASH_W_O), D, Hq * hd), M, D,
                              Hq * hd, nullptr, eps, dc ? EPI_STORE_F32 : EPI_RESID);
+      g.a_pair = pairs;
       g.e.h = w.h;
       g.e.ldh = D;
       g.e.out = w.xa;
@@ -367,6 +376,7 @@ int run_layers(const dflash_model* m, const dflash_kv* kv, int batch, int B, con
       g.e.act = w.act;
       g.e.F = F;
       g.e.afrag = afrag;
+      g.e.act_pair = pairs;
       g.split = w.split;
       if (int s = run_gemm(DFLASH_KERNEL_GEMM_GATE_UP, dt, g, st)) return s;
     }
@@ -375,6 +385,7 @@ int run_layers(const dflash_model* m, const dflash_kv* kv, int batch, int B, con
        // convolved below)
       GemmArgs g = gemm_args(w.act, F, one_seg(W(m, l, DFLASH_W_DOWN), D, F), M, D, F, nullptr, eps,
                              dc ? EPI_STORE_F32 : EPI_RESID);
+      g.a_pair = pairs;
       g.e.h = w.h;
       g.e.ldh = D;
       g.e.out = w.xa;
@@ -416,6 +427,7 @@ int run_lm_head(const dflash_model* m, const StepWs& w, int rows, int skipB, flo
   g.e.keys = w.keys;
   g.e.logits = logits;
   g.e.skipB = skipB;
+  g.split = w.split;
   if (smp.temperature > 0.f) {
     g.e.sample = 1;
     g.e.temperature = smp.temperature;

@@ -45,8 +45,8 @@ struct AttnArgs {
   int n_splits, split_len, n_rg, causal;
   float scale_log2;
   float* part;         // [(b, kvh, rg, s)][64][PSTRIDE]  (O, then m, l per row)
-  float* out;          // [batch*B, Hq*AD], A-fragment order when out_afrag
-  int out_afrag;
+  float* out;          // [batch*B, Hq*AD], A-fragment order when out_afrag == 1, operand
+  int out_afrag;       // planes (bf16 pairs, pfrag_off) when 2
 };
 
 // LDS layouts of one 64-key step (one page slice of one KV head), padded by 16 bytes per row
@@ -448,8 +448,19 @@ __global__ __launch_bounds__(256) void attn_merge_bf16(AttnArgs a) {
   const float inv = 1.f / lt;
   const int gq = rho / a.B, j = rho % a.B;
   const int m = b * a.B + j, k = (kvh * a.G + gq) * AD + 4 * t;
-  float* out = a.out + (a.out_afrag ? afrag_off(m, k, (a.Hq * AD) >> 5) : (size_t)m * a.Hq * AD + k);
-  *(float4*)out = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+  const float4 y = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+  if (a.out_afrag == 2) {
+    // 4 consecutive k of one lane: 8 bytes in each plane
+    bf16* p = (bf16*)a.out + pfrag_off(m, k, (a.Hq * AD) >> 5);
+    const bf16x4 hi = {(bf16)y.x, (bf16)y.y, (bf16)y.z, (bf16)y.w};
+    const bf16x4 lo = {(bf16)(y.x - (float)hi[0]), (bf16)(y.y - (float)hi[1]), (bf16)(y.z - (float)hi[2]),
+                       (bf16)(y.w - (float)hi[3])};
+    *(bf16x4*)p = hi;
+    *(bf16x4*)(p + 512) = lo;
+  } else {
+    float* out = a.out + (a.out_afrag ? afrag_off(m, k, (a.Hq * AD) >> 5) : (size_t)m * a.Hq * AD + k);
+    *(float4*)out = y;
+  }
 }
 
 // ---------------------------------------------------------------------------------------

@@ -55,6 +55,18 @@ DF_DEV size_t afrag_off(int m, int k, int KS) {
   return ((size_t)(((m >> 4) * KS + (k >> 5)) * 2 + ((k & 7) >> 2))) * 256 +
          (((k & 31) >> 3) * 16 + (m & 15)) * 4 + (k & 3);
 }
+//  * the same activations as compensated operand planes (bf16, the M > 16 GEMMs' input):
+//    per (16-row block, step) 2 KB, the hi plane (lane (m % 16) + 16 ((k % 32) / 8) holding
+//    8 consecutive k) then the lo plane 512 elements further.  pfrag_off is the hi element.
+DF_DEV size_t pfrag_off(int m, int k, int KS) {
+  return ((size_t)((m >> 4) * KS + (k >> 5))) * 1024 + (((k & 31) >> 3) * 16 + (m & 15)) * 8 + (k & 7);
+}
+// v as a (hi, lo) bf16 pair in the planes at hi element p
+DF_DEV void store_pair(bf16* planes, size_t p, float v) {
+  const bf16 h = (bf16)v;
+  planes[p] = h;
+  planes[p + 512] = (bf16)(v - (float)h);
+}
 
 // Entry i (< 8) of a small pointer table held in a kernel argument, by unrolled selects:
 // a dynamically indexed private array would be placed in scratch memory.

@@ -66,7 +66,9 @@ DF_DEV void epi_pair(const EpiArgs& e, int row, int col, float v0, float v1) {
   switch (KIND) {
     case EPI_SWIGLU: {
       const int c = col >> 1;
-      e.act[e.afrag ? afrag_off(row, c, e.F >> 5) : (size_t)row * e.F + c] = v0 / (1.f + expf(-v0)) * v1;
+      const float y = v0 / (1.f + expf(-v0)) * v1;
+      if (e.act_pair) store_pair((bf16*)e.act, pfrag_off(row, c, e.F >> 5), y);
+      else e.act[e.afrag ? afrag_off(row, c, e.F >> 5) : (size_t)row * e.F + c] = y;
       break;
     }
     case EPI_QKV: {

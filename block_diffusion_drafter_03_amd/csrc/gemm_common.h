@@ -103,6 +103,15 @@ DF_DEV void tile_epilogue(const GemmArgs& ga, int row0, int col, const float v[4
 // (hi, lo) bf16 pair (two MFMAs per W fragment); TA = bf16: caller rows, one MFMA.
 template <typename TA> struct AIsFloat { static constexpr bool value = false; };
 template <> struct AIsFloat<float> { static constexpr bool value = true; };
+// TA = pairf: the activations already split into (hi, lo) bf16 planes by pair_split.  Per
+// 16-row block and 32-wide k-step the 2 KB of the float32 A-fragment layout hold the hi
+// plane (lane l: 8 bf16 at byte 16 l) and then the lo plane, so a 4-byte pairf steps
+// through the planes exactly as float32 steps through the fragments: the kernels address
+// both alike and only skip the conversion (and the norm, folded in by pair_split).
+struct pairf { float bits; };
+template <> struct AIsFloat<pairf> { static constexpr bool value = true; };
+template <typename TA> struct AIsPair { static constexpr bool value = false; };
+template <> struct AIsPair<pairf> { static constexpr bool value = true; };
 
 // v (8 raw A values) -> operand pair; with NORM, the sum of squares of the raw values is
 // added to *ss and v is multiplied by the gain slice gv first.
@@ -145,6 +154,18 @@ static hipError_t launch1(K kernel, dim3 grid, dim3 block, hipStream_t st, const
 template <typename F>
 static hipError_t dispatch_gemm(const GemmArgs& ga, hipStream_t st) {
   const bool norm = ga.norm_g != nullptr;
+  if (ga.a_pair) {
+    if (norm || ga.a_bf16) return hipErrorInvalidValue;
+    switch (ga.e.kind) {
+      case EPI_QKV: return F::template run<pairf, false, EPI_QKV>(ga, st);
+      case EPI_SWIGLU: return F::template run<pairf, false, EPI_SWIGLU>(ga, st);
+      case EPI_ARGMAX: return F::template run<pairf, false, EPI_ARGMAX>(ga, st);
+      case EPI_INJECT_KV: return F::template run<pairf, false, EPI_INJECT_KV>(ga, st);
+      case EPI_RESID: return F::template run<pairf, false, EPI_RESID>(ga, st);
+      case EPI_STORE_F32: return F::template run<pairf, false, EPI_STORE_F32>(ga, st);
+      default: return hipErrorInvalidValue;
+    }
+  }
   if (ga.a_bf16) {
     if (norm || ga.e.kind != EPI_STORE_F32) return hipErrorInvalidValue;
     return F::template run<bf16, false, EPI_STORE_F32>(ga, st);

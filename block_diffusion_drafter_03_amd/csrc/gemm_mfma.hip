@@ -115,7 +115,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_mfma_bf16(GemmArgs ga) {
       const int ks = stage * KSUB + u;
 #pragma unroll
       for (int j = 0; j < AS; ++j) {
-        if constexpr (TWO) {
+        if constexpr (AIsPair<TA>::value) {
+          As[buf][a_h[j]][u][a_rb[j]][a_lane[j]] = *(const bf16x8*)&st.ra[u][j][0];
+        } else if constexpr (TWO) {
           float v[8];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -339,7 +341,10 @@ __global__ __launch_bounds__(256) void gemm_wdirect_bf16(GemmArgs ga) {
       const int ks = stage * KSUB + u;
 #pragma unroll
       for (int j = 0; j < AS; ++j) {
-        if constexpr (TWO) {
+        if constexpr (AIsPair<TA>::value) {
+          // this slot's 16 bytes are plane a_h of its lane: copied as they are
+          As[buf][a_h[j]][u][a_rb[j]][a_lane[j]] = *(const bf16x8*)&ra[u][j][0];
+        } else if constexpr (TWO) {
           float v[8];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {

@@ -142,7 +142,10 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_rows_bf16(GemmArgs ga, SplitA
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
         bf16x8 hi, lo;
-        if constexpr (TWO) {
+        if constexpr (AIsPair<TA>::value) {
+          hi = *(const bf16x8*)&st.a[u][i][0];
+          lo = *(const bf16x8*)&st.a[u][i][1];
+        } else if constexpr (TWO) {
           const float4 x0 = *(const float4*)&st.a[u][i][0], x1 = *(const float4*)&st.a[u][i][1];
           float v[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
           if constexpr (NORM) {

@@ -257,6 +257,9 @@ __global__ __launch_bounds__(NW * 64) void gemm_gemv_bf16(GemmArgs ga) {
 struct GemvLaunch {
   template <typename TA, bool NORM, int KIND>
   static hipError_t run(const GemmArgs& ga, hipStream_t st) {
+    if constexpr (AIsPair<TA>::value) {
+      return hipErrorInvalidValue;   // the GEMV splits its activations itself
+    } else {
     const int n_tiles = (ga.N + 15) / 16;
     // few tiles (up to one per CU) or K != 4096: one workgroup
     // per tile, A streamed with W, so that several workgroups may share a CU and every tile
@@ -277,6 +280,7 @@ struct GemvLaunch {
       if (KIND != EPI_ARGMAX && grid * GEMV_MAX_TILES < n_tiles)
         grid = (n_tiles + GEMV_MAX_TILES - 1) / GEMV_MAX_TILES;
       return launch1(gemm_gemv_bf16<TA, GEMV_NW, NORM, true, KIND>, dim3(grid), dim3(GEMV_NW * 64), st, ga);
+    }
     }
   }
 };

@@ -37,6 +37,7 @@ enum EpiKind {
 struct EpiArgs {
   int kind;
   int afrag;      // 1: out / h / act are float32 in the A-fragment order (row stride ignored)
+  int act_pair;   // EPI_SWIGLU: act holds compensated operand planes (bf16) instead
   // EPI_STORE_*
   void* out;
   int ldo;
@@ -90,14 +91,20 @@ struct EpiArgs {
   int dconv_accumulate;
 };
 
-// K-split scratch of the row-resident GEMM (gemm_rows.hip): raw partial accumulators of
-// every split in fragment order, [splits][16-row blocks][16-column tiles][256] floats, and
-// partial sums of squares [splits][row blocks * 16].  part == NULL: never split.
+// Scratch of the M > 16 GEMMs of bf16 models.
+//  * K splits of the row-resident GEMM (gemm_rows.hip): raw partial accumulators of every
+//    split in fragment order, [splits][16-row blocks][16-column tiles][256] floats, and
+//    partial sums of squares [splits][row blocks * 16].  part == NULL: never split.
+//  * pair: the float32 activations of one GEMM as compensated (hi, lo) bf16 planes with the
+//    A-side RMSNorm folded in (pair_split), 4 bytes per element; NULL: the GEMM kernels
+//    split the activations themselves.
 struct SplitArgs {
   float* part;
   float* ss;
   size_t part_bytes;   // capacity of `part`
   int splits, mb_pad, nt_pad;
+  void* pair;
+  size_t pair_bytes;   // capacity of `pair`
 };
 #define ROWS_MAX_SPLITS 8
 #define ROWS_MAX_NORM_K 16384          // A-side norm gains held in LDS
@@ -113,11 +120,14 @@ struct GemmArgs {
   const void* norm_g;   // A-side RMSNorm gain [K] (model dtype) or NULL
   float eps;
   EpiArgs e;
-  SplitArgs split;      // bf16 models, M > 16: K-split scratch (or part = NULL)
+  SplitArgs split;      // bf16 models, M > 16: K-split and operand scratch
+  int a_pair;           // set by launch_gemm: A holds (hi, lo) planes (pair_split), no norm
 };
 // split scratch bytes for GEMMs of up to `rows` rows and `max_n` columns: (part, ss)
 size_t rows_split_bytes(int rows, int max_n);
 size_t rows_split_ss_bytes(int rows);
+// operand-plane scratch bytes for GEMMs of up to `rows` rows and `max_k` reduction length
+size_t pair_plane_bytes(int rows, int max_k);
 
 // acc = A x W^T over the full K, then the epilogue.
 hipError_t launch_gemm(int dt, const GemmArgs& g, hipStream_t st);
@@ -152,6 +162,7 @@ hipError_t launch_attention(int dt, const AttnPlan& p, const float* q, const voi
                             const void* vblkT, const void* kblk_lo, const void* vblkT_lo,
                             const KvLayer& kv, int batch, int B, int Bp, int Hq, int Hkv, int d,
                             int causal, float* part, float* o, int o_afrag, hipStream_t st);
+// o_afrag: 0 row-major float32, 1 A-fragment order, 2 compensated operand planes (bf16)
 
 // ---- row kernels (elementwise.hip) ----
 struct EmbedArgs {
