@@ -482,6 +482,7 @@ struct SelWs {
   void* gather;
   float* P;
   float* S;
+  SplitArgs split;    // K-split scratch of the projection GEMMs
 };
 
 size_t sel_ws(const dflash_model* m, const dflash_selector* s, int batch, int B, void* base,
@@ -497,6 +498,8 @@ size_t sel_ws(const dflash_model* m, const dflash_selector* s, int batch, int B,
   t.gather = cv.take(msel * D * esz(m->d.dtype));
   t.P = (float*)cv.take(msel * 2 * r * 4);
   t.S = (float*)cv.take(rows * 16 * 16 * 4);
+  // K splits of the projection GEMMs (the [A | B] one has msel rows)
+  t.split = carve_split(cv, m->d.dtype, (int)msel, 2 * r, D);
   if (w) *w = t;
   return cv.off;
 }
@@ -760,6 +763,7 @@ int dflash_draft_block_select(const dflash_model* m, const dflash_kv* kv, const 
     g.a_bf16 = dt == DFLASH_BF16;
     g.e.out = sw.P;
     g.e.ldo = 2 * r;
+    g.split = sw.split;
     HIPCHK(launch_gemm(dt, g, st));
   }
   HIPCHK(launch_select(sw.P, sw.hh, draft_logits, sw.cand, batch, B, k, r, V, sw.S, draft_ids, st));

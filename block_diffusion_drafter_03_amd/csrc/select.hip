@@ -64,6 +64,57 @@ DF_DEV void wave_topk(unsigned long long (&key)[N], int n, int k, unsigned long 
   }
 }
 
+// Pruning before the rounds.  T = the k-th largest of the 64 lane maxima bounds the wave's
+// top k from below (those k maxima are k distinct keys >= T), so the rounds need only the
+// keys >= T - usually a little over k of the wave's N x 64.  They are compacted into one
+// key per lane through LDS slots `cs` (64 per wave; the caller's barrier between the two
+// halves makes them visible).  Step 1 returns the lane's candidates' first slot; step 2 runs
+// the rounds over the compacted keys, or over all of them when T = 0 (fewer than k keys) or
+// more than 64 keys tie at or above T.
+template <int N>
+DF_DEV void prune_stage(const unsigned long long (&key)[N], int k, unsigned long long* cs,
+                        unsigned long long& T, int& total) {
+  const int lane = threadIdx.x & 63;
+  unsigned long long m = 0ull;
+#pragma unroll
+  for (int i = 0; i < N; ++i) m = key[i] > m ? key[i] : m;
+  unsigned long long mm = m;
+  T = 0ull;
+  for (int r = 0; r < k; ++r) {
+    const unsigned long long x = wave_max_u64(mm);
+    mm = mm == x ? 0ull : mm;
+    T = x;
+  }
+  int cnt = 0;
+#pragma unroll
+  for (int i = 0; i < N; ++i) cnt += key[i] && key[i] >= T ? 1 : 0;
+  int incl = cnt;   // inclusive prefix of the counts over the wave
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += y;
+  }
+  total = __shfl(incl, 63, 64);
+  int pos = incl - cnt;
+#pragma unroll
+  for (int i = 0; i < N; ++i)
+    if (key[i] && key[i] >= T) {
+      if (pos < 64) cs[pos] = key[i];
+      ++pos;
+    }
+}
+template <int N>
+DF_DEV void prune_finish(unsigned long long (&key)[N], int k, const unsigned long long* cs,
+                         unsigned long long T, int total, unsigned long long* out) {
+  const int lane = threadIdx.x & 63;
+  if (T != 0ull && total <= 64) {
+    unsigned long long c[1] = {lane < total ? cs[lane] : 0ull};
+    wave_topk<1>(c, 1, k, out);
+  } else {
+    wave_topk<N>(key, N, k, out);
+  }
+}
+
 // grid (rows, chunks): chunk c of row `row` covers ids [c * clen, min(V, (c + 1) * clen)),
 // clen <= TOPK_CHUNK; writes keys[(row * chunks + c) * TOPK_MAX + r], r < k.
 __global__ __launch_bounds__(TOPK_THREADS) void topk_partial_kernel(const float* z, int V, int clen,
@@ -71,6 +122,7 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_partial_kernel(const float*
                                                                      unsigned long long* keys) {
   constexpr int N = TOPK_CHUNK / TOPK_THREADS;
   __shared__ unsigned long long wk[TOPK_THREADS / 64][TOPK_MAX];
+  __shared__ unsigned long long cs[TOPK_THREADS / 64][64];
   const int row = blockIdx.x, c = blockIdx.y, w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const float* zr = z + (size_t)row * V;
   const int v0 = c * clen, v1 = min(V, v0 + clen);
@@ -81,7 +133,11 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_partial_kernel(const float*
     const float x = zr[min(v, v1 - 1)];
     key[i] = v < v1 ? pack_argmax_key(x, v) : 0ull;
   }
-  wave_topk<N>(key, N, k, wk[w]);
+  unsigned long long T;
+  int total;
+  prune_stage<N>(key, k, cs[w], T, total);
+  __syncthreads();
+  prune_finish<N>(key, k, cs[w], T, total, wk[w]);
   __syncthreads();
   if (w == 0) {
     // the 4 waves' lists (k <= 16 each, 64 keys) are one key per lane
@@ -104,25 +160,32 @@ struct TopkMergeArgs {
   void* gather;                     // [batch * (1 + (B - 1) k)][D] model dtype
 };
 
-// grid (rows), 256 threads: wave 0 merges the chunk lists (one list per lane, chunks <= 64),
-// then the workgroup copies the candidates' embedding rows (and, at position 1, the
-// anchor's) into the gather rows of the projection GEMM.
+// grid (rows, parts), 256 threads: wave 0 of every workgroup merges the row's chunk lists
+// (one list per lane, chunks <= 64; the same result in each), then each of the row's `parts`
+// workgroups copies its share of the candidates' embedding rows (and, at position 1, the
+// anchor's) into the gather rows of the projection GEMM; part 0 writes the candidate ids.
 __global__ __launch_bounds__(256) void topk_merge_kernel(TopkMergeArgs a) {
   __shared__ unsigned long long top[TOPK_MAX];
+  __shared__ unsigned long long cs[64];
   const int row = blockIdx.x, lane = threadIdx.x & 63;
   const int b = row / (a.B - 1), t = row % (a.B - 1) + 1;
+  // wave 0 merges (the other waves only pass the barriers)
+  unsigned long long key[TOPK_MAX];
+  unsigned long long T = 0ull;
+  int ncand = 0;
   if (threadIdx.x < 64) {
-    unsigned long long key[TOPK_MAX];
     // unconditional loads (clamped to valid entries), masked afterwards
     const unsigned long long* src = a.keys + ((size_t)row * a.chunks + min(lane, a.chunks - 1)) * TOPK_MAX;
 #pragma unroll
     for (int i = 0; i < TOPK_MAX; ++i) key[i] = src[i];
 #pragma unroll
     for (int i = 0; i < TOPK_MAX; ++i) key[i] = lane < a.chunks && i < a.k ? key[i] : 0ull;
-    wave_topk<TOPK_MAX>(key, TOPK_MAX, a.k, top);
+    prune_stage<TOPK_MAX>(key, a.k, cs, T, ncand);
   }
   __syncthreads();
-  if (threadIdx.x < a.k) {
+  if (threadIdx.x < 64) prune_finish<TOPK_MAX>(key, a.k, cs, T, ncand, top);
+  __syncthreads();
+  if (blockIdx.y == 0 && threadIdx.x < a.k) {
     const unsigned long long kk = top[threadIdx.x];
     const int id = kk ? unpack_argmax_idx(kk) : 0;   // fewer than k ids: id 0 (never when V >= k)
     a.cand[(size_t)row * TOPK_MAX + threadIdx.x] = id;
@@ -141,6 +204,9 @@ __global__ __launch_bounds__(256) void topk_merge_kernel(TopkMergeArgs a) {
     if (threadIdx.x == 0 && t == 1) flag_error(a.err, DEVERR_TOKEN);
     aid = 0;
   }
+  // this workgroup's share of the copies
+  const int per = (total + gridDim.y - 1) / gridDim.y;
+  const int p0 = blockIdx.y * per, p1 = min(total, p0 + per);
   // 8 independent 16-byte copies per thread in flight at a time (named registers: an array
   // here ends up in scratch)
   auto src = [&](int idx) {
@@ -150,12 +216,12 @@ __global__ __launch_bounds__(256) void topk_merge_kernel(TopkMergeArgs a) {
     return *(const uint4*)((const char*)a.embed + (size_t)id * rb + (size_t)(idx - j * n16i) * 16);
   };
   auto put = [&](int idx, const uint4& v) {
-    if (idx >= total) return;
+    if (idx >= p1) return;
     const int j = idx / n16i;
     const size_t drow = j < a.k ? b * rps + 1 + (size_t)(t - 1) * a.k + j : b * rps;
     *(uint4*)(g + drow * rb + (size_t)(idx - j * n16i) * 16) = v;
   };
-  for (int i0 = threadIdx.x; i0 < total; i0 += 256 * 8) {
+  for (int i0 = p0 + threadIdx.x; i0 < p1; i0 += 256 * 8) {
     const uint4 v0 = src(i0), v1 = src(i0 + 256), v2 = src(i0 + 512), v3 = src(i0 + 768);
     const uint4 v4 = src(i0 + 1024), v5 = src(i0 + 1280), v6 = src(i0 + 1536), v7 = src(i0 + 1792);
     put(i0, v0);
@@ -275,7 +341,8 @@ hipError_t launch_topk_merge(const unsigned long long* keys, int chunks, int k, 
   if (batch <= 0 || B < 2) return hipSuccess;
   if ((D * esz) % 16) return hipErrorInvalidValue;
   TopkMergeArgs a{keys, chunks, k, B, embed, D, esz, anchor, V, err, cand, cand_out, gather};
-  hipLaunchKernelGGL(topk_merge_kernel, dim3(batch * (B - 1)), dim3(256), 0, st, a);
+  // the gather (k or k + 1 embedding rows per row) over 4 workgroups per row
+  hipLaunchKernelGGL(topk_merge_kernel, dim3(batch * (B - 1), 4), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
