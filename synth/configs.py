@@ -106,8 +106,16 @@ WIDE = Workload(
     ctx=(130, 0, 257, 1, 64), target=_WIDE_TARGET, taps=(0, 1),
     note="test-only bf16 model: vocab 40000, batch 5, contexts 130 / 0 / 257 / 1 / 64")
 
-WORKLOADS = {w.cid: w for w in (TINY, CFG2, CFG3, CFG4, CFG5, MID, WIDE)}
-WORKLOADS.update({w.name: w for w in (TINY, CFG2, CFG3, CFG4, CFG5, MID, WIDE)})
+# Test-only: the mid model at batch 24 (384 block rows: more than one 256-row tile with a
+# ragged last one, and LM-head / projection shapes that take the LDS-staged M > 16 GEMM),
+# ragged contexts in [1, 300].
+MANY = Workload(
+    cid=103, name="many_bf16", dtype="bf16", draft=_MID_DRAFT, n_taps=2, block=16, batch=24,
+    ctx=None, ctx_rule=("uniform", 1, 300), target=_MID_TARGET, taps=(1, 3),
+    note="test-only bf16 model at batch 24: 384 block rows, contexts uniform in [1, 300]")
+
+WORKLOADS = {w.cid: w for w in (TINY, CFG2, CFG3, CFG4, CFG5, MID, WIDE, MANY)}
+WORKLOADS.update({w.name: w for w in (TINY, CFG2, CFG3, CFG4, CFG5, MID, WIDE, MANY)})
 
 
 def workload(key) -> Workload:

@@ -1,7 +1,8 @@
 """GPU vs oracle parity at sizes the oracle finishes in seconds: the tiny fp32 drafter, a
 small bf16 GQA model whose shapes span several tiles and leave ragged tails (vocab 3000,
-contexts 200 / 333 / 64, pages handed out in shuffled order), and a wide-vocabulary bf16
-model (80 block rows x 40000 LM-head columns; contexts 130 / 0 / 257 / 1 / 64)."""
+contexts 200 / 333 / 64, pages handed out in shuffled order), the same model at batch 24
+(384 block rows, contexts in [1, 300]), and a wide-vocabulary bf16 model (80 block rows x
+40000 LM-head columns; contexts 130 / 0 / 257 / 1 / 64)."""
 import numpy as np
 import pytest
 import torch
@@ -16,8 +17,9 @@ from harness import (DEV, TOL, Setup, assert_accept, assert_close, assert_ids, a
 pytestmark = pytest.mark.gpu
 
 WORKLOADS = ["tiny_f32", "mid_bf16"]
-# plus a wide-vocabulary model with empty and one-row contexts for the draft / verify checks
-WITH_WIDE = WORKLOADS + ["wide_bf16"]
+# plus a wide-vocabulary model with empty and one-row contexts, and the mid model at batch 24
+# (384 block rows) for the draft / verify checks
+WITH_WIDE = WORKLOADS + ["wide_bf16", "many_bf16"]
 
 
 def _feats(w, lens):
