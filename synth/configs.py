@@ -114,8 +114,20 @@ MANY = Workload(
     ctx=None, ctx_rule=("uniform", 1, 300), target=_MID_TARGET, taps=(1, 3),
     note="test-only bf16 model at batch 24: 384 block rows, contexts uniform in [1, 300]")
 
-WORKLOADS = {w.cid: w for w in (TINY, CFG2, CFG3, CFG4, CFG5, MID, WIDE, MANY)}
-WORKLOADS.update({w.name: w for w in (TINY, CFG2, CFG3, CFG4, CFG5, MID, WIDE, MANY)})
+# Test-only: a narrow bf16 model (hidden 256) at batch 12: 192 block rows whose GEMMs are too
+# short in K to split and too small in N for the weight-direct tiles, i.e. the LDS-staged
+# M > 16 GEMM on compensated operand planes.
+_NARROW_DRAFT = ModelShape(n_layers=2, hidden=256, n_q_heads=2, n_kv_heads=1, head_dim=128,
+                           ffn=768, vocab=4000)
+_NARROW_TARGET = ModelShape(n_layers=3, hidden=256, n_q_heads=2, n_kv_heads=1, head_dim=128,
+                            ffn=768, vocab=4000)
+NARROW = Workload(
+    cid=104, name="narrow_bf16", dtype="bf16", draft=_NARROW_DRAFT, n_taps=2, block=16, batch=12,
+    ctx=None, ctx_rule=("uniform", 1, 200), target=_NARROW_TARGET, taps=(0, 2),
+    note="test-only bf16 model: hidden 256, batch 12 (192 block rows), contexts in [1, 200]")
+
+WORKLOADS = {w.cid: w for w in (TINY, CFG2, CFG3, CFG4, CFG5, MID, WIDE, MANY, NARROW)}
+WORKLOADS.update({w.name: w for w in (TINY, CFG2, CFG3, CFG4, CFG5, MID, WIDE, MANY, NARROW)})
 
 
 def workload(key) -> Workload:

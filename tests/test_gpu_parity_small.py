@@ -17,9 +17,10 @@ from harness import (DEV, TOL, Setup, assert_accept, assert_close, assert_ids, a
 pytestmark = pytest.mark.gpu
 
 WORKLOADS = ["tiny_f32", "mid_bf16"]
-# plus a wide-vocabulary model with empty and one-row contexts, and the mid model at batch 24
-# (384 block rows) for the draft / verify checks
-WITH_WIDE = WORKLOADS + ["wide_bf16", "many_bf16"]
+# plus a wide-vocabulary model with empty and one-row contexts, the mid model at batch 24
+# (384 block rows) and a narrow model at batch 12 (192 rows, the LDS-staged GEMM) for the
+# draft / verify checks
+WITH_WIDE = WORKLOADS + ["wide_bf16", "many_bf16", "narrow_bf16"]
 
 
 def _feats(w, lens):
