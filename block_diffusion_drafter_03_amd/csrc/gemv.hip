@@ -266,9 +266,11 @@ struct GemvLaunch {
     // is in flight at once; otherwise one workgroup per CU with the A slice stationary,
     // walking the tiles (the deferred epilogue buffer bounds the tiles per workgroup)
     if (n_tiles <= num_cus() || ga.K != 32 * GEMV_NW * GEMV_CH) {
-      // very few tiles (a quarter of the CUs or fewer, e.g. the 512-column correction maps
-      // of the convolutions): 16 waves split K, so each wave's share is one chunk in flight
-      if (n_tiles * 4 <= num_cus() && ga.K % (32 * 16) == 0)
+      // 16 waves split K whenever it divides (one workgroup per tile, up to the 8-wave form's
+      // grid): each wave's share is then one chunk in flight at K = 4096 (O), three at 12288
+      // (down), instead of two and six - these launches are bound by their chain of load
+      // round trips, not by bytes (O and down: 21.0 -> 20.2 us)
+      if (ga.K % (32 * 16) == 0 && n_tiles <= 8 * num_cus())
         return launch1(gemm_gemv_bf16<TA, 16, NORM, false, KIND>, dim3(n_tiles), dim3(16 * 64), st, ga);
       int grid = n_tiles;
       if (grid > 8 * num_cus()) grid = 8 * num_cus();
