@@ -243,11 +243,14 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_mfma_bf16(GemmArgs ga) {
 // double-buffered LDS stage of KSUB k-steps (fragment order; float32 rows split into (hi,
 // lo) bf16 pairs on the way in, RMSNorm statistics gathered there).  Per k-step a wave reads
 // BM/16 A fragments (per plane) from LDS and issues TN MFMAs on each, so LDS reads take
-// 1/TN of the MFMA time.  Weights run three stages ahead in a register ring, the
-// activations one stage ahead.  Grid: tiles M-fastest, remapped so the row tiles of one weight column
-// block run on one XCD (their second weight read hits that XCD's L2).
+// 1/TN of the MFMA time.  Weights run three stages ahead in a register ring (two at TN = 8,
+// whose 128 accumulators leave room for no more at two waves per SIMD), the activations one
+// stage ahead.  Grid: tiles M-fastest, rounded up to a multiple of 8 and remapped so each
+// XCD gets a contiguous range: the row tiles of one weight column block run on one XCD
+// (their repeated weight reads hit that XCD's L2).
 template <typename TA, int BM, int TN, int KSUB, bool NORM, int KIND>
-__global__ __launch_bounds__(256) void gemm_wdirect_bf16(GemmArgs ga) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TN >= 8 ? 2 : 1, 8)))
+void gemm_wdirect_bf16(GemmArgs ga) {
   constexpr bool TWO = AIsFloat<TA>::value;
   constexpr int NT_ = 256;
   constexpr int RB = BM / 16, BN = 64 * TN;
@@ -257,8 +260,9 @@ __global__ __launch_bounds__(256) void gemm_wdirect_bf16(GemmArgs ga) {
   constexpr int AS = TWO ? RB * 2 * 64 / NT_ : RB * 64 / NT_;
   static_assert(AS >= 1 && AS * NT_ == (TWO ? RB * 128 : RB * 64), "row tile does not split over the threads");
   
-  // epilogue chunk: EPC row blocks of accumulators per wave go through LDS at a time
-  constexpr int EPC = RB * TN * 4 <= 128 ? RB : RB / 2;
+  // epilogue chunk: EPC row blocks of accumulators per wave go through LDS at a time (two at
+  // TN = 8, so that two workgroups' LDS fit one CU)
+  constexpr int EPC = TN >= 8 ? 2 : (RB * TN * 4 <= 128 ? RB : RB / 2);
   constexpr int AS_BYTES = 2 * NP * KSUB * RB * 1024, EP_BYTES = 4 * EPC * TN * 1024;
   __shared__ __attribute__((aligned(16))) char smem[AS_BYTES > EP_BYTES ? AS_BYTES : EP_BYTES];
   bf16x8 (*As)[NP][KSUB][RB][64] = (bf16x8 (*)[NP][KSUB][RB][64])smem;
@@ -271,8 +275,10 @@ __global__ __launch_bounds__(256) void gemm_wdirect_bf16(GemmArgs ga) {
   const int MB = (M + 15) >> 4, NTl = (N + 15) >> 4;
   const int mt_n = (M + BM - 1) / BM, nt_n = (N + BN - 1) / BN;
   const int T = mt_n * nt_n;
+  const int G = gridDim.x;
   int t = blockIdx.x;
-  if ((T & 7) == 0) t = (blockIdx.x & 7) * (T >> 3) + (blockIdx.x >> 3);
+  if ((G & 7) == 0) t = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
+  if (t >= T) return;
   const int m0 = (t % mt_n) * BM, n0 = (t / mt_n) * BN;
 
   // ---- activation staging slots ----
@@ -406,19 +412,20 @@ __global__ __launch_bounds__(256) void gemm_wdirect_bf16(GemmArgs ga) {
     }
   };
 
-  // ring: stage q is computed with its weights from ring slot q % 3 and its activations
-  // from LDS buffer q % 2; then the activations of stage q + 1 (loaded one body earlier) go
-  // to the other buffer, and the freed slots reload stage q + 2 (activations) and q + 3
-  // (weights).  Loads past the last stage are clamped to it (L2 hits), so every body issues
+  // ring: stage q is computed with its weights from ring slot q % WDEPTH and its
+  // activations from LDS buffer q % 2; then the activations of stage q + 1 (loaded one body
+  // earlier) go to the other buffer, and the freed slots reload stage q + 2 (activations)
+  // and q + WDEPTH (weights).  Loads past the last stage are clamped to it (L2 hits), so every body issues
   // the same instructions and the compiler keeps the ring in flight.  (A deeper ring - four
   // weight stages, two activation stages - measured slower: it leaves the compiler too few
   // registers to schedule the MFMAs.)
   const int last = NST - 1;
+  constexpr int WDEPTH = TN >= 8 ? 2 : 3;
   WStage w0, w1, w2;
   AStage an;
   gload_w(w0, 0);
   gload_w(w1, min(1, last));
-  gload_w(w2, min(2, last));
+  if constexpr (WDEPTH == 3) gload_w(w2, min(2, last));
   gload_a(an, 0);
   lstore_a(an, 0, 0, true);
   gload_a(an, min(1, last));
@@ -427,13 +434,20 @@ __global__ __launch_bounds__(256) void gemm_wdirect_bf16(GemmArgs ga) {
     if (q < NST) compute(q & 1, wr);
     lstore_a(an, (q + 1) & 1, min(q + 1, last), q + 1 < NST);
     gload_a(an, min(q + 2, last));
-    gload_w(wr, min(q + 3, last));
+    gload_w(wr, min(q + WDEPTH, last));
     __syncthreads();
   };
-  for (int q = 0; q < NST; q += 3) {
-    body(q, w0);
-    body(q + 1, w1);
-    body(q + 2, w2);
+  if constexpr (WDEPTH == 3) {
+    for (int q = 0; q < NST; q += 3) {
+      body(q, w0);
+      body(q + 1, w1);
+      body(q + 2, w2);
+    }
+  } else {
+    for (int q = 0; q < NST; q += 2) {
+      body(q, w0);
+      body(q + 1, w1);
+    }
   }
   if (NORM) {
     // row rb*16 + (lane & 15) collects its 8 contributors (lane >> 4, half) in a fixed order
@@ -490,7 +504,10 @@ struct MfmaLaunch {
     auto wgs = [&](int bm, int bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
     const int ks = ga.K >> 5;
 #define WD_LAUNCH(BM, TN)                                                                     \
-  return launch1(gemm_wdirect_bf16<TA, BM, TN, 2, NORM, KIND>, dim3(wgs(BM, 64 * TN)),     \
+  return launch1(gemm_wdirect_bf16<TA, BM, TN, 2, NORM, KIND>, dim3((wgs(BM, 64 * TN) + 7) / 8 * 8), \
+                 dim3(256), st, ga)
+#define WD_LAUNCH1(BM, TN)                                                                    \
+  return launch1(gemm_wdirect_bf16<TA, BM, TN, 1, NORM, KIND>, dim3((wgs(BM, 64 * TN) + 7) / 8 * 8), \
                  dim3(256), st, ga)
 #define MFMA_LAUNCH(WGM, WGN, TM, TN, KSUB, DEPTH)                                             \
   return launch1(gemm_mfma_bf16<TA, WGM, WGN, TM, TN, KSUB, DEPTH, NORM, KIND>,               \
@@ -511,6 +528,12 @@ struct MfmaLaunch {
           const int n = wgs(64, 64 * tn);
           return (double)n / ((double)((n + slots - 1) / slots) * slots);
         };
+        // operand planes over a wide N (the LM head at 256 rows): 64 x 512 tiles, one k-step
+        // per stage, halve the LDS reads and the activation re-reads per MFMA (LM head
+        // 655 -> 584 us)
+        if constexpr (AIsPair<TA>::value) {
+          if (wgs(64, 512) >= 4 * num_cus()) WD_LAUNCH1(64, 8);
+        }
         const int tn = wgs(64, 256) >= slots ? 4 : 2;
         if constexpr (AIsFloat<TA>::value) {
           if (wgs(64, 192) >= num_cus() && fill(3) > fill(tn) + 0.1) WD_LAUNCH(64, 3);
@@ -531,6 +554,7 @@ struct MfmaLaunch {
     MFMA_LAUNCH(2, 2, 2, 2, 2, 3);
 #undef MFMA_LAUNCH
 #undef WD_LAUNCH
+#undef WD_LAUNCH1
   }
 };
 

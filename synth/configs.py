@@ -126,8 +126,21 @@ NARROW = Workload(
     ctx=None, ctx_rule=("uniform", 1, 200), target=_NARROW_TARGET, taps=(0, 2),
     note="test-only bf16 model: hidden 256, batch 12 (192 block rows), contexts in [1, 200]")
 
-WORKLOADS = {w.cid: w for w in (TINY, CFG2, CFG3, CFG4, CFG5, MID, WIDE, MANY, NARROW)}
-WORKLOADS.update({w.name: w for w in (TINY, CFG2, CFG3, CFG4, CFG5, MID, WIDE, MANY, NARROW)})
+# Test-only: the narrow model with a vocabulary of 120001 rows at batch 17: an LM head of 272
+# block rows (five 64-row tiles, the last with 16 rows) over 235 column tiles of 512, more
+# than four per CU, i.e. the widest weight-direct tile, with ragged row and column tails.
+_VAST_DRAFT = ModelShape(n_layers=1, hidden=256, n_q_heads=2, n_kv_heads=1, head_dim=128,
+                         ffn=768, vocab=120001)
+_VAST_TARGET = ModelShape(n_layers=2, hidden=256, n_q_heads=2, n_kv_heads=1, head_dim=128,
+                          ffn=768, vocab=120001)
+VAST = Workload(
+    cid=105, name="vast_bf16", dtype="bf16", draft=_VAST_DRAFT, n_taps=2, block=16, batch=17,
+    ctx=None, ctx_rule=("uniform", 1, 150), target=_VAST_TARGET, taps=(0, 1),
+    note="test-only bf16 model: hidden 256, vocab 120001, batch 17 (272 block rows)")
+
+_ALL = (TINY, CFG2, CFG3, CFG4, CFG5, MID, WIDE, MANY, NARROW, VAST)
+WORKLOADS = {w.cid: w for w in _ALL}
+WORKLOADS.update({w.name: w for w in _ALL})
 
 
 def workload(key) -> Workload:
