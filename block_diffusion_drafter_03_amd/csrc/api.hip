@@ -73,6 +73,7 @@ struct StepWs {
   float* xa;          // DFlash 2 convolutions: a convolution's input or output [Mp, D]
   float* dk;          // and its correction coefficients [M, D / 8]
   SplitArgs split;    // K-split scratch of the M > 16 GEMMs
+  GemvSplitArgs gsplit;  // K-split scratch of the M <= 16 O and down GEMVs
   AttnPlan plan;
 };
 
@@ -120,6 +121,14 @@ size_t step_ws(const dflash_model* m, int batch, int B, int ctx_cap, void* base,
   t.dk = (float*)cv.take(dc ? (size_t)M * (D / 8) * 4 : 0);
   const int max_k = std::max(std::max(D, Hq * hd), d.ffn);
   t.split = carve_split(cv, dt, M, (Hq + 2 * Hkv) * hd > D ? (Hq + 2 * Hkv) * hd : D, max_k);
+  memset(&t.gsplit, 0, sizeof(t.gsplit));
+  if (dt == DFLASH_BF16 && M <= 16) {   // the M <= 16 GEMVs of the layers: N <= max(D, Nqkv)
+    const int max_n = std::max(D, (Hq + 2 * Hkv) * hd);
+    t.gsplit.max_tiles = gemv_split_tiles(max_n);
+    t.gsplit.part = (float*)cv.take(gemv_split_part_bytes(max_n));
+    t.gsplit.ss = (float*)cv.take(gemv_split_ss_bytes(max_n));
+    t.gsplit.cnt = (unsigned*)cv.take((size_t)t.gsplit.max_tiles * 4);
+  }
   if (w) *w = t;
   return cv.off;
 }
@@ -158,6 +167,8 @@ EmbedArgs embed_args(const dflash_model* m, const dflash_kv* kv, const StepWs& w
   a.err = kv->error_flags;
   a.seq_len = kv->seq_len;
   a.hd = d.head_dim;
+  a.zero = w.gsplit.cnt;
+  a.n_zero = w.gsplit.cnt ? w.gsplit.max_tiles : 0;
   a.rope_base = d.rope_base;
   a.rope = w.rope;
   return a;
@@ -347,6 +358,7 @@ int run_layers(const dflash_model* m, const dflash_kv* kv, int batch, int B, con
       e.batch = kv->batch;
       e.err = kv->error_flags;
       g.split = w.split;
+      g.gsplit = w.gsplit;
       if (int s = run_gemm(DFLASH_KERNEL_GEMM_QKV, dt, g, st)) return s;
     }
     {
@@ -364,6 +376,7 @@ int run_layers(const dflash_model* m, const dflash_kv* kv, int batch, int B, con
       g.e.ldo = D;
       g.e.afrag = afrag;
       g.split = w.split;
+      g.gsplit = w.gsplit;
       if (int s = run_gemm(DFLASH_KERNEL_GEMM_O, dt, g, st)) return s;
     }
     if (dc) {
@@ -401,6 +414,7 @@ int run_layers(const dflash_model* m, const dflash_kv* kv, int batch, int B, con
           }
       }
       g.split = w.split;
+      g.gsplit = w.gsplit;
       if (int s = run_gemm(DFLASH_KERNEL_GEMM_DOWN, dt, g, st)) return s;
     }
     if (dc)

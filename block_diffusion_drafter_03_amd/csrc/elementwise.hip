@@ -50,9 +50,11 @@ __global__ __launch_bounds__(256) void embed_kernel(EmbedArgs a) {
     rope_cs(pos, i, a.hd, a.rope_base, &c, &s);
     a.rope[(size_t)row * (a.hd / 2) + i] = make_float2(c, s);
   }
-  // arm this call's argmax keys
-  if (row == 0)
+  // arm this call's argmax keys and arrival counters
+  if (row == 0) {
     for (int i = threadIdx.x; i < a.n_keys; i += 256) a.keys[i] = 0ull;
+    for (int i = threadIdx.x; i < a.n_zero; i += 256) a.zero[i] = 0u;
+  }
 }
 
 hipError_t launch_embed(int dt, const EmbedArgs& a, hipStream_t st) {

@@ -254,6 +254,170 @@ __global__ __launch_bounds__(NW * 64) void gemm_gemv_bf16(GemmArgs ga) {
   }
 }
 
+// ---------------------------------------------------------------------------------------
+// K-split M <= 16 GEMV.  Every 16-column tile needs the whole A, so one workgroup per tile
+// re-reads all of A per tile.  Here a workgroup takes TW tiles (one column group) over one
+// of S K ranges - A is read once per group, in S parts - and the splits meet without a
+// grid-wide barrier or a release fence (which writes back the whole L2 of an XCD): each
+// workgroup stores its partial tiles (and, with the A-side norm, its rows' partial sums of
+// squares) with agent-scope stores, which are coherent across the XCDs' L2s once complete,
+// waits for them to complete, then counts itself in on the group's counter; the workgroup
+// that arrives last reads the S partials with agent-scope loads, sums them in split order
+// (so the result does not depend on which one that is), applies rstd and runs the
+// epilogue, then re-arms the counter for the next launch.  The counters start at zero
+// (zeroed by the step's embedding kernel).
+template <int TW, int NW, bool NORM, int KIND>
+__global__ __launch_bounds__(NW * 64) void gemm_gemv_splitk_bf16(GemmArgs ga) {
+  constexpr int CHS = 4;   // steps loaded together per wave
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int r = lane & 15, g = lane >> 4;
+  const int KS = ga.K >> 5;
+  const int n_tiles = (ga.N + 15) >> 4, n_groups = (n_tiles + TW - 1) / TW;
+  const int S = (int)gridDim.x / n_groups;          // the launcher makes gridDim.x = groups S
+  const int grp = blockIdx.x % n_groups, sp = blockIdx.x / n_groups;
+  const int spw = KS / (S * NW);                    // the launcher checks KS % (S NW) == 0
+  const int ks0 = (sp * NW + w) * spw;
+  const bf16* wp[TW];
+#pragma unroll
+  for (int j = 0; j < TW; ++j) wp[j] = wblock(ga.B, min(grp * TW + j, n_tiles - 1), 0, KS) + lane * 8;
+  const bf16* gk = NORM ? (const bf16*)ga.norm_g + g * 8 : nullptr;
+  f32x4 acc[TW], acc2[TW];
+#pragma unroll
+  for (int j = 0; j < TW; ++j) acc[j] = acc2[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float ss = 0.f;
+  for (int c0 = 0; c0 < spw; c0 += CHS) {
+    // a chunk's weights, activations and gains loaded together, unconditionally (steps
+    // past spw clamped to the last one, their activations zeroed)
+    bf16x8 wf[CHS][TW], gv[CHS];
+    float av[CHS][8];
+#pragma unroll
+    for (int s = 0; s < CHS; ++s) {
+      const int k = ks0 + min(c0 + s, spw - 1);
+#pragma unroll
+      for (int j = 0; j < TW; ++j) wf[s][j] = *(const bf16x8*)(wp[j] + (size_t)k * 512);
+      afrag_load8((const float*)ga.A, 0, k, KS, lane, av[s]);
+      if constexpr (NORM) gv[s] = *(const bf16x8*)(gk + (size_t)k * 32);
+    }
+    // (left to itself the compiler waits for each step's loads right after issuing them)
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int s = 0; s < CHS; ++s) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) av[s][e] = c0 + s < spw ? av[s][e] : 0.f;
+      bf16x8 hi, lo;
+      a_operand<NORM>(av[s], gv[s], &ss, hi, lo);
+#pragma unroll
+      for (int j = 0; j < TW; ++j) {
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, wf[s][j], acc[j], 0, 0, 0);
+        acc2[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, wf[s][j], acc2[j], 0, 0, 0);
+      }
+    }
+  }
+  // the split's partial tiles: wave j < TW sums tile j over the waves in wave order (and
+  // wave TW the rows' sums of squares)
+  __shared__ f32x4 red[NW][TW][64];
+  __shared__ float ss_red[NORM ? NW : 1][16];
+  __shared__ float rstd[16];
+  __shared__ unsigned arrived;
+#pragma unroll
+  for (int j = 0; j < TW; ++j) red[w][j][lane] = acc[j] + acc2[j];
+  if (NORM) {
+    ss += __shfl_xor(ss, 16, 64);
+    ss += __shfl_xor(ss, 32, 64);
+    if (g == 0) ss_red[w][r] = ss;
+  }
+  __syncthreads();
+  const GemvSplitArgs& gs = ga.gsplit;
+  const size_t slot = (size_t)sp * n_groups + grp;
+  if (w < TW) {
+    f32x4 p = red[0][w][lane];
+#pragma unroll
+    for (int ww = 1; ww < NW; ++ww) p += red[ww][w][lane];
+    float* q = gs.part + ((slot * TW + w) * 64 + lane) * 4;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) __hip_atomic_store(q + e, p[e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  } else if (NORM && w == TW && lane < 16) {
+    float t = ss_red[0][lane];
+#pragma unroll
+    for (int ww = 1; ww < NW; ++ww) t += ss_red[ww][lane];
+    __hip_atomic_store(gs.ss + slot * 16 + lane, t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  // every partial store of this workgroup has completed before it counts itself in
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __syncthreads();
+  if (threadIdx.x == 0)
+    arrived = __hip_atomic_fetch_add(gs.cnt + grp, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  if (arrived != (unsigned)(S - 1)) return;
+  // the group's last workgroup: the S partials summed in split order, then the epilogue
+  if (NORM) {
+    if (threadIdx.x < 16) {
+      float t = 0.f;
+      for (int s = 0; s < S; ++s)
+        t += __hip_atomic_load(gs.ss + ((size_t)s * n_groups + grp) * 16 + threadIdx.x, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+      rstd[threadIdx.x] = 1.0f / sqrtf(t / (float)ga.K + ga.eps);
+    }
+    __syncthreads();
+  }
+  if (w < TW) {
+    f32x4 v = {0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < S; ++s) {
+      const float* q = gs.part + ((((size_t)s * n_groups + grp) * TW + w) * 64 + lane) * 4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] += __hip_atomic_load(q + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    float vv[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) vv[e] = NORM ? v[e] * rstd[g * 4 + e] : v[e];
+    unsigned long long best[4];
+    tile_epilogue<bf16, KIND>(ga, g * 4, (grp * TW + w) * 16 + r, vv, r, best);
+  }
+  if (threadIdx.x == 0) __hip_atomic_store(gs.cnt + grp, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+int gemv_split_tiles(int max_n) { return (max_n + 15) / 16 + 3; }
+size_t gemv_split_part_bytes(int max_n) { return (size_t)GEMV_SPLIT_MAX * gemv_split_tiles(max_n) * 1024; }
+size_t gemv_split_ss_bytes(int max_n) { return (size_t)GEMV_SPLIT_MAX * gemv_split_tiles(max_n) * 64; }
+
+#define GEMV_SPLIT_NW 8     // waves per workgroup of the K-split GEMV
+
+// Which GEMVs take the K-split form (measured on the Qwen3-8B shapes, M = 16): QKV (the
+// A-side norm; 384 tiles over 128 groups of 3, two splits: 20.2 -> 18.6 us, the
+// stationary form's per-workgroup prologue of the whole normalised A slice gone) and the
+// down projection (K = 12288: 27.7 -> 25.7 us).  Not O (K = 4096, no norm: the streamed
+// 16-wave form has one chunk per wave already; 12.4 -> 14.0 us split), nor gate/up and the
+// LM head (too many tiles for one resident grid).
+template <bool NORM, int KIND>
+constexpr bool gemv_split_kind() {
+  return NORM ? KIND == EPI_QKV : (KIND == EPI_RESID || KIND == EPI_STORE_F32);
+}
+
+// Tile width and splits of the K-split GEMV for this shape (false when it does not apply):
+// a grid resident at once (one 8-wave workgroup per CU: 3 waves per SIMD by registers)
+// that keeps the most CUs busy, each wave with at least one 4-step chunk; among equals the
+// widest column group (the least A traffic).  Without the norm only for K > 4096.
+static bool gemv_split_plan(const GemmArgs& ga, int* tw, int* splits) {
+  const GemvSplitArgs& gs = ga.gsplit;
+  const int n_tiles = (ga.N + 15) / 16, KS = ga.K / 32;
+  if (!gs.part || !gs.cnt || (ga.norm_g && !gs.ss) || ga.a_bf16 || ga.K % 32 || n_tiles + 3 > gs.max_tiles)
+    return false;
+  if (!ga.norm_g && ga.K <= 4096) return false;
+  int best = 0;
+  for (int t = 4; t >= 2; --t) {
+    const int groups = (n_tiles + t - 1) / t;
+    for (int S = GEMV_SPLIT_MAX; S >= 2; S /= 2)
+      if (KS % (S * GEMV_SPLIT_NW) == 0 && KS / (S * GEMV_SPLIT_NW) >= 4 && groups * S <= num_cus() &&
+          groups * S > best) {
+        best = groups * S;
+        *tw = t;
+        *splits = S;
+      }
+  }
+  return best > 0;
+}
+
 struct GemvLaunch {
   template <typename TA, bool NORM, int KIND>
   static hipError_t run(const GemmArgs& ga, hipStream_t st) {
@@ -261,6 +425,17 @@ struct GemvLaunch {
       return hipErrorInvalidValue;   // the GEMV splits its activations itself
     } else {
     const int n_tiles = (ga.N + 15) / 16;
+    if constexpr (gemv_split_kind<NORM, KIND>() && AIsFloat<TA>::value) {
+      int tw = 0, S = 0;
+      if (gemv_split_plan(ga, &tw, &S)) {
+        const dim3 grid(((n_tiles + tw - 1) / tw) * S), block(GEMV_SPLIT_NW * 64);
+        switch (tw) {
+          case 4: return launch1(gemm_gemv_splitk_bf16<4, GEMV_SPLIT_NW, NORM, KIND>, grid, block, st, ga);
+          case 3: return launch1(gemm_gemv_splitk_bf16<3, GEMV_SPLIT_NW, NORM, KIND>, grid, block, st, ga);
+          default: return launch1(gemm_gemv_splitk_bf16<2, GEMV_SPLIT_NW, NORM, KIND>, grid, block, st, ga);
+        }
+      }
+    }
     // few tiles (up to one per CU) or K != 4096: one workgroup
     // per tile, A streamed with W, so that several workgroups may share a CU and every tile
     // is in flight at once; otherwise one workgroup per CU with the A slice stationary,

@@ -110,6 +110,21 @@ struct SplitArgs {
 #define ROWS_MAX_NORM_K 16384          // A-side norm gains held in LDS
 #define ROWS_SPLIT_BYTES ((size_t)32 << 20)
 
+// Scratch of the K-split M <= 16 GEMV: each workgroup takes 2-4 16-column tiles over one
+// of `splits` K ranges; the last of a column group's workgroups to arrive sums the partial
+// tiles in split order and runs the epilogue.
+#define GEMV_SPLIT_MAX 8
+struct GemvSplitArgs {
+  float* part;          // [splits][groups][tiles a group][64 lanes][4]: partial tiles
+  float* ss;            // [splits][groups][16]: partial sums of squares (A-side norm)
+  unsigned* cnt;        // [groups]: arrivals within the running launch; zero between launches
+  int max_tiles;        // capacity: splits x groups x tiles a group <= GEMV_SPLIT_MAX max_tiles
+};
+// scratch for GEMMs of up to max_n columns: tile capacity and the bytes of part and ss
+int gemv_split_tiles(int max_n);
+size_t gemv_split_part_bytes(int max_n);
+size_t gemv_split_ss_bytes(int max_n);
+
 struct GemmArgs {
   const void* A;        // [M, K]: float32 activations (A-fragment order for bf16 models), or
                         // caller-supplied bf16 rows (row-major, stride lda) when a_bf16
@@ -122,6 +137,7 @@ struct GemmArgs {
   EpiArgs e;
   SplitArgs split;      // bf16 models, M > 16: K-split and operand scratch
   int a_pair;           // set by launch_gemm: A holds (hi, lo) planes (pair_split), no norm
+  GemvSplitArgs gsplit; // bf16 models, M <= 16, no norm: K-split scratch (or none)
 };
 // split scratch bytes for GEMMs of up to `rows` rows and `max_n` columns: (part, ss)
 size_t rows_split_bytes(int rows, int max_n);
@@ -181,10 +197,12 @@ struct EmbedArgs {
   int hd;
   double rope_base;
   float2* rope;             // [batch*B, hd/2] out
+  unsigned* zero;           // [n_zero] counters zeroed for the step (K-split GEMV arrivals)
+  int n_zero;
 };
 // h[r] = E[token(r)] (float32), r = b*B + j:
 // token = anchor[b] for j == 0, else mask_id (mode 0) or ids[b*(B-1) + j-1] (mode 1).
-// Also writes the rows' RoPE (cos, sin) table and zeroes the argmax keys.
+// Also writes the rows' RoPE (cos, sin) table and zeroes the argmax keys and `zero`.
 hipError_t launch_embed(int dt, const EmbedArgs& a, hipStream_t st);
 
 // RoPE (cos, sin) table of injection rows: position row_pos[r] (+ seq_len[row_seq[r]]).

@@ -138,7 +138,20 @@ VAST = Workload(
     ctx=None, ctx_rule=("uniform", 1, 150), target=_VAST_TARGET, taps=(0, 1),
     note="test-only bf16 model: hidden 256, vocab 120001, batch 17 (272 block rows)")
 
-_ALL = (TINY, CFG2, CFG3, CFG4, CFG5, MID, WIDE, MANY, NARROW, VAST)
+# Test-only: a batch-1 model whose M = 16 GEMVs take the K-split form on ragged shapes:
+# QKV (K = 2560, 192 tiles: two-tile groups, two splits of five steps a wave, the last
+# chunk clamped) and down (K = 8192 over 160 tiles: three-tile groups, the last holding
+# one tile, four splits).
+_SPLIT_DRAFT = ModelShape(n_layers=2, hidden=2560, n_q_heads=16, n_kv_heads=4, head_dim=128,
+                          ffn=8192, vocab=5000)
+_SPLIT_TARGET = ModelShape(n_layers=2, hidden=2560, n_q_heads=16, n_kv_heads=4, head_dim=128,
+                           ffn=8192, vocab=5000)
+SPLIT = Workload(
+    cid=106, name="split_bf16", dtype="bf16", draft=_SPLIT_DRAFT, n_taps=2, block=16, batch=1,
+    ctx=(300,), target=_SPLIT_TARGET, taps=(0, 1),
+    note="test-only bf16 model: hidden 2560, FFN 8192, batch 1 (the K-split M = 16 GEMVs)")
+
+_ALL = (TINY, CFG2, CFG3, CFG4, CFG5, MID, WIDE, MANY, NARROW, VAST, SPLIT)
 WORKLOADS = {w.cid: w for w in _ALL}
 WORKLOADS.update({w.name: w for w in _ALL})
 

@@ -3,7 +3,8 @@ small bf16 GQA model whose shapes span several tiles and leave ragged tails (voc
 contexts 200 / 333 / 64, pages handed out in shuffled order), the same model at batch 24
 (384 block rows, contexts in [1, 300]), a wide-vocabulary bf16 model (80 block rows x
 40000 LM-head columns; contexts 130 / 0 / 257 / 1 / 64), a narrow one (hidden 256, 192 block
-rows) and a narrow one with a vocabulary of 120001 at batch 17 (272 x 120001 LM head)."""
+rows), a narrow one with a vocabulary of 120001 at batch 17 (272 x 120001 LM head) and a
+batch-1 model (hidden 2560, FFN 8192) whose M = 16 GEMVs split K over workgroups."""
 import numpy as np
 import pytest
 import torch
@@ -20,9 +21,10 @@ pytestmark = pytest.mark.gpu
 WORKLOADS = ["tiny_f32", "mid_bf16"]
 # plus a wide-vocabulary model with empty and one-row contexts, the mid model at batch 24
 # (384 block rows), a narrow model at batch 12 (192 rows, the LDS-staged GEMM) and the narrow
-# model over 120001 vocabulary rows at batch 17 (the widest weight-direct LM-head tile) for
-# the draft / verify checks
-WITH_WIDE = WORKLOADS + ["wide_bf16", "many_bf16", "narrow_bf16", "vast_bf16"]
+# model over 120001 vocabulary rows at batch 17 (the widest weight-direct LM-head tile) and
+# a batch-1 model whose QKV and down GEMVs take the K-split form on ragged shapes, for the
+# draft / verify checks
+WITH_WIDE = WORKLOADS + ["wide_bf16", "many_bf16", "narrow_bf16", "vast_bf16", "split_bf16"]
 
 
 def _feats(w, lens):
