@@ -127,7 +127,8 @@ size_t step_ws(const dflash_model* m, int batch, int B, int ctx_cap, void* base,
     t.gsplit.max_tiles = gemv_split_tiles(max_n);
     t.gsplit.part = (float*)cv.take(gemv_split_part_bytes(max_n));
     t.gsplit.ss = (float*)cv.take(gemv_split_ss_bytes(max_n));
-    t.gsplit.cnt = (unsigned*)cv.take((size_t)t.gsplit.max_tiles * 4);
+    // (one more counter: the LM head's draft-id decode)
+    t.gsplit.cnt = (unsigned*)cv.take((size_t)(t.gsplit.max_tiles + 1) * 4);
   }
   if (w) *w = t;
   return cv.off;
@@ -168,7 +169,7 @@ EmbedArgs embed_args(const dflash_model* m, const dflash_kv* kv, const StepWs& w
   a.seq_len = kv->seq_len;
   a.hd = d.head_dim;
   a.zero = w.gsplit.cnt;
-  a.n_zero = w.gsplit.cnt ? w.gsplit.max_tiles : 0;
+  a.n_zero = w.gsplit.cnt ? w.gsplit.max_tiles + 1 : 0;
   a.rope_base = d.rope_base;
   a.rope = w.rope;
   return a;
@@ -434,7 +435,8 @@ struct Sampling {
 };
 
 int run_lm_head(const dflash_model* m, const StepWs& w, int rows, int skipB, float* logits,
-                hipStream_t st, int B = 0, const Sampling& smp = Sampling()) {
+                hipStream_t st, int B = 0, const Sampling& smp = Sampling(), int32_t* draft_ids = nullptr,
+                bool* ids_done = nullptr) {
   const dflash_model_desc& d = m->d;
   GemmArgs g = gemm_args(w.h, d.hidden, one_seg(d.lm_head, d.vocab, d.hidden), rows, d.vocab,
                          d.hidden, d.final_norm, d.rms_eps, EPI_ARGMAX);
@@ -449,6 +451,14 @@ int run_lm_head(const dflash_model* m, const StepWs& w, int rows, int skipB, flo
     g.e.counter = smp.counter;
     g.e.B = B;
   }
+  // the M <= 16 GEMV decodes the draft ids itself (its last workgroup), saving a launch
+  const bool fold = draft_ids && B > 1 && w.gsplit.cnt && gemm_takes_gemv(d.dtype, g);
+  if (fold) {
+    g.e.ids_out = draft_ids;
+    g.e.ids_cnt = w.gsplit.cnt + w.gsplit.max_tiles;
+    g.e.ids_B = B;
+  }
+  if (ids_done) *ids_done = fold;
   return run_gemm(DFLASH_KERNEL_LM_HEAD, d.dtype, g, st);
 }
 
@@ -684,9 +694,10 @@ static int draft_block_impl(const dflash_model* m, const dflash_kv* kv, const in
   e = run_layers(m, kv, batch, B, w, /*causal=*/0, /*write_cache=*/0, nullptr, hidden_dbg, st);
   if (e) return e;
   if (B == 1) return DFLASH_OK;   // a block of one has no masked position to draft
-  e = run_lm_head(m, w, M, B, logits_dbg, st, B, smp);
+  bool ids_done = false;
+  e = run_lm_head(m, w, M, B, logits_dbg, st, B, smp, draft_ids, &ids_done);
   if (e) return e;
-  HIPCHK(launch_unpack_ids(w.keys, batch, B, draft_ids, st));
+  if (!ids_done) HIPCHK(launch_unpack_ids(w.keys, batch, B, draft_ids, st));
   return DFLASH_OK;
 }
 

@@ -88,12 +88,11 @@ hipError_t launch_rope_rows(const int32_t* row_seq, const int32_t* row_pos, int 
 }
 
 // ---------------------------------------------------------------------------------------
-DF_DEV int key_index(unsigned long long k) { return (int)(0xFFFFFFFFu - (unsigned)(k & 0xFFFFFFFFull)); }
 
 // draft ids of the masked rows j = 1 .. B-1 of every block (the anchor rows' argmax is unused)
 __global__ void unpack_ids_kernel(const unsigned long long* keys, int n, int B, int32_t* ids) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) ids[i] = key_index(keys[(i / (B - 1)) * B + i % (B - 1) + 1]);
+  if (i < n) ids[i] = unpack_argmax_idx(keys[(i / (B - 1)) * B + i % (B - 1) + 1]);
 }
 
 hipError_t launch_unpack_ids(const unsigned long long* keys, int batch, int B, int32_t* ids,
@@ -110,7 +109,7 @@ hipError_t launch_unpack_ids(const unsigned long long* keys, int batch, int B, i
 __global__ __launch_bounds__(64) void accept_kernel(const unsigned long long* keys, const int32_t* drafts,
                                                     int B, int32_t* g, int32_t* tau, int32_t* bonus) {
   const int b = blockIdx.x, j = threadIdx.x;
-  const int gj = j < B ? key_index(keys[(size_t)b * B + j]) : -1;
+  const int gj = j < B ? unpack_argmax_idx(keys[(size_t)b * B + j]) : -1;
   if (j < B) g[(size_t)b * B + j] = gj;
   const int gprev = __shfl_up(gj, 1, 64);
   const bool miss = j >= 1 && j < B && drafts[(size_t)b * (B - 1) + j - 1] != gprev;

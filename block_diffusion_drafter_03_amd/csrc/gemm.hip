@@ -174,6 +174,10 @@ size_t pair_plane_bytes(int rows, int max_k) { return (size_t)((rows + 15) / 16)
 hipError_t launch_gemv(const GemmArgs& ga, hipStream_t st);
 hipError_t launch_gemm_rows(const GemmArgs& ga, hipStream_t st);
 
+bool gemm_takes_gemv(int dt, const GemmArgs& ga) {
+  return dt != F32 && !ga.a_pair && ga.M >= 1 && ga.M <= 16 && ga.K % (32 * GEMV_NW) == 0;
+}
+
 hipError_t launch_gemm(int dt, const GemmArgs& ga, hipStream_t st) {
   if (ga.M <= 0 || ga.N <= 0) return hipSuccess;
   if (ga.a_pair) {
@@ -182,7 +186,7 @@ hipError_t launch_gemm(int dt, const GemmArgs& ga, hipStream_t st) {
     return launch_gemm_rows(ga, st);
   }
   if (dt == F32) return dispatch_gemm<F32Launch>(ga, st);
-  if (ga.M <= 16 && ga.K % (32 * GEMV_NW) == 0) return launch_gemv(ga, st);
+  if (gemm_takes_gemv(dt, ga)) return launch_gemv(ga, st);
   if (!ga.a_bf16 && ga.split.pair && pair_plane_bytes(ga.M, ga.K) <= ga.split.pair_bytes) {
     // about 256 workgroups over (row groups, K chunks)
     const int KS = ga.K / 32, groups = (ga.M + 15) / 16 * (ga.norm_g ? 4 : 1);

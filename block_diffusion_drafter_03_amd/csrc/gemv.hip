@@ -252,6 +252,28 @@ __global__ __launch_bounds__(NW * 64) void gemm_gemv_bf16(GemmArgs ga) {
       if (row < M && k) atomicMax(&ga.e.keys[row], k);
     }
   }
+  if constexpr (KIND == EPI_ARGMAX) {
+    if (ga.e.ids_out) {
+      // the draft ids, decoded by the last workgroup to arrive: every key update of a
+      // workgroup (device-coherent atomics) has completed before it counts itself in
+      __shared__ unsigned arrived;
+      __builtin_amdgcn_s_waitcnt(0);
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      __syncthreads();
+      if (threadIdx.x == 0)
+        arrived = __hip_atomic_fetch_add(ga.e.ids_cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __syncthreads();
+      if (arrived == gridDim.x - 1) {
+        const int B = ga.e.ids_B, n = (M / B) * (B - 1);
+        for (int i = threadIdx.x; i < n; i += NW * 64) {
+          const unsigned long long k = __hip_atomic_load(ga.e.keys + (i / (B - 1)) * B + i % (B - 1) + 1,
+                                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          ga.e.ids_out[i] = unpack_argmax_idx(k);
+        }
+        if (threadIdx.x == 0) __hip_atomic_store(ga.e.ids_cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------------------

@@ -76,6 +76,12 @@ struct EpiArgs {
   unsigned long long* keys;
   float* logits;
   int skipB;
+  // and, when ids_out != NULL (taken by the M <= 16 GEMV only), the draft ids of the
+  // masked rows: ids_out[b (ids_B - 1) + j - 1] = argmax of row b ids_B + j, j >= 1,
+  // written by the launch's last workgroup (arrival counter ids_cnt, zero between launches)
+  int32_t* ids_out;
+  unsigned* ids_cnt;
+  int ids_B;
   // sampling instead of argmax: key = logit / temperature + Gumbel noise of draw (counter,
   // purpose 0, b = row / B, i = row % B, v = column)
   int sample;
@@ -147,6 +153,8 @@ size_t pair_plane_bytes(int rows, int max_k);
 
 // acc = A x W^T over the full K, then the epilogue.
 hipError_t launch_gemm(int dt, const GemmArgs& g, hipStream_t st);
+// whether launch_gemm takes the M <= 16 GEMV for these arguments
+bool gemm_takes_gemv(int dt, const GemmArgs& g);
 // The DFlash 2 convolution fused into its correction GEMM (EPI_DCONV): bf16 models, M <= 16,
 // N = K / 8 with K a multiple of 512 and at most one 16-column tile per four CUs.
 bool gemv_dconv_supported(int M, int K);
