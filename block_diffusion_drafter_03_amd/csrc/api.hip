@@ -434,9 +434,15 @@ struct Sampling {
   unsigned counter = 0;
 };
 
+// With draft_ids (drafter) or acc (verifier) the M <= 16 GEMV also decodes the draft ids
+// or runs the greedy acceptance (its last workgroup); *done tells whether it did.
+struct AcceptOut {
+  const int32_t* drafts;
+  int32_t *g, *tau, *bonus;
+};
 int run_lm_head(const dflash_model* m, const StepWs& w, int rows, int skipB, float* logits,
                 hipStream_t st, int B = 0, const Sampling& smp = Sampling(), int32_t* draft_ids = nullptr,
-                bool* ids_done = nullptr) {
+                bool* ids_done = nullptr, const AcceptOut* acc = nullptr) {
   const dflash_model_desc& d = m->d;
   GemmArgs g = gemm_args(w.h, d.hidden, one_seg(d.lm_head, d.vocab, d.hidden), rows, d.vocab,
                          d.hidden, d.final_norm, d.rms_eps, EPI_ARGMAX);
@@ -451,12 +457,18 @@ int run_lm_head(const dflash_model* m, const StepWs& w, int rows, int skipB, flo
     g.e.counter = smp.counter;
     g.e.B = B;
   }
-  // the M <= 16 GEMV decodes the draft ids itself (its last workgroup), saving a launch
-  const bool fold = draft_ids && B > 1 && w.gsplit.cnt && gemm_takes_gemv(d.dtype, g);
+  // the M <= 16 GEMV decodes the draft ids (or accepts) itself, saving a launch
+  const bool fold = (draft_ids || acc) && B > 1 && B <= 64 && w.gsplit.cnt && gemm_takes_gemv(d.dtype, g);
   if (fold) {
     g.e.ids_out = draft_ids;
     g.e.ids_cnt = w.gsplit.cnt + w.gsplit.max_tiles;
     g.e.ids_B = B;
+    if (acc) {
+      g.e.acc_drafts = acc->drafts;
+      g.e.acc_g = acc->g;
+      g.e.acc_tau = acc->tau;
+      g.e.acc_bonus = acc->bonus;
+    }
   }
   if (ids_done) *ids_done = fold;
   return run_gemm(DFLASH_KERNEL_LM_HEAD, d.dtype, g, st);
@@ -816,9 +828,11 @@ int dflash_verify_accept(const dflash_model* m, dflash_kv* kv, const int32_t* an
   HIPCHK(launch_embed(d.dtype, embed_args(m, kv, w, 1, draft_ids, anchor, B, hidden_dbg), st));
   e = run_layers(m, kv, batch, B, w, /*causal=*/1, /*write_cache=*/1, feats_out, hidden_dbg, st);
   if (e) return e;
-  e = run_lm_head(m, w, M, 0, logits_dbg, st);
+  const AcceptOut acc{draft_ids, target_argmax, tau, bonus};
+  bool accepted = false;
+  e = run_lm_head(m, w, M, 0, logits_dbg, st, B, Sampling(), nullptr, &accepted, &acc);
   if (e) return e;
-  HIPCHK(launch_accept(w.keys, draft_ids, batch, B, target_argmax, tau, bonus, st));
+  if (!accepted) HIPCHK(launch_accept(w.keys, draft_ids, batch, B, target_argmax, tau, bonus, st));
   return DFLASH_OK;
 }
 

@@ -108,19 +108,7 @@ hipError_t launch_unpack_ids(const unsigned long long* keys, int batch, int B, i
 // scan; tau = a + 1 and bonus = g_a.
 __global__ __launch_bounds__(64) void accept_kernel(const unsigned long long* keys, const int32_t* drafts,
                                                     int B, int32_t* g, int32_t* tau, int32_t* bonus) {
-  const int b = blockIdx.x, j = threadIdx.x;
-  const int gj = j < B ? unpack_argmax_idx(keys[(size_t)b * B + j]) : -1;
-  if (j < B) g[(size_t)b * B + j] = gj;
-  const int gprev = __shfl_up(gj, 1, 64);
-  const bool miss = j >= 1 && j < B && drafts[(size_t)b * (B - 1) + j - 1] != gprev;
-  const unsigned long long mask = __ballot(miss);
-  // drafts 1 .. a match, draft a + 1 (if any) does not: a = (lowest mismatching lane) - 1
-  const int a = mask ? __ffsll((long long)mask) - 2 : B - 1;
-  const int ga = __shfl(gj, a, 64);
-  if (j == 0) {
-    tau[b] = a + 1;
-    bonus[b] = ga;
-  }
+  accept_wave<false>(keys, drafts, B, blockIdx.x, g, tau, bonus);
 }
 
 hipError_t launch_accept(const unsigned long long* keys, const int32_t* drafts, int batch, int B,

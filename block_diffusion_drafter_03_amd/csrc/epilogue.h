@@ -27,6 +27,33 @@ DF_DEV int unpack_argmax_idx(unsigned long long key) {
   return (int)(0xFFFFFFFFu - (unsigned)(key & 0xFFFFFFFFull));
 }
 
+// Greedy acceptance of sequence b by one wavefront (B <= 64): lane j decodes g_j, the
+// target's argmax after row j, from its packed key; lane j >= 1 compares draft d_j with
+// g_{j-1} (its neighbour's id); a ballot of the mismatches gives the leading run of matches
+// a by a bit scan; tau = a + 1 and bonus = g_a.  AGENT: the keys are read with agent-scope
+// loads (they were updated by other workgroups of the same launch).
+template <bool AGENT>
+DF_DEV void accept_wave(const unsigned long long* keys, const int32_t* drafts, int B, int b, int32_t* g,
+                        int32_t* tau, int32_t* bonus) {
+  const int j = threadIdx.x & 63;
+  unsigned long long k = 0ull;
+  if (j < B)
+    k = AGENT ? __hip_atomic_load(keys + (size_t)b * B + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+              : keys[(size_t)b * B + j];
+  const int gj = j < B ? unpack_argmax_idx(k) : -1;
+  if (j < B) g[(size_t)b * B + j] = gj;
+  const int gprev = __shfl_up(gj, 1, 64);
+  const bool miss = j >= 1 && j < B && drafts[(size_t)b * (B - 1) + j - 1] != gprev;
+  const unsigned long long mask = __ballot(miss);
+  // drafts 1 .. a match, draft a + 1 (if any) does not: a = (lowest mismatching lane) - 1
+  const int a = mask ? __ffsll((long long)mask) - 2 : B - 1;
+  const int ga = __shfl(gj, a, 64);
+  if (j == 0) {
+    tau[b] = a + 1;
+    bonus[b] = ga;
+  }
+}
+
 template <typename T, int KIND>
 DF_DEV void epi_elem(const EpiArgs& e, int row, int col, float v) {
   switch (KIND) {

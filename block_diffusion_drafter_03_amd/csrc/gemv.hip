@@ -253,9 +253,10 @@ __global__ __launch_bounds__(NW * 64) void gemm_gemv_bf16(GemmArgs ga) {
     }
   }
   if constexpr (KIND == EPI_ARGMAX) {
-    if (ga.e.ids_out) {
-      // the draft ids, decoded by the last workgroup to arrive: every key update of a
-      // workgroup (device-coherent atomics) has completed before it counts itself in
+    if (ga.e.ids_cnt) {
+      // the draft ids (or the greedy acceptance), by the last workgroup to arrive: every
+      // key update of a workgroup (device-coherent atomics) has completed before it counts
+      // itself in
       __shared__ unsigned arrived;
       __builtin_amdgcn_s_waitcnt(0);
       __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -264,12 +265,18 @@ __global__ __launch_bounds__(NW * 64) void gemm_gemv_bf16(GemmArgs ga) {
         arrived = __hip_atomic_fetch_add(ga.e.ids_cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __syncthreads();
       if (arrived == gridDim.x - 1) {
-        const int B = ga.e.ids_B, n = (M / B) * (B - 1);
-        for (int i = threadIdx.x; i < n; i += NW * 64) {
-          const unsigned long long k = __hip_atomic_load(ga.e.keys + (i / (B - 1)) * B + i % (B - 1) + 1,
-                                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          ga.e.ids_out[i] = unpack_argmax_idx(k);
+        const int B = ga.e.ids_B;
+        if (ga.e.ids_out) {
+          const int n = (M / B) * (B - 1);
+          for (int i = threadIdx.x; i < n; i += NW * 64) {
+            const unsigned long long k = __hip_atomic_load(ga.e.keys + (i / (B - 1)) * B + i % (B - 1) + 1,
+                                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            ga.e.ids_out[i] = unpack_argmax_idx(k);
+          }
         }
+        if (ga.e.acc_tau)   // one wave per sequence
+          for (int b = w; b < M / B; b += NW)
+            accept_wave<true>(ga.e.keys, ga.e.acc_drafts, B, b, ga.e.acc_g, ga.e.acc_tau, ga.e.acc_bonus);
         if (threadIdx.x == 0) __hip_atomic_store(ga.e.ids_cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }

@@ -76,12 +76,19 @@ struct EpiArgs {
   unsigned long long* keys;
   float* logits;
   int skipB;
-  // and, when ids_out != NULL (taken by the M <= 16 GEMV only), the draft ids of the
-  // masked rows: ids_out[b (ids_B - 1) + j - 1] = argmax of row b ids_B + j, j >= 1,
-  // written by the launch's last workgroup (arrival counter ids_cnt, zero between launches)
+  // and, when ids_cnt != NULL (taken by the M <= 16 GEMV only), work on the finished keys
+  // by the launch's last workgroup (arrival counter ids_cnt, zero between launches), for
+  // blocks of ids_B rows: the draft ids of the masked rows when ids_out != NULL
+  // (ids_out[b (ids_B - 1) + j - 1] = argmax of row b ids_B + j, j >= 1), the greedy
+  // acceptance of acc_drafts when acc_tau != NULL (acc_g, acc_tau, acc_bonus as
+  // launch_accept writes them)
   int32_t* ids_out;
   unsigned* ids_cnt;
   int ids_B;
+  const int32_t* acc_drafts;
+  int32_t* acc_g;
+  int32_t* acc_tau;
+  int32_t* acc_bonus;
   // sampling instead of argmax: key = logit / temperature + Gumbel noise of draw (counter,
   // purpose 0, b = row / B, i = row % B, v = column)
   int sample;

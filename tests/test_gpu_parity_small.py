@@ -140,6 +140,40 @@ def test_verify_accept(name):
         assert int(tau[0]) == B
 
 
+@pytest.mark.parametrize("B", [16, 8])
+def test_verify_accept_batch1_forced_prefixes(B):
+    """Batch 1 of a bf16 model (the M <= 16 LM head whose last workgroup runs the greedy
+    acceptance): blocks whose first f drafts are the target's greedy continuation, for f = 0,
+    a middle run and B - 1, verified at the same position, against the oracle's argmax, tau
+    and bonus."""
+    w = synth.workload("split_bf16")
+    S = Setup(w, target=True)
+    lens = synth.ctx_lengths(w)
+    m = w.target
+    kv, np_cache = _target_cache(S, lens, B)
+    rng = np.random.default_rng(11)
+    anchor = int(synth.anchors(w, "cpu").numpy()[0])
+    ws = S.workspace(S.target, B, kv.capacity)
+    k = len(w.taps)
+    for f in sorted({0, min(5, B - 1), B - 1}):
+        block = _forced_block(S, np_cache[0], lens[0], anchor, B, f, rng)
+        ids = torch.tensor([block], dtype=torch.int32, device=DEV)
+        feats = torch.zeros(1, B, k * m.hidden, dtype=S.st, device=DEV)
+        g = torch.zeros(1, B, dtype=torch.int32, device=DEV)
+        tau = torch.zeros(1, dtype=torch.int32, device=DEV)
+        bonus = torch.zeros(1, dtype=torch.int32, device=DEV)
+        rt.verify_accept(S.target, kv, ids[:, 0].contiguous(), ids[:, 1:].contiguous(), B, feats, g, tau,
+                         bonus, ws)
+        torch.cuda.synchronize()
+        assert kv.err.item() == 0
+        og, oz, _, _, _ = O.verify(S.np_tw, S.np_shared, m, np_cache[0], block, lens[0], w.taps,
+                                   store=S.store)
+        assert_ids(g[0].cpu().numpy(), og, oz, f"B {B} f {f} target argmax")
+        assert_accept(tau[0], bonus[0], g[0].cpu().numpy(), block[1:], og, oz, f"B {B} f {f} accept")
+        if np.all(O.top2_gap(oz) >= 1e-2):
+            assert int(tau[0]) >= f + 1, f"B {B} f {f}: tau {int(tau[0])}"
+
+
 @pytest.mark.parametrize("name", WORKLOADS)
 def test_block_of_one_is_single_token_decode(name):
     """B = 1: the drafter's one row attends to the context and itself; verify of one token
