@@ -29,7 +29,9 @@
  *    that could write or read past the mapped pages returns DFLASH_E_CAPACITY instead of
  *    launching.
  *  - The workspace `ws` is scratch for the duration of the call's kernels: calls that may
- *    overlap on the device (different streams) need separate workspaces.
+ *    overlap on the device (different streams) need separate workspaces.  Its contents on
+ *    entry do not matter: a draft or verify call clears the arrival counters its split
+ *    GEMMs keep there in its first kernel.
  *  - Errors the host cannot see (an unmapped page, an out-of-range token id or tau) are
  *    detected on the device: the offending row or sequence is skipped and a bit is OR-ed
  *    into dflash_kv.error_flags (when that pointer is non-NULL).
