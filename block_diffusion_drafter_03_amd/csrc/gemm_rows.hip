@@ -321,6 +321,10 @@ struct RowsLaunch {
       // gemm_mfma.hip, whose 64-row tiles keep two workgroups on every CU (measured on the
       // Qwen3-8B shapes at 128 and 256 rows)
       if (M > 128 || !AIsFloat<TA>::value) return launch_gemm_mfma(ga, st);
+      // over a vocabulary-wide N (the LM head at 65 - 128 rows): 4 waves of 32 rows, so each
+      // W fragment read from LDS feeds four MFMAs instead of two (batch-8 drafting 1675 ->
+      // 1596-1612 us, verify + inject + commit 2596-2612 -> 2514-2532 us on one box)
+      if (M > 64 && N >= 65536) ROWS_GO(4, 2, 8, 3, false);
       if (M > 64) ROWS_GO(8, 1, 8, 3, false);
       else ROWS_GO(4, 1, 8, 3, false);
       return hipGetLastError();

@@ -151,7 +151,15 @@ SPLIT = Workload(
     ctx=(300,), target=_SPLIT_TARGET, taps=(0, 1),
     note="test-only bf16 model: hidden 2560, FFN 8192, batch 1 (the K-split M = 16 GEMVs)")
 
-_ALL = (TINY, CFG2, CFG3, CFG4, CFG5, MID, WIDE, MANY, NARROW, VAST, SPLIT)
+# Test-only: the same model at batch 5: an LM head of 80 block rows over 120001 columns (the
+# four-wave row-resident GEMM of vocabulary-wide N, one ragged 128-row tile), contexts as
+# in the wide model (empty and one-row ones included).
+VAST5 = Workload(
+    cid=108, name="vast5_bf16", dtype="bf16", draft=_VAST_DRAFT, n_taps=2, block=16, batch=5,
+    ctx=(130, 0, 257, 1, 64), target=_VAST_TARGET, taps=(0, 1),
+    note="test-only bf16 model: hidden 256, vocab 120001, batch 5 (80 block rows)")
+
+_ALL = (TINY, CFG2, CFG3, CFG4, CFG5, MID, WIDE, MANY, NARROW, VAST, SPLIT, VAST5)
 WORKLOADS = {w.cid: w for w in _ALL}
 WORKLOADS.update({w.name: w for w in _ALL})
 

@@ -22,9 +22,9 @@ WORKLOADS = ["tiny_f32", "mid_bf16"]
 # plus a wide-vocabulary model with empty and one-row contexts, the mid model at batch 24
 # (384 block rows), a narrow model at batch 12 (192 rows, the LDS-staged GEMM) and the narrow
 # model over 120001 vocabulary rows at batch 17 (the widest weight-direct LM-head tile) and
-# a batch-1 model whose QKV and down GEMVs take the K-split form on ragged shapes, for the
-# draft / verify checks
-WITH_WIDE = WORKLOADS + ["wide_bf16", "many_bf16", "narrow_bf16", "vast_bf16", "split_bf16"]
+# at batch 5 (the four-wave row-resident LM head), and a batch-1 model whose QKV and down
+# GEMVs take the K-split form on ragged shapes, for the draft / verify checks
+WITH_WIDE = WORKLOADS + ["wide_bf16", "many_bf16", "narrow_bf16", "vast_bf16", "vast5_bf16", "split_bf16"]
 
 
 def _feats(w, lens):
