@@ -27,6 +27,11 @@ DF_DEV const bf16* wblock(const BSeg& b, int t, int ks, int KS) {
   return (const bf16*)pick8(b.ptr, s) + ((size_t)(t - s * tps) * KS + ks) * 512;
 }
 
+// one lane's 16 bytes of a weight fragment.  A launch reads every weight once: the loads
+// carry the non-temporal hint (streamed, not kept in the caches), which measured faster on
+// the M <= 16 GEMVs (LM head 205 -> 190 us, down 25.8 -> 23.8, QKV 18.7 -> 17.4).
+DF_DEV bf16x8 wload(const bf16* p) { return __builtin_nontemporal_load((const bf16x8*)p); }
+
 // the 8 A values of lane (r = lane % 16, g = lane / 16) at row block mb, step ks of
 // fragment-ordered float32 activations
 DF_DEV void afrag_load8(const float* A, int mb, int ks, int KS, int lane, float v[8]) {

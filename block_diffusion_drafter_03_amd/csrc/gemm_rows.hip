@@ -114,8 +114,14 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_rows_bf16(GemmArgs ga, SplitA
         }
       }
     }
+    // bf16 rows (the fusion GEMM over tapped features, K = 20480): the weights stream with
+    // the non-temporal hint (134 -> 123 us at 512 rows); with float rows it measured slower
+    // (the K-split QKV / O / down at 256 rows, 33 -> 37 and 39 -> 42 us)
 #pragma unroll
-    for (int j = 0; j < WPT; ++j) st.wv[j] = *(const bf16x8*)(wp[j] + (size_t)(stage * KSUB + w_u[j]) * 512);
+    for (int j = 0; j < WPT; ++j) {
+      const bf16* p = wp[j] + (size_t)(stage * KSUB + w_u[j]) * 512;
+      st.wv[j] = AIsFloat<TA>::value ? *(const bf16x8*)p : wload(p);
+    }
   };
   auto wstore = [&](const Stage& st, int buf) {
 #pragma unroll
