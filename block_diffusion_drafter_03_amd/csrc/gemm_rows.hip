@@ -317,6 +317,7 @@ struct RowsLaunch {
     sp.nt_pad = (N + 15) / 16;
     auto grid_of = [&](int bm_, int bn_) { return ((M + bm_ - 1) / bm_) * ((N + bn_ - 1) / bn_); };
 #define ROWS_K(NWV, TMV, TNV, DV, SPL) gemm_rows_bf16<TA, NWV, TMV, TNV, DV, NORM, KIND, SPL>
+// (ROWS_GO launches and does not return: its uses form one if / else chain)
 #define ROWS_GO(NWV, TMV, TNV, DV, SPL)                                                          \
   hipLaunchKernelGGL((ROWS_K(NWV, TMV, TNV, DV, SPL)),                                          \
                      dim3(rows_grid(grid_of(NWV * 16 * TMV, 16 * TNV) * (SPL ? S : 1))), dim3(NWV * 64), \
@@ -331,7 +332,7 @@ struct RowsLaunch {
       // W fragment read from LDS feeds four MFMAs instead of two (batch-8 drafting 1675 ->
       // 1596-1612 us, verify + inject + commit 2596-2612 -> 2514-2532 us on one box)
       if (M > 64 && N >= 65536) ROWS_GO(4, 2, 8, 3, false);
-      if (M > 64) ROWS_GO(8, 1, 8, 3, false);
+      else if (M > 64) ROWS_GO(8, 1, 8, 3, false);
       else ROWS_GO(4, 1, 8, 3, false);
       return hipGetLastError();
     }
