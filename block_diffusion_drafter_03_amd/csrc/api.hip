@@ -98,7 +98,7 @@ size_t step_ws(const dflash_model* m, int batch, int B, int ctx_cap, void* base,
   const int dt = d.dtype, M = batch * B, Mp = round_up(M, 16), Bp = round_up(B, 32);
   const int D = d.hidden, Hq = d.n_q_heads, Hkv = d.n_kv_heads, hd = d.head_dim;
   StepWs t;
-  t.plan = attn_plan(dt, batch, Hkv, Hq / Hkv, B, ctx_cap);
+  t.plan = attn_plan(dt, batch, Hkv, Hq / Hkv, B, ctx_cap, d.n_layers, hd);
   Carve cv(base);
   t.h = (float*)cv.take((size_t)Mp * D * 4);
   t.q = (float*)cv.take((size_t)M * Hq * hd * 4);

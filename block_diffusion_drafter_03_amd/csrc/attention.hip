@@ -70,6 +70,11 @@ DF_DEV int krow_phys(int kk) { return (kk & 35) | ((kk >> 1) & 12) | ((kk << 2) 
 // 3-deep ring of register-staged steps: up to 96 KB of K/V in flight per CU while a fourth
 // step is computed from LDS.
 #define ATTN_THREADS 512
+// KV_NT: the context K/V loads carry the non-temporal hint (a context far larger than the
+// caches: the 64K and 262K layers 64.2 -> 60.6 and 193.6 -> 185.8 us; at 4K, where the K/V
+// of every layer stays in the 256 MB last-level cache from one block to the next, plain
+// loads are faster)
+template <bool KV_NT>
 __global__ __launch_bounds__(ATTN_THREADS, 1) void attn_splitk_bf16(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) bf16 kt[2][KTILE];
   __shared__ __attribute__((aligned(16))) bf16 vt[2][VTILE];
@@ -129,8 +134,13 @@ __global__ __launch_bounds__(ATTN_THREADS, 1) void attn_splitk_bf16(AttnArgs a) 
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int idx = tid + ATTN_THREADS * j;
-      st[j] = *(const bf16x8*)(ks + (size_t)idx * 8);
-      st[2 + j] = *(const bf16x8*)(vs + (size_t)idx * 8);
+      if constexpr (KV_NT) {
+        st[j] = __builtin_nontemporal_load((const bf16x8*)(ks + (size_t)idx * 8));
+        st[2 + j] = __builtin_nontemporal_load((const bf16x8*)(vs + (size_t)idx * 8));
+      } else {
+        st[j] = *(const bf16x8*)(ks + (size_t)idx * 8);
+        st[2 + j] = *(const bf16x8*)(vs + (size_t)idx * 8);
+      }
     }
   };
   // the block's own keys (split 0 only): K rows from k_blk, V^T columns from v_blk^T
@@ -569,9 +579,13 @@ static int attn_num_cus() {
   return n;
 }
 
-AttnPlan attn_plan(int dt, int batch, int Hkv, int G, int B, int ctx_cap) {
+AttnPlan attn_plan(int dt, int batch, int Hkv, int G, int B, int ctx_cap, int n_layers, int d) {
   AttnPlan p;
   p.n_rg = (G * B + 63) / 64;
+  // stream the context past the caches once the K/V of all layers (bf16) is well beyond
+  // what the 256 MB last-level cache could keep from one call to the next
+  p.kv_stream = (double)batch * Hkv * (double)(ctx_cap > 0 ? ctx_cap : 1) * d * 2 * 2 * n_layers >
+                192.0 * (1 << 20);
   if (dt != BF16) {
     p.n_ctx_splits = 1;
     p.split_len = 0;
@@ -638,7 +652,8 @@ hipError_t launch_attention(int dt, const AttnPlan& p, const float* q, const voi
     if (p.split_len > 64 * ATTN_MAX_SPLIT_PAGES || p.n_ctx_splits > MERGE_MAX_SPLITS)
       return hipErrorInvalidValue;
     dim3 grid(p.n_ctx_splits, Hkv * p.n_rg, batch);
-    hipLaunchKernelGGL(attn_splitk_bf16, grid, dim3(ATTN_THREADS), 0, st, a);
+    if (p.kv_stream) hipLaunchKernelGGL(attn_splitk_bf16<true>, grid, dim3(ATTN_THREADS), 0, st, a);
+    else hipLaunchKernelGGL(attn_splitk_bf16<false>, grid, dim3(ATTN_THREADS), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     dim3 g2((p.n_rg * 64 + 7) / 8, Hkv, batch);

@@ -181,8 +181,11 @@ struct AttnPlan {
   int n_ctx_splits;   // context splits (grid dimension, before the block split)
   int split_len;      // keys per context split (multiple of 64)
   int n_rg;           // 64-row groups of the G*B query rows of one KV head
+  int kv_stream;      // context K/V loads carry the non-temporal hint
 };
-AttnPlan attn_plan(int dt, int batch, int Hkv, int G, int B, int ctx_cap);
+// n_layers, d: the model's layers and head size (the K/V footprint of all its layers decides
+// whether the context is streamed past the caches)
+AttnPlan attn_plan(int dt, int batch, int Hkv, int G, int B, int ctx_cap, int n_layers = 1, int d = 128);
 size_t attn_partial_floats(const AttnPlan& p, int batch, int Hkv, int d);
 
 // o[M, Hq d] = softmax(q k^T / sqrt(d)) v over [context ; block] (causal inside the block
