@@ -88,8 +88,9 @@ def main():
     ap.add_argument("--no-context-sweep", action="store_true",
                     help="skip the draft block / attention timing at 4K, 64K and 262K contexts")
     ap.add_argument("--probe-copy", type=int, default=0, metavar="MB",
-                    help="after the run, one elementwise pass reading and writing MB MiB "
-                         "(calibrates HBM byte counters of profiler runs)")
+                    help="after the run, one elementwise pass reading and writing MB MiB, then "
+                         "two reads of MB MiB with plain and non-temporal loads (calibrate the "
+                         "HBM byte counters of profiler runs)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the drafter step is data-parallel over sequences, "
@@ -326,6 +327,15 @@ def main():
         torch.neg(src, out=dst)      # reads and writes exactly probe_copy MiB each
         torch.cuda.synchronize()
         log(f"probe copy: {args.probe_copy} MiB read + {args.probe_copy} MiB written")
+        # one read of the same bytes in each load form of the library (plain, then with the
+        # non-temporal hint of its weight streams)
+        import ctypes
+        sink = torch.empty(16 << 10, dtype=torch.uint8, device=dev)
+        for nt in (False, True):
+            _lib.probe_read(ctypes.c_void_p(src.data_ptr()), src.numel() * 4, nt,
+                            ctypes.c_void_p(sink.data_ptr()), rt._stream())
+            torch.cuda.synchronize()
+        log(f"probe reads: {args.probe_copy} MiB with plain loads, then with non-temporal loads")
 
 
 def tiny_timing(dev, reps=STATS_REPS):

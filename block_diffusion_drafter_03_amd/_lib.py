@@ -22,7 +22,7 @@ EXPORTS = ("dflash_model_create", "dflash_model_destroy", "dflash_status_str",
            "dflash_verify_accept", "dflash_kv_commit", "dflash_timing_arm",
            "dflash_timing_read", "dflash_draft_block_sampled", "dflash_verify_sampled",
            "dflash_selector_workspace_bytes", "dflash_draft_block_select",
-           "dflash_draft_block_noalloc")
+           "dflash_draft_block_noalloc", "dflash_probe_read")
 NOALLOC_SCRATCH_BYTES = 64 << 20
 KERNEL_LM_HEAD, KERNEL_GEMM_QKV, KERNEL_GEMM_O, KERNEL_GEMM_GATE_UP, KERNEL_GEMM_DOWN, \
     KERNEL_ATTENTION, KERNEL_INJECT_FUSE, KERNEL_INJECT_KV = range(8)
@@ -109,6 +109,8 @@ def lib():
         L.dflash_timing_arm.restype = c_int32
         L.dflash_timing_read.argtypes = [POINTER(c_float), c_int32]
         L.dflash_timing_read.restype = c_int32
+        L.dflash_probe_read.argtypes = [c_void_p, ctypes.c_size_t, c_int32, c_void_p, c_void_p]
+        L.dflash_probe_read.restype = c_int32
         _lib = L
     return _lib
 
@@ -196,6 +198,12 @@ def timing_read(capacity: int) -> list:
     if n < 0:
         raise DFlashError(n, "dflash_timing_read")
     return [float(buf[i]) for i in range(n)]
+
+
+def probe_read(src, nbytes: int, nontemporal: bool, sink, stream):
+    """Measurement utility: one read of nbytes at device pointer src (plain or non-temporal
+    loads) into the 16 KiB device buffer sink."""
+    _check(lib().dflash_probe_read(src, nbytes, 1 if nontemporal else 0, sink, stream), "dflash_probe_read")
 
 
 def kv_commit(target_kv, draft_kv, tau, block, stream) -> int:

@@ -902,6 +902,12 @@ int dflash_timing_arm(int32_t kernel, int32_t capacity) {
   return DFLASH_OK;
 }
 
+int dflash_probe_read(const void* src, size_t bytes, int32_t nontemporal, void* sink, void* stream) {
+  if (!src || !sink || bytes % 16) return DFLASH_E_ARG;
+  HIPCHK(launch_probe_read(src, bytes / 16, nontemporal, sink, (hipStream_t)stream));
+  return DFLASH_OK;
+}
+
 int dflash_timing_read(float* ms, int32_t capacity) {
   if (!ms || capacity < 0) return DFLASH_E_ARG;
   const int n = g_timing.count < capacity ? g_timing.count : capacity;

@@ -57,6 +57,30 @@ __global__ __launch_bounds__(256) void embed_kernel(EmbedArgs a) {
   }
 }
 
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+template <bool NT>
+__global__ __launch_bounds__(256) void probe_read_kernel(const u32x4* src, size_t n16, u32x4* sink) {
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (size_t)gridDim.x * 256)
+    acc ^= NT ? __builtin_nontemporal_load(src + i) : src[i];
+  __shared__ u32x4 red[256];
+  red[threadIdx.x] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    u32x4 x = red[0];
+    for (int t = 1; t < 256; ++t) x ^= red[t];
+    sink[blockIdx.x] = x;
+  }
+}
+
+hipError_t launch_probe_read(const void* src, size_t n16, int nontemporal, void* sink, hipStream_t st) {
+  if (nontemporal)
+    hipLaunchKernelGGL(probe_read_kernel<true>, dim3(1024), dim3(256), 0, st, (const u32x4*)src, n16, (u32x4*)sink);
+  else
+    hipLaunchKernelGGL(probe_read_kernel<false>, dim3(1024), dim3(256), 0, st, (const u32x4*)src, n16, (u32x4*)sink);
+  return hipGetLastError();
+}
+
 hipError_t launch_embed(int dt, const EmbedArgs& a, hipStream_t st) {
   const int rows = a.batch * a.B;
   if (dt == BF16)

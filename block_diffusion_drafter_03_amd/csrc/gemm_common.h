@@ -29,8 +29,14 @@ DF_DEV const bf16* wblock(const BSeg& b, int t, int ks, int KS) {
 
 // one lane's 16 bytes of a weight fragment.  A launch reads every weight once: the loads
 // carry the non-temporal hint (streamed, not kept in the caches), which measured faster on
-// the M <= 16 GEMVs (LM head 205 -> 190 us, down 25.8 -> 23.8, QKV 18.7 -> 17.4).
+// the M <= 16 GEMVs (LM head 205 -> 190 us, down 25.8 -> 23.8, QKV 18.7 -> 17.4).  Not for
+// gate/up (epilogue kind SwiGLU): no faster there, and its HBM reads grew 15 % (FETCH_SIZE).
 DF_DEV bf16x8 wload(const bf16* p) { return __builtin_nontemporal_load((const bf16x8*)p); }
+template <int KIND>
+DF_DEV bf16x8 wload_k(const bf16* p) {
+  if constexpr (KIND == EPI_SWIGLU) return *(const bf16x8*)p;
+  else return wload(p);
+}
 
 // the 8 A values of lane (r = lane % 16, g = lane / 16) at row block mb, step ks of
 // fragment-ordered float32 activations

@@ -68,7 +68,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_gemv_bf16(GemmArgs ga) {
   auto load_w = [&](bf16x8 (&wn)[ASTAT ? CH : 1], int t) {
     const bf16* p = wblock(ga.B, t, ks0, KS) + lane * 8;
 #pragma unroll
-    for (int s = 0; s < CH; ++s) wn[s] = wload(p + (size_t)s * 512);
+    for (int s = 0; s < CH; ++s) wn[s] = wload_k<KIND>(p + (size_t)s * 512);
   };
   const int G = gridDim.x;
   const int t_last = blockIdx.x < n_tiles ? blockIdx.x + (n_tiles - 1 - blockIdx.x) / G * G : 0;
@@ -160,7 +160,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_gemv_bf16(GemmArgs ga) {
       for (int s = 0; s < CH; ++s) {
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[s], wa[s], acc, 0, 0, 0);
         if constexpr (TWO) acc2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo[w][s][lane], wa[s], acc2, 0, 0, 0);
-        wa[s] = wload(pn + (size_t)s * 512);
+        wa[s] = wload_k<KIND>(pn + (size_t)s * 512);
       }
       finish(t, acc, acc2);
     }
@@ -177,7 +177,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_gemv_bf16(GemmArgs ga) {
 #pragma unroll
         for (int s = 0; s < CHS; ++s) {
           const int k = ks0 + min(c0 + s, spw - 1);
-          wf[s] = wload(pt + (size_t)k * 512);
+          wf[s] = wload_k<KIND>(pt + (size_t)k * 512);
           load_a(k, av[s]);
           if constexpr (NORM) gv[s] = *(const bf16x8*)(gk + (size_t)k * 32);
         }
@@ -323,7 +323,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_gemv_splitk_bf16(GemmArgs ga) {
     for (int s = 0; s < CHS; ++s) {
       const int k = ks0 + min(c0 + s, spw - 1);
 #pragma unroll
-      for (int j = 0; j < TW; ++j) wf[s][j] = wload(wp[j] + (size_t)k * 512);
+      for (int j = 0; j < TW; ++j) wf[s][j] = wload_k<KIND>(wp[j] + (size_t)k * 512);
       afrag_load8((const float*)ga.A, 0, k, KS, lane, av[s]);
       if constexpr (NORM) gv[s] = *(const bf16x8*)(gk + (size_t)k * 32);
     }

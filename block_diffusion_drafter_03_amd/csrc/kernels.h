@@ -222,6 +222,9 @@ struct EmbedArgs {
 // token = anchor[b] for j == 0, else mask_id (mode 0) or ids[b*(B-1) + j-1] (mode 1).
 // Also writes the rows' RoPE (cos, sin) table and zeroes the argmax keys and `zero`.
 hipError_t launch_embed(int dt, const EmbedArgs& a, hipStream_t st);
+// one read of n16 16-byte words at src (plain or non-temporal loads), 1024 workgroups, one
+// 16-byte xor per workgroup to sink
+hipError_t launch_probe_read(const void* src, size_t n16, int nontemporal, void* sink, hipStream_t st);
 
 // RoPE (cos, sin) table of injection rows: position row_pos[r] (+ seq_len[row_seq[r]]).
 hipError_t launch_rope_rows(const int32_t* row_seq, const int32_t* row_pos, int pos_relative,

@@ -409,6 +409,17 @@ typedef enum {
 int dflash_timing_arm(int32_t kernel, int32_t capacity);
 int dflash_timing_read(float* ms, int32_t capacity);
 
+/*
+ * Measurement utility (benchmarks only): reads `bytes` (a multiple of 16) of device memory
+ * at `src` once, on `stream`, with plain loads (nontemporal == 0) or with the non-temporal
+ * hint that the weight streams use (nontemporal != 0), and writes one 16-byte value per
+ * workgroup (1024 workgroups) to the device memory at `sink` (at least 16 KiB) so that the
+ * loads are kept.  A read of known size in each load form calibrates the hardware read
+ * counters for kernels that use that form.  Returns DFLASH_E_ARG on NULL pointers or a size
+ * that is not a multiple of 16, DFLASH_E_HIP when the launch fails.
+ */
+int dflash_probe_read(const void* src, size_t bytes, int32_t nontemporal, void* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -232,3 +232,12 @@ def test_product_path_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError):
         _lib.lib()
+
+
+def test_probe_read_validates_before_any_launch():
+    # NULL source or sink, or a size that is not a multiple of 16: refused on the host
+    L = _lib.lib()
+    p = ctypes.c_void_p(16)    # never dereferenced: validation fails first
+    assert L.dflash_probe_read(None, 1024, 0, p, None) == -1   # DFLASH_E_ARG
+    assert L.dflash_probe_read(p, 1024, 1, None, None) == -1   # DFLASH_E_ARG
+    assert L.dflash_probe_read(p, 1000, 0, p, None) == -1   # DFLASH_E_ARG
