@@ -16,8 +16,11 @@ namespace dflash {
 //    loads go out right after the MFMAs, in flight across the reduction.
 //  * streamed (few tiles, or K > 4096): A and W are loaded together in chunks of CHS
 //    steps; no LDS for A, so several workgroups share a CU and every tile is in flight.
+//  * the K-split form further below (QKV, down): column groups over K ranges that meet in
+//    the last-arriving workgroup.
 // 8 waves of 512 threads leave each wave 256 registers, so the stationary A, a full tile
-// of W in flight and the epilogue never spill.
+// of W in flight and the epilogue never spill.  Weights load through wload_k: streamed
+// past the caches (non-temporal) except for gate/up.
 #define GEMV_MAX_TILES 8   // tiles per workgroup whose epilogue is deferred (non-argmax kinds)
 
 template <typename TA, int NW, bool NORM, bool ASTAT, int KIND>
