@@ -279,14 +279,24 @@ __global__ __launch_bounds__(256) void gemm_rows_reduce(GemmArgs ga, SplitArgs s
   if (tile >= MB * NT) return;
   const int mb = tile / NT, nb = tile % NT;
   const int S = sp.splits, MBp = sp.mb_pad, NTp = sp.nt_pad;
+  // every split's partial is loaded at once (index clamped to a valid split, the extra
+  // ones not added), so the sum waits for one memory round trip, not S of them; the sum
+  // runs in split order
+  f32x4 x[ROWS_MAX_SPLITS];
+#pragma unroll
+  for (int s = 0; s < ROWS_MAX_SPLITS; ++s)
+    x[s] = *(const f32x4*)(sp.part + (((size_t)min(s, S - 1) * MBp + mb) * NTp + nb) * 256 + lane * 4);
   f32x4 a = {0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < S; ++s) a += *(const f32x4*)(sp.part + (((size_t)s * MBp + mb) * NTp + nb) * 256 + lane * 4);
+#pragma unroll
+  for (int s = 0; s < ROWS_MAX_SPLITS; ++s)
+    if (s < S) a += x[s];
   float v[4] = {a[0], a[1], a[2], a[3]};
   if constexpr (NORM) {
     float sum[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < S; ++s)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) sum[e] += sp.ss[(size_t)s * MBp * 16 + mb * 16 + 4 * g + e];
+    for (int s = 0; s < ROWS_MAX_SPLITS; ++s)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sum[e] += s < S ? sp.ss[(size_t)min(s, S - 1) * MBp * 16 + mb * 16 + 4 * g + e] : 0.f;
 #pragma unroll
     for (int e = 0; e < 4; ++e) v[e] *= 1.0f / sqrtf(sum[e] / (float)ga.K + ga.eps);
   }

@@ -151,6 +151,16 @@ def test_qwen3_8b_batch1_ctx4k():
     conv.close()
 
 
+def _no_copy_matches(S, kv, anchor, B, batch, ws, ids, what):
+    """Drafting without the logits and hidden-state copies (a decoding loop's call) gives
+    the same ids, bit for bit."""
+    ids2 = torch.zeros_like(ids)
+    rt.draft_block(S.draft, kv, anchor, B, ids2, ws)
+    torch.cuda.synchronize()
+    assert kv.err.item() == 0
+    assert torch.equal(ids2, ids), f"{what}: ids depend on the logits copy"
+
+
 def test_qwen3_8b_batch16_paged_ragged():
     w = synth.workload("qwen3_8b_b16_paged")
     S = Setup(w)
@@ -177,6 +187,7 @@ def test_qwen3_8b_batch16_paged_ragged():
         checked += _check_draft(S, b, ctx_np[b], n, anchor[b], ids, logits, hid, f"cfg b16 seq {b}")
     assert checked >= 10 * batch
     _repeat_is_bitwise(S, kv, anchor, B, batch, ws, (ids, logits, hid), "cfg b16")
+    _no_copy_matches(S, kv, anchor, B, batch, ws, ids, "cfg b16")
     # injection of every sequence's 16 block rows at its own (ragged) position, M = 256
     feats = synth.features(w, batch * B, DEV, tag="cycle.feats")
     rs = torch.arange(batch, dtype=torch.int32, device=DEV).repeat_interleave(B)
@@ -332,6 +343,15 @@ def test_qwen3_8b_cycle_batch8_target8():
             while a2 < B - 1 and int(drafts[b, a2]) == int(g_np[b, a2]):
                 a2 += 1
             assert (int(tau_np[b]), int(bonus_np[b])) == (a2 + 1, int(g_np[b, a2]))
+        if c == 0:
+            # the same verification without the logits and hidden-state copies (it rewrites
+            # the same block rows): the same argmax, tau and bonus, bit for bit
+            g2, tau2, bonus2 = torch.zeros_like(g), torch.zeros_like(tau), torch.zeros_like(bonus)
+            rt.verify_accept(S.target, tkv, a_dev, d_dev, B, torch.zeros_like(feats), g2, tau2, bonus2, ws_t)
+            torch.cuda.synchronize()
+            assert tkv.err.item() == 0
+            for x, y, what in ((g2, g, "argmax"), (tau2, tau, "tau"), (bonus2, bonus, "bonus")):
+                assert torch.equal(x, y), f"cycle 0: {what} depends on the logits copy"
         oracle_commit = {}
         for b in sorted(active):
             block = [int(anchor[b])] + [int(x) for x in drafts[b]]

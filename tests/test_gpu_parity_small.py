@@ -47,8 +47,12 @@ def test_inject_and_draft_block(name):
     logits = torch.zeros(w.batch, B - 1, m.vocab, device=DEV)
     hid = torch.zeros(m.n_layers + 1, w.batch, B, m.hidden, device=DEV)
     rt.draft_block(S.draft, kv, anchor, B, ids, ws, logits, hid)
+    # without the logits and hidden-state copies (a decoding loop's call): the same ids
+    ids2 = torch.zeros_like(ids)
+    rt.draft_block(S.draft, kv, anchor, B, ids2, ws)
     torch.cuda.synchronize()
     assert kv.err.item() == 0
+    assert torch.equal(ids2, ids), f"{name}: ids depend on the logits copy"
     a_np = anchor.cpu().numpy()
     for b, n in enumerate(lens):
         ctx = O.inject(synth.to_numpy(feats[b]), np.arange(n), S.np_dw, m, store=S.store)
@@ -114,8 +118,17 @@ def test_verify_accept(name):
     ws = S.workspace(S.target, B, kv.capacity)
     rt.verify_accept(S.target, kv, block_ids[:, 0].contiguous(), block_ids[:, 1:].contiguous(), B,
                      feats, g, tau, bonus, ws, logits, hid)
+    # the same verification without the logits and hidden-state copies (a decoding loop's
+    # call): it rewrites the same block rows and must give the same decisions, bit for bit
+    g2, tau2, bonus2 = torch.zeros_like(g), torch.zeros_like(tau), torch.zeros_like(bonus)
+    feats2 = torch.zeros_like(feats)
+    rt.verify_accept(S.target, kv, block_ids[:, 0].contiguous(), block_ids[:, 1:].contiguous(), B,
+                     feats2, g2, tau2, bonus2, ws)
     torch.cuda.synchronize()
     assert kv.err.item() == 0
+    assert torch.equal(feats2, feats)
+    for x, y, what in ((g2, g, "argmax"), (tau2, tau, "tau"), (bonus2, bonus, "bonus")):
+        assert torch.equal(x, y), f"{name}: {what} depends on the logits copy"
     for b, n in enumerate(lens):
         og, oz, of, onew, ohid = O.verify(S.np_tw, S.np_shared, m, np_cache[b], blocks[b], n, w.taps,
                                           store=S.store)
@@ -126,6 +139,7 @@ def test_verify_accept(name):
         assert_ids(g[b].cpu().numpy(), og, oz, f"{name} target argmax seq {b}")
         assert_accept(tau[b], bonus[b], g[b].cpu().numpy(), blocks[b][1:], og, oz, f"{name} accept seq {b}")
         assert 1 <= int(tau[b]) <= B
+
         # the block's K/V were written at n .. n+B-1
         for l in range(m.n_layers):
             K, V = read_cache(kv, l, b, n + B)
