@@ -47,6 +47,16 @@ def test_convolution_fused_into_its_correction_gemv_matches_oracle():
     _check_against_oracle(w, "mid_bf16 batch 1")
 
 
+def test_convolution_fused_into_a_wider_correction_gemv_matches_oracle():
+    """One sequence of a model with hidden 2560 (M = 16): 20 correction tiles of 128
+    channels each, K = 2560 over 16 waves (5 steps a wave), every convolution the epilogue
+    of its correction GEMV; the full-size 4K drafter with convolutions is checked in
+    test_gpu_parity_full.py."""
+    w = synth.workload("split_bf16")
+    assert w.batch * w.block <= 16
+    _check_against_oracle(w, "split_bf16 batch 1")
+
+
 def _check_against_oracle(w, name):
     S = Setup(w, dconv=synth.dconv_weights(w, DEV))
     B, m, tol = w.block, w.draft, TOL[w.dtype]
