@@ -1,7 +1,10 @@
 """The block size B as a runtime schedule: the kernels take B per call, so a drafter and
 target built around B = 16 run blocks of 8 and 10 (the smaller-B inference and the B = 10
 variant the DFlash notes page reports), and a decoding loop may change B from one cycle to
-the next.  Parity with the oracle at each B, and losslessness of a mixed schedule."""
+the next.  Parity with the oracle at each B - also at the largest block the calls take (64:
+a 64-key block step, a full 64-lane acceptance wave, 192 block rows), a ragged one (33) and
+the smallest that drafts (2, whose 6 rows take the M <= 16 GEMVs) - and losslessness of a
+mixed schedule."""
 import numpy as np
 import pytest
 import torch
@@ -15,7 +18,7 @@ from harness import (DEV, TOL, Setup, assert_accept, assert_ids, assert_rows_clo
 pytestmark = pytest.mark.gpu
 
 NAME = "mid_bf16"
-SIZES = (16, 8, 10)
+SIZES = (16, 8, 10, 64, 33, 2)
 
 
 def test_draft_and_verify_at_each_block_size():
