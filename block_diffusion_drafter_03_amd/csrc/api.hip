@@ -1,12 +1,13 @@
 // libdflash C ABI: argument validation, workspace layout and launch sequencing.
 // The operations are specified in include/dflash.h.
 //
-// One decoder layer is six launches (the norms, RoPE, SwiGLU and residual adds are fused
-// into them):
 // Activations stay float32 between launches (the bf16 MFMAs take them as compensated
 // hi/lo pairs); K/V and tapped features are written in the model dtype.  For bfloat16
 // models the GEMM inputs (h, attention output, SwiGLU output, fused injection rows) live in
 // the MFMA A-fragment order, their row count padded to a multiple of 16.
+//
+// One decoder layer of up to 16 rows is six launches (the norms, RoPE, SwiGLU and residual
+// adds are fused into them):
 //   QKV GEMM   A = h, RMSNorm(g_in) applied on the A side; epilogue: RoPE,
 //              q / k_blk / v_blk^T (and, for verification, the block K/V into the cache)
 //   attention  split-K over [context ; block], then the log-sum-exp merge of the splits
@@ -14,6 +15,8 @@
 //   GATE/UP    A = h, RMSNorm(g_post) on the A side; epilogue: SiLU(gate) * up
 //   DOWN GEMM  epilogue: h += act W_d^T (+ tapped-feature / debug copies)
 // and the LM head is one GEMM with RMSNorm(g_f) on the A side and an argmax epilogue.
+// Beyond 16 rows a GEMM with an A-side norm first splits its rows into operand planes
+// (pair_split), and the K-split GEMMs add a reduce launch.
 #include <string.h>
 
 #include <algorithm>
