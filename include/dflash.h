@@ -43,9 +43,9 @@
  *        ((n / 16 * (K / 32) + k / 32) * 64 + (k % 32) / 8 * 16 + n % 16) * 8 + k % 8,
  *    i.e. one contiguous 1 KB block per 16-row x 32-column tile, tiles row-major, which
  *    is the operand order of a 16x16x32 bf16 matrix instruction (lane l = 16 g + r holds
- *    row r, columns 8 g .. 8 g + 7).  The embedding stays row-major [vocab, hidden].  Storage dtype (weights, caches,
- *    tapped features) is the model's dtype: float32 or bfloat16; logits and debug hidden
- *    states are always float32; ids are int32.  Between kernels the activations of a
+ *    row r, columns 8 g .. 8 g + 7).  The embedding stays row-major [vocab, hidden].
+ *    Storage dtype (weights, caches, tapped features) is the model's dtype: float32 or
+ *    bfloat16; logits and debug hidden states are always float32; ids are int32.  Between kernels the activations of a
  *    step live in the workspace in float32; a bfloat16 model's matrix units take them as
  *    a compensated pair of bfloat16 values (about 16 significant bits), so the result
  *    tracks a float32 evaluation over bfloat16 weights and caches.
