@@ -238,10 +238,10 @@ struct Timed {
   hipStream_t st;
   int slot;
   Timed(int kernel, hipStream_t s) : st(s), slot(timing_slot(kernel)) {
-    if (slot >= 0) hipEventRecord(g_timing.ev[2 * slot], st);
+    if (slot >= 0) (void)hipEventRecord(g_timing.ev[2 * slot], st);
   }
   ~Timed() {
-    if (slot >= 0) hipEventRecord(g_timing.ev[2 * slot + 1], st);
+    if (slot >= 0) (void)hipEventRecord(g_timing.ev[2 * slot + 1], st);
   }
 };
 
@@ -895,7 +895,7 @@ int dflash_kv_commit(dflash_kv* tkv, dflash_kv* dkv, const int32_t* tau, int32_t
 
 int dflash_timing_arm(int32_t kernel, int32_t capacity) {
   if (kernel < 0 || kernel >= DFLASH_KERNEL_COUNT || capacity < 1) return DFLASH_E_ARG;
-  for (hipEvent_t e : g_timing.ev) hipEventDestroy(e);
+  for (hipEvent_t e : g_timing.ev) (void)hipEventDestroy(e);
   g_timing.ev.assign(2 * (size_t)capacity, nullptr);
   for (auto& e : g_timing.ev)
     if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return DFLASH_E_HIP;

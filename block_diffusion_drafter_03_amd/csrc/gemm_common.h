@@ -145,7 +145,7 @@ static inline int num_cus() {
   static int n = 0;
   if (!n) {
     int dev = 0;
-    hipGetDevice(&dev);
+    if (hipGetDevice(&dev) != hipSuccess) dev = 0;
     hipDeviceProp_t p;
     n = (hipGetDeviceProperties(&p, dev) == hipSuccess && p.multiProcessorCount > 0) ? p.multiProcessorCount : 256;
   }

@@ -112,7 +112,6 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_mfma_bf16(GemmArgs ga) {
   auto lstore = [&](Stage& st, int buf, int stage) {
 #pragma unroll
     for (int u = 0; u < KSUB; ++u) {
-      const int ks = stage * KSUB + u;
 #pragma unroll
       for (int j = 0; j < AS; ++j) {
         if constexpr (AIsPair<TA>::value) {
@@ -344,7 +343,6 @@ void gemm_wdirect_bf16(GemmArgs ga) {
     const auto& rg = sa.rg;
 #pragma unroll
     for (int u = 0; u < KSUB; ++u) {
-      const int ks = stage * KSUB + u;
 #pragma unroll
       for (int j = 0; j < AS; ++j) {
         if constexpr (AIsPair<TA>::value) {

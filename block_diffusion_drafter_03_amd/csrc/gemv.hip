@@ -74,7 +74,8 @@ __global__ __launch_bounds__(NW * 64) void gemm_gemv_bf16(GemmArgs ga) {
     for (int s = 0; s < CH; ++s) wn[s] = wload_k<KIND>(p + (size_t)s * 512);
   };
   const int G = gridDim.x;
-  const int t_last = blockIdx.x < n_tiles ? blockIdx.x + (n_tiles - 1 - blockIdx.x) / G * G : 0;
+  const int bx = blockIdx.x;
+  const int t_last = bx < n_tiles ? bx + (n_tiles - 1 - bx) / G * G : 0;
   if constexpr (ASTAT) {
     // The norm gains (K = 8 per thread) and every A step of this wave are loaded at once;
     // the first W tile goes out only when this wave's A has arrived.  W issued earlier

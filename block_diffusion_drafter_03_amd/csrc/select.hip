@@ -185,7 +185,7 @@ __global__ __launch_bounds__(256) void topk_merge_kernel(TopkMergeArgs a) {
   __syncthreads();
   if (threadIdx.x < 64) prune_finish<TOPK_MAX>(key, a.k, cs, T, ncand, top);
   __syncthreads();
-  if (blockIdx.y == 0 && threadIdx.x < a.k) {
+  if (blockIdx.y == 0 && (int)threadIdx.x < a.k) {
     const unsigned long long kk = top[threadIdx.x];
     const int id = kk ? unpack_argmax_idx(kk) : 0;   // fewer than k ids: id 0 (never when V >= k)
     a.cand[(size_t)row * TOPK_MAX + threadIdx.x] = id;
