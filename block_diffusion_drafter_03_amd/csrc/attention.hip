@@ -2,7 +2,7 @@
 // inside the block) and for the target's verification pass (causal inside the block).
 //
 // bf16 path (head_dim 128): one workgroup of 8 waves per CU and per (sequence, KV head,
-// 64-row query group, key split); split 0 also takes the block's own B keys, first.  The
+// 64-row query group, key split); the last split also takes the block's own B keys.  The
 // G*B query rows that share a KV head are split into 4 tiles of 16 rows (held in registers
 // as MFMA operands) and each tile is taken by two waves, one per 32-key half of every step,
 // so every context K/V byte is read from HBM once per workgroup.  A step is one 64-token
@@ -88,6 +88,17 @@ __global__ __launch_bounds__(ATTN_THREADS, 1) void attn_splitk_bf16(AttnArgs a) 
   const int b = blockIdx.z;
   const int R = a.G * a.B;
 
+  // the page-table entries of the planned layout (split s from s * split_len on) are read
+  // together with seq_len: when this sequence's context fills planned splits (a context
+  // within about a step per split of the capacity, as for a cache sized to its sequence)
+  // they are the split's own and the start-up waits for one round trip less; otherwise
+  // they are read again below, once seq_len is known
+  constexpr int PPT = ATTN_MAX_SPLIT_PAGES / ATTN_THREADS;
+  int pg[PPT];
+#pragma unroll
+  for (int j = 0; j < PPT; ++j)
+    pg[j] = a.block_table[(size_t)b * a.max_pages +
+                          min(((s * a.split_len) >> 6) + tid + j * ATTN_THREADS, a.max_pages - 1)];
   int n_ctx = a.seq_len[b];
   n_ctx = max(0, min(n_ctx, a.max_pages * 64));
   // keys per split: this sequence's context spread evenly over the splits in whole pages
@@ -97,9 +108,14 @@ __global__ __launch_bounds__(ATTN_THREADS, 1) void attn_splitk_bf16(AttnArgs a) 
   const int kbeg = s * slen;                         // multiple of 64
   const int kend = min(kbeg + slen, n_ctx);
   const int n_ctx_steps = kend > kbeg ? (kend - kbeg + 63) / 64 : 0;
-  // split 0 also takes the block's own keys
+  // one split also takes the block's own keys: the last one when it holds fewer context
+  // steps than the first (the splits before it are full), so that the longest workgroup is
+  // one of the context's and not one with a step more; the first one when all are equal
+  // (it starts first)
+  const int last_steps = max(0, (n_ctx - (a.n_splits - 1) * slen + 63) / 64);
+  const bool own = s == (last_steps < min(slen, n_ctx + 63) / 64 ? a.n_splits - 1 : 0);
 
-  // Start-up takes two memory round trips: the query rows, the block's own keys (split 0)
+  // Start-up takes two memory round trips: the query rows, the block's own keys (own)
   // and the split's page-table entries are fetched together, then the first context steps
   // (their addresses need the page table), while the queries are converted.
 
@@ -122,28 +138,33 @@ __global__ __launch_bounds__(ATTN_THREADS, 1) void attn_splitk_bf16(AttnArgs a) 
   __shared__ int pages_s[ATTN_MAX_SPLIT_PAGES];
 
   // ---- global -> register staging of one step: 4 x 16 B per thread (K then V^T) ----
-  // Every context step issues exactly these 4 loads, unconditionally and to valid
-  // addresses, so the compiler can count them and keep several steps in flight; masking
-  // happens when a step is copied to LDS.  An unmapped page is flagged and read as page 0
-  // (the outputs of that sequence are then invalid, which the error flag reports).
+  // Every ring slot issues exactly these 4 loads, unconditionally and to valid addresses,
+  // so the compiler can count them and keep several steps in flight; masking happens when
+  // a step is copied to LDS.  A slot past the split's last step (the ring's tail, or a
+  // split of fewer steps than the ring is deep) is never computed: its loads all point at
+  // the first 16 bytes of the last page, one cache line per load instead of 1 KB of K / V
+  // fetched again.  An unmapped page is flagged and read as page 0 (the outputs of that
+  // sequence are then invalid, which the error flag reports).
   bf16x8 st0[4], st1[4], st2[4];
   auto load_ctx = [&](int i, bf16x8 (&st)[4]) {
-    const size_t pb = (size_t)pages_s[i] * a.Hkv + kvh;
+    const bool tail = i >= n_ctx_steps;
+    const size_t pb = (size_t)pages_s[tail ? n_ctx_steps - 1 : i] * a.Hkv + kvh;
+    const size_t per = tail ? 0 : 8;   // elements per thread index
     const bf16* ks = a.kpool + pb * 64 * AD;
     const bf16* vs = a.vpool + pb * AD * 64;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int idx = tid + ATTN_THREADS * j;
       if constexpr (KV_NT) {
-        st[j] = __builtin_nontemporal_load((const bf16x8*)(ks + (size_t)idx * 8));
-        st[2 + j] = __builtin_nontemporal_load((const bf16x8*)(vs + (size_t)idx * 8));
+        st[j] = __builtin_nontemporal_load((const bf16x8*)(ks + (size_t)idx * per));
+        st[2 + j] = __builtin_nontemporal_load((const bf16x8*)(vs + (size_t)idx * per));
       } else {
-        st[j] = *(const bf16x8*)(ks + (size_t)idx * 8);
-        st[2 + j] = *(const bf16x8*)(vs + (size_t)idx * 8);
+        st[j] = *(const bf16x8*)(ks + (size_t)idx * per);
+        st[2 + j] = *(const bf16x8*)(vs + (size_t)idx * per);
       }
     }
   };
-  // the block's own keys (split 0 only): K rows from k_blk, V^T columns from v_blk^T
+  // the block's own keys (last split only): K rows from k_blk, V^T columns from v_blk^T
   // (B <= 64), high or low parts; rows and columns past B are read from valid places and
   // masked at the copy
   auto load_blk = [&](bf16x8 (&st)[4], const bf16* kb, const bf16* vb) {
@@ -285,21 +306,21 @@ __global__ __launch_bounds__(ATTN_THREADS, 1) void attn_splitk_bf16(AttnArgs a) 
       }
     }
   };
-  // the block's own keys first (split 0), high and low parts
+  // the block's own keys first (last split), high and low parts
   bf16x8 stb[4], stl[4];
   const int last = n_ctx_steps - 1;
-  if (s == 0) {
+  if (own) {
     load_blk(stb, a.kblk, a.vblkT);
     load_blk(stl, a.kblk_lo, a.vblkT_lo);
   }
   // (every thread reads and writes its slots unconditionally - past the split's last page
   // the index is clamped to a valid entry - so every thread waits here for its loads and
   // the query conversion below needs no wait on the context loads issued after it)
-  constexpr int PPT = ATTN_MAX_SPLIT_PAGES / ATTN_THREADS;
-  int pg[PPT];
+  if (slen != a.split_len) {
 #pragma unroll
-  for (int j = 0; j < PPT; ++j)
-    pg[j] = a.block_table[(size_t)b * a.max_pages + (kbeg >> 6) + min(tid + j * ATTN_THREADS, max(n_ctx_steps - 1, 0))];
+    for (int j = 0; j < PPT; ++j)
+      pg[j] = a.block_table[(size_t)b * a.max_pages + (kbeg >> 6) + min(tid + j * ATTN_THREADS, max(n_ctx_steps - 1, 0))];
+  }
 #pragma unroll
   for (int j = 0; j < PPT; ++j) {
     const int i = tid + j * ATTN_THREADS;
@@ -313,8 +334,8 @@ __global__ __launch_bounds__(ATTN_THREADS, 1) void attn_splitk_bf16(AttnArgs a) 
   __syncthreads();
   if (n_ctx_steps > 0) {
     load_ctx(0, st0);
-    load_ctx(min(1, last), st1);
-    load_ctx(min(2, last), st2);
+    load_ctx(1, st1);
+    load_ctx(2, st2);
   }
 #pragma unroll
   for (int cs = 0; cs < 4; ++cs) {
@@ -322,7 +343,7 @@ __global__ __launch_bounds__(ATTN_THREADS, 1) void attn_splitk_bf16(AttnArgs a) 
     for (int e = 0; e < 8; ++e) qv[cs][e] = rho < R ? qv[cs][e] * a.scale_log2 : 0.f;
     split8(qv[cs], qh[cs], ql[cs]);
   }
-  if (s == 0) {
+  if (own) {
     store_step(0, a.B, stb);
     store_step(1, a.B, stl);
     __syncthreads();
@@ -331,13 +352,14 @@ __global__ __launch_bounds__(ATTN_THREADS, 1) void attn_splitk_bf16(AttnArgs a) 
   }
   // ring over the context steps: while step i is computed from LDS buffer i % 2, steps
   // i+1 .. i+3 are in flight in the staging registers; step i+1 then moves to the other
-  // LDS buffer.  Loads and copies run for every slot (indices clamped to the last step) so
-  // each ring slot issues the same instructions; only the compute is skipped past the end.
+  // LDS buffer.  Loads and copies run for every slot (past the last step, loads of one
+  // cache line) so each ring slot issues the same instructions; only the compute is
+  // skipped past the end.
   if (n_ctx_steps > 0) {
     store_step(0, step_lim(0), st0);
     __syncthreads();
     auto body = [&](int i, bf16x8 (&ld)[4], bf16x8 (&nx)[4]) {
-      load_ctx(min(i + 3, last), ld);
+      load_ctx(i + 3, ld);
       if (i < n_ctx_steps) compute(i & 1, false, step_lim(i));
       store_step((i + 1) & 1, step_lim(min(i + 1, last)), nx);
       __syncthreads();
